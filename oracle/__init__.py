@@ -1,0 +1,241 @@
+"""Oracle for the decode step — TEST INFRASTRUCTURE ONLY.
+
+Only tests, ``__graft_entry__.smoke()`` and ``bench.py``'s CPU-baseline leg may import
+this package.  It wraps ``liboracle.so`` (built from oracle.c, plain fp64 C with
+OpenMP over independent rows and heads) with ctypes; the arithmetic is all in
+oracle.c.  It shares no code with the HIP path.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_LIB_PATH = os.path.join(_HERE, "liboracle.so")
+_lib = None
+
+_dp = ctypes.POINTER(ctypes.c_double)
+_u16p = ctypes.c_void_p
+
+
+class OrcConfig(ctypes.Structure):
+    _fields_ = [("n_layers", ctypes.c_int), ("d", ctypes.c_int), ("hq", ctypes.c_int), ("hk", ctypes.c_int),
+                ("dh", ctypes.c_int), ("f", ctypes.c_int), ("v", ctypes.c_int), ("eps", ctypes.c_double),
+                ("theta", ctypes.c_double), ("tied", ctypes.c_int), ("qkv_bias", ctypes.c_int)]
+
+
+def build_lib(force: bool = False) -> str:
+    src = os.path.join(_HERE, "oracle.c")
+    hdr = os.path.join(_HERE, "oracle.h")
+    newest = max(os.path.getmtime(src), os.path.getmtime(hdr))
+    if force or not os.path.exists(_LIB_PATH) or os.path.getmtime(_LIB_PATH) < newest:
+        tmp = _LIB_PATH + ".tmp%d" % os.getpid()
+        subprocess.check_call(["gcc", "-O2", "-ffp-contract=off", "-fopenmp", "-fPIC", "-shared", "-Wall", src,
+                               "-o", tmp, "-lm"])
+        os.replace(tmp, _LIB_PATH)
+    return _LIB_PATH
+
+
+def lib():
+    global _lib
+    if _lib is None:
+        if not os.path.exists(_LIB_PATH):
+            build_lib()
+        L = ctypes.CDLL(_LIB_PATH)
+        L.orc_create.restype = ctypes.c_void_p
+        L.orc_create.argtypes = [ctypes.POINTER(OrcConfig), ctypes.c_void_p, ctypes.c_int, ctypes.c_int]
+        L.orc_destroy.restype = None
+        L.orc_destroy.argtypes = [ctypes.c_void_p]
+        L.orc_set_kv.restype = ctypes.c_int
+        L.orc_set_kv.argtypes = [ctypes.c_void_p] + [ctypes.c_int] * 4 + [_u16p, _u16p]
+        L.orc_get_kv.restype = ctypes.c_int
+        L.orc_get_kv.argtypes = [ctypes.c_void_p] + [ctypes.c_int] * 4 + [_u16p, _u16p]
+        L.orc_step.restype = ctypes.c_int
+        L.orc_step.argtypes = [ctypes.c_void_p, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_double, _dp]
+        L.orc_forward_nocache.restype = ctypes.c_int
+        L.orc_forward_nocache.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int, ctypes.c_double, _dp]
+        L.orc_rmsnorm.restype = None
+        L.orc_rmsnorm.argtypes = [_dp, _u16p, ctypes.c_int, ctypes.c_double, _dp]
+        L.orc_gemv.restype = None
+        L.orc_gemv.argtypes = [_u16p, ctypes.c_int, ctypes.c_int, _dp, _u16p, _dp]
+        L.orc_rope.restype = None
+        L.orc_rope.argtypes = [_dp, ctypes.c_int, ctypes.c_double, ctypes.c_double]
+        L.orc_softmax.restype = None
+        L.orc_softmax.argtypes = [_dp, ctypes.c_int]
+        L.orc_attention.restype = None
+        L.orc_attention.argtypes = [_dp, _u16p, _u16p] + [ctypes.c_int] * 4 + [_dp]
+        L.orc_silu.restype = ctypes.c_double
+        L.orc_silu.argtypes = [ctypes.c_double]
+        L.orc_swiglu.restype = None
+        L.orc_swiglu.argtypes = [_dp, _dp, ctypes.c_int, _dp]
+        L.orc_argmax.restype = ctypes.c_int
+        L.orc_argmax.argtypes = [_dp, ctypes.c_int]
+        L.orc_bf16.restype = ctypes.c_uint16
+        L.orc_bf16.argtypes = [ctypes.c_double]
+        L.orc_from_bf16.restype = ctypes.c_double
+        L.orc_from_bf16.argtypes = [ctypes.c_uint16]
+        L.orc_threads.restype = ctypes.c_int
+        L.orc_threads.argtypes = []
+        L.orc_set_threads.restype = None
+        L.orc_set_threads.argtypes = [ctypes.c_int]
+        _lib = L
+    return _lib
+
+
+def _d(a):
+    return a.ctypes.data_as(_dp)
+
+
+def _f64(a):
+    return np.ascontiguousarray(a, dtype=np.float64)
+
+
+def _u16(a):
+    return np.ascontiguousarray(a, dtype=np.uint16)
+
+
+# ----------------------------------------------------------------- pieces
+def rmsnorm(x, g, eps):
+    x = _f64(x); g = _u16(g); out = np.empty_like(x)
+    lib().orc_rmsnorm(_d(x), g.ctypes.data, x.size, eps, _d(out))
+    return out
+
+
+def gemv(w, x, bias=None):
+    w = _u16(w); x = _f64(x); n, k = w.shape
+    assert x.size == k
+    y = np.empty(n, dtype=np.float64)
+    b = _u16(bias) if bias is not None else None
+    lib().orc_gemv(w.ctypes.data, n, k, _d(x), b.ctypes.data if b is not None else None, _d(y))
+    return y
+
+
+def rope(u, pos, theta):
+    u = _f64(u).copy()
+    lib().orc_rope(_d(u), u.size, float(pos), float(theta))
+    return u
+
+
+def softmax(s):
+    s = _f64(s).copy()
+    lib().orc_softmax(_d(s), s.size)
+    return s
+
+
+def attention(q, kc, vc, hq, hk, dh):
+    """q [hq*dh] float; kc, vc [npos, hk, dh] bf16 bits -> out [hq*dh]."""
+    q = _f64(q); kc = _u16(kc); vc = _u16(vc)
+    npos = kc.shape[0]
+    out = np.empty(hq * dh, dtype=np.float64)
+    lib().orc_attention(_d(q), kc.ctypes.data, vc.ctypes.data, npos, hq, hk, dh, _d(out))
+    return out
+
+
+def silu(z):
+    return lib().orc_silu(float(z))
+
+
+def swiglu(a, b):
+    a = _f64(a); b = _f64(b); h = np.empty_like(a)
+    lib().orc_swiglu(_d(a), _d(b), a.size, _d(h))
+    return h
+
+
+def argmax(v):
+    v = _f64(v)
+    return lib().orc_argmax(_d(v), v.size)
+
+
+def bf16(x):
+    return lib().orc_bf16(float(x))
+
+
+def from_bf16(b):
+    return lib().orc_from_bf16(int(b))
+
+
+def bf16_to_f64(a):
+    """bf16 bit patterns -> float64 (exact)."""
+    return (np.asarray(a, dtype=np.uint16).astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+
+
+def threads():
+    return lib().orc_threads()
+
+
+def set_threads(n):
+    lib().orc_set_threads(int(n))
+
+
+# ----------------------------------------------------------------- model
+class OracleModel:
+    """The decode step of one model over n_seqs sequences with max_pos cache positions each."""
+
+    def __init__(self, shape, weights: dict, n_seqs: int = 1, max_pos: int = 64):
+        self.shape = shape
+        m = shape
+        self.cfg = OrcConfig(m.n_layers, m.d_model, m.n_q_heads, m.n_kv_heads, m.head_dim, m.d_ffn, m.vocab,
+                             float(m.rms_eps), float(m.rope_theta), int(bool(m.tied_embeddings)),
+                             int(bool(m.qkv_bias)))
+        names = ["embed", "final_norm", None if m.tied_embeddings else "lm_head"]
+        for l in range(m.n_layers):
+            p = "layers.%d." % l
+            for t in ["attn_norm", "wq", "wk", "wv", "bq", "bk", "bv", "wo", "ffn_norm", "wg", "wu", "wd"]:
+                names.append(p + t if (m.qkv_bias or t not in ("bq", "bk", "bv")) else None)
+        self._keep = []
+        ptrs = (ctypes.c_void_p * len(names))()
+        for i, nme in enumerate(names):
+            if nme is None:
+                ptrs[i] = None
+            else:
+                a = _u16(weights[nme])
+                self._keep.append(a)
+                ptrs[i] = a.ctypes.data
+        self._ptrs = ptrs
+        self.n_seqs, self.max_pos = n_seqs, max_pos
+        self._h = lib().orc_create(ctypes.byref(self.cfg), ctypes.cast(ptrs, ctypes.c_void_p), n_seqs, max_pos)
+        if not self._h:
+            raise ValueError("orc_create rejected the model or could not allocate its cache")
+
+    def close(self):
+        if self._h:
+            lib().orc_destroy(self._h)
+            self._h = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+    def step(self, seq, token, pos, rope_pos=None):
+        logits = np.empty(self.shape.vocab, dtype=np.float64)
+        tok = lib().orc_step(self._h, seq, int(token), pos, float(pos if rope_pos is None else rope_pos), _d(logits))
+        if tok < 0:
+            raise ValueError("orc_step rejected its arguments")
+        return tok, logits
+
+    def set_kv(self, layer, seq, pos0, k, v):
+        k = _u16(k); v = _u16(v)
+        npos = k.shape[0]
+        if lib().orc_set_kv(self._h, layer, seq, pos0, npos, k.ctypes.data, v.ctypes.data):
+            raise ValueError("orc_set_kv rejected its arguments")
+
+    def get_kv(self, layer, seq, pos0, npos):
+        m = self.shape
+        k = np.empty((npos, m.n_kv_heads, m.head_dim), dtype=np.uint16)
+        v = np.empty_like(k)
+        if lib().orc_get_kv(self._h, layer, seq, pos0, npos, k.ctypes.data, v.ctypes.data):
+            raise ValueError("orc_get_kv rejected its arguments")
+        return k, v
+
+    def forward_nocache(self, tokens, rope_off=0.0):
+        t = np.ascontiguousarray(tokens, dtype=np.int32)
+        logits = np.empty(self.shape.vocab, dtype=np.float64)
+        tok = lib().orc_forward_nocache(self._h, t.ctypes.data, t.size, float(rope_off), _d(logits))
+        if tok < 0:
+            raise ValueError("orc_forward_nocache rejected its arguments")
+        return tok, logits
