@@ -1,0 +1,155 @@
+"""Benchmark: per-token decode latency of the persistent megakernel on one MI355X.
+
+Workload (default): the Llama-3-8B-shaped decoder at batch 1 with bf16 random weights
+N(0, 0.02) (about 16 GB). A 39-token uniform-random prompt runs through the step, then
+greedy decode steps follow at positions 39, 40, ... This is the latency workload shape
+of the MegaKernel article (39-token prompt, 512 generated tokens). Weights and the KV
+cache are resident in HBM before timing starts.
+
+Prints ONE JSON line on stdout. Progress goes to stderr.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "decode ms/token (batch 1, 8B-shape bf16); achieved HBM GB/s vs peak"
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def cpu_baseline(shape, weights, prompt, seconds):
+    """The oracle as it stands, on this host's cores: decode steps of the same model from
+    position 0 (teacher-forced on the prompt tokens) until `seconds` have passed."""
+    import oracle as orc
+    cores = len(os.sched_getaffinity(0))
+    orc.set_threads(cores)
+    n_max = max(2, len(prompt))
+    om = orc.OracleModel(shape, weights, 1, n_max)
+    times = []
+    t_all = time.perf_counter()
+    for i in range(n_max):
+        t0 = time.perf_counter()
+        om.step(0, int(prompt[i]), i)
+        times.append(time.perf_counter() - t0)
+        if time.perf_counter() - t_all > seconds and len(times) >= 2:
+            break
+    om.close()
+    ms = 1e3 * sum(times) / len(times)
+    return {"value": ms, "unit": "ms/token", "tokens_per_s": 1e3 / ms, "cores": orc.threads(), "kind": "oracle",
+            "sample": "%d decode steps of the full model at positions 0..%d (fp64 oracle, all weights streamed "
+                      "from host memory each step)" % (len(times), len(times) - 1)}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=512)
+    ap.add_argument("--warmup", type=int, default=8)
+    ap.add_argument("--workload", default="llama8b")
+    ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print("bench.py measures one GPU: this build has no multi-GPU path (--gpus %d requested)" % args.gpus,
+              file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+    import persistent_megakernel_03_amd as mk
+    from persistent_megakernel_03_amd import roofline as rf
+    import seeded_inputs as si
+
+    wl = si.WORKLOADS[args.workload]
+    m = wl.model
+    if wl.n_seqs != 1 or wl.prompt_len == 0:
+        print("bench.py times the batch-1 prompt workloads (tiny, qwen0.5b, llama8b)", file=sys.stderr)
+        sys.exit(2)
+    K, W = args.steps, args.warmup
+    P = wl.prompt_len
+    n_pos = P + max(K, W)
+    t0 = time.time()
+    weights = si.gen_weights(m)
+    prompt = si.prompt_tokens(wl)
+    log("weights generated in %.1fs" % (time.time() - t0))
+    nb = (n_pos + 15) // 16
+    cfg = mk.make_config(m, max_seqs=1, max_blocks_per_seq=nb, num_blocks=nb)
+    dec = mk.Decoder(cfg, 0)
+    t0 = time.time()
+    dec.load_weights(weights)
+    log("weights loaded in %.1fs" % (time.time() - t0))
+    dec.set_page_table(np.arange(nb, dtype=np.int32).reshape(1, nb))
+    dec.set_ctx_lens([0])
+    g0 = torch.zeros(1, dtype=torch.int32, device=dec.dev)
+    dec.prefill(list(prompt), g0)
+    tokens = g0.clone()
+    for _ in range(W):
+        dec.step(tokens)
+    dec.sync_check()
+    # timed region: K greedy steps at positions P .. P+K-1 starting from the first generated token
+    dec.set_ctx_lens([P])
+    tokens.copy_(g0)
+    stream = torch.cuda.current_stream(dec.dev)
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize(dec.dev)
+    ev0.record(stream)
+    for _ in range(K):
+        dec.step(tokens)
+    ev1.record(stream)
+    torch.cuda.synchronize(dec.dev)
+    ms_total = ev0.elapsed_time(ev1)
+    dec.sync_check()
+    assert int(dec.ctx_lens.item()) == P + K
+    ms = ms_total / K
+    bytes_avg = sum(rf.step_bytes(m, [P + i + 1]) for i in range(K)) / K
+    achieved = bytes_avg / (ms * 1e-3) / 1e9
+    log("decode: %.4f ms/token, %.1f tok/s, %.1f GB/s (%.1f%% of %.0f GB/s)" %
+        (ms, 1e3 / ms, achieved, 100 * achieved / rf.MI355X_HBM_PEAK_GBS, rf.MI355X_HBM_PEAK_GBS))
+    dec.close()
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        t0 = time.time()
+        cpu = cpu_baseline(m, weights, prompt, args.cpu_seconds)
+        log("cpu baseline: %.1f ms/token on %d cores (%.1fs)" % (cpu["value"], cpu["cores"], time.time() - t0))
+
+    out = {
+        "metric": METRIC,
+        "value": round(ms, 5),
+        "unit": "ms/token",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": W,
+        "ms_per_step": round(ms, 5),
+        "tokens_per_s": round(1e3 / ms, 2),
+        "achieved_hbm_gbs": round(achieved, 1),
+        "higher_is_better": False,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "weights_dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": "%s decode, batch 1, %d-token prompt, greedy steps at positions %d..%d"
+                               % (wl.name, P, P, P + K - 1),
+                   "batch": 1, "prompt_len": P, "decode_steps": K,
+                   "weight_bytes_per_token": rf.weight_bytes_per_token(m),
+                   "kv": "bf16, paged in 16-token blocks"},
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": rf.MI355X_HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(achieved / rf.MI355X_HBM_PEAK_GBS, 4), "traffic": None,
+                     "bytes_per_launch": int(bytes_avg), "kernel": "mk_megakernel (one launch per decode step)"},
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

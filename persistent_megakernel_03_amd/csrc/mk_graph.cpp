@@ -1,0 +1,590 @@
+// Host-side task-graph builder, validator and interleaving simulator.
+//
+// The builder refines the decode step's operators into per-CU tasks over the
+// data units that really depend on each other ("LLMs in einen MegaKernel
+// kompilieren", "Part 1. Compiler": one task per SM, events as sync points,
+// a fine-grained task graph; "MPK: A Compiler and Runtime for
+// Mega-Kernelizing Tensor Programs", analogy 2, the SM-level graph).
+//
+// The decode graph is fixed, so the builder emits it directly, ahead of time.
+// Every CU's queue follows one global topological order. All workgroups are
+// co-resident, so this order makes the graph deadlock-free. Each task runs on
+// one CU. The tasks of one operator stage are spread evenly, one per CU, so
+// every CU streams an equal share of each weight matrix.
+#include <algorithm>
+#include <cstring>
+#include <numeric>
+#include <string>
+
+#include "mk_host.h"
+
+namespace mk {
+
+static int64_t align_up(int64_t x, int64_t a) { return (x + a - 1) / a * a; }
+
+GemvGeom choose_geom(int K) {
+  GemvGeom g{};
+  g.K = K;
+  g.P = K / 8;
+  int lpr = 0;
+  for (int c : {64, 32, 16})
+    if (g.P % c == 0) { lpr = c; break; }
+  if (!lpr)
+    for (int c : {64, 32, 16, 8, 4, 2, 1}) {
+      const int64_t padded = (int64_t)(g.P + c - 1) / c * c;
+      if ((padded - g.P) * 16 <= g.P) { lpr = c; break; }
+    }
+  g.lpr = lpr;
+  g.rg = 64 / lpr;
+  g.S = (g.P + lpr - 1) / lpr;
+  return g;
+}
+
+namespace {
+
+struct Range { int r0, r1; };
+
+// Rows [0, N) in units of A rows, split as evenly as possible over n CUs.
+std::vector<Range> distribute(int N, int A, int n) {
+  std::vector<Range> out(n);
+  const int64_t units = (N + A - 1) / A;
+  for (int c = 0; c < n; ++c) {
+    const int64_t u0 = units * c / n, u1 = units * (c + 1) / n;
+    out[c].r0 = (int)std::min<int64_t>(N, u0 * A);
+    out[c].r1 = (int)std::min<int64_t>(N, u1 * A);
+  }
+  return out;
+}
+
+struct Builder {
+  HostGraph& g;
+  const mk_model_config& c;
+  std::vector<int32_t> task_cu;
+  std::vector<std::vector<std::pair<int, int>>> task_sig;  // (event, producer index) per task
+  std::vector<int> ev_producers;                            // producer count per event
+  int64_t packed = 0;
+
+  Builder(HostGraph& g_, const mk_model_config& c_) : g(g_), c(c_) {}
+
+  int new_event(int nprod) {
+    ev_producers.push_back(nprod);
+    return (int)ev_producers.size() - 1;
+  }
+  int add_task(const TaskDesc& t, int cu) {
+    g.tasks.push_back(t);
+    g.acc.emplace_back();
+    g.comb_acc.emplace_back();
+    task_cu.push_back(cu);
+    task_sig.emplace_back();
+    return (int)g.tasks.size() - 1;
+  }
+  void acc(int t, int buf, int64_t lo, int64_t hi, int w) {
+    if (hi > lo) g.acc[t].push_back(Access{buf, lo, hi, w});
+  }
+  void cacc(int t, int buf, int64_t lo, int64_t hi, int w) {
+    if (hi > lo) g.comb_acc[t].push_back(Access{buf, lo, hi, w});
+  }
+  int64_t tile_bytes(int geom, int rows) const {
+    const GemvGeom& q = g.geoms[geom];
+    return (int64_t)((rows + q.rg - 1) / q.rg) * q.S * 1024;
+  }
+  // A GEMV stage: one task per CU with a non-empty row range.
+  std::vector<int> gemv_stage(int type, int layer, int geom, int N, int A, int wait_ev) {
+    std::vector<int> ids;
+    auto rs = distribute(N, A, g.n_cus);
+    for (int cu = 0; cu < g.n_cus; ++cu) {
+      if (rs[cu].r1 <= rs[cu].r0) continue;
+      TaskDesc t{};
+      t.type = type;
+      t.layer = layer;
+      t.wait_ev = wait_ev;
+      t.row0 = rs[cu].r0;
+      t.row1 = rs[cu].r1;
+      t.geom = geom;
+      t.wofs = packed;
+      packed += tile_bytes(geom, t.row1 - t.row0);
+      ids.push_back(add_task(t, cu));
+    }
+    return ids;
+  }
+};
+
+int lcm_i(int a, int b) { return a / std::gcd(a, b) * b; }
+
+}  // namespace
+
+std::string build_graph(const mk_model_config& c, int n_cus, HostGraph& g) {
+  g = HostGraph{};
+  if (n_cus < 1 || n_cus > 4096) return "n_cus out of range";
+  if (c.n_layers < 1 || c.d_model < 8 || c.n_q_heads < 1 || c.n_kv_heads < 1 || c.head_dim < 4 || c.d_ffn < 8 ||
+      c.vocab < 2)
+    return "non-positive model dimension";
+  if (c.n_q_heads % c.n_kv_heads) return "n_q_heads must be a multiple of n_kv_heads";
+    if (c.d_model % 8 || c.d_ffn % 8 || (c.n_q_heads * c.head_dim) % 8) return "GEMV inner dims must be multiples of 8";
+  if (c.n_q_heads / c.n_kv_heads > 8) return "at most 8 query heads per KV head";
+  if (c.head_dim != 64 && c.head_dim != 128) return "head_dim must be 64 or 128";
+  if (c.block_size != 16) return "block_size must be 16";
+  if (c.max_seqs != 1) return "this build runs batch-1 graphs (max_seqs == 1)";
+  if (c.max_blocks_per_seq < 1 || c.num_blocks < 1) return "empty KV cache";
+  if (!(c.rms_eps >= 0.f) || !(c.rope_theta > 0.f)) return "bad rms_eps or rope_theta";
+  if (c.attn_splits < 0 || c.attn_splits > 64) return "attn_splits out of range";
+  g.cfg = c;
+  g.n_cus = n_cus;
+  g.max_pos = c.max_blocks_per_seq * c.block_size;
+  const int L = c.n_layers, d = c.d_model, hq = c.n_q_heads, hk = c.n_kv_heads, dh = c.head_dim, f = c.d_ffn,
+            V = c.vocab, S = c.max_seqs, G = hq / hk;
+  const int qd = hq * dh, Nqkv = qkv_rows(c), Rg = (G + 2) * dh;
+  if (c.attn_splits > 0) {
+    g.splits = c.attn_splits;
+  } else {
+    int sp = (c.max_blocks_per_seq + 3) / 4;
+    sp = std::min(sp, 32);
+    sp = std::min(sp, std::max(1, 2 * n_cus / (S * hk)));
+    g.splits = std::max(1, sp);
+  }
+  g.geoms[G_QKV] = choose_geom(d);
+  g.geoms[G_O] = choose_geom(qd);
+  g.geoms[G_GU] = choose_geom(d);
+  g.geoms[G_D] = choose_geom(f);
+  g.geoms[G_LM] = choose_geom(d);
+
+  g.sym_size[S_X] = (int64_t)S * d;
+  g.sym_size[S_Q] = (int64_t)S * qd;
+  g.sym_size[S_KVCUR] = (int64_t)L * S * hk * 2 * dh;
+  g.sym_size[S_PART] = (int64_t)S * hq * g.splits;
+  g.sym_size[S_O] = (int64_t)S * qd;
+  g.sym_size[S_H] = (int64_t)S * f;
+  g.sym_size[S_LOGITS] = (int64_t)S * V;
+  g.sym_size[S_CTX] = S;
+  g.sym_size[S_TOKOUT] = S;
+
+  Builder b(g, c);
+  int ev_x = -1;  // event "residual stream ready for this layer" (none before layer 0)
+  int max_task_rows = 0;
+  std::vector<int> down_ids;
+  for (int l = 0; l < L; ++l) {
+    // ---- QKV: RMSNorm + GEMV + bias + RoPE + KV append
+    const int aq = lcm_i(4, g.geoms[G_QKV].rg);
+    auto qkv = b.gemv_stage(T_QKV, l, G_QKV, Nqkv, aq, ev_x);
+    std::vector<int> ev_qkv(hk);
+    std::vector<int> nprod(hk, 0);
+    for (int t : qkv) {
+      const TaskDesc& td = g.tasks[t];
+      for (int grp = td.row0 / Rg; grp <= (td.row1 - 1) / Rg; ++grp) b.task_sig[t].push_back({-1 - grp, nprod[grp]++});
+    }
+    for (int grp = 0; grp < hk; ++grp) ev_qkv[grp] = b.new_event(nprod[grp]);
+    for (int t : qkv) {
+      for (auto& s : b.task_sig[t]) s.first = ev_qkv[-1 - s.first];
+      const TaskDesc& td = g.tasks[t];
+      max_task_rows = std::max(max_task_rows, td.row1 - td.row0);
+      for (int s = 0; s < S; ++s) {
+        if (l > 0) b.acc(t, S_X, (int64_t)s * d, (int64_t)(s + 1) * d, 0);
+        b.acc(t, S_CTX, s, s + 1, 0);
+        // packed rows -> written q / k / v elements (pairs [a/2, b/2) and their + dh/2 partners)
+        for (int r = td.row0; r < td.row1;) {
+          const int grp = r / Rg, within = r % Rg, slot = within / dh;
+          const int hs = grp * Rg + slot * dh;                       // packed start of this head
+          const int e = std::min(td.row1, hs + dh);
+          const int p0 = (r - hs) / 2, p1 = (e - hs) / 2;
+          if (slot < G) {
+            const int64_t base = (int64_t)s * qd + (int64_t)(grp * G + slot) * dh;
+            b.acc(t, S_Q, base + p0, base + p1, 1);
+            b.acc(t, S_Q, base + p0 + dh / 2, base + p1 + dh / 2, 1);
+          } else {
+            const int64_t base = (((int64_t)l * S + s) * hk + grp) * 2 * dh + (slot == G ? 0 : dh);
+            b.acc(t, S_KVCUR, base + p0, base + p1, 1);
+            b.acc(t, S_KVCUR, base + p0 + dh / 2, base + p1 + dh / 2, 1);
+          }
+          r = e;
+        }
+      }
+    }
+    // ---- attention splits; the last split of each (seq, kv head) merges and signals
+    const int ev_att = b.new_event(S * hk);
+    {
+      const int n_attn = S * hk * g.splits;
+      int k = 0;
+      for (int s = 0; s < S; ++s)
+        for (int grp = 0; grp < hk; ++grp)
+          for (int j = 0; j < g.splits; ++j, ++k) {
+            TaskDesc t{};
+            t.type = T_ATTN;
+            t.layer = l;
+            t.wait_ev = ev_qkv[grp];
+            t.a0 = s;
+            t.a1 = grp;
+            t.a2 = j;
+            t.a3 = (l * S + s) * hk + grp;
+            const int cu = (int)((int64_t)k * n_cus / n_attn);
+            const int id = b.add_task(t, cu);
+            b.task_sig[id].push_back({ev_att, s * hk + grp});
+            b.acc(id, S_Q, (int64_t)s * qd + (int64_t)grp * G * dh, (int64_t)s * qd + (int64_t)(grp + 1) * G * dh, 0);
+            b.acc(id, S_KVCUR, (((int64_t)l * S + s) * hk + grp) * 2 * dh, (((int64_t)l * S + s) * hk + grp + 1) * 2 * dh, 0);
+            b.acc(id, S_CTX, s, s + 1, 0);
+            for (int h = grp * G; h < (grp + 1) * G; ++h)
+              b.acc(id, S_PART, ((int64_t)s * hq + h) * g.splits + j, ((int64_t)s * hq + h) * g.splits + j + 1, 1);
+            for (int h = grp * G; h < (grp + 1) * G; ++h)
+              b.cacc(id, S_PART, ((int64_t)s * hq + h) * g.splits, ((int64_t)s * hq + h + 1) * g.splits, 0);
+            b.cacc(id, S_O, (int64_t)s * qd + (int64_t)grp * G * dh, (int64_t)s * qd + (int64_t)(grp + 1) * G * dh, 1);
+          }
+      g.n_counters = std::max(g.n_counters, (l + 1) * S * hk);
+    }
+    // ---- O projection + residual
+    auto op = b.gemv_stage(T_OPROJ, l, G_O, d, g.geoms[G_O].rg, ev_att);
+    const int ev_o = b.new_event((int)op.size());
+    for (size_t i = 0; i < op.size(); ++i) {
+      const int t = op[i];
+      const TaskDesc& td = g.tasks[t];
+      max_task_rows = std::max(max_task_rows, td.row1 - td.row0);
+      b.task_sig[t].push_back({ev_o, (int)i});
+      for (int s = 0; s < S; ++s) {
+        b.acc(t, S_O, (int64_t)s * qd, (int64_t)(s + 1) * qd, 0);
+        if (l > 0) b.acc(t, S_X, (int64_t)s * d + td.row0, (int64_t)s * d + td.row1, 0);
+        b.acc(t, S_X, (int64_t)s * d + td.row0, (int64_t)s * d + td.row1, 1);
+      }
+    }
+    // ---- RMSNorm + gate/up + SwiGLU
+    auto gu = b.gemv_stage(T_GATEUP, l, G_GU, 2 * f, lcm_i(2, g.geoms[G_GU].rg), ev_o);
+    const int ev_gu = b.new_event((int)gu.size());
+    for (size_t i = 0; i < gu.size(); ++i) {
+      const int t = gu[i];
+      const TaskDesc& td = g.tasks[t];
+      max_task_rows = std::max(max_task_rows, td.row1 - td.row0);
+      b.task_sig[t].push_back({ev_gu, (int)i});
+      for (int s = 0; s < S; ++s) {
+        b.acc(t, S_X, (int64_t)s * d, (int64_t)(s + 1) * d, 0);
+        b.acc(t, S_H, (int64_t)s * f + td.row0 / 2, (int64_t)s * f + td.row1 / 2, 1);
+      }
+    }
+    // ---- down projection + residual
+    auto dn = b.gemv_stage(T_DOWN, l, G_D, d, g.geoms[G_D].rg, ev_gu);
+    ev_x = b.new_event((int)dn.size());
+    for (size_t i = 0; i < dn.size(); ++i) {
+      const int t = dn[i];
+      const TaskDesc& td = g.tasks[t];
+      max_task_rows = std::max(max_task_rows, td.row1 - td.row0);
+      b.task_sig[t].push_back({ev_x, (int)i});
+      for (int s = 0; s < S; ++s) {
+        b.acc(t, S_H, (int64_t)s * f, (int64_t)(s + 1) * f, 0);
+        b.acc(t, S_X, (int64_t)s * d + td.row0, (int64_t)s * d + td.row1, 0);
+        b.acc(t, S_X, (int64_t)s * d + td.row0, (int64_t)s * d + td.row1, 1);
+      }
+    }
+  }
+  // ---- final RMSNorm + LM head + partial argmax
+  auto lm = b.gemv_stage(T_LMHEAD, L, G_LM, V, g.geoms[G_LM].rg, ev_x);
+  g.n_lm_parts = (int)lm.size();
+  g.sym_size[S_AMAX] = (int64_t)S * g.n_lm_parts;
+  const int ev_lm = b.new_event((int)lm.size());
+  for (size_t i = 0; i < lm.size(); ++i) {
+    const int t = lm[i];
+    TaskDesc& td = g.tasks[t];
+    td.a0 = (int)i;
+    max_task_rows = std::max(max_task_rows, td.row1 - td.row0);
+    b.task_sig[t].push_back({ev_lm, (int)i});
+    for (int s = 0; s < S; ++s) {
+      b.acc(t, S_X, (int64_t)s * d, (int64_t)(s + 1) * d, 0);
+      b.acc(t, S_LOGITS, (int64_t)s * V + td.row0, (int64_t)s * V + td.row1, 1);
+      b.acc(t, S_AMAX, (int64_t)s * g.n_lm_parts + (int64_t)i, (int64_t)s * g.n_lm_parts + (int64_t)i + 1, 1);
+    }
+  }
+  // ---- argmax per sequence
+  for (int s = 0; s < S; ++s) {
+    TaskDesc t{};
+    t.type = T_ARGMAX;
+    t.layer = L;
+    t.wait_ev = ev_lm;
+    t.a0 = s;
+    const int id = b.add_task(t, (int)((int64_t)s * n_cus / S));
+    b.acc(id, S_AMAX, (int64_t)s * g.n_lm_parts, (int64_t)(s + 1) * g.n_lm_parts, 0);
+    b.acc(id, S_CTX, s, s + 1, 0);
+    b.acc(id, S_CTX, s, s + 1, 1);
+    b.acc(id, S_TOKOUT, s, s + 1, 1);
+  }
+
+  // ---- events -> contiguous flag slots; task signal lists -> absolute slots
+  g.events.resize(b.ev_producers.size());
+  int32_t slot = 0;
+  for (size_t e = 0; e < g.events.size(); ++e) {
+    g.events[e].slot0 = slot;
+    g.events[e].nslots = b.ev_producers[e];
+    slot += b.ev_producers[e];
+  }
+  g.n_flag_slots = slot;
+  for (size_t t = 0; t < g.tasks.size(); ++t) {
+    g.tasks[t].sig_off = (int32_t)g.sig_slots.size();
+    g.tasks[t].sig_n = (int32_t)b.task_sig[t].size();
+    for (auto& s : b.task_sig[t]) g.sig_slots.push_back(g.events[s.first].slot0 + s.second);
+  }
+  // ---- per-CU queues in global order
+  g.queue_off.assign(n_cus + 1, 0);
+  for (int32_t cu : b.task_cu) g.queue_off[cu + 1]++;
+  for (int i = 0; i < n_cus; ++i) g.queue_off[i + 1] += g.queue_off[i];
+  g.queue_idx.assign(g.tasks.size(), 0);
+  {
+    std::vector<int32_t> fill(g.queue_off.begin(), g.queue_off.end() - 1);
+    for (size_t t = 0; t < g.tasks.size(); ++t) g.queue_idx[fill[b.task_cu[t]]++] = (int32_t)t;
+  }
+
+  // ---- weights buffer layout
+  g.wl.packed_bytes = align_up(b.packed, 256);
+  g.wl.embed = g.wl.packed_bytes;
+  g.wl.norms = align_up(g.wl.embed + (int64_t)V * d * 2, 256);
+  g.wl.bias = align_up(g.wl.norms + (int64_t)(2 * L + 1) * d * 2, 256);
+  g.wl.total = align_up(g.wl.bias + (c.qkv_bias ? (int64_t)L * Nqkv * 2 : 0), 256);
+
+  // ---- scratch layout
+  int64_t o = 0;
+  auto take = [&](int64_t bytes) { const int64_t at = o; o = align_up(o + std::max<int64_t>(bytes, 4), 256); return at; };
+  g.sl.tasks = take((int64_t)g.tasks.size() * sizeof(TaskDesc));
+  g.sl.queue_off = take((int64_t)g.queue_off.size() * 4);
+  g.sl.queue_idx = take((int64_t)g.queue_idx.size() * 4);
+  g.sl.events = take((int64_t)g.events.size() * sizeof(EventDesc));
+  g.sl.sig_slots = take((int64_t)g.sig_slots.size() * 4);
+  g.sl.geoms = take((int64_t)G_COUNT * sizeof(GemvGeom));
+  g.sl.rope = take((int64_t)g.max_pos * (dh / 2) * 8);
+  g.sl.flags = take((int64_t)g.n_flag_slots * 4);
+  g.sl.counters = take((int64_t)g.n_counters * 4);
+  g.sl.err = take((int64_t)E_COUNT * 4);
+  g.sl.x = take((int64_t)S * d * 4);
+  g.sl.q = take((int64_t)S * qd * 4);
+  g.sl.o = take((int64_t)S * qd * 4);
+  g.sl.h = take((int64_t)S * f * 4);
+  g.sl.part = take((int64_t)S * hq * g.splits * (dh + 2) * 4);
+  g.sl.amax = take((int64_t)S * g.n_lm_parts * 8);
+  g.sl.tokbuf = take((int64_t)std::max(g.max_pos, 64) * 4);
+  g.sl.tokout = take(64 * 4);
+  g.sl.pools = take((int64_t)2 * L * 8);
+  g.sl.total = o;
+
+  // ---- LDS: padded GEMV input vector + per-row results, or the attention working set
+  int64_t xs = 0;
+  for (int i = 0; i < G_COUNT; ++i) xs = std::max<int64_t>(xs, (int64_t)g.geoms[i].S * g.geoms[i].lpr * 8);
+  const int64_t gemv_lds = xs * 4 + (int64_t)align_up(max_task_rows, 64) * 4 * S + 1024;
+  const int64_t attn_lds = (int64_t)G * 512 * 4 /* scores chunk */ + (int64_t)8 * G * dh * 4 /* per-wave o */;
+  g.lds_bytes = align_up(std::max(gemv_lds, attn_lds), 256) + 1024;  // + control block
+  if (g.lds_bytes > 160 * 1024) return "working set exceeds 160 KB of LDS";
+  return "";
+}
+
+// ----------------------------------------------------------------------------- validation
+std::string validate_graph(const HostGraph& g) {
+  const int nt = (int)g.tasks.size();
+  // every task in exactly one queue, queues in increasing global order
+  std::vector<int> seen(nt, 0);
+  for (int cu = 0; cu < g.n_cus; ++cu) {
+    int prev = -1;
+    for (int i = g.queue_off[cu]; i < g.queue_off[cu + 1]; ++i) {
+      const int t = g.queue_idx[i];
+      if (t < 0 || t >= nt) return "queue index out of range";
+      if (t <= prev) return "queue not in global order on CU " + std::to_string(cu);
+      prev = t;
+      seen[t]++;
+    }
+  }
+  for (int t = 0; t < nt; ++t)
+    if (seen[t] != 1) return "task " + std::to_string(t) + " is not in exactly one queue";
+  // slot writers: each slot has one writer task, or one (seq, kv head) group of attention splits
+  std::vector<int> writer(g.n_flag_slots, -1);
+  for (int t = 0; t < nt; ++t) {
+    const TaskDesc& td = g.tasks[t];
+    for (int i = 0; i < td.sig_n; ++i) {
+      const int s = g.sig_slots[td.sig_off + i];
+      if (s < 0 || s >= g.n_flag_slots) return "signal slot out of range";
+      const int key = td.type == T_ATTN ? -2 - td.a3 : t;   // all splits of one group share their slot
+      if (writer[s] != -1 && writer[s] != key) return "flag slot " + std::to_string(s) + " has two writers";
+      writer[s] = key;
+    }
+  }
+  for (int s = 0; s < g.n_flag_slots; ++s)
+    if (writer[s] == -1) return "flag slot " + std::to_string(s) + " has no writer";
+  // every producer of a task's event comes before the task in global order
+  std::vector<int> last_writer_task(g.n_flag_slots, -1);
+  for (int t = 0; t < nt; ++t)
+    for (int i = 0; i < g.tasks[t].sig_n; ++i) {
+      const int s = g.sig_slots[g.tasks[t].sig_off + i];
+      last_writer_task[s] = std::max(last_writer_task[s], t);
+    }
+  for (int t = 0; t < nt; ++t) {
+    const int e = g.tasks[t].wait_ev;
+    if (e < -1 || e >= (int)g.events.size()) return "wait event out of range";
+    if (e < 0) continue;
+    const EventDesc& ev = g.events[e];
+    if (ev.nslots <= 0) return "event with no producers";
+    for (int s = ev.slot0; s < ev.slot0 + ev.nslots; ++s)
+      if (last_writer_task[s] >= t) return "task " + std::to_string(t) + " waits on a later producer";
+  }
+  // GEMV tiles: rows covered exactly once per stage, tiles disjoint and in range
+  int64_t end = 0;
+  for (int t = 0; t < nt; ++t) {
+    const TaskDesc& td = g.tasks[t];
+    if (td.type == T_ATTN || td.type == T_ARGMAX) continue;
+    const GemvGeom& q = g.geoms[td.geom];
+    if (td.row1 <= td.row0) return "empty GEMV task";
+    if (td.wofs != end) return "GEMV tiles not contiguous in stage order";
+    end += (int64_t)((td.row1 - td.row0 + q.rg - 1) / q.rg) * q.S * 1024;
+    if (td.type == T_QKV && (td.row0 % 4 || td.row1 % 4)) return "QKV task not aligned to RoPE pair sets";
+    if (td.type == T_GATEUP && (td.row0 % 2 || td.row1 % 2)) return "gate/up task splits a pair";
+  }
+  if (end > g.wl.packed_bytes) return "tiles exceed the packed weights";
+  if (g.lds_bytes > 160 * 1024) return "LDS over budget";
+  return "";
+}
+
+// ----------------------------------------------------------------------------- simulation
+namespace {
+uint64_t sm_next(uint64_t& s) {
+  uint64_t z = (s += 0x9E3779B97F4A7C15ULL);
+  z = (z ^ (z >> 30)) * 0xBF58476D1CE4E5B9ULL;
+  z = (z ^ (z >> 27)) * 0x94D049BB133111EBULL;
+  return z ^ (z >> 31);
+}
+}  // namespace
+
+std::string simulate_graph(const HostGraph& g, uint64_t seed, int n_steps) {
+  const int nt = (int)g.tasks.size();
+  // Static writer/reader lists per element (a writer of an ATTN merge is attributed to the
+  // group's last split in global order).
+  std::vector<int> comb_pos(nt, -1);
+  {
+    std::vector<int> last_of_group(g.n_counters, -1);
+    for (int t = 0; t < nt; ++t)
+      if (g.tasks[t].type == T_ATTN) last_of_group[g.tasks[t].a3] = t;
+    for (int t = 0; t < nt; ++t)
+      if (g.tasks[t].type == T_ATTN) comb_pos[t] = last_of_group[g.tasks[t].a3];
+  }
+  std::vector<std::vector<std::vector<int>>> writers(S_COUNT), readers(S_COUNT);
+  for (int b = 0; b < S_COUNT; ++b) {
+    writers[b].resize(g.sym_size[b]);
+    readers[b].resize(g.sym_size[b]);
+  }
+  auto add = [&](const Access& a, int pos) {
+    if (a.lo < 0 || a.hi > g.sym_size[a.buf]) return false;
+    for (int64_t e = a.lo; e < a.hi; ++e) (a.write ? writers : readers)[a.buf][e].push_back(pos);
+    return true;
+  };
+  for (int t = 0; t < nt; ++t) {
+    for (const Access& a : g.acc[t])
+      if (!add(a, t)) return "access out of symbolic range";
+    if (comb_pos[t] == t)
+      for (const Access& a : g.comb_acc[t])
+        if (!add(a, t)) return "merge access out of symbolic range";
+  }
+  for (int b = 0; b < S_COUNT; ++b)
+    for (auto& v : writers[b]) {
+      std::sort(v.begin(), v.end());
+      v.erase(std::unique(v.begin(), v.end()), v.end());
+    }
+  // Dynamic state.
+  std::vector<std::vector<int64_t>> ver(S_COUNT);  // step * nt + writer position, or -1
+  for (int b = 0; b < S_COUNT; ++b) ver[b].assign(g.sym_size[b], -1);
+  std::vector<uint32_t> flags(g.n_flag_slots, 0), counters(g.n_counters, 0);
+  uint64_t rng = seed;
+  for (int step = 0; step < n_steps; ++step) {
+    const uint32_t epoch = (uint32_t)step + 1;
+    std::vector<char> ended(nt, 0), started(nt, 0);
+    std::vector<int> qpos(g.n_cus), running(g.n_cus, -1);
+    for (int cu = 0; cu < g.n_cus; ++cu) qpos[cu] = g.queue_off[cu];
+    // Expected version of element e for a reader at global position pos: the last writer before
+    // pos in this step (at or before pos for a merge, which runs after its own split's write).
+    auto expected = [&](int b, int64_t e, int pos, bool inclusive) -> int64_t {
+      const auto& w = writers[b][e];
+      auto it = inclusive ? std::upper_bound(w.begin(), w.end(), pos) : std::lower_bound(w.begin(), w.end(), pos);
+      if (it != w.begin()) return (int64_t)step * nt + *(it - 1);
+      if (!w.empty() && step > 0) return (int64_t)(step - 1) * nt + w.back();
+      return ver[b][e] == -1 ? -1 : ver[b][e];  // written outside the graph (initial state)
+    };
+    auto check_reads = [&](const std::vector<Access>& as, int pos, bool inclusive, std::string& err) {
+      for (const Access& a : as) {
+        if (a.write) continue;
+        for (int64_t e = a.lo; e < a.hi; ++e)
+          if (ver[a.buf][e] != expected(a.buf, e, pos, inclusive)) {
+            err = "task " + std::to_string(pos) + " read buffer " + std::to_string(a.buf) + " element " +
+                  std::to_string(e) + " before its producer finished";
+            return false;
+          }
+      }
+      return true;
+    };
+    auto apply_writes = [&](const std::vector<Access>& as, int pos, std::string& err) {
+      for (const Access& a : as) {
+        if (!a.write) continue;
+        for (int64_t e = a.lo; e < a.hi; ++e) {
+          const auto& w = writers[a.buf][e];
+          auto it = std::lower_bound(w.begin(), w.end(), pos);
+          const int prev = it != w.begin() ? *(it - 1) : -1;
+          for (int r : readers[a.buf][e])
+            if (r > prev && r < pos && !ended[r]) {
+              err = "task " + std::to_string(pos) + " overwrote buffer " + std::to_string(a.buf) + " element " +
+                    std::to_string(e) + " while task " + std::to_string(r) + " still needed it";
+              return false;
+            }
+          ver[a.buf][e] = (int64_t)step * nt + pos;
+        }
+      }
+      return true;
+    };
+    auto ready = [&](int t) {
+      const int e = g.tasks[t].wait_ev;
+      if (e < 0) return true;
+      for (int s = g.events[e].slot0; s < g.events[e].slot0 + g.events[e].nslots; ++s)
+        if (flags[s] < epoch) return false;
+      return true;
+    };
+    int done = 0;
+    std::vector<int> cand;
+    while (done < nt) {
+      cand.clear();
+      for (int cu = 0; cu < g.n_cus; ++cu) {
+        if (running[cu] >= 0) cand.push_back(cu);
+        else if (qpos[cu] < g.queue_off[cu + 1] && ready(g.queue_idx[qpos[cu]])) cand.push_back(cu);
+      }
+      if (cand.empty()) return "deadlock at step " + std::to_string(step) + " after " + std::to_string(done) + " tasks";
+      const int cu = cand[sm_next(rng) % cand.size()];
+      std::string err;
+      if (running[cu] < 0) {
+        const int t = g.queue_idx[qpos[cu]++];
+        if (!check_reads(g.acc[t], t, false, err)) return err;
+        started[t] = 1;
+        running[cu] = t;
+      } else {
+        const int t = running[cu];
+        running[cu] = -1;
+        const TaskDesc& td = g.tasks[t];
+        if (!apply_writes(g.acc[t], t, err)) return err;
+        ended[t] = 1;
+        ++done;
+        if (td.type == T_ATTN) {
+          if (++counters[td.a3] == epoch * (uint32_t)g.splits) {
+            if (!check_reads(g.comb_acc[t], comb_pos[t], true, err)) return err;
+            if (!apply_writes(g.comb_acc[t], comb_pos[t], err)) return err;
+            for (int i = 0; i < td.sig_n; ++i) flags[g.sig_slots[td.sig_off + i]] = epoch;
+          }
+        } else {
+          for (int i = 0; i < td.sig_n; ++i) flags[g.sig_slots[td.sig_off + i]] = epoch;
+        }
+      }
+    }
+  }
+  return "";
+}
+
+uint64_t graph_hash(const HostGraph& g) {
+  uint64_t h = 0xcbf29ce484222325ULL;
+  auto mix = [&](const void* p, size_t n) {
+    const unsigned char* c = (const unsigned char*)p;
+    for (size_t i = 0; i < n; ++i) {
+      h ^= c[i];
+      h *= 0x100000001b3ULL;
+    }
+  };
+  mix(g.tasks.data(), g.tasks.size() * sizeof(TaskDesc));
+  mix(g.queue_off.data(), g.queue_off.size() * 4);
+  mix(g.queue_idx.data(), g.queue_idx.size() * 4);
+  mix(g.events.data(), g.events.size() * sizeof(EventDesc));
+  mix(g.sig_slots.data(), g.sig_slots.size() * 4);
+  mix(g.geoms, sizeof(g.geoms));
+  return h;
+}
+
+}  // namespace mk

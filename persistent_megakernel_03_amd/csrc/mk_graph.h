@@ -1,0 +1,128 @@
+// Task-graph data structures shared by the host builder (mk_graph.cpp), the host
+// runtime (mk_api.cpp) and the megakernel (mk_kernel.hip).
+//
+// The decode step is split into tasks, each run by one workgroup (one CU). A
+// task waits on at most one event and, when done, publishes its epoch number
+// into one or more flag slots. An event is a contiguous range of flag slots,
+// one per producer task. It is satisfied for step `epoch` once every slot
+// holds a value >= epoch. So no counter is ever reset, and a slot has
+// exactly one writer. This follows the pages' events with counters and
+// thresholds ("LLMs in einen MegaKernel kompilieren", "Ereignisbasierte
+// Ausführung"). A count of producers becomes a set of per-producer flags, so
+// that no two CUs contend for one atomic.
+#pragma once
+#include <stdint.h>
+
+namespace mk {
+
+enum TaskType : int32_t {
+  T_QKV = 1,     // RMSNorm + QKV GEMV (+bias) + RoPE + KV append
+  T_ATTN = 2,    // one split of paged GQA attention; the last split of a (seq, kv head) also merges
+  T_OPROJ = 3,   // O projection + residual
+  T_GATEUP = 4,  // RMSNorm + gate/up GEMV + SiLU(gate) * up
+  T_DOWN = 5,    // down projection + residual
+  T_LMHEAD = 6,  // final RMSNorm + LM head GEMV + partial argmax
+  T_ARGMAX = 7,  // argmax over the LM-head partials, token out, context length + 1
+};
+
+// Geometry of one GEMV operand in the packed (streaming) layout. A row of K
+// bf16 values is P = K/8 pieces of 16 bytes. A "unit" is 1 KB: 64 lanes x 16 B.
+// Rows go in groups of RG = 64/LPR rows. A group is S units. In unit u of a
+// group, lane l holds piece u*LPR + l%LPR of row l/LPR. Pieces past P are zero.
+struct GemvGeom {
+  int32_t K, P, lpr, rg, S;
+  int32_t pad[3];
+};
+enum GeomIndex : int32_t { G_QKV = 0, G_O = 1, G_GU = 2, G_D = 3, G_LM = 4, G_COUNT = 5 };
+
+struct TaskDesc {       // 64 bytes; read with scalar loads
+  int32_t type;
+  int32_t layer;
+  int32_t wait_ev;      // event index, or -1
+  int32_t sig_off;      // this task's flag slots: sig_slots[sig_off .. sig_off + sig_n)
+  int32_t sig_n;
+  int32_t row0, row1;   // GEMV: packed output rows [row0, row1)
+  int32_t geom;         // GEMV: GeomIndex
+  int64_t wofs;         // GEMV: byte offset of the tile in the packed weights
+  int32_t a0, a1, a2, a3;  // ATTN: seq, kv head, split, counter | LMHEAD: part index | ARGMAX: seq
+  int32_t pad[2];
+};
+static_assert(sizeof(TaskDesc) == 64, "TaskDesc is 64 bytes");
+
+struct EventDesc {
+  int32_t slot0, nslots;
+};
+
+// Byte offsets of the regions inside the caller's scratch buffer.
+struct ScratchLayout {
+  int64_t tasks, queue_off, queue_idx, events, sig_slots, geoms, rope;
+  int64_t flags, counters, err;
+  int64_t x, q, o, h, part, amax, tokbuf, tokout, pools;
+  int64_t total;
+};
+
+// Byte offsets inside the caller's weights buffer (after the packed tiles).
+struct WeightLayout {
+  int64_t packed_bytes;  // tiles of every GEMV stage
+  int64_t embed;         // natural [V, d] copy for the embedding gather
+  int64_t norms;         // [L][2][d] (attn, ffn) then final [d]
+  int64_t bias;          // packed-QKV-order bias [L][Nqkv] (when qkv_bias)
+  int64_t total;
+};
+
+// Device error word layout (uint32 slots in scratch).
+enum ErrSlot : int32_t { E_CODE = 0, E_INFO0 = 1, E_INFO1 = 2, E_ABORT = 3, E_COUNT = 16 };
+enum ErrCode : uint32_t { ERR_NONE = 0, ERR_TOKEN = 1, ERR_PAGE = 2, ERR_TIMEOUT = 3, ERR_CTX = 4 };
+
+// Everything the megakernel reads, passed by value.
+struct KernelParams {
+  const TaskDesc* tasks;
+  const int32_t* queue_off;   // [n_cus + 1]
+  const int32_t* queue_idx;
+  const EventDesc* events;
+  const int32_t* sig_slots;
+  const GemvGeom* geoms;
+  const float* rope;          // [max_pos][dh/2][2] (cos, sin)
+  uint32_t* flags;
+  uint32_t* counters;
+  uint32_t* err;
+  const uint8_t* wpacked;     // packed tiles
+  const uint16_t* embed;      // natural embedding [V, d]
+  const uint16_t* norms;      // [L][2][d] + final [d]
+  const uint16_t* bias;       // packed QKV bias or nullptr
+  uint16_t* const* kpool;     // [L] device array of per-layer K pool pointers
+  uint16_t* const* vpool;
+  const int32_t* page_table;  // [max_seqs][max_blocks]
+  int32_t* ctx_lens;          // [max_seqs]
+  float* x;                   // [max_seqs][d] residual stream
+  float* q;                   // [max_seqs][hq*dh] rotated queries
+  float* o;                   // [max_seqs][hq*dh] attention output
+  float* h;                   // [max_seqs][f] SwiGLU output
+  float* part;                // [max_seqs][hq][splits][dh + 2] attention partials (m, l, o[dh])
+  float* logits;              // [max_seqs][V]
+  uint64_t* amax;             // [max_seqs][n_lm_parts] packed argmax keys
+  const int32_t* tokens_in;   // [max_seqs]
+  int32_t* tokens_out;        // [max_seqs]
+  int32_t n_layers, d, hq, hk, dh, f, vocab;
+  float eps;
+  int32_t max_seqs, n_active, max_blocks, num_blocks, block_size, splits, n_lm_parts, max_pos;
+  uint32_t epoch;
+  uint32_t watchdog_ticks;    // s_memrealtime ticks (100 MHz) a wait may spin before the kernel aborts
+};
+
+// Arguments of the weight re-layout kernel: one stage's tasks [task0, task0 + ntasks), whose
+// tiles are contiguous in the packed buffer.
+enum RepackKind : int32_t { RK_PLAIN = 0, RK_QKV = 1, RK_GU = 2 };
+struct RepackArgs {
+  const TaskDesc* tasks;  // device copy of the task array
+  int32_t task0, ntasks;
+  GemvGeom gm;
+  int32_t kind;
+  const uint16_t* w0;     // plain: W; QKV: wq; gate/up: wg
+  const uint16_t* w1;     // QKV: wk; gate/up: wu
+  const uint16_t* w2;     // QKV: wv
+  int32_t G, dh;
+  uint8_t* out;           // packed weights base
+};
+
+}  // namespace mk

@@ -1,0 +1,79 @@
+"""Helpers shared by the GPU parity tests, smoke() and the benchmark: set up the HIP path
+and the oracle on the same seeded inputs, then compare per-step logits.
+
+The oracle is test infrastructure; this module is used only by tests, smoke() and the
+benchmark's CPU-baseline leg.
+"""
+from __future__ import annotations
+
+import numpy as np
+
+import seeded_inputs as si
+
+REL_L2_BAR = 5e-3     # teacher-forced per-step logits, relative L2 (the stated bar)
+BUG_BAR = 1e-4        # fp32 GPU vs fp64 oracle is expected near 1e-6; above this is a bug
+
+
+def rel_l2(a, b) -> float:
+    a = np.asarray(a, dtype=np.float64)
+    b = np.asarray(b, dtype=np.float64)
+    return float(np.linalg.norm(a - b) / max(np.linalg.norm(b), 1e-300))
+
+
+def capacity_blocks(n_positions: int, block_size: int = 16) -> int:
+    return (n_positions + block_size - 1) // block_size
+
+
+def make_gpu(shape, weights, n_positions, paging="identity", attn_splits=0, device=0, seed_ns=None):
+    """A Decoder with a one-sequence cache of n_positions, weights loaded, ctx 0."""
+    import persistent_megakernel_03_amd as mk
+    nb = capacity_blocks(n_positions)
+    cfg = mk.make_config(shape, max_seqs=1, max_blocks_per_seq=nb, num_blocks=nb, attn_splits=attn_splits)
+    dec = mk.Decoder(cfg, device)
+    dec.load_weights(weights)
+    if paging == "permuted":
+        table = si.permutation(si.tensor_seed(seed_ns or shape.name, "pages"), nb).reshape(1, nb)
+    else:
+        table = np.arange(nb, dtype=np.int32).reshape(1, nb)
+    dec.set_page_table(table)
+    dec.set_ctx_lens([0])
+    return dec, table
+
+
+def gpu_step(dec, token: int):
+    """One decode step with a host-given token; returns (device token, logits)."""
+    import torch
+    dec.tokens[0] = int(token)
+    out = torch.zeros(1, dtype=torch.int32, device=dec.dev)
+    dec.step(dec.tokens, 1, out)
+    logits = dec.read_logits(0)
+    return int(out.item()), logits
+
+
+def teacher_forced(shape, weights, prompt, n_decode, paging="identity", attn_splits=0, oracle_model=None,
+                   n_positions=None, record_kv=False):
+    """Run prompt + n_decode steps on both sides; the oracle's greedy token is fed to both.
+
+    Returns a dict with per-step rel-L2, device tokens, oracle tokens, device-argmax agreement
+    and the final GPU decoder (for further checks)."""
+    import oracle as orc
+    total = len(prompt) + n_decode
+    n_positions = n_positions or total
+    orm = oracle_model or orc.OracleModel(shape, weights, 1, n_positions)
+    dec, table = make_gpu(shape, weights, n_positions, paging, attn_splits)
+    rels, dev_tok, orc_tok, self_argmax, gaps = [], [], [], [], []
+    tok = int(prompt[0])
+    for i in range(total):
+        if i < len(prompt):
+            tok = int(prompt[i])
+        o_tok, o_logits = orm.step(0, tok, i)
+        d_tok, d_logits = gpu_step(dec, tok)
+        rels.append(rel_l2(d_logits, o_logits))
+        dev_tok.append(d_tok)
+        orc_tok.append(o_tok)
+        self_argmax.append(d_tok == int(np.argmax(d_logits)))
+        srt = np.sort(o_logits)
+        gaps.append(float(srt[-1] - srt[-2]))
+        tok = o_tok
+    return dict(rel=rels, dev_tok=dev_tok, orc_tok=orc_tok, self_argmax=self_argmax, gaps=gaps, dec=dec,
+                oracle=orm, table=table)

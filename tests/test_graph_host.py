@@ -1,0 +1,146 @@
+"""Host-only checks of the C-ABI library and its task-graph builder (no GPU needed).
+
+The library must load and export every symbol include/mk.h declares. The graph it builds
+for each workload shape must validate:
+  - each queue follows one global topological order;
+  - every consumer comes after its producers;
+  - each flag slot has one writer;
+  - each tile is contiguous.
+Random interleavings of the per-CU queues, simulated against symbolic buffers, must find
+neither a read before its producer finished nor an overwrite while a reader still needs
+the old value.
+"""
+import ctypes
+import dataclasses
+import os
+import re
+
+import pytest
+
+import persistent_megakernel_03_amd as mk
+import seeded_inputs as si
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+@pytest.fixture(scope="module")
+def L():
+    if not os.path.exists(mk.LIB_PATH):
+        mk.build(force=True)
+    return mk.lib()
+
+
+def declared_symbols():
+    text = open(os.path.join(ROOT, "include", "mk.h")).read()
+    return sorted(set(re.findall(r"^(?:mk_status|void|const char\*)\s+(mk_\w+)\(", text, re.M)))
+
+
+def test_exports_every_declared_symbol(L):
+    names = declared_symbols()
+    assert len(names) >= 15
+    for n in names:
+        assert hasattr(L, n), n
+    assert set(names) == set(mk.EXPORTS)
+
+
+def cfg_for(shape, max_blocks=64, num_blocks=64, splits=0):
+    return mk.make_config(shape, max_seqs=1, max_blocks_per_seq=max_blocks, num_blocks=num_blocks, attn_splits=splits)
+
+
+@pytest.mark.parametrize("shape,blocks", [(si.TINY, 3), (si.QWEN05B, 35), (si.LLAMA8B, 35), (si.LLAMA8B, 2053)])
+def test_graph_validates(L, shape, blocks):
+    ctx = mk.mk_create_host(cfg_for(shape, blocks, blocks), 256)
+    try:
+        mk.mk_graph_validate(ctx)
+        info = mk.mk_graph_stats(ctx)
+        assert info.n_tasks > 0 and info.lds_bytes <= 160 * 1024
+        # the packed tiles hold every GEMV weight once (plus zero padding of partial groups)
+        m = shape
+        gemv = (m.n_layers * ((m.n_q_heads + 2 * m.n_kv_heads) * m.head_dim * m.d_model
+                              + m.d_model * m.n_q_heads * m.head_dim + 3 * m.d_ffn * m.d_model)
+                + m.vocab * m.d_model) * 2
+        assert gemv <= info.weight_bytes <= gemv * 1.07
+    finally:
+        mk.mk_destroy(ctx)
+
+
+def test_8b_tiles_have_no_padding(L):
+    ctx = mk.mk_create_host(cfg_for(si.LLAMA8B, 35, 35), 256)
+    try:
+        info = mk.mk_graph_stats(ctx)
+        m = si.LLAMA8B
+        gemv = (m.n_layers * (6144 * 4096 + 4096 * 4096 + 3 * 14336 * 4096) + m.vocab * 4096) * 2
+        assert info.weight_bytes == gemv
+    finally:
+        mk.mk_destroy(ctx)
+
+
+def test_graph_is_deterministic(L):
+    hs = []
+    for _ in range(2):
+        ctx = mk.mk_create_host(cfg_for(si.QWEN05B, 35, 35), 256)
+        hs.append(mk.mk_graph_stats(ctx).hash)
+        mk.mk_destroy(ctx)
+    assert hs[0] == hs[1]
+    ctx = mk.mk_create_host(cfg_for(si.QWEN05B, 35, 35), 128)   # different CU count, different graph
+    assert mk.mk_graph_stats(ctx).hash != hs[0]
+    mk.mk_destroy(ctx)
+
+
+@pytest.mark.parametrize("n_cus,splits", [(256, 0), (7, 2), (3, 1), (64, 3)])
+def test_random_interleavings(L, n_cus, splits):
+    ctx = mk.mk_create_host(cfg_for(si.TINY, 3, 3, splits), n_cus)
+    try:
+        for seed in range(12):
+            mk.mk_graph_simulate(ctx, seed, 3)
+    finally:
+        mk.mk_destroy(ctx)
+
+
+def test_interleavings_small_qwen_shape(L):
+    shape = si.shrink(si.QWEN05B, "q-small", n_layers=2, vocab=4096)
+    ctx = mk.mk_create_host(cfg_for(shape, 8, 8), 32)
+    try:
+        for seed in range(4):
+            mk.mk_graph_simulate(ctx, seed, 2)
+    finally:
+        mk.mk_destroy(ctx)
+
+
+def test_rejects_bad_configs(L):
+    bad = [
+        dataclasses.replace(si.TINY, n_q_heads=3),       # not a multiple of kv heads
+        dataclasses.replace(si.TINY, head_dim=96),       # unsupported head dim
+        dataclasses.replace(si.TINY, d_model=250),       # not a multiple of 8
+        dataclasses.replace(si.TINY, n_q_heads=32, n_kv_heads=2),  # 16 q heads per kv head
+    ]
+    for shape in bad:
+        with pytest.raises(mk.MKError) as e:
+            mk.mk_create_host(cfg_for(shape, 4, 4), 256)
+        assert e.value.status == -2
+    c = cfg_for(si.TINY, 4, 4)
+    c.block_size = 32
+    with pytest.raises(mk.MKError):
+        mk.mk_create_host(c, 256)
+    with pytest.raises(mk.MKError) as e:
+        mk.mk_create_host(cfg_for(si.TINY, 4, 4), 0)
+    assert e.value.status == -2
+
+
+def test_host_context_refuses_device_calls(L):
+    ctx = mk.mk_create_host(cfg_for(si.TINY, 3, 3), 16)
+    try:
+        w, kv, s = mk.mk_workspace_size(ctx)
+        assert w > 0 and kv == 3 * 2 * 16 * 64 * 2 and s > 0
+        one = ctypes.c_void_p(256)
+        arr = (ctypes.c_void_p * 2)(256, 256)
+        st = L.mk_bind_memory(ctx, one, arr, arr, one, one, one, one)
+        assert st == -3   # MK_ERR_STATE
+        assert "host-only" in mk.mk_last_error()
+        st = L.mk_decode_step(ctx, one, 1, one, None)
+        assert st == -3
+        assert L.mk_decode_step(ctx, None, 1, one, None) == -1
+        assert L.mk_graph_validate(None) == -1
+        assert mk.mk_status_str(-5) == "MK_ERR_DEVICE_TIMEOUT"
+    finally:
+        mk.mk_destroy(ctx)
