@@ -14,8 +14,9 @@ import subprocess
 import numpy as np
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-_LIB_PATH = os.path.join(_HERE, "liboracle.so")
-_lib = None
+_LIB_PATHS = {"f64": os.path.join(_HERE, "liboracle.so"), "f32": os.path.join(_HERE, "liboracle_f32.so")}
+_LIB_PATH = _LIB_PATHS["f64"]
+_libs = {}
 
 _dp = ctypes.POINTER(ctypes.c_double)
 _u16p = ctypes.c_void_p
@@ -28,23 +29,26 @@ class OrcConfig(ctypes.Structure):
 
 
 def build_lib(force: bool = False) -> str:
+    """Build liboracle.so (fp64) and liboracle_f32.so (fp32 arithmetic, same definition)."""
     src = os.path.join(_HERE, "oracle.c")
     hdr = os.path.join(_HERE, "oracle.h")
     newest = max(os.path.getmtime(src), os.path.getmtime(hdr))
-    if force or not os.path.exists(_LIB_PATH) or os.path.getmtime(_LIB_PATH) < newest:
-        tmp = _LIB_PATH + ".tmp%d" % os.getpid()
-        subprocess.check_call(["gcc", "-O2", "-ffp-contract=off", "-fopenmp", "-fPIC", "-shared", "-Wall", src,
-                               "-o", tmp, "-lm"])
-        os.replace(tmp, _LIB_PATH)
+    for prec, path in _LIB_PATHS.items():
+        if force or not os.path.exists(path) or os.path.getmtime(path) < newest:
+            tmp = path + ".tmp%d" % os.getpid()
+            extra = ["-DORC_FP32"] if prec == "f32" else []
+            subprocess.check_call(["gcc", "-O2", "-ffp-contract=off", "-fopenmp", "-fPIC", "-shared", "-Wall"] + extra
+                                  + [src, "-o", tmp, "-lm"])
+            os.replace(tmp, path)
     return _LIB_PATH
 
 
-def lib():
-    global _lib
-    if _lib is None:
-        if not os.path.exists(_LIB_PATH):
+def lib(precision: str = "f64"):
+    if precision not in _libs:
+        path = _LIB_PATHS[precision]
+        if not os.path.exists(path):
             build_lib()
-        L = ctypes.CDLL(_LIB_PATH)
+        L = ctypes.CDLL(path)
         L.orc_create.restype = ctypes.c_void_p
         L.orc_create.argtypes = [ctypes.POINTER(OrcConfig), ctypes.c_void_p, ctypes.c_int, ctypes.c_int]
         L.orc_destroy.restype = None
@@ -81,8 +85,8 @@ def lib():
         L.orc_threads.argtypes = []
         L.orc_set_threads.restype = None
         L.orc_set_threads.argtypes = [ctypes.c_int]
-        _lib = L
-    return _lib
+        _libs[precision] = L
+    return _libs[precision]
 
 
 def _d(a):
@@ -174,8 +178,9 @@ def set_threads(n):
 class OracleModel:
     """The decode step of one model over n_seqs sequences with max_pos cache positions each."""
 
-    def __init__(self, shape, weights: dict, n_seqs: int = 1, max_pos: int = 64):
+    def __init__(self, shape, weights: dict, n_seqs: int = 1, max_pos: int = 64, precision: str = "f64"):
         self.shape = shape
+        self.L = lib(precision)
         m = shape
         self.cfg = OrcConfig(m.n_layers, m.d_model, m.n_q_heads, m.n_kv_heads, m.head_dim, m.d_ffn, m.vocab,
                              float(m.rms_eps), float(m.rope_theta), int(bool(m.tied_embeddings)),
@@ -196,13 +201,13 @@ class OracleModel:
                 ptrs[i] = a.ctypes.data
         self._ptrs = ptrs
         self.n_seqs, self.max_pos = n_seqs, max_pos
-        self._h = lib().orc_create(ctypes.byref(self.cfg), ctypes.cast(ptrs, ctypes.c_void_p), n_seqs, max_pos)
+        self._h = self.L.orc_create(ctypes.byref(self.cfg), ctypes.cast(ptrs, ctypes.c_void_p), n_seqs, max_pos)
         if not self._h:
             raise ValueError("orc_create rejected the model or could not allocate its cache")
 
     def close(self):
         if self._h:
-            lib().orc_destroy(self._h)
+            self.L.orc_destroy(self._h)
             self._h = None
 
     def __del__(self):
@@ -213,7 +218,7 @@ class OracleModel:
 
     def step(self, seq, token, pos, rope_pos=None):
         logits = np.empty(self.shape.vocab, dtype=np.float64)
-        tok = lib().orc_step(self._h, seq, int(token), pos, float(pos if rope_pos is None else rope_pos), _d(logits))
+        tok = self.L.orc_step(self._h, seq, int(token), pos, float(pos if rope_pos is None else rope_pos), _d(logits))
         if tok < 0:
             raise ValueError("orc_step rejected its arguments")
         return tok, logits
@@ -221,21 +226,21 @@ class OracleModel:
     def set_kv(self, layer, seq, pos0, k, v):
         k = _u16(k); v = _u16(v)
         npos = k.shape[0]
-        if lib().orc_set_kv(self._h, layer, seq, pos0, npos, k.ctypes.data, v.ctypes.data):
+        if self.L.orc_set_kv(self._h, layer, seq, pos0, npos, k.ctypes.data, v.ctypes.data):
             raise ValueError("orc_set_kv rejected its arguments")
 
     def get_kv(self, layer, seq, pos0, npos):
         m = self.shape
         k = np.empty((npos, m.n_kv_heads, m.head_dim), dtype=np.uint16)
         v = np.empty_like(k)
-        if lib().orc_get_kv(self._h, layer, seq, pos0, npos, k.ctypes.data, v.ctypes.data):
+        if self.L.orc_get_kv(self._h, layer, seq, pos0, npos, k.ctypes.data, v.ctypes.data):
             raise ValueError("orc_get_kv rejected its arguments")
         return k, v
 
     def forward_nocache(self, tokens, rope_off=0.0):
         t = np.ascontiguousarray(tokens, dtype=np.int32)
         logits = np.empty(self.shape.vocab, dtype=np.float64)
-        tok = lib().orc_forward_nocache(self._h, t.ctypes.data, t.size, float(rope_off), _d(logits))
+        tok = self.L.orc_forward_nocache(self._h, t.ctypes.data, t.size, float(rope_off), _d(logits))
         if tok < 0:
             raise ValueError("orc_forward_nocache rejected its arguments")
         return tok, logits

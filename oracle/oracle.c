@@ -21,6 +21,20 @@
 #include <stdlib.h>
 #include <string.h>
 
+/* Arithmetic type of every activation and accumulation. The default build is fp64, the
+ * reference for parity. Built with -DORC_FP32 it is fp32 throughout: the same definition in
+ * the precision a GPU computes in. It measures how much fp32 rounding alone moves the results.
+ * Rotary angles are formed in double in both builds, then rounded to `real`. */
+#ifdef ORC_FP32
+typedef float real;
+#define R_SQRT sqrtf
+#define R_EXP expf
+#else
+typedef double real;
+#define R_SQRT sqrt
+#define R_EXP exp
+#endif
+
 struct orc_model {
   orc_config c;
   const uint16_t** t;
@@ -51,46 +65,48 @@ void orc_set_threads(int n) {
   if (n > 0) omp_set_num_threads(n);
 }
 
+static real bf(uint16_t b) { return (real)orc_from_bf16(b); }
+
 /* RMSNorm: out_i = x_i / sqrt(mean_j x_j^2 + eps) * g_i. */
-void orc_rmsnorm(const double* x, const uint16_t* g, int d, double eps, double* out) {
-  double ss = 0.0;
+static void rmsnorm_r(const real* x, const uint16_t* g, int d, real eps, real* out) {
+  real ss = 0;
   for (int i = 0; i < d; ++i) ss += x[i] * x[i];
-  const double r = 1.0 / sqrt(ss / d + eps);
-  for (int i = 0; i < d; ++i) out[i] = x[i] * r * orc_from_bf16(g[i]);
+  const real r = (real)1 / R_SQRT(ss / (real)d + eps);
+  for (int i = 0; i < d; ++i) out[i] = x[i] * r * bf(g[i]);
 }
 
 /* y = W x (+ b), W row-major [n, k]: y_r = sum_c W[r][c] * x[c], summed in column order.
  * The matrix-vector product that dominates decode ([IE] sections 1.2 and 3.2). */
-void orc_gemv(const uint16_t* w, int n, int k, const double* x, const uint16_t* bias, double* y) {
+static void gemv_r(const uint16_t* w, int n, int k, const real* x, const uint16_t* bias, real* y) {
 #pragma omp parallel for schedule(static)
   for (int r = 0; r < n; ++r) {
     const uint16_t* row = w + (size_t)r * k;
-    double s = 0.0;
-    for (int c = 0; c < k; ++c) s += orc_from_bf16(row[c]) * x[c];
-    y[r] = bias ? s + orc_from_bf16(bias[r]) : s;
+    real s = 0;
+    for (int c = 0; c < k; ++c) s += bf(row[c]) * x[c];
+    y[r] = bias ? s + bf(bias[r]) : s;
   }
 }
 
 /* Rotary position embedding, rotate-half pairing: for i < dh/2, angle a = pos * theta^(-2i/dh),
  * (u_i, u_{i+dh/2}) -> (u_i cos a - u_{i+dh/2} sin a, u_{i+dh/2} cos a + u_i sin a). */
-void orc_rope(double* u, int dh, double pos, double theta) {
+static void rope_r(real* u, int dh, double pos, double theta) {
   const int h = dh / 2;
   for (int i = 0; i < h; ++i) {
     const double a = pos * pow(theta, -2.0 * i / dh);
-    const double c = cos(a), s = sin(a);
-    const double x0 = u[i], x1 = u[i + h];
+    const real c = (real)cos(a), s = (real)sin(a);
+    const real x0 = u[i], x1 = u[i + h];
     u[i] = x0 * c - x1 * s;
     u[i + h] = x1 * c + x0 * s;
   }
 }
 
 /* softmax: subtract the max, exponentiate, divide by the sum. */
-void orc_softmax(double* s, int n) {
-  double m = -INFINITY;
+static void softmax_r(real* s, int n) {
+  real m = -INFINITY;
   for (int j = 0; j < n; ++j) m = s[j] > m ? s[j] : m;
-  double z = 0.0;
+  real z = 0;
   for (int j = 0; j < n; ++j) {
-    s[j] = exp(s[j] - m);
+    s[j] = R_EXP(s[j] - m);
     z += s[j];
   }
   for (int j = 0; j < n; ++j) s[j] /= z;
@@ -100,39 +116,93 @@ void orc_softmax(double* s, int n) {
  * several query heads share one K/V pair; query head h reads KV head h / (hq/hk)).
  * kc, vc: [npos][hk][dh] bf16. Scores q.k / sqrt(dh), softmax over positions, weighted sum of V:
  * the plain (materialised-score) attention of [KN], one query row at a time. */
-void orc_attention(const double* q, const uint16_t* kc, const uint16_t* vc, int npos, int hq, int hk, int dh,
-                   double* out) {
+static void attention_r(const real* q, const uint16_t* kc, const uint16_t* vc, int npos, int hq, int hk, int dh,
+                        real* out) {
   const int grp = hq / hk;
-  const double scale = 1.0 / sqrt((double)dh);
+  const real scale = (real)1 / R_SQRT((real)dh);
 #pragma omp parallel for schedule(static)
   for (int h = 0; h < hq; ++h) {
     const int kh = h / grp;
-    double* s = (double*)malloc(sizeof(double) * (size_t)(npos > 0 ? npos : 1));
+    real* s = (real*)malloc(sizeof(real) * (size_t)(npos > 0 ? npos : 1));
     for (int j = 0; j < npos; ++j) {
       const uint16_t* kr = kc + ((size_t)j * hk + kh) * dh;
-      double a = 0.0;
-      for (int i = 0; i < dh; ++i) a += q[(size_t)h * dh + i] * orc_from_bf16(kr[i]);
+      real a = 0;
+      for (int i = 0; i < dh; ++i) a += q[(size_t)h * dh + i] * bf(kr[i]);
       s[j] = a * scale;
     }
-    orc_softmax(s, npos);
-    for (int i = 0; i < dh; ++i) out[(size_t)h * dh + i] = 0.0;
+    softmax_r(s, npos);
+    for (int i = 0; i < dh; ++i) out[(size_t)h * dh + i] = 0;
     for (int j = 0; j < npos; ++j) {
       const uint16_t* vr = vc + ((size_t)j * hk + kh) * dh;
-      for (int i = 0; i < dh; ++i) out[(size_t)h * dh + i] += s[j] * orc_from_bf16(vr[i]);
+      for (int i = 0; i < dh; ++i) out[(size_t)h * dh + i] += s[j] * bf(vr[i]);
     }
     free(s);
   }
 }
 
 /* SiLU(z) = z / (1 + e^-z). */
-double orc_silu(double z) { return z / (1.0 + exp(-z)); }
+static real silu_r(real z) { return z / ((real)1 + R_EXP(-z)); }
 
 /* SwiGLU combination of the gate (a) and up (b) projections: h = silu(a) * b. */
-void orc_swiglu(const double* a, const double* b, int n, double* h) {
-  for (int i = 0; i < n; ++i) h[i] = orc_silu(a[i]) * b[i];
+static void swiglu_r(const real* a, const real* b, int n, real* h) {
+  for (int i = 0; i < n; ++i) h[i] = silu_r(a[i]) * b[i];
 }
 
 /* argmax with the lowest index on ties (greedy decoding). */
+static int argmax_r(const real* v, int n) {
+  int best = 0;
+  for (int i = 1; i < n; ++i)
+    if (v[i] > v[best]) best = i;
+  return best;
+}
+
+/* ---- the pieces with a double interface (for the pins); they compute in `real` */
+static real* to_real(const double* x, int n) {
+  real* r = (real*)malloc(sizeof(real) * (size_t)(n > 0 ? n : 1));
+  for (int i = 0; i < n; ++i) r[i] = (real)x[i];
+  return r;
+}
+static void from_real(const real* r, int n, double* x) {
+  for (int i = 0; i < n; ++i) x[i] = (double)r[i];
+}
+void orc_rmsnorm(const double* x, const uint16_t* g, int d, double eps, double* out) {
+  real* xr = to_real(x, d);
+  real* o = (real*)malloc(sizeof(real) * (size_t)(d > 0 ? d : 1));
+  rmsnorm_r(xr, g, d, (real)eps, o);
+  from_real(o, d, out);
+  free(xr); free(o);
+}
+void orc_gemv(const uint16_t* w, int n, int k, const double* x, const uint16_t* bias, double* y) {
+  real* xr = to_real(x, k);
+  real* yr = (real*)malloc(sizeof(real) * (size_t)(n > 0 ? n : 1));
+  gemv_r(w, n, k, xr, bias, yr);
+  from_real(yr, n, y);
+  free(xr); free(yr);
+}
+void orc_rope(double* u, int dh, double pos, double theta) {
+  real* r = to_real(u, dh);
+  rope_r(r, dh, pos, theta);
+  from_real(r, dh, u);
+  free(r);
+}
+void orc_softmax(double* s, int n) {
+  real* r = to_real(s, n);
+  softmax_r(r, n);
+  from_real(r, n, s);
+  free(r);
+}
+void orc_attention(const double* q, const uint16_t* kc, const uint16_t* vc, int npos, int hq, int hk, int dh,
+                   double* out) {
+  real* qr = to_real(q, hq * dh);
+  real* o = (real*)malloc(sizeof(real) * (size_t)(hq * dh > 0 ? hq * dh : 1));
+  attention_r(qr, kc, vc, npos, hq, hk, dh, o);
+  from_real(o, hq * dh, out);
+  free(qr); free(o);
+}
+double orc_silu(double z) { return (double)silu_r((real)z); }
+void orc_swiglu(const double* a, const double* b, int n, double* h) {
+  for (int i = 0; i < n; ++i) h[i] = (double)silu_r((real)a[i]) * (real)b[i];
+}
 int orc_argmax(const double* v, int n) {
   int best = 0;
   for (int i = 1; i < n; ++i)
@@ -214,42 +284,45 @@ int orc_get_kv(const orc_model* m, int layer, int seq, int pos0, int npos, uint1
 }
 
 /* Final RMSNorm, LM head and greedy argmax. */
-static int lm_head(const orc_model* m, const double* x, double* logits) {
+static int lm_head(const orc_model* m, const real* x, double* logits) {
   const orc_config* c = &m->c;
-  double* xn = (double*)malloc(sizeof(double) * c->d);
-  orc_rmsnorm(x, T_FNORM(m), c->d, c->eps, xn);
-  orc_gemv(lm_weight(m), c->v, c->d, xn, NULL, logits);
-  free(xn);
-  return orc_argmax(logits, c->v);
+  real* xn = (real*)malloc(sizeof(real) * c->d);
+  real* lg = (real*)malloc(sizeof(real) * c->v);
+  rmsnorm_r(x, T_FNORM(m), c->d, (real)c->eps, xn);
+  gemv_r(lm_weight(m), c->v, c->d, xn, NULL, lg);
+  from_real(lg, c->v, logits);
+  const int tok = argmax_r(lg, c->v);
+  free(xn); free(lg);
+  return tok;
 }
 
 /* SwiGLU feed-forward with residual: x += Wd (silu(Wg xn) * (Wu xn)), xn = RMSNorm(x, g_ffn). */
-static void ffn_block(const orc_model* m, int l, double* x) {
+static void ffn_block(const orc_model* m, int l, real* x) {
   const orc_config* c = &m->c;
-  double* xn = (double*)malloc(sizeof(double) * c->d);
-  double* a = (double*)malloc(sizeof(double) * c->f);
-  double* b = (double*)malloc(sizeof(double) * c->f);
-  double* h = (double*)malloc(sizeof(double) * c->f);
-  double* y = (double*)malloc(sizeof(double) * c->d);
-  orc_rmsnorm(x, T_LAYER(m, l, L_FNORM), c->d, c->eps, xn);
-  orc_gemv(T_LAYER(m, l, L_WG), c->f, c->d, xn, NULL, a);
-  orc_gemv(T_LAYER(m, l, L_WU), c->f, c->d, xn, NULL, b);
-  orc_swiglu(a, b, c->f, h);
-  orc_gemv(T_LAYER(m, l, L_WD), c->d, c->f, h, NULL, y);
+  real* xn = (real*)malloc(sizeof(real) * c->d);
+  real* a = (real*)malloc(sizeof(real) * c->f);
+  real* b = (real*)malloc(sizeof(real) * c->f);
+  real* h = (real*)malloc(sizeof(real) * c->f);
+  real* y = (real*)malloc(sizeof(real) * c->d);
+  rmsnorm_r(x, T_LAYER(m, l, L_FNORM), c->d, (real)c->eps, xn);
+  gemv_r(T_LAYER(m, l, L_WG), c->f, c->d, xn, NULL, a);
+  gemv_r(T_LAYER(m, l, L_WU), c->f, c->d, xn, NULL, b);
+  swiglu_r(a, b, c->f, h);
+  gemv_r(T_LAYER(m, l, L_WD), c->d, c->f, h, NULL, y);
   for (int i = 0; i < c->d; ++i) x[i] += y[i];
   free(xn); free(a); free(b); free(h); free(y);
 }
 
 /* QKV projection of the normed input, plus rotary embedding of every q and k head. */
-static void qkv_rope(const orc_model* m, int l, const double* x, double rope_pos, double* q, double* k, double* v) {
+static void qkv_rope(const orc_model* m, int l, const real* x, double rope_pos, real* q, real* k, real* v) {
   const orc_config* c = &m->c;
-  double* xn = (double*)malloc(sizeof(double) * c->d);
-  orc_rmsnorm(x, T_LAYER(m, l, L_ANORM), c->d, c->eps, xn);
-  orc_gemv(T_LAYER(m, l, L_WQ), c->hq * c->dh, c->d, xn, T_LAYER(m, l, L_BQ), q);
-  orc_gemv(T_LAYER(m, l, L_WK), c->hk * c->dh, c->d, xn, T_LAYER(m, l, L_BK), k);
-  orc_gemv(T_LAYER(m, l, L_WV), c->hk * c->dh, c->d, xn, T_LAYER(m, l, L_BV), v);
-  for (int h = 0; h < c->hq; ++h) orc_rope(q + (size_t)h * c->dh, c->dh, rope_pos, c->theta);
-  for (int h = 0; h < c->hk; ++h) orc_rope(k + (size_t)h * c->dh, c->dh, rope_pos, c->theta);
+  real* xn = (real*)malloc(sizeof(real) * c->d);
+  rmsnorm_r(x, T_LAYER(m, l, L_ANORM), c->d, (real)c->eps, xn);
+  gemv_r(T_LAYER(m, l, L_WQ), c->hq * c->dh, c->d, xn, T_LAYER(m, l, L_BQ), q);
+  gemv_r(T_LAYER(m, l, L_WK), c->hk * c->dh, c->d, xn, T_LAYER(m, l, L_BK), k);
+  gemv_r(T_LAYER(m, l, L_WV), c->hk * c->dh, c->d, xn, T_LAYER(m, l, L_BV), v);
+  for (int h = 0; h < c->hq; ++h) rope_r(q + (size_t)h * c->dh, c->dh, rope_pos, c->theta);
+  for (int h = 0; h < c->hk; ++h) rope_r(k + (size_t)h * c->dh, c->dh, rope_pos, c->theta);
   free(xn);
 }
 
@@ -261,14 +334,14 @@ int orc_step(orc_model* m, int seq, int token, int pos, double rope_pos, double*
   if (!logits || seq < 0 || seq >= m->n_seqs || token < 0 || token >= c->v || pos < 0 || pos >= m->max_pos)
     return -1;
   const int qd = c->hq * c->dh, kd = c->hk * c->dh;
-  double* x = (double*)malloc(sizeof(double) * c->d);
-  double* q = (double*)malloc(sizeof(double) * qd);
-  double* k = (double*)malloc(sizeof(double) * kd);
-  double* v = (double*)malloc(sizeof(double) * kd);
-  double* o = (double*)malloc(sizeof(double) * qd);
-  double* y = (double*)malloc(sizeof(double) * c->d);
+  real* x = (real*)malloc(sizeof(real) * c->d);
+  real* q = (real*)malloc(sizeof(real) * qd);
+  real* k = (real*)malloc(sizeof(real) * kd);
+  real* v = (real*)malloc(sizeof(real) * kd);
+  real* o = (real*)malloc(sizeof(real) * qd);
+  real* y = (real*)malloc(sizeof(real) * c->d);
   /* embedding lookup: token id -> its row of E ([IE] section 1.1) */
-  for (int i = 0; i < c->d; ++i) x[i] = orc_from_bf16(T_EMBED(m)[(size_t)token * c->d + i]);
+  for (int i = 0; i < c->d; ++i) x[i] = bf(T_EMBED(m)[(size_t)token * c->d + i]);
   for (int l = 0; l < c->n_layers; ++l) {
     qkv_rope(m, l, x, rope_pos, q, k, v);
     /* append this position's key and value to the cache in its bf16 storage format */
@@ -279,8 +352,8 @@ int orc_step(orc_model* m, int seq, int token, int pos, double rope_pos, double*
       vr[i] = orc_bf16(v[i]);
     }
     /* attend to positions 0..pos, the current one included */
-    orc_attention(q, m->kc + kv_index(m, l, seq, 0), m->vc + kv_index(m, l, seq, 0), pos + 1, c->hq, c->hk, c->dh, o);
-    orc_gemv(T_LAYER(m, l, L_WO), c->d, qd, o, NULL, y);
+    attention_r(q, m->kc + kv_index(m, l, seq, 0), m->vc + kv_index(m, l, seq, 0), pos + 1, c->hq, c->hk, c->dh, o);
+    gemv_r(T_LAYER(m, l, L_WO), c->d, qd, o, NULL, y);
     for (int i = 0; i < c->d; ++i) x[i] += y[i];
     ffn_block(m, l, x);
   }
@@ -299,16 +372,16 @@ int orc_forward_nocache(const orc_model* m, const int* tokens, int n, double rop
   for (int t = 0; t < n; ++t)
     if (tokens[t] < 0 || tokens[t] >= c->v) return -1;
   const int qd = c->hq * c->dh, kd = c->hk * c->dh;
-  double* X = (double*)malloc(sizeof(double) * (size_t)n * c->d);
-  double* Q = (double*)malloc(sizeof(double) * (size_t)n * qd);
+  real* X = (real*)malloc(sizeof(real) * (size_t)n * c->d);
+  real* Q = (real*)malloc(sizeof(real) * (size_t)n * qd);
   uint16_t* K = (uint16_t*)malloc(2 * (size_t)n * kd);
   uint16_t* V = (uint16_t*)malloc(2 * (size_t)n * kd);
-  double* k = (double*)malloc(sizeof(double) * kd);
-  double* v = (double*)malloc(sizeof(double) * kd);
-  double* o = (double*)malloc(sizeof(double) * qd);
-  double* y = (double*)malloc(sizeof(double) * c->d);
+  real* k = (real*)malloc(sizeof(real) * kd);
+  real* v = (real*)malloc(sizeof(real) * kd);
+  real* o = (real*)malloc(sizeof(real) * qd);
+  real* y = (real*)malloc(sizeof(real) * c->d);
   for (int t = 0; t < n; ++t)
-    for (int i = 0; i < c->d; ++i) X[(size_t)t * c->d + i] = orc_from_bf16(T_EMBED(m)[(size_t)tokens[t] * c->d + i]);
+    for (int i = 0; i < c->d; ++i) X[(size_t)t * c->d + i] = bf(T_EMBED(m)[(size_t)tokens[t] * c->d + i]);
   for (int l = 0; l < c->n_layers; ++l) {
     for (int t = 0; t < n; ++t) {
       qkv_rope(m, l, X + (size_t)t * c->d, rope_off + t, Q + (size_t)t * qd, k, v);
@@ -318,8 +391,8 @@ int orc_forward_nocache(const orc_model* m, const int* tokens, int n, double rop
       }
     }
     for (int t = 0; t < n; ++t) {
-      orc_attention(Q + (size_t)t * qd, K, V, t + 1, c->hq, c->hk, c->dh, o);
-      orc_gemv(T_LAYER(m, l, L_WO), c->d, qd, o, NULL, y);
+      attention_r(Q + (size_t)t * qd, K, V, t + 1, c->hq, c->hk, c->dh, o);
+      gemv_r(T_LAYER(m, l, L_WO), c->d, qd, o, NULL, y);
       for (int i = 0; i < c->d; ++i) X[(size_t)t * c->d + i] += y[i];
       ffn_block(m, l, X + (size_t)t * c->d);
     }

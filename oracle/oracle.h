@@ -3,8 +3,11 @@
  * INFRASTRUCTURE ONLY. Only tests, the smoke check and the benchmark's CPU
  * baseline may load it. The HIP path never links, includes or calls it.
  *
- * Plain, slow and obviously correct. Every activation is a double. Weights and
- * the KV cache are bf16 bit patterns (uint16_t) read exactly as double.
+ * Plain, slow and obviously correct. Every activation is a double in the default
+ * build (liboracle.so), the parity reference. A second build with -DORC_FP32
+ * (liboracle_f32.so) computes the same definition in fp32 throughout; it measures
+ * how far fp32 rounding alone moves the results. The interface is double in both.
+ * Weights and the KV cache are bf16 bit patterns (uint16_t), read exactly.
  * Loops run in a fixed order, so results do not depend on the thread count
  * (OpenMP splits only independent rows and heads).
  *

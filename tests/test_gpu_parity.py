@@ -1,7 +1,8 @@
 """GPU parity: the HIP megakernel against the oracle, element by element, teacher-forced.
 
-Bars: logits within 5e-3 relative L2 at every step (fp32 device vs fp64 oracle, measured
-near 1e-6, so anything above 1e-4 also fails as a bug); the device token equals the
+Bars: logits within 5e-3 relative L2 at every step; and no further from the fp64 oracle
+than twice the oracle's own fp32 build on the same steps (floor 1e-5), since the device
+computes in fp32 and deep random models amplify fp32 rounding; the device token equals the
 argmax of the device's own logits on every step (integer, exact); device token equals
 the oracle's greedy token on >= 99% of steps, and every disagreement is a near-tie of
 the oracle (top-2 gap below 1e-3 of the logit scale).  Integer work (page slots, KV
@@ -16,7 +17,7 @@ import pytest
 import oracle as orc
 import persistent_megakernel_03_amd as mk
 import seeded_inputs as si
-from parity_util import BUG_BAR, REL_L2_BAR, gpu_step, make_gpu, rel_l2, teacher_forced
+from parity_util import REL_L2_BAR, bug_bar, gpu_step, make_gpu, rel_l2, teacher_forced
 
 pytestmark = pytest.mark.gpu
 
@@ -28,9 +29,10 @@ def log(*a):
 
 def check(res, name):
     rel = np.array(res["rel"])
-    log("%s: steps %d max rel L2 %.3e mean %.3e" % (name, len(rel), rel.max(), rel.mean()))
+    log("%s: steps %d max rel L2 %.3e mean %.3e (fp32 oracle vs fp64: max %.3e)" %
+        (name, len(rel), rel.max(), rel.mean(), max(res["rel_f32"]) if res["rel_f32"] else float("nan")))
     assert rel.max() <= REL_L2_BAR
-    assert rel.max() <= BUG_BAR, "fp32 path far from the fp64 oracle"
+    assert rel.max() <= bug_bar(res), "less accurate than a plain fp32 evaluation of the same definition"
     assert all(res["self_argmax"])
     dev, ref, gaps = np.array(res["dev_tok"]), np.array(res["orc_tok"]), np.array(res["gaps"])
     agree = float((dev == ref).mean())
@@ -63,9 +65,16 @@ def test_tiny_teacher_forced(tiny):
         kg = np.stack([kp[tab[p // 16], :, p % 16] for p in range(n)])
         vg = np.stack([vp[tab[p // 16], :, p % 16] for p in range(n)])
         for g, r in ((kg, k_ref), (vg, v_ref)):
-            diff = np.abs(g.astype(np.int32) - r.astype(np.int32))
-            assert (diff <= 1).all()                   # at most one bf16 ulp (fp32 vs fp64 rounding)
-            assert (diff == 0).mean() > 0.99
+            gf, rf = orc.bf16_to_f64(g), orc.bf16_to_f64(r)
+            err = np.abs(gf - rf)
+            # one bf16 ulp of the element, plus the fp32 path's error relative to the head row's scale
+            # (near-cancelling elements carry an absolute error of ~1e-7 of the row, above their own ulp)
+            scale = np.abs(rf).max(axis=-1, keepdims=True)
+            ulp = np.maximum(np.abs(rf), np.abs(gf)) * 2.0 ** -7 + 1e-5 * scale
+            worst = int(np.argmax(err - ulp))
+            log("layer %d: KV equal %.4f, worst |diff| %.3e at value %.3e" % (l, (g == r).mean(), err.flat[worst], rf.flat[worst]))
+            assert (err <= ulp + 1e-30).all()
+            assert (g == r).mean() > 0.99
     dec.close()
 
 
@@ -190,4 +199,17 @@ def test_qwen_shape_teacher_forced():
     prompt = si.prompt_tokens(wl)
     res = teacher_forced(m, w, prompt, 8, n_positions=wl.prompt_len + wl.steps)
     check(res, "qwen0.5b")
+    res["dec"].close()
+
+
+def test_llama8b_full_size_teacher_forced():
+    # the 8B shape at full size, in the launch configuration the benchmark times
+    # (cache capacity 39 + 512 positions): prompt 39 + 3 greedy steps against the oracle
+    wl = si.WORKLOADS["llama8b"]
+    m = wl.model
+    log("case: llama8b full size, prompt 39 + 3 decode (weights ~16 GB)")
+    w = si.gen_weights(m)
+    prompt = si.prompt_tokens(wl)
+    res = teacher_forced(m, w, prompt, 3, n_positions=wl.prompt_len + wl.steps)
+    check(res, "llama8b")
     res["dec"].close()
