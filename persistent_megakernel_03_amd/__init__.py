@@ -51,7 +51,7 @@ class mk_graph_info(ctypes.Structure):
 
 EXPORTS = ["mk_create", "mk_create_host", "mk_workspace_size", "mk_bind_memory", "mk_load_weights", "mk_decode_step",
            "mk_prefill", "mk_read_logits", "mk_sync_check", "mk_graph_stats", "mk_graph_validate",
-           "mk_graph_simulate", "mk_destroy", "mk_status_str", "mk_last_error"]
+           "mk_graph_simulate", "mk_set_trace", "mk_destroy", "mk_status_str", "mk_last_error"]
 
 
 def build(force: bool = True) -> str:
@@ -89,6 +89,7 @@ def lib():
             "mk_graph_stats": [vp, ctypes.POINTER(mk_graph_info)],
             "mk_graph_validate": [vp],
             "mk_graph_simulate": [vp, ctypes.c_uint64, ctypes.c_int],
+            "mk_set_trace": [vp, vp, sz],
         }
         for name, args in sig.items():
             f = getattr(L, name)
@@ -191,6 +192,10 @@ def mk_graph_simulate(ctx, seed: int, n_steps: int):
     _check(lib().mk_graph_simulate(ctx, seed, n_steps))
 
 
+def mk_set_trace(ctx, buf, nbytes):
+    _check(lib().mk_set_trace(ctx, _vp(buf), nbytes))
+
+
 def mk_destroy(ctx):
     lib().mk_destroy(ctx)
 
@@ -268,6 +273,20 @@ class Decoder:
 
     def sync_check(self):
         mk_sync_check(self.ctx, self.stream_ptr())
+
+    def enable_trace(self):
+        n = mk_graph_stats(self.ctx).n_tasks
+        self.trace_buf = self.torch.zeros(n * 32, dtype=self.torch.uint8, device=self.dev)
+        mk_set_trace(self.ctx, self.trace_buf, n * 32)
+
+    def read_trace(self):
+        """Per-task records of the last step: structured numpy array (t_queue, t_ready, t_done, cu, type,
+        layer, epoch), indexed by the task's position in the global order."""
+        import numpy as np
+        self.torch.cuda.synchronize(self.dev)
+        dt = np.dtype([("t_queue", "<u8"), ("t_ready", "<u8"), ("t_done", "<u8"), ("cu", "<u2"), ("type", "u1"),
+                       ("layer", "u1"), ("epoch", "<u4")])
+        return self.trace_buf.cpu().numpy().view(dt)
 
     def close(self):
         if self.ctx:

@@ -18,7 +18,7 @@
 
 namespace mk {
 hipError_t launch_megakernel(const KernelParams& p, int grid, size_t lds_bytes, hipStream_t stream);
-hipError_t megakernel_occupancy(int* blocks_per_cu, size_t lds_bytes);
+hipError_t megakernel_occupancy(int* blocks_per_cu, size_t lds_bytes, int dh, int hq, int hk);
 hipError_t launch_repack(const RepackArgs& a, int64_t units, hipStream_t stream);
 hipError_t launch_repack_bias(const uint16_t* bq, const uint16_t* bk, const uint16_t* bv, int G, int dh, int nrows,
                               uint16_t* out, hipStream_t stream);
@@ -38,6 +38,7 @@ struct mk_ctx {
   float* d_logits = nullptr;
   uint32_t epoch = 0;
   uint32_t watchdog_ticks = 200000000u;  // 2 s at 100 MHz
+  TraceRec* d_trace = nullptr;
 };
 
 namespace {
@@ -167,6 +168,8 @@ KernelParams make_params(mk_ctx* c) {
   p.n_lm_parts = g.n_lm_parts;
   p.max_pos = g.max_pos;
   p.watchdog_ticks = c->watchdog_ticks;
+  p.max_queue = g.max_queue;
+  p.trace = c->d_trace;
   return p;
 }
 
@@ -198,7 +201,9 @@ mk_status mk_create(const mk_model_config* cfg, int device, mk_ctx** out) {
   (*out)->device = device;
   DeviceGuard dg(device);
   int blocks = 0;
-  if (megakernel_occupancy(&blocks, (size_t)(*out)->g.lds_bytes) != hipSuccess || blocks < 1) {
+  if (megakernel_occupancy(&blocks, (size_t)(*out)->g.lds_bytes, cfg->head_dim, cfg->n_q_heads, cfg->n_kv_heads) !=
+          hipSuccess ||
+      blocks < 1) {
     mk_destroy(*out);
     *out = nullptr;
     return fail(MK_ERR_UNSUPPORTED, "one workgroup per CU does not fit (LDS or registers)");
@@ -399,6 +404,18 @@ mk_status mk_sync_check(mk_ctx* c, void* stream) {
   if (!c->bound) return fail(MK_ERR_STATE, "memory not bound");
   DeviceGuard dg(c->device);
   return read_error_word(c, (hipStream_t)stream);
+}
+
+mk_status mk_set_trace(mk_ctx* c, void* d_buf, size_t bytes) {
+  if (!c) return fail(MK_ERR_INVALID_ARG, "null context");
+  if (!d_buf) {
+    c->d_trace = nullptr;
+    return MK_OK;
+  }
+  if (bytes < c->g.tasks.size() * sizeof(TraceRec)) return fail(MK_ERR_INVALID_ARG, "trace buffer too small");
+  if (((uintptr_t)d_buf & 31) != 0) return fail(MK_ERR_INVALID_ARG, "trace buffer must be 32-byte aligned");
+  c->d_trace = (TraceRec*)d_buf;
+  return MK_OK;
 }
 
 mk_status mk_graph_stats(const mk_ctx* c, mk_graph_info* out) {

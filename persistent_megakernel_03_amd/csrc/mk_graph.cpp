@@ -137,7 +137,9 @@ std::string build_graph(const mk_model_config& c, int n_cus, HostGraph& g) {
   if (c.attn_splits > 0) {
     g.splits = c.attn_splits;
   } else {
-    int sp = (c.max_blocks_per_seq + 3) / 4;
+    // about one staged chunk of positions per split (8 waves x 64/(dh/8) positions x 4 slots)
+    const int chunk_blocks = 8 * (64 / (dh / 8)) * 4 / 16;
+    int sp = (c.max_blocks_per_seq + chunk_blocks - 1) / chunk_blocks;
     sp = std::min(sp, 32);
     sp = std::min(sp, std::max(1, 2 * n_cus / (S * hk)));
     g.splits = std::max(1, sp);
@@ -312,6 +314,10 @@ std::string build_graph(const mk_model_config& c, int n_cus, HostGraph& g) {
   }
   g.n_flag_slots = slot;
   for (size_t t = 0; t < g.tasks.size(); ++t) {
+    if (g.tasks[t].wait_ev >= 0) {
+      g.tasks[t].wait_slot0 = g.events[g.tasks[t].wait_ev].slot0;
+      g.tasks[t].wait_nslots = g.events[g.tasks[t].wait_ev].nslots;
+    }
     g.tasks[t].sig_off = (int32_t)g.sig_slots.size();
     g.tasks[t].sig_n = (int32_t)b.task_sig[t].size();
     for (auto& s : b.task_sig[t]) g.sig_slots.push_back(g.events[s.first].slot0 + s.second);
@@ -361,8 +367,19 @@ std::string build_graph(const mk_model_config& c, int n_cus, HostGraph& g) {
   int64_t xs = 0;
   for (int i = 0; i < G_COUNT; ++i) xs = std::max<int64_t>(xs, (int64_t)g.geoms[i].S * g.geoms[i].lpr * 8);
   const int64_t gemv_lds = xs * 4 + (int64_t)align_up(max_task_rows, 64) * 4 * S + 1024;
-  const int64_t attn_lds = (int64_t)G * 512 * 4 /* scores chunk */ + (int64_t)8 * G * dh * 4 /* per-wave o */;
-  g.lds_bytes = align_up(std::max(gemv_lds, attn_lds), 256) + 1024;  // + control block
+  // attention: scores of one register chunk (8 waves x 64/(dh/8) positions x 8 slots), per-wave
+  // partial outputs and the staged queries
+  // attention: K and V staging (4 slots x 8 waves x 1 KB each), the scores of one chunk
+  // (8 waves x 64/(dh/8) positions x 4 slots), per-wave partial outputs and the staged queries
+  const int64_t attn_chunk = (int64_t)8 * (64 / (dh / 8)) * 4;
+  const int64_t attn_lds = (int64_t)2 * 4 * 8 * 1024 + (int64_t)G * attn_chunk * 4 + (int64_t)8 * G * dh * 4 +
+                           (int64_t)G * dh * 4;
+  int max_q = 0;
+  for (int cu = 0; cu < n_cus; ++cu) max_q = std::max(max_q, g.queue_off[cu + 1] - g.queue_off[cu]);
+  g.max_queue = max_q;
+  // control block + this CU's task descriptors + the larger of the GEMV and attention working sets
+  g.lds_bytes = 1024 + align_up((int64_t)2 * L * 8, 256) + align_up((int64_t)max_q * (int64_t)sizeof(TaskDesc), 256) +
+                align_up(std::max(gemv_lds, attn_lds), 256);
   if (g.lds_bytes > 160 * 1024) return "working set exceeds 160 KB of LDS";
   return "";
 }
@@ -411,6 +428,7 @@ std::string validate_graph(const HostGraph& g) {
     if (e < 0) continue;
     const EventDesc& ev = g.events[e];
     if (ev.nslots <= 0) return "event with no producers";
+    if (g.tasks[t].wait_slot0 != ev.slot0 || g.tasks[t].wait_nslots != ev.nslots) return "task's copy of its event differs";
     for (int s = ev.slot0; s < ev.slot0 + ev.nslots; ++s)
       if (last_writer_task[s] >= t) return "task " + std::to_string(t) + " waits on a later producer";
   }

@@ -45,7 +45,7 @@ struct TaskDesc {       // 64 bytes; read with scalar loads
   int32_t geom;         // GEMV: GeomIndex
   int64_t wofs;         // GEMV: byte offset of the tile in the packed weights
   int32_t a0, a1, a2, a3;  // ATTN: seq, kv head, split, counter | LMHEAD: part index | ARGMAX: seq
-  int32_t pad[2];
+  int32_t wait_slot0, wait_nslots;  // the wait event's flag slots (copied from events[wait_ev])
 };
 static_assert(sizeof(TaskDesc) == 64, "TaskDesc is 64 bytes");
 
@@ -73,6 +73,18 @@ struct WeightLayout {
 // Device error word layout (uint32 slots in scratch).
 enum ErrSlot : int32_t { E_CODE = 0, E_INFO0 = 1, E_INFO1 = 2, E_ABORT = 3, E_COUNT = 16 };
 enum ErrCode : uint32_t { ERR_NONE = 0, ERR_TOKEN = 1, ERR_PAGE = 2, ERR_TIMEOUT = 3, ERR_CTX = 4 };
+
+// One task's timestamps (s_memrealtime, 100 MHz), written when tracing is on.
+struct TraceRec {
+  uint64_t t_queue;   // the CU reached the task in its queue
+  uint64_t t_ready;   // its input event was satisfied
+  uint64_t t_done;    // its outputs were published
+  uint16_t cu;
+  uint8_t type;       // TaskType
+  uint8_t layer;      // layer index (n_layers for the LM head and argmax), mod 256
+  uint32_t epoch;
+};
+static_assert(sizeof(TraceRec) == 32, "TraceRec is 32 bytes");
 
 // Everything the megakernel reads, passed by value.
 struct KernelParams {
@@ -108,6 +120,8 @@ struct KernelParams {
   int32_t max_seqs, n_active, max_blocks, num_blocks, block_size, splits, n_lm_parts, max_pos;
   uint32_t epoch;
   uint32_t watchdog_ticks;    // s_memrealtime ticks (100 MHz) a wait may spin before the kernel aborts
+  int32_t max_queue;          // longest per-CU queue (its descriptors are staged in LDS)
+  TraceRec* trace;            // per-task timestamps of the last step, or nullptr
 };
 
 // Arguments of the weight re-layout kernel: one stage's tasks [task0, task0 + ntasks), whose

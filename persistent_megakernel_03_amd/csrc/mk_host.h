@@ -27,6 +27,7 @@ struct HostGraph {
   int max_pos = 0;
   int n_counters = 0;
   int n_lm_parts = 0;
+  int max_queue = 0;
   int64_t lds_bytes = 0;
   GemvGeom geoms[G_COUNT]{};
   std::vector<TaskDesc> tasks;               // global topological order

@@ -53,6 +53,15 @@ __device__ __forceinline__ uint32_t f2bf(float f) {
 
 __device__ __forceinline__ void wait_stores() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 
+// Workgroup barrier that orders LDS only. __syncthreads() also carries a workgroup release fence,
+// which waits for every outstanding global load (vmcnt(0)) and would stall the weight prefetch
+// in flight across task boundaries. Global memory is ordered explicitly in this kernel: a wave
+// waits for its own stores (wait_stores) before any flag is published, and cross-CU data is read
+// with agent-scope loads issued after the flags were observed.
+__device__ __forceinline__ void bar() {
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
 __device__ __forceinline__ float wave_sum(float v) {
 #pragma unroll
   for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off);
@@ -66,6 +75,8 @@ __device__ __forceinline__ float wave_max(float v) {
 
 // Small control block at the start of LDS.
 struct Ctl {
+  GemvGeom geoms[G_COUNT];  // copied once per launch
+  int32_t ctx[16];          // context lengths of the first 16 sequences, read once per launch
   float red[NW * 8];
   float m_run[16], l_run[16], scale[16];
   uint32_t flag;
@@ -76,9 +87,9 @@ struct Ctl {
 __device__ __forceinline__ float block_sum(float v, Ctl* ctl) {
   v = wave_sum(v);
   const int w = threadIdx.x >> 6, l = threadIdx.x & 63;
-  __syncthreads();
+  bar();
   if (l == 0) ctl->red[w] = v;
-  __syncthreads();
+  bar();
   float s = 0.f;
 #pragma unroll
   for (int i = 0; i < NW; ++i) s += ctl->red[i];
@@ -97,21 +108,20 @@ __device__ void raise_error(const KernelParams& p, uint32_t code, uint32_t a, ui
 // ----------------------------------------------------------------------------- events
 // Wave 0 polls every producer flag of the event until all hold >= epoch. A watchdog on the
 // 100 MHz real-time counter turns a wait that never ends into an error and a kernel-wide abort.
-__device__ void wait_event(const KernelParams& p, int ev, Ctl* ctl) {
+__device__ __forceinline__ void wait_event(const KernelParams& p, const TaskDesc& t, Ctl* ctl) {
   if (threadIdx.x < 64) {
-    const EventDesc e = p.events[ev];
     const uint64_t t0 = __builtin_amdgcn_s_memrealtime();
     const int lane = threadIdx.x;
     uint32_t ab = 0;
     while (true) {
       bool ok = true;
-      for (int i = lane; i < e.nslots; i += 64) ok = ok && (ldc(&p.flags[e.slot0 + i]) >= p.epoch);
+      for (int i = lane; i < t.wait_nslots; i += 64) ok = ok && (ldc(&p.flags[t.wait_slot0 + i]) >= p.epoch);
       if (__all(ok)) break;
       ab = ldc(&p.err[E_ABORT]);
       if (ab) break;
       if (__builtin_amdgcn_s_memrealtime() - t0 > p.watchdog_ticks) {
         if (lane == 0) {
-          raise_error(p, ERR_TIMEOUT, (uint32_t)ev, p.epoch);
+          raise_error(p, ERR_TIMEOUT, (uint32_t)t.wait_ev, p.epoch);
           stc(&p.err[E_ABORT], 1u);
         }
         ab = 1;
@@ -121,14 +131,15 @@ __device__ void wait_event(const KernelParams& p, int ev, Ctl* ctl) {
     }
     if (lane == 0) ctl->aborted = ab;
   }
-  __syncthreads();
+  bar();
 }
 
-// Every wave waits for its own stores, then one lane per slot publishes the epoch.
-__device__ void signal_slots(const KernelParams& p, const TaskDesc& t) {
-  wait_stores();
-  __syncthreads();
-  if ((int)threadIdx.x < t.sig_n) stc(&p.flags[p.sig_slots[t.sig_off + threadIdx.x]], p.epoch);
+// Publishing a finished task: every wave waits for its own stores, the workgroup meets at a
+// barrier, and then one lane per slot stores the epoch. `my_sig` is this thread's slot (loaded
+// when the task started, so no load sits on the publish path), or -1. Only wave 0 holds slots
+// (a task has at most 64).
+__device__ __forceinline__ void publish(const KernelParams& p, int my_sig) {
+  if (my_sig >= 0) stc(&p.flags[my_sig], p.epoch);
 }
 
 // ----------------------------------------------------------------------------- GEMV tile
@@ -136,83 +147,232 @@ __device__ void signal_slots(const KernelParams& p, const TaskDesc& t) {
 // the 8 waves. Each wave streams its contiguous run of 1 KB units with nontemporal dwordx4
 // loads, two batches of UB units in flight. The xs entries past K are zero, and so are the
 // padded weights.
-__device__ __forceinline__ void unit_fma(const v4u w, const float* xp, float& acc) {
-  const v4f a = *(const v4f*)xp;
-  const v4f b = *(const v4f*)(xp + 4);
-  acc = fmaf(bf_lo(w.x), a.x, acc);
-  acc = fmaf(bf_hi(w.x), a.y, acc);
-  acc = fmaf(bf_lo(w.y), a.z, acc);
-  acc = fmaf(bf_hi(w.y), a.w, acc);
-  acc = fmaf(bf_lo(w.z), b.x, acc);
-  acc = fmaf(bf_hi(w.z), b.y, acc);
-  acc = fmaf(bf_lo(w.w), b.z, acc);
-  acc = fmaf(bf_hi(w.w), b.w, acc);
+// The GEMV input vector sits in LDS as two planes: plane A holds elements 8p..8p+3 of every
+// 16-byte weight piece p at A[4p..4p+3], plane B holds 8p+4..8p+7 at B[4p..4p+3]. Lanes that
+// read consecutive pieces then read consecutive 16-byte words of each plane, free of bank
+// conflicts (a plain [K] layout puts lanes 32 bytes apart: an 8-way conflict).
+__device__ __forceinline__ int xs_index(int i, int npieces) {
+  const int p = i >> 3, e = i & 7;
+  return (e < 4) ? (p << 2) + e : (npieces << 2) + (p << 2) + (e - 4);
 }
 
-__device__ void gemv_tile(const KernelParams& p, const TaskDesc& t, const GemvGeom gm, const float* xs, float* ys) {
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+__device__ __forceinline__ void unit_fma(const v4u w, const float* xa, const float* xb, float& acc0, float& acc1) {
+  const v4f a = *(const v4f*)xa;
+  const v4f b = *(const v4f*)xb;
+  acc0 = fmaf(bf_lo(w.x), a.x, acc0);
+  acc1 = fmaf(bf_hi(w.x), a.y, acc1);
+  acc0 = fmaf(bf_lo(w.y), a.z, acc0);
+  acc1 = fmaf(bf_hi(w.y), a.w, acc1);
+  acc0 = fmaf(bf_lo(w.z), b.x, acc0);
+  acc1 = fmaf(bf_hi(w.z), b.y, acc1);
+  acc0 = fmaf(bf_lo(w.w), b.z, acc0);
+  acc1 = fmaf(bf_hi(w.w), b.w, acc1);
+}
+
+// Register pipeline of one wave's weight stream: two batches of UB units. The batches of the
+// NEXT task are loaded before that task's event is satisfied: weights do not depend on
+// activations, so the HBM stream keeps running across the dependency wait. The pipeline is
+// refilled unconditionally at the end of every task (a cached dummy unit when the next task is
+// not a GEMV), so the registers flow straight from the loads into the next GEMV without copies
+// (a copy would have to wait for the loads to land).
+struct WPipe {
+  v4u A[UB], B[UB];
+};
+
+struct WaveRun {
+  const v4u* src;  // this lane's first 16-byte piece of the wave's run of units
+  int nunits, g0;  // units in the run; first row group
+};
+
+__device__ __forceinline__ WaveRun wave_run(const KernelParams& p, const TaskDesc& t, const GemvGeom& gm) {
+  // The wave index is made explicitly wave-uniform so that unit counts and loop bounds live in
+  // scalar registers and loads need no per-lane branches.
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int rows = t.row1 - t.row0;
   const int ngroups = (rows + gm.rg - 1) / gm.rg;
   const int gA = ngroups * wave / NW, gB = ngroups * (wave + 1) / NW;
-  const int S = gm.S, lpr = gm.lpr;
-  const int nunits = (gB - gA) * S;
-  const int sub = lane & (lpr - 1), rin = lane / lpr;
-  const v4u* src = (const v4u*)(p.wpacked + t.wofs) + (size_t)gA * S * 64 + lane;
-  int g = gA, ug = 0;
-  float acc = 0.f;
-  v4u A[UB], B[UB];
+  WaveRun r;
+  r.g0 = gA;
+  r.nunits = (gB - gA) * gm.S;
+  r.src = (const v4u*)(p.wpacked + t.wofs) + (size_t)gA * gm.S * 64 + (threadIdx.x & 63);
+  return r;
+}
 
-  auto load = [&](v4u(&R)[UB], int i0) {
+// Loads are unconditional (units past the run re-read its last unit, a cache hit, and are never
+// consumed), so the in-order wait counter is exact: a batch is waited for only when consumed.
+__device__ __forceinline__ void load_batch(v4u (&R)[UB], const WaveRun& w, int i0) {
 #pragma unroll
-    for (int j = 0; j < UB; ++j)
-      if (i0 + j < nunits) R[j] = __builtin_nontemporal_load(src + (size_t)(i0 + j) * 64);
-  };
+  for (int j = 0; j < UB; ++j) R[j] = __builtin_nontemporal_load(w.src + (size_t)min(i0 + j, w.nunits - 1) * 64);
+}
+
+__device__ __forceinline__ bool is_gemv(int type) {
+  return type == T_QKV || type == T_OPROJ || type == T_GATEUP || type == T_DOWN || type == T_LMHEAD;
+}
+
+// Attention tiling shared by the prefetch and the attention task (see the attention section).
+constexpr int ASLOTS = 4;  // register-free K/V slots per wave per chunk, staged in LDS
+
+template <int DH>
+struct AttnShape {
+  static constexpr int LPP = DH / 8;              // lanes per position (8 dims each)
+  static constexpr int PPW = 64 / LPP;            // positions per wave per slot
+  static constexpr int CHUNK = NW * PPW * ASLOTS; // positions per chunk
+};
+
+struct AttnRange {
+  int p0, p1;  // the split's positions [p0, p1)
+  int pos;     // the current position, or -1 when the sequence is inactive or out of range
+};
+
+__device__ __forceinline__ AttnRange attn_range(const KernelParams& p, const TaskDesc& t, const Ctl* ctl) {
+  AttnRange r;
+  r.p0 = r.p1 = 0;
+  r.pos = -1;
+  const int s = t.a0;
+  if (s >= p.n_active) return r;
+  const int pos = ctl->ctx[s];
+  if (pos < 0 || pos >= p.max_pos) return r;
+  const int n = pos + 1, nb = (n + 15) >> 4, pps = (nb + p.splits - 1) / p.splits;
+  r.p0 = min(n, t.a2 * pps * 16);
+  r.p1 = min(n, (t.a2 + 1) * pps * 16);
+  r.pos = pos;
+  return r;
+}
+
+// LDS staging of one chunk: K rows then V rows, each [ASLOTS][NW][64 lanes] x 16 bytes. Slot i of
+// wave w, lane l holds 8 dims (l % LPP) of position cs + (i * NW + w) * PPW + l / LPP: exactly the
+// layout one wave-wide 16-byte-per-lane load writes, so the cache rows go straight from memory
+// to LDS with global_load_lds (no registers), and each wave later reads back only its own slots.
+template <int DH>
+__device__ __forceinline__ v4u* attn_kbuf(float* lds) { return (v4u*)lds; }
+template <int DH>
+__device__ __forceinline__ v4u* attn_vbuf(float* lds) { return (v4u*)lds + ASLOTS * NW * 64; }
+
+// Issue the loads of positions [cs, min(cs + CHUNK, ce)) of the task's (seq, kv head) into the
+// LDS staging buffers. The chunk's page-table entries are fetched first, all at once, so the
+// row loads issue together; slots past the range load a dummy row (block 0, offset 0).
+template <int DH>
+__device__ __forceinline__ void attn_stage_chunk(const KernelParams& p, const TaskDesc& t, int cs, int ce,
+                                                 uint16_t* const* pools, float* lds) {
+  constexpr int LPP = AttnShape<DH>::LPP, PPW = AttnShape<DH>::PPW;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63, pg = lane / LPP, c = lane % LPP;
+  const int s = t.a0, grp = t.a1;
+  const uint16_t* kpool = pools[t.layer];
+  const uint16_t* vpool = pools[p.n_layers + t.layer];
+  const int32_t* ptab = p.page_table + (size_t)s * p.max_blocks;
+  int blk[ASLOTS];
+#pragma unroll
+  for (int i = 0; i < ASLOTS; ++i) {
+    const int pp = cs + (i * NW + wave) * PPW + pg;
+    blk[i] = (pp < ce) ? ptab[pp >> 4] : 0;
+  }
+#pragma unroll
+  for (int i = 0; i < ASLOTS; ++i) {
+    const int pp = cs + (i * NW + wave) * PPW + pg;
+    int b = blk[i];
+    if (b < 0 || b >= p.num_blocks) {
+      raise_error(p, ERR_PAGE, (uint32_t)s, (uint32_t)b);
+      b = 0;
+    }
+    const size_t row = (((size_t)b * p.hk + grp) * 16 + (pp < ce ? (pp & 15) : 0)) * DH + c * 8;
+    __attribute__((address_space(3))) void* kd =
+        (__attribute__((address_space(3))) void*)(attn_kbuf<DH>(lds) + (i * NW + wave) * 64);
+    __attribute__((address_space(3))) void* vd =
+        (__attribute__((address_space(3))) void*)(attn_vbuf<DH>(lds) + (i * NW + wave) * 64);
+    __builtin_amdgcn_global_load_lds((const void*)(kpool + row), kd, 16, 0, 0);
+    __builtin_amdgcn_global_load_lds((const void*)(vpool + row), vd, 16, 0, 0);
+  }
+}
+
+template <int DH>
+__device__ __forceinline__ void prefetch_next(const KernelParams& p, const TaskDesc& tn, bool has_next, WPipe& wp,
+                                              const Ctl* ctl, uint16_t* const* pools, float* lds) {
+  if (has_next && tn.type == T_ATTN) {  // the split's first chunk of cached keys and values, into LDS
+    const AttnRange r = attn_range(p, tn, ctl);
+    attn_stage_chunk<DH>(p, tn, r.p0, min(r.p1, r.pos), pools, lds);
+    return;
+  }
+  WaveRun w;
+  w.nunits = 0;
+  if (has_next && is_gemv(tn.type)) w = wave_run(p, tn, ctl->geoms[tn.geom]);
+  if (w.nunits <= 0) {  // nothing to stream: re-read the first unit of the weights (valid, cached)
+    w.src = (const v4u*)p.wpacked + (threadIdx.x & 63);
+    w.nunits = 1;
+  }
+  load_batch(wp.A, w, 0);
+  load_batch(wp.B, w, UB);
+}
+
+__device__ __forceinline__ void gemv_tile(const KernelParams& p, const TaskDesc& t, const GemvGeom gm, const float* xs, float* ys,
+                          WPipe& wp) {
+  const WaveRun w = wave_run(p, t, gm);
+  const int nunits = w.nunits;
+  if (nunits <= 0) return;
+  const int lane = threadIdx.x & 63;
+  const int rows = t.row1 - t.row0;
+  const int S = gm.S, lpr = gm.lpr;
+  const int sub = lane & (lpr - 1), rin = lane / lpr;
+  const float* xa = xs + sub * 4;
+  const float* xb = xs + S * lpr * 4 + sub * 4;
+  int g = w.g0, ug = 0;
+  float acc0 = 0.f, acc1 = 0.f;
+
   auto consume = [&](v4u(&R)[UB], int i0) {
 #pragma unroll
     for (int j = 0; j < UB; ++j) {
       if (i0 + j < nunits) {
-        unit_fma(R[j], xs + (ug * lpr + sub) * 8, acc);
+        unit_fma(R[j], xa + ug * lpr * 4, xb + ug * lpr * 4, acc0, acc1);
         if (++ug == S) {
+          float acc = acc0 + acc1;
           for (int off = lpr >> 1; off >= 1; off >>= 1) acc += __shfl_xor(acc, off);
           const int r = g * gm.rg + rin;
           if (sub == 0 && r < rows) ys[r] = acc;
-          acc = 0.f;
+          acc0 = 0.f;
+          acc1 = 0.f;
           ug = 0;
           ++g;
         }
       }
     }
   };
-  load(A, 0);
-  for (int i0 = 0; i0 < nunits; i0 += 2 * UB) {
-    load(B, i0 + UB);
-    consume(A, i0);
-    load(A, i0 + 2 * UB);
-    consume(B, i0 + UB);
+  // wp holds this task's first two batches (loaded by prefetch_next)
+  consume(wp.A, 0);
+  load_batch(wp.A, w, 2 * UB);
+  consume(wp.B, UB);
+  for (int i0 = 2 * UB; i0 < nunits; i0 += 2 * UB) {
+    load_batch(wp.B, w, i0 + UB);
+    consume(wp.A, i0);
+    load_batch(wp.A, w, i0 + 2 * UB);
+    consume(wp.B, i0 + UB);
   }
 }
 
-// xs[0, K) = RMSNorm(src) * gain; xs[K, padded) = 0. src is the residual stream (fp32, coherent
-// loads) or, for the first layer, the token's embedding row (bf16).
-__device__ void rmsnorm_to_lds(const KernelParams& p, const float* xsrc, const uint16_t* esrc, const uint16_t* gain,
+// xs (two-plane layout, `padded` = 8 * pieces elements) = RMSNorm(src) * gain, zero past d.
+// src is the residual stream (fp32, coherent loads) or, for the first layer, the token's
+// embedding row (bf16).
+__device__ __forceinline__ void rmsnorm_to_lds(const KernelParams& p, const float* xsrc, const uint16_t* esrc, const uint16_t* gain,
                                int d, int padded, float* xs, Ctl* ctl) {
+  const int np = padded >> 3;
   float ss = 0.f;
-  for (int i = threadIdx.x; i < d; i += NT) {
-    const float v = esrc ? bf2f(esrc[i]) : ldc(&xsrc[i]);
-    xs[i] = v;
+  for (int i = threadIdx.x; i < padded; i += NT) {
+    const float v = (i < d) ? (esrc ? bf2f(esrc[i]) : ldc(&xsrc[i])) : 0.f;
+    xs[xs_index(i, np)] = v;
     ss += v * v;
   }
-  for (int i = d + threadIdx.x; i < padded; i += NT) xs[i] = 0.f;
   ss = block_sum(ss, ctl);
   const float r = 1.0f / sqrtf(ss / (float)d + p.eps);
-  for (int i = threadIdx.x; i < d; i += NT) xs[i] = xs[i] * r * bf2f(gain[i]);
-  __syncthreads();
+  for (int i = threadIdx.x; i < d; i += NT) {  // each thread rescales the entries it wrote
+    const int k = xs_index(i, np);
+    xs[k] = xs[k] * r * bf2f(gain[i]);
+  }
+  bar();
 }
 
-__device__ void load_vec_to_lds(const float* src, int n, int padded, float* xs) {
-  for (int i = threadIdx.x; i < n; i += NT) xs[i] = ldc(&src[i]);
-  for (int i = n + threadIdx.x; i < padded; i += NT) xs[i] = 0.f;
-  __syncthreads();
+__device__ __forceinline__ void load_vec_to_lds(const float* src, int n, int padded, float* xs) {
+  const int np = padded >> 3;
+  for (int i = threadIdx.x; i < padded; i += NT) xs[xs_index(i, np)] = (i < n) ? ldc(&src[i]) : 0.f;
+  bar();
 }
 
 __device__ __forceinline__ int token_of(const KernelParams& p, int s) {
@@ -225,8 +385,8 @@ __device__ __forceinline__ int token_of(const KernelParams& p, int s) {
 }
 
 // Position of sequence s's current token, or -1 (error latched) when the cache cannot hold it.
-__device__ __forceinline__ int checked_pos(const KernelParams& p, int s) {
-  const int pos = p.ctx_lens[s];
+__device__ __forceinline__ int checked_pos(const KernelParams& p, const Ctl* ctl, int s) {
+  const int pos = ctl->ctx[s];
   if (pos < 0 || pos >= p.max_pos) {
     if (threadIdx.x == 0) raise_error(p, ERR_CTX, (uint32_t)s, (uint32_t)pos);
     return -1;
@@ -239,35 +399,62 @@ __device__ __forceinline__ const uint16_t* layer_norm_gain(const KernelParams& p
 }
 
 // ----------------------------------------------------------------------------- QKV
-__device__ void task_qkv(const KernelParams& p, const TaskDesc& t, float* lds, Ctl* ctl) {
-  const GemvGeom gm = p.geoms[G_QKV];
+// Per 4-row set of the packed QKV rows: what the epilogue needs besides the GEMV results. Loaded
+// before the GEMV so that these loads' latency hides under the weight stream.
+struct QkvSet {
+  float2 cs0, cs1;  // rotary cos/sin of the set's two pairs (q and k heads)
+  float b0, b1, b2, b3;
+  int blk;          // KV block of the current position (k and v heads)
+};
+
+__device__ __forceinline__ QkvSet qkv_set_consts(const KernelParams& p, int l, int r, int pos, int s) {
+  const int G = p.hq / p.hk, dh = p.dh, Rg = (G + 2) * dh;
+  const int grp = r / Rg, within = r % Rg, slot = within / dh, jh = within % dh, i0 = jh >> 1;
+  QkvSet c;
+  c.cs0 = make_float2(1.f, 0.f);
+  c.cs1 = make_float2(1.f, 0.f);
+  c.b0 = c.b1 = c.b2 = c.b3 = 0.f;
+  c.blk = 0;
+  (void)grp;
+  if (p.bias) {
+    const uint16_t* b = p.bias + (size_t)l * (p.hq + 2 * p.hk) * dh + r;
+    c.b0 = bf2f(b[0]); c.b1 = bf2f(b[1]); c.b2 = bf2f(b[2]); c.b3 = bf2f(b[3]);
+  }
+  if (slot <= G) {
+    c.cs0 = ((const float2*)p.rope)[(size_t)pos * (dh / 2) + i0];
+    c.cs1 = ((const float2*)p.rope)[(size_t)pos * (dh / 2) + i0 + 1];
+  }
+  if (slot >= G) c.blk = p.page_table[(size_t)s * p.max_blocks + pos / 16];
+  return c;
+}
+
+__device__ __forceinline__ void task_qkv(const KernelParams& p, const TaskDesc& t, float* lds, Ctl* ctl, WPipe& wp,
+                                         uint16_t* const* pools) {
+  const GemvGeom gm = ctl->geoms[G_QKV];
   const int padded = gm.S * gm.lpr * 8;
   float* xs = lds;
   float* ys = lds + padded;
   const int s = 0;
   const int l = t.layer;
+  const int G = p.hq / p.hk, dh = p.dh, Rg = (G + 2) * dh;
+  const int pos = checked_pos(p, ctl, s);
+  const int nsets = pos < 0 ? 0 : (t.row1 - t.row0) >> 2;
+  QkvSet pre;
+  if ((int)threadIdx.x < nsets) pre = qkv_set_consts(p, l, t.row0 + 4 * threadIdx.x, pos, s);
   const uint16_t* esrc = nullptr;
   if (l == 0) esrc = p.embed + (size_t)token_of(p, s) * p.d;
   rmsnorm_to_lds(p, p.x + (size_t)s * p.d, esrc, layer_norm_gain(p, l, 0), p.d, padded, xs, ctl);
-  gemv_tile(p, t, gm, xs, ys);
-  __syncthreads();
-  const int G = p.hq / p.hk, dh = p.dh, Rg = (G + 2) * dh;
-  const int pos = checked_pos(p, s);
-  const int nsets = pos < 0 ? 0 : (t.row1 - t.row0) >> 2;
+  gemv_tile(p, t, gm, xs, ys, wp);
+  bar();
   for (int m = threadIdx.x; m < nsets; m += NT) {
     const int r = t.row0 + 4 * m;
     const int grp = r / Rg, within = r % Rg, slot = within / dh, jh = within % dh;
     const int i0 = jh >> 1;  // even dim index; the set holds dims i0, i0 + dh/2, i0 + 1, i0 + 1 + dh/2
-    float y0 = ys[4 * m], y1 = ys[4 * m + 1], y2 = ys[4 * m + 2], y3 = ys[4 * m + 3];
-    if (p.bias) {
-      const uint16_t* b = p.bias + (size_t)l * (p.hq + 2 * p.hk) * dh + r;
-      y0 += bf2f(b[0]); y1 += bf2f(b[1]); y2 += bf2f(b[2]); y3 += bf2f(b[3]);
-    }
+    const QkvSet c = (m == (int)threadIdx.x) ? pre : qkv_set_consts(p, l, r, pos, s);
+    float y0 = ys[4 * m] + c.b0, y1 = ys[4 * m + 1] + c.b1, y2 = ys[4 * m + 2] + c.b2, y3 = ys[4 * m + 3] + c.b3;
     if (slot <= G) {  // rotate q and k: pair (i0, i0 + dh/2) and pair (i0 + 1, i0 + 1 + dh/2)
-      const float2 cs0 = ((const float2*)p.rope)[(size_t)pos * (dh / 2) + i0];
-      const float2 cs1 = ((const float2*)p.rope)[(size_t)pos * (dh / 2) + i0 + 1];
-      const float a0 = y0 * cs0.x - y1 * cs0.y, b0 = y1 * cs0.x + y0 * cs0.y;
-      const float a1 = y2 * cs1.x - y3 * cs1.y, b1 = y3 * cs1.x + y2 * cs1.y;
+      const float a0 = y0 * c.cs0.x - y1 * c.cs0.y, b0 = y1 * c.cs0.x + y0 * c.cs0.y;
+      const float a1 = y2 * c.cs1.x - y3 * c.cs1.y, b1 = y3 * c.cs1.x + y2 * c.cs1.y;
       y0 = a0; y1 = b0; y2 = a1; y3 = b1;
     }
     if (slot < G) {
@@ -277,59 +464,72 @@ __device__ void task_qkv(const KernelParams& p, const TaskDesc& t, float* lds, C
       stc(&q[i0 + 1], y2);
       stc(&q[i0 + 1 + dh / 2], y3);
     } else {
-      const int blk = p.page_table[(size_t)s * p.max_blocks + pos / 16];
+      const int blk = c.blk;
       if (blk < 0 || blk >= p.num_blocks) {
         raise_error(p, ERR_PAGE, (uint32_t)s, (uint32_t)blk);
         continue;
       }
-      uint16_t* pool = (slot == G ? p.kpool : p.vpool)[l];
+      uint16_t* pool = pools[(slot == G ? 0 : p.n_layers) + l];
       uint32_t* row = (uint32_t*)(pool + (((size_t)blk * p.hk + grp) * 16 + (pos & 15)) * dh);
       stc(&row[i0 >> 1], f2bf(y0) | (f2bf(y2) << 16));
       stc(&row[(i0 + dh / 2) >> 1], f2bf(y1) | (f2bf(y3) << 16));
     }
   }
-  signal_slots(p, t);
 }
 
 // ----------------------------------------------------------------------------- attention
-// One split of grouped-query attention for (seq, kv head): its range of cache blocks.
-// The G query heads that share the KV head read each key and value row once. Online
-// softmax runs over chunks of up to 512 positions. The running max and sum rescale the
-// output ([SL] slide 13 and the kernel page's online-softmax passage). The partial
-// (m, l, unnormalised o) goes to `part`. The split that finishes last merges all partials
-// by log-sum-exp and publishes the group's slot.
+// One split of grouped-query attention for (seq, kv head): a contiguous range of cache blocks.
+// The G query heads that share the KV head read each key and value row once ([SL] slide 28).
+// Keys and values of earlier positions do not change during a step. The worker loads the
+// split's first chunk of them (K into the pipeline's A registers, V into B) while the previous
+// task finishes, before this task waits for its queries ("MPK: A Compiler and Runtime for
+// Mega-Kernelizing Tensor Programs", analogy 4: inputs load while the previous task runs).
+// After the wait, only q and the current position's key and value are fetched. Softmax runs
+// online across chunks. The running max and sum rescale the output ([SL] slide 13; the online
+// softmax of "Hạt nhân là gì và tại sao mọi người lại viết hạt nhân mới"). The partial
+// (m, l, unnormalised o) goes to `part`. The split that finishes last merges all partials by
+// log-sum-exp and publishes the group's slot.
+// Coherent read of this lane's 16 bytes of the current position's row (written in this step).
+__device__ __forceinline__ v4u ldc_row(const uint16_t* rp) {
+  const uint32_t* r32 = (const uint32_t*)rp;
+  v4u v;
+  v.x = ldc(&r32[0]);
+  v.y = ldc(&r32[1]);
+  v.z = ldc(&r32[2]);
+  v.w = ldc(&r32[3]);
+  return v;
+}
+
 template <int DH, int GMAX>
-__device__ void task_attn(const KernelParams& p, const TaskDesc& t, float* lds, Ctl* ctl) {
-  constexpr int LPP = DH / 8;       // lanes per position (8 dims each)
-  constexpr int PPW = 64 / LPP;     // positions per wave per step
-  constexpr int CH = 512;           // positions per chunk
+__device__ __forceinline__ void task_attn(const KernelParams& p, const TaskDesc& t, float* lds, Ctl* ctl,
+                                          uint16_t* const* pools) {
+  constexpr int LPP = AttnShape<DH>::LPP, PPW = AttnShape<DH>::PPW, CHUNK = AttnShape<DH>::CHUNK;
   const int s = t.a0, grp = t.a1, j = t.a2;
   const int G = p.hq / p.hk, h0 = grp * G;
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63, pg = lane / LPP, c = lane % LPP;
-  const int cpos = s < p.n_active ? checked_pos(p, s) : -1;
-  const bool active = cpos >= 0;
-  float* scores = lds;                  // [G][CH]
-  float* obuf = lds + G * CH;           // [NW][G][DH]
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63, pg = lane / LPP, c = lane % LPP;
+  const AttnRange r = attn_range(p, t, ctl);
+  if (s < p.n_active && r.pos < 0 && threadIdx.x == 0) raise_error(p, ERR_CTX, (uint32_t)s, (uint32_t)ctl->ctx[s]);
+  const bool active = r.pos >= 0;
+  const int pos = r.pos;
+  v4u* kb = attn_kbuf<DH>(lds);
+  v4u* vb = attn_vbuf<DH>(lds);
+  float* scores = (float*)(vb + ASLOTS * NW * 64);  // [G][CHUNK]
+  float* obuf = scores + G * CHUNK;                  // [NW][G][DH]
+  float* qs = obuf + NW * G * DH;                    // [G][2][DH/2]: dims 8c..8c+3 at 4c, 8c+4..8c+7 at DH/2 + 4c
   const int splits = p.splits;
   float* part = p.part + ((size_t)s * p.hq) * splits * (DH + 2);
-
-  int p0 = 0, p1 = 0, pos = 0;
-  if (active) {
-    pos = cpos;
-    const int n = pos + 1, nb = (n + 15) >> 4, pps = (nb + splits - 1) / splits;
-    p0 = min(n, j * pps * 16);
-    p1 = min(n, (j + 1) * pps * 16);
-  }
-  const uint16_t* kpool = p.kpool[t.layer];
-  const uint16_t* vpool = p.vpool[t.layer];
-  const int32_t* ptab = p.page_table + (size_t)s * p.max_blocks;
+  const uint16_t* kpool = pools[t.layer];
+  const uint16_t* vpool = pools[p.n_layers + t.layer];
   const float scale = 1.0f / sqrtf((float)DH);
 
-  float qr[GMAX][8];  // this lane's 8 dims of each query head of the group
-#pragma unroll
-  for (int h = 0; h < GMAX; ++h)
-#pragma unroll
-    for (int e = 0; e < 8; ++e) qr[h][e] = (h < G && active) ? ldc(&p.q[(size_t)s * p.hq * DH + (size_t)(h0 + h) * DH + c * 8 + e]) : 0.f;
+  wait_stores();  // this wave's staged rows (issued before the wait) have landed in LDS
+  // the group's queries, staged in LDS (two planes per head, so lanes reading consecutive
+  // 8-dim pieces read consecutive 16-byte words)
+  for (int i = threadIdx.x; i < G * DH; i += NT) {
+    const int h = i / DH, d = i % DH, pc = d >> 3, e = d & 7;
+    qs[h * DH + (e < 4 ? 0 : DH / 2) + pc * 4 + (e & 3)] = active ? ldc(&p.q[(size_t)s * p.hq * DH + (size_t)(h0 + h) * DH + d]) : 0.f;
+  }
   float oacc[GMAX][8];
 #pragma unroll
   for (int h = 0; h < GMAX; ++h)
@@ -339,60 +539,60 @@ __device__ void task_attn(const KernelParams& p, const TaskDesc& t, float* lds, 
     ctl->m_run[threadIdx.x] = -INFINITY;
     ctl->l_run[threadIdx.x] = 0.f;
   }
-  __syncthreads();
-
-  auto row_ptr = [&](const uint16_t* pool, int pp) -> const uint16_t* {
-    int blk = ptab[pp >> 4];
-    if (blk < 0 || blk >= p.num_blocks) {
-      raise_error(p, ERR_PAGE, (uint32_t)s, (uint32_t)blk);
-      blk = 0;
+  const int old_end = min(r.p1, pos);  // rows before the current position are staged ahead
+  for (int cs = r.p0; cs < r.p1; cs += CHUNK) {
+    const int ce = min(r.p1, cs + CHUNK);
+    if (cs != r.p0) {
+      bar();  // every wave is done with the previous chunk's scores
+      attn_stage_chunk<DH>(p, t, cs, old_end, pools, lds);
+      wait_stores();
     }
-    return pool + (((size_t)blk * p.hk + grp) * 16 + (pp & 15)) * DH + c * 8;
-  };
-  auto load_row = [&](const uint16_t* pool, int pp) -> v4u {
-    const uint16_t* rp = row_ptr(pool, pp);
-    if (pp == pos) {  // written by another CU in this step: coherent loads
-      const uint32_t* r32 = (const uint32_t*)rp;
-      v4u v;
-      v.x = ldc(&r32[0]); v.y = ldc(&r32[1]); v.z = ldc(&r32[2]); v.w = ldc(&r32[3]);
-      return v;
+    // the current position's key and value come from this step: coherent loads into its slot
+    if (pos >= cs && pos < ce) {
+      const int idx = pos - cs, ic = idx / (NW * PPW), wc = (idx / PPW) % NW, pc = idx % PPW;
+      if (wave == wc && pg == pc) {
+        const size_t row = 0;
+        (void)row;
+        int b = p.page_table[(size_t)s * p.max_blocks + (pos >> 4)];
+        if (b < 0 || b >= p.num_blocks) b = 0;  // already reported when the row was appended
+        const size_t off = (((size_t)b * p.hk + grp) * 16 + (pos & 15)) * DH + c * 8;
+        kb[(ic * NW + wc) * 64 + lane] = ldc_row(kpool + off);
+        vb[(ic * NW + wc) * 64 + lane] = ldc_row(vpool + off);
+      }
     }
-    return __builtin_nontemporal_load((const v4u*)rp);
-  };
-
-  for (int cs = p0; cs < p1; cs += CH) {
-    const int ce = min(p1, cs + CH);
+    bar();  // queries staged; patched rows visible
     // scores = q . k * scale
-    for (int base = cs + wave * PPW; base < ce; base += NW * PPW) {
-      const int pp = base + pg;
-      const bool valid = pp < ce;
-      v4u kv = {0u, 0u, 0u, 0u};
-      if (valid) kv = load_row(kpool, pp);
-      float kf[8] = {bf_lo(kv.x), bf_hi(kv.x), bf_lo(kv.y), bf_hi(kv.y), bf_lo(kv.z), bf_hi(kv.z), bf_lo(kv.w), bf_hi(kv.w)};
+#pragma unroll
+    for (int i = 0; i < ASLOTS; ++i) {
+      const int pp = cs + (i * NW + wave) * PPW + pg;
+      const v4u kv = kb[(i * NW + wave) * 64 + lane];
+      const float kf[8] = {bf_lo(kv.x), bf_hi(kv.x), bf_lo(kv.y), bf_hi(kv.y), bf_lo(kv.z), bf_hi(kv.z), bf_lo(kv.w), bf_hi(kv.w)};
 #pragma unroll
       for (int h = 0; h < GMAX; ++h) {
         if (h >= G) break;
+        const v4f qa = *(const v4f*)(qs + h * DH + c * 4);
+        const v4f qb = *(const v4f*)(qs + h * DH + DH / 2 + c * 4);
         float a = 0.f;
-#pragma unroll
-        for (int e = 0; e < 8; ++e) a = fmaf(qr[h][e], kf[e], a);
+        a = fmaf(qa.x, kf[0], a); a = fmaf(qa.y, kf[1], a); a = fmaf(qa.z, kf[2], a); a = fmaf(qa.w, kf[3], a);
+        a = fmaf(qb.x, kf[4], a); a = fmaf(qb.y, kf[5], a); a = fmaf(qb.z, kf[6], a); a = fmaf(qb.w, kf[7], a);
 #pragma unroll
         for (int off = LPP >> 1; off >= 1; off >>= 1) a += __shfl_xor(a, off);
-        if (c == 0 && valid) scores[h * CH + (pp - cs)] = a * scale;
+        if (c == 0 && pp < ce) scores[h * CHUNK + (pp - cs)] = a * scale;
       }
     }
-    __syncthreads();
+    bar();
     // chunk max and running-max update, one wave per head
     const int nch = ce - cs;
     for (int h = wave; h < G; h += NW) {
       float mx = -INFINITY;
-      for (int i = lane; i < nch; i += 64) mx = fmaxf(mx, scores[h * CH + i]);
+      for (int i = lane; i < nch; i += 64) mx = fmaxf(mx, scores[h * CHUNK + i]);
       mx = wave_max(mx);
       const float m_old = ctl->m_run[h];
       const float m_new = fmaxf(m_old, mx);
       float sum = 0.f;
       for (int i = lane; i < nch; i += 64) {
-        const float e = expf(scores[h * CH + i] - m_new);
-        scores[h * CH + i] = e;
+        const float e = expf(scores[h * CHUNK + i] - m_new);
+        scores[h * CHUNK + i] = e;
         sum += e;
       }
       sum = wave_sum(sum);
@@ -403,7 +603,7 @@ __device__ void task_attn(const KernelParams& p, const TaskDesc& t, float* lds, 
         ctl->m_run[h] = m_new;
       }
     }
-    __syncthreads();
+    bar();
 #pragma unroll
     for (int h = 0; h < GMAX; ++h) {
       if (h >= G) break;
@@ -412,21 +612,21 @@ __device__ void task_attn(const KernelParams& p, const TaskDesc& t, float* lds, 
       for (int e = 0; e < 8; ++e) oacc[h][e] *= sc;
     }
     // o += p * v
-    for (int base = cs + wave * PPW; base < ce; base += NW * PPW) {
-      const int pp = base + pg;
+#pragma unroll
+    for (int i = 0; i < ASLOTS; ++i) {
+      const int pp = cs + (i * NW + wave) * PPW + pg;
       if (pp < ce) {
-        const v4u vv = load_row(vpool, pp);
+        const v4u vv = vb[(i * NW + wave) * 64 + lane];
         const float vf[8] = {bf_lo(vv.x), bf_hi(vv.x), bf_lo(vv.y), bf_hi(vv.y), bf_lo(vv.z), bf_hi(vv.z), bf_lo(vv.w), bf_hi(vv.w)};
 #pragma unroll
         for (int h = 0; h < GMAX; ++h) {
           if (h >= G) break;
-          const float pw = scores[h * CH + (pp - cs)];
+          const float pw = scores[h * CHUNK + (pp - cs)];
 #pragma unroll
           for (int e = 0; e < 8; ++e) oacc[h][e] = fmaf(pw, vf[e], oacc[h][e]);
         }
       }
     }
-    __syncthreads();
   }
   // reduce o over the position groups of each wave, then over waves
 #pragma unroll
@@ -444,7 +644,7 @@ __device__ void task_attn(const KernelParams& p, const TaskDesc& t, float* lds, 
 #pragma unroll
       for (int e = 0; e < 8; ++e) obuf[(wave * G + h) * DH + c * 8 + e] = oacc[h][e];
     }
-  __syncthreads();
+  bar();
   if (active) {
     for (int i = threadIdx.x; i < G * DH; i += NT) {
       const int h = i / DH, dd = i % DH;
@@ -459,70 +659,82 @@ __device__ void task_attn(const KernelParams& p, const TaskDesc& t, float* lds, 
   }
   // arrive; the last split of the group merges
   wait_stores();
-  __syncthreads();
+  bar();
   if (threadIdx.x == 0) {
     const uint32_t old = __hip_atomic_fetch_add(&p.counters[t.a3], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     ctl->flag = (old + 1 == p.epoch * (uint32_t)splits) ? 1u : 0u;
   }
-  __syncthreads();
-  if (!ctl->flag) return;
+  bar();
+  if (!ctl->flag) return;  // only the last split merges and publishes
   if (active) {
+    // log-sum-exp merge; each split's three loads are independent of the previous split's values
     for (int i = threadIdx.x; i < G * DH; i += NT) {
       const int h = i / DH, dd = i % DH;
       const float* ph = part + (size_t)(h0 + h) * splits * (DH + 2);
-      float M = -INFINITY;
-      for (int k = 0; k < splits; ++k) M = fmaxf(M, ldc(&ph[k * (DH + 2)]));
-      float Lsum = 0.f, acc = 0.f;
-      for (int k = 0; k < splits; ++k) {
-        const float mk = ldc(&ph[k * (DH + 2)]);
-        if (mk == -INFINITY) continue;
-        const float w = expf(mk - M);
-        Lsum += ldc(&ph[k * (DH + 2) + 1]) * w;
-        acc += ldc(&ph[k * (DH + 2) + 2 + dd]) * w;
+      float M = -INFINITY, Lsum = 0.f, acc = 0.f;
+      for (int k0 = 0; k0 < splits; k0 += 4) {
+        float mk[4], lk[4], ok[4];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          const int k = min(k0 + u, splits - 1);
+          mk[u] = ldc(&ph[k * (DH + 2)]);
+          lk[u] = ldc(&ph[k * (DH + 2) + 1]);
+          ok[u] = ldc(&ph[k * (DH + 2) + 2 + dd]);
+        }
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          if (k0 + u >= splits || mk[u] == -INFINITY) continue;
+          const float mn = fmaxf(M, mk[u]);
+          const float a = (M == -INFINITY) ? 0.f : expf(M - mn), b = expf(mk[u] - mn);
+          Lsum = Lsum * a + lk[u] * b;
+          acc = acc * a + ok[u] * b;
+          M = mn;
+        }
       }
       stc(&p.o[(size_t)s * p.hq * DH + (size_t)(h0 + h) * DH + dd], acc / Lsum);
     }
   }
-  signal_slots(p, t);
 }
 
 // ----------------------------------------------------------------------------- O / down projection
-__device__ void task_residual_gemv(const KernelParams& p, const TaskDesc& t, float* lds, Ctl* ctl, int geom,
-                                   const float* in, int n_in) {
-  const GemvGeom gm = p.geoms[geom];
+__device__ __forceinline__ void task_residual_gemv(const KernelParams& p, const TaskDesc& t, float* lds, Ctl* ctl,
+                                                   int geom, const float* in, int n_in, WPipe& wp) {
+  const GemvGeom gm = ctl->geoms[geom];
   const int padded = gm.S * gm.lpr * 8;
   float* xs = lds;
   float* ys = lds + padded;
   const int s = 0;
-  load_vec_to_lds(in + (size_t)s * n_in, n_in, padded, xs);
-  gemv_tile(p, t, gm, xs, ys);
-  __syncthreads();
   const bool from_embed = (t.type == T_OPROJ && t.layer == 0);
   const uint16_t* erow = from_embed ? p.embed + (size_t)token_of(p, s) * p.d : nullptr;
-  for (int r = t.row0 + threadIdx.x; r < t.row1; r += NT) {
-    const float resid = from_embed ? bf2f(erow[r]) : ldc(&p.x[(size_t)s * p.d + r]);
+  // the residual rows are loaded together with the input vector, ahead of the GEMV
+  const int r_pre = t.row0 + threadIdx.x;
+  float resid_pre = 0.f;
+  if (r_pre < t.row1) resid_pre = from_embed ? bf2f(erow[r_pre]) : ldc(&p.x[(size_t)s * p.d + r_pre]);
+  load_vec_to_lds(in + (size_t)s * n_in, n_in, padded, xs);
+  gemv_tile(p, t, gm, xs, ys, wp);
+  bar();
+  for (int r = r_pre; r < t.row1; r += NT) {
+    const float resid = (r == r_pre) ? resid_pre : from_embed ? bf2f(erow[r]) : ldc(&p.x[(size_t)s * p.d + r]);
     stc(&p.x[(size_t)s * p.d + r], resid + ys[r - t.row0]);
   }
-  signal_slots(p, t);
 }
 
 // ----------------------------------------------------------------------------- gate/up + SwiGLU
-__device__ void task_gateup(const KernelParams& p, const TaskDesc& t, float* lds, Ctl* ctl) {
-  const GemvGeom gm = p.geoms[G_GU];
+__device__ __forceinline__ void task_gateup(const KernelParams& p, const TaskDesc& t, float* lds, Ctl* ctl, WPipe& wp) {
+  const GemvGeom gm = ctl->geoms[G_GU];
   const int padded = gm.S * gm.lpr * 8;
   float* xs = lds;
   float* ys = lds + padded;
   const int s = 0;
   rmsnorm_to_lds(p, p.x + (size_t)s * p.d, nullptr, layer_norm_gain(p, t.layer, 1), p.d, padded, xs, ctl);
-  gemv_tile(p, t, gm, xs, ys);
-  __syncthreads();
+  gemv_tile(p, t, gm, xs, ys, wp);
+  bar();
   const int npairs = (t.row1 - t.row0) >> 1;
   for (int m = threadIdx.x; m < npairs; m += NT) {
     const float a = ys[2 * m], b = ys[2 * m + 1];
     const float silu = a / (1.0f + expf(-a));
     stc(&p.h[(size_t)s * p.f + (t.row0 >> 1) + m], silu * b);
   }
-  signal_slots(p, t);
 }
 
 // ----------------------------------------------------------------------------- LM head + argmax
@@ -533,30 +745,30 @@ __device__ __forceinline__ uint64_t argmax_key(float v, int idx) {
   return ((uint64_t)u << 32) | (uint64_t)(0xFFFFFFFFu - (uint32_t)idx);
 }
 
-__device__ uint64_t block_max_u64(uint64_t k, Ctl* ctl) {
+__device__ __forceinline__ uint64_t block_max_u64(uint64_t k, Ctl* ctl) {
 #pragma unroll
   for (int off = 32; off >= 1; off >>= 1) {
     const uint64_t o = __shfl_xor(k, off);
     k = o > k ? o : k;
   }
   const int w = threadIdx.x >> 6, l = threadIdx.x & 63;
-  __syncthreads();
+  bar();
   if (l == 0) ctl->kred[w] = k;
-  __syncthreads();
+  bar();
   uint64_t m = 0;
   for (int i = 0; i < NW; ++i) m = ctl->kred[i] > m ? ctl->kred[i] : m;
   return m;
 }
 
-__device__ void task_lmhead(const KernelParams& p, const TaskDesc& t, float* lds, Ctl* ctl) {
-  const GemvGeom gm = p.geoms[G_LM];
+__device__ __forceinline__ void task_lmhead(const KernelParams& p, const TaskDesc& t, float* lds, Ctl* ctl, WPipe& wp) {
+  const GemvGeom gm = ctl->geoms[G_LM];
   const int padded = gm.S * gm.lpr * 8;
   float* xs = lds;
   float* ys = lds + padded;
   const int s = 0;
   rmsnorm_to_lds(p, p.x + (size_t)s * p.d, nullptr, p.norms + (size_t)p.n_layers * 2 * p.d, p.d, padded, xs, ctl);
-  gemv_tile(p, t, gm, xs, ys);
-  __syncthreads();
+  gemv_tile(p, t, gm, xs, ys, wp);
+  bar();
   uint64_t best = 0;
   for (int r = t.row0 + threadIdx.x; r < t.row1; r += NT) {
     const float v = ys[r - t.row0];
@@ -566,10 +778,9 @@ __device__ void task_lmhead(const KernelParams& p, const TaskDesc& t, float* lds
   }
   best = block_max_u64(best, ctl);
   if (threadIdx.x == 0) stc(&p.amax[(size_t)s * p.n_lm_parts + t.a0], best);
-  signal_slots(p, t);
 }
 
-__device__ void task_argmax(const KernelParams& p, const TaskDesc& t, Ctl* ctl) {
+__device__ __forceinline__ void task_argmax(const KernelParams& p, const TaskDesc& t, Ctl* ctl) {
   const int s = t.a0;
   uint64_t best = 0;
   for (int i = threadIdx.x; i < p.n_lm_parts; i += NT) {
@@ -584,35 +795,88 @@ __device__ void task_argmax(const KernelParams& p, const TaskDesc& t, Ctl* ctl) 
 }
 
 // ----------------------------------------------------------------------------- the megakernel
-extern "C" __global__ __launch_bounds__(NT, 1) void mk_megakernel(KernelParams p) {
+// One instantiation per (head dim, query heads per KV head rounded up to 2, 4 or 8): the
+// attention tile keeps GMAX x 8 query values and accumulators per lane in registers, and a
+// kernel's register budget is set by its largest path.
+template <int DH, int GMAX>
+__global__ __launch_bounds__(NT, 1) void mk_megakernel(KernelParams p) {
   extern __shared__ __attribute__((aligned(16))) unsigned char lds_raw[];
+  static_assert(sizeof(Ctl) <= 1024, "control block fits its 1 KB");
   Ctl* ctl = (Ctl*)lds_raw;
-  float* lds = (float*)(lds_raw + ((sizeof(Ctl) + 255) & ~size_t(255)));
+  // LDS: control block | per-layer K/V pool pointers | this CU's queue | working set
+  uint16_t** pools = (uint16_t**)(lds_raw + 1024);
+  const size_t pools_bytes = ((size_t)2 * p.n_layers * sizeof(void*) + 255) & ~size_t(255);
+  TaskDesc* tq = (TaskDesc*)(lds_raw + 1024 + pools_bytes);
+  float* lds = (float*)(lds_raw + 1024 + pools_bytes + (((size_t)p.max_queue * sizeof(TaskDesc) + 255) & ~size_t(255)));
   const int cu = blockIdx.x;
   const int q0 = p.queue_off[cu], q1 = p.queue_off[cu + 1];
+  if (threadIdx.x < G_COUNT * (int)(sizeof(GemvGeom) / 4))
+    ((int32_t*)ctl->geoms)[threadIdx.x] = ((const int32_t*)p.geoms)[threadIdx.x];
+  for (int i = threadIdx.x; i < p.n_layers; i += NT) {
+    pools[i] = p.kpool[i];
+    pools[p.n_layers + i] = p.vpool[i];
+  }
+  // context lengths change only at the end of the step (the argmax task), after every reader
+  if (threadIdx.x < 16) ctl->ctx[threadIdx.x] = (int)threadIdx.x < p.max_seqs ? p.ctx_lens[threadIdx.x] : 0;
+  // Stage the queue's descriptors in LDS: a task switch then costs an LDS read instead of two
+  // dependent scalar loads from memory on the path between one task's publish and the next wait.
+  for (int i = threadIdx.x; i < (q1 - q0) * 16; i += NT) {
+    const int k = i >> 4, w = i & 15;
+    ((int32_t*)&tq[k])[w] = ((const int32_t*)&p.tasks[p.queue_idx[q0 + k]])[w];
+  }
+  bar();
+  WPipe wp;
+  int ti_next = q0 < q1 ? p.queue_idx[q0] : 0;
+  TaskDesc tn = tq[0];
+  prefetch_next<DH>(p, tn, q0 < q1, wp, ctl, pools, lds);
   for (int qi = q0; qi < q1; ++qi) {
-    const TaskDesc t = p.tasks[p.queue_idx[qi]];
+    const int ti = ti_next;
+    const TaskDesc t = tn;
+    if (qi + 1 < q1) {
+      tn = tq[qi + 1 - q0];
+      ti_next = p.trace ? p.queue_idx[qi + 1] : 0;
+    }
+    const int my_sig = (int)threadIdx.x < t.sig_n ? p.sig_slots[t.sig_off + threadIdx.x] : -1;
+    uint64_t t_queue = 0, t_ready = 0;
+    if (p.trace && threadIdx.x == 0) t_queue = __builtin_amdgcn_s_memrealtime();
+    bool aborted = false;
     if (t.wait_ev >= 0) {
-      wait_event(p, t.wait_ev, ctl);
-      if (ctl->aborted) {  // drain: publish without computing so no other CU waits forever
-        signal_slots(p, t);
-        continue;
+      wait_event(p, t, ctl);
+      aborted = ctl->aborted != 0;
+    }
+    if (p.trace && threadIdx.x == 0) t_ready = __builtin_amdgcn_s_memrealtime();
+    bool pub = true;  // publish this task's flag slots (attention: only the split that merged)
+    if (!aborted) {  // when aborted: publish without computing, so no other CU waits forever
+      switch (t.type) {
+        case T_QKV: task_qkv(p, t, lds, ctl, wp, pools); break;
+        case T_ATTN:
+          task_attn<DH, GMAX>(p, t, lds, ctl, pools);
+          pub = ctl->flag != 0;
+          break;
+        case T_OPROJ: task_residual_gemv(p, t, lds, ctl, G_O, p.o, p.hq * p.dh, wp); break;
+        case T_GATEUP: task_gateup(p, t, lds, ctl, wp); break;
+        case T_DOWN: task_residual_gemv(p, t, lds, ctl, G_D, p.h, p.f, wp); break;
+        case T_LMHEAD: task_lmhead(p, t, lds, ctl, wp); break;
+        case T_ARGMAX: task_argmax(p, t, ctl); break;
+        default: break;
       }
     }
-    switch (t.type) {
-      case T_QKV: task_qkv(p, t, lds, ctl); break;
-      case T_ATTN:
-        if (p.dh == 128) task_attn<128, 8>(p, t, lds, ctl);
-        else task_attn<64, 8>(p, t, lds, ctl);
-        break;
-      case T_OPROJ: task_residual_gemv(p, t, lds, ctl, G_O, p.o, p.hq * p.dh); break;
-      case T_GATEUP: task_gateup(p, t, lds, ctl); break;
-      case T_DOWN: task_residual_gemv(p, t, lds, ctl, G_D, p.h, p.f); break;
-      case T_LMHEAD: task_lmhead(p, t, lds, ctl); break;
-      case T_ARGMAX: task_argmax(p, t, ctl); break;
-      default: break;
+    wait_stores();
+    bar();
+    // Publish, then start streaming the next task's weights before waiting for its inputs.
+    if (pub) publish(p, my_sig);
+    prefetch_next<DH>(p, tn, qi + 1 < q1, wp, ctl, pools, lds);
+    if (p.trace && threadIdx.x == 0) {
+      TraceRec r;
+      r.t_queue = t_queue;
+      r.t_ready = t_ready;
+      r.t_done = __builtin_amdgcn_s_memrealtime();
+      r.cu = (uint16_t)cu;
+      r.type = (uint8_t)t.type;
+      r.layer = (uint8_t)t.layer;
+      r.epoch = p.epoch;
+      p.trace[ti] = r;
     }
-    __syncthreads();
   }
 }
 
@@ -670,14 +934,21 @@ extern "C" __global__ __launch_bounds__(256) void mk_repack_bias(const uint16_t*
 }
 
 // ----------------------------------------------------------------------------- host-side launchers
+static const void* megakernel_for(int dh, int hq, int hk) {
+  const int g = hq / hk;
+  if (dh == 128) return g <= 2 ? (const void*)mk_megakernel<128, 2> : g <= 4 ? (const void*)mk_megakernel<128, 4> : (const void*)mk_megakernel<128, 8>;
+  return g <= 2 ? (const void*)mk_megakernel<64, 2> : g <= 4 ? (const void*)mk_megakernel<64, 4> : (const void*)mk_megakernel<64, 8>;
+}
+
 hipError_t launch_megakernel(const KernelParams& p, int grid, size_t lds_bytes, hipStream_t stream) {
   KernelParams copy = p;
   void* args[] = {(void*)&copy};
-  return hipLaunchCooperativeKernel((const void*)mk_megakernel, dim3(grid), dim3(NT), args, (unsigned)lds_bytes, stream);
+  return hipLaunchCooperativeKernel(megakernel_for(p.dh, p.hq, p.hk), dim3(grid), dim3(NT), args, (unsigned)lds_bytes,
+                                    stream);
 }
 
-hipError_t megakernel_occupancy(int* blocks_per_cu, size_t lds_bytes) {
-  return hipOccupancyMaxActiveBlocksPerMultiprocessor(blocks_per_cu, (const void*)mk_megakernel, NT, lds_bytes);
+hipError_t megakernel_occupancy(int* blocks_per_cu, size_t lds_bytes, int dh, int hq, int hk) {
+  return hipOccupancyMaxActiveBlocksPerMultiprocessor(blocks_per_cu, megakernel_for(dh, hq, hk), NT, lds_bytes);
 }
 
 hipError_t launch_repack(const RepackArgs& a, int64_t units, hipStream_t stream) {
