@@ -57,7 +57,19 @@ def main():
     ap.add_argument("--workload", default="llama8b")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="only run a plain 1 GiB device-to-device copy 5 times (to scale HBM byte counters)")
     args = ap.parse_args()
+    if args.copy_calibration:
+        import torch
+        src = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
+        dst = torch.empty_like(src)
+        src.fill_(1)
+        for _ in range(5):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_calibration_bytes_per_dispatch": 1 << 30, "dispatches": 5}))
+        return
     if args.gpus != 1:
         print("bench.py measures one GPU: this build has no multi-GPU path (--gpus %d requested)" % args.gpus,
               file=sys.stderr)
@@ -116,6 +128,10 @@ def main():
         (ms, 1e3 / ms, achieved, 100 * achieved / rf.MI355X_HBM_PEAK_GBS, rf.MI355X_HBM_PEAK_GBS))
     dec.close()
 
+    traffic = None
+    if wl.name == "llama8b":
+        traffic = rf.profiled_traffic(os.path.join(ROOT, "profiles", "mk_megakernel_llama8b_b1_decode.md"))
+
     cpu = None
     if not args.no_cpu_baseline:
         t0 = time.time()
@@ -144,7 +160,8 @@ def main():
                    "weight_bytes_per_token": rf.weight_bytes_per_token(m),
                    "kv": "bf16, paged in 16-token blocks"},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": rf.MI355X_HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": round(achieved / rf.MI355X_HBM_PEAK_GBS, 4), "traffic": None,
+                     "frac": round(achieved / rf.MI355X_HBM_PEAK_GBS, 4), "traffic": traffic,
+                     "traffic_unit": "HBM bytes/launch (FETCH_SIZE + WRITE_SIZE, copy-calibrated)",
                      "bytes_per_launch": int(bytes_avg), "kernel": "mk_megakernel (one launch per decode step)"},
         "cpu_baseline": cpu,
     }

@@ -46,3 +46,36 @@ def step_bytes(m, ctxs) -> int:
 
 def roofline_ms(bytes_: float, peak_gbs: float = MI355X_HBM_PEAK_GBS) -> float:
     return bytes_ / (peak_gbs * 1e9) * 1e3
+
+
+# Sources whose change alters what the decode kernel reads or writes per launch: the kernel
+# itself and the graph builder that lays out its tasks.
+_KERNEL_SOURCES = ("csrc/mk_kernel.hip", "csrc/mk_graph.h", "csrc/mk_graph.cpp")
+
+
+def kernel_source_hash() -> str:
+    """First 16 hex digits of SHA-256 over the decode kernel's sources."""
+    import hashlib
+    import os
+    here = os.path.dirname(os.path.abspath(__file__))
+    h = hashlib.sha256()
+    for f in _KERNEL_SOURCES:
+        with open(os.path.join(here, f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def profiled_traffic(summary_path: str):
+    """HBM bytes per launch measured with FETCH_SIZE/WRITE_SIZE (scaled by a copy-kernel
+    calibration) as recorded in a profile summary, or None when the summary is missing or the
+    kernel sources have changed since it was taken."""
+    import os
+    import re
+    if not os.path.exists(summary_path):
+        return None
+    txt = open(summary_path).read()
+    mb = re.search(r"traffic_bytes_per_dispatch = (\d+)", txt)
+    mh = re.search(r"source_sha256_16 = ([0-9a-f]{16})", txt)
+    if not mb or not mh or mh.group(1) != kernel_source_hash():
+        return None
+    return int(mb.group(1))

@@ -90,3 +90,43 @@ def teacher_forced(shape, weights, prompt, n_decode, paging="identity", attn_spl
 
 def bug_bar(res) -> float:
     return max(BUG_FLOOR, 2.0 * max(res["rel_f32"])) if res["rel_f32"] else REL_L2_BAR
+
+
+def prefilled_case(wl, n_decode, attn_splits=0, device=0, precision_check=False):
+    """A decode workload whose sequences start from a pre-filled KV cache (N(0, 1) bf16 K/V at
+    positions < ctx, keys taken as already rotated), on both sides. Returns (decoder, oracle,
+    ctx lengths, block table)."""
+    import torch
+    import oracle as orc
+    import persistent_megakernel_03_amd as mk
+    m = wl.model
+    ctx = si.context_lengths(wl)
+    cap = ctx + n_decode
+    table, nblocks = si.block_tables(wl, cap)
+    weights = si.gen_weights(m)
+    cfg = mk.make_config(m, max_seqs=wl.n_seqs, max_blocks_per_seq=table.shape[1], num_blocks=nblocks,
+                         attn_splits=attn_splits)
+    dec = mk.Decoder(cfg, device)
+    dec.load_weights(weights)
+    dec.set_page_table(table)
+    dec.set_ctx_lens(ctx)
+    om = orc.OracleModel(m, weights, wl.n_seqs, int(cap.max()))
+    for l in range(m.n_layers):
+        kpool = torch.zeros((nblocks, m.n_kv_heads, 16, m.head_dim), dtype=torch.int16)
+        vpool = torch.zeros_like(kpool)
+        for s in range(wl.n_seqs):
+            n = int(ctx[s])
+            k = si.kv_fill(wl, l, s, n, "k")
+            v = si.kv_fill(wl, l, s, n, "v")
+            om.set_kv(l, s, 0, k, v)
+            nb = (n + 15) // 16
+            pad = nb * 16 - n
+            kk = np.concatenate([k, np.zeros((pad,) + k.shape[1:], np.uint16)]).reshape(nb, 16, m.n_kv_heads, m.head_dim)
+            vv = np.concatenate([v, np.zeros((pad,) + v.shape[1:], np.uint16)]).reshape(nb, 16, m.n_kv_heads, m.head_dim)
+            rows = torch.from_numpy(table[s, :nb].astype(np.int64))
+            kpool[rows] = torch.from_numpy(kk.transpose(0, 2, 1, 3).copy().view(np.int16))
+            vpool[rows] = torch.from_numpy(vv.transpose(0, 2, 1, 3).copy().view(np.int16))
+        dec.k_pools[l].copy_(kpool.reshape(-1))
+        dec.v_pools[l].copy_(vpool.reshape(-1))
+    torch.cuda.synchronize()
+    return dec, om, ctx, table, weights

@@ -213,3 +213,26 @@ def test_llama8b_full_size_teacher_forced():
     res = teacher_forced(m, w, prompt, 3, n_positions=wl.prompt_len + wl.steps)
     check(res, "llama8b")
     res["dec"].close()
+
+
+def test_llama8b_long_context_paged():
+    # 8B shape, one sequence whose paged KV cache (16-token blocks, permuted block table) is
+    # pre-filled to 32768 positions; decode steps attend to all of them (32 splits per KV head)
+    import torch
+    from parity_util import prefilled_case
+    wl = si.WORKLOADS["llama8b_long"]
+    n = 3
+    log("case: llama8b long context, 32768 prefilled positions, %d decode steps" % n)
+    dec, om, ctx, table, w = prefilled_case(wl, n)
+    tok = int(si.first_tokens(wl)[0])
+    rels = []
+    for i in range(n):
+        o_tok, o_logits = om.step(0, tok, int(ctx[0]) + i)
+        d_tok, d_logits = gpu_step(dec, tok)
+        rels.append(rel_l2(d_logits, o_logits))
+        assert d_tok == int(np.argmax(d_logits))
+        log("  step %d: rel L2 %.3e, tokens %d/%d" % (i, rels[-1], d_tok, o_tok))
+        tok = o_tok
+    assert max(rels) <= REL_L2_BAR
+    assert int(dec.ctx_lens.item()) == int(ctx[0]) + n
+    dec.close()
