@@ -38,6 +38,7 @@ struct mk_ctx {
   float* d_logits = nullptr;
   uint32_t epoch = 0;
   uint32_t watchdog_ticks = 200000000u;  // 2 s at 100 MHz
+  int32_t touch = 0;                      // cache warming at task boundaries (MK_TOUCH=0 turns it off)
   TraceRec* d_trace = nullptr;
 };
 
@@ -82,6 +83,7 @@ mk_status build(const mk_model_config* cfg, int n_cus, mk_ctx** out) {
     const long us = std::atol(w);
     if (us > 0 && us < 40000000L) c->watchdog_ticks = (uint32_t)(us * 100L);
   }
+  if (const char* t = std::getenv("MK_TOUCH")) c->touch = std::atoi(t) != 0;  // off by default: it delayed the waits
   *out = c;
   return MK_OK;
 }
@@ -116,6 +118,8 @@ mk_status read_error_word(mk_ctx* c, hipStream_t st) {
   if (e[E_ABORT] || s == MK_ERR_DEVICE_TIMEOUT) {
     HIPCHK(hipMemset(c->d_scratch + c->g.sl.flags, 0, (size_t)c->g.n_flag_slots * 4));
     HIPCHK(hipMemset(c->d_scratch + c->g.sl.counters, 0, (size_t)c->g.n_counters * 4));
+    // epochs restart at 1, so tags of the aborted steps must not survive
+    HIPCHK(hipMemset(c->d_scratch + c->g.sl.tagged_begin, 0, (size_t)(c->g.sl.tagged_end - c->g.sl.tagged_begin)));
     HIPCHK(hipDeviceSynchronize());
     c->epoch = 0;
   }
@@ -145,10 +149,11 @@ KernelParams make_params(mk_ctx* c) {
   p.vpool = (uint16_t* const*)(S + g.sl.pools + (size_t)m.n_layers * 8);
   p.page_table = c->d_page_table;
   p.ctx_lens = c->d_ctx_lens;
-  p.x = (float*)(S + g.sl.x);
-  p.q = (float*)(S + g.sl.q);
-  p.o = (float*)(S + g.sl.o);
-  p.h = (float*)(S + g.sl.h);
+  p.xt = (uint64_t*)(S + g.sl.xt);
+  p.qt = (uint64_t*)(S + g.sl.qt);
+  p.kvt = (uint64_t*)(S + g.sl.kvt);
+  p.ot = (uint64_t*)(S + g.sl.ot);
+  p.ht = (uint64_t*)(S + g.sl.ht);
   p.part = (float*)(S + g.sl.part);
   p.logits = c->d_logits;
   p.amax = (uint64_t*)(S + g.sl.amax);
@@ -168,6 +173,7 @@ KernelParams make_params(mk_ctx* c) {
   p.n_lm_parts = g.n_lm_parts;
   p.max_pos = g.max_pos;
   p.watchdog_ticks = c->watchdog_ticks;
+  p.touch = c->touch;
   p.max_queue = g.max_queue;
   p.trace = c->d_trace;
   return p;
@@ -260,6 +266,7 @@ mk_status mk_bind_memory(mk_ctx* c, void* d_weights, void* const* d_k_pools, voi
   HIPCHK(hipMemset(S + g.sl.flags, 0, (size_t)g.n_flag_slots * 4));
   HIPCHK(hipMemset(S + g.sl.counters, 0, (size_t)std::max(g.n_counters, 1) * 4));
   HIPCHK(hipMemset(S + g.sl.err, 0, E_COUNT * 4));
+  HIPCHK(hipMemset(S + g.sl.tagged_begin, 0, (size_t)(g.sl.tagged_end - g.sl.tagged_begin)));
   HIPCHK(hipDeviceSynchronize());
   c->epoch = 0;
   c->bound = true;

@@ -123,6 +123,8 @@ std::string build_graph(const mk_model_config& c, int n_cus, HostGraph& g) {
     if (c.d_model % 8 || c.d_ffn % 8 || (c.n_q_heads * c.head_dim) % 8) return "GEMV inner dims must be multiples of 8";
   if (c.n_q_heads / c.n_kv_heads > 8) return "at most 8 query heads per KV head";
   if (c.head_dim != 64 && c.head_dim != 128) return "head_dim must be 64 or 128";
+  // a workgroup polls each tagged activation vector with at most 16 (d, hq*dh) or 32 (d_ffn) words per thread
+  if (c.d_model > 8192 || c.n_q_heads * c.head_dim > 8192 || c.d_ffn > 16384) return "model too wide for the activation polls";
   if (c.block_size != 16) return "block_size must be 16";
   if (c.max_seqs != 1) return "this build runs batch-1 graphs (max_seqs == 1)";
   if (c.max_blocks_per_seq < 1 || c.num_blocks < 1) return "empty KV cache";
@@ -322,6 +324,9 @@ std::string build_graph(const mk_model_config& c, int n_cus, HostGraph& g) {
     g.tasks[t].sig_n = (int32_t)b.task_sig[t].size();
     for (auto& s : b.task_sig[t]) g.sig_slots.push_back(g.events[s.first].slot0 + s.second);
   }
+  // the O and down tasks keep their residual rows in registers: at most 4 per thread of 512
+  for (const TaskDesc& td : g.tasks)
+    if ((td.type == T_OPROJ || td.type == T_DOWN) && td.row1 - td.row0 > 4 * 512) return "residual task too tall";
   // ---- per-CU queues in global order
   g.queue_off.assign(n_cus + 1, 0);
   for (int32_t cu : b.task_cu) g.queue_off[cu + 1]++;
@@ -352,10 +357,13 @@ std::string build_graph(const mk_model_config& c, int n_cus, HostGraph& g) {
   g.sl.flags = take((int64_t)g.n_flag_slots * 4);
   g.sl.counters = take((int64_t)g.n_counters * 4);
   g.sl.err = take((int64_t)E_COUNT * 4);
-  g.sl.x = take((int64_t)S * d * 4);
-  g.sl.q = take((int64_t)S * qd * 4);
-  g.sl.o = take((int64_t)S * qd * 4);
-  g.sl.h = take((int64_t)S * f * 4);
+  g.sl.tagged_begin = o;
+  g.sl.xt = take((int64_t)L * 2 * S * d * 8);
+  g.sl.qt = take((int64_t)L * S * qd * 8);
+  g.sl.kvt = take((int64_t)L * S * 2 * hk * (dh / 2) * 8);
+  g.sl.ot = take((int64_t)L * S * qd * 8);
+  g.sl.ht = take((int64_t)L * S * f * 8);
+  g.sl.tagged_end = o;
   g.sl.part = take((int64_t)S * hq * g.splits * (dh + 2) * 4);
   g.sl.amax = take((int64_t)S * g.n_lm_parts * 8);
   g.sl.tokbuf = take((int64_t)std::max(g.max_pos, 64) * 4);
@@ -373,13 +381,14 @@ std::string build_graph(const mk_model_config& c, int n_cus, HostGraph& g) {
   // (8 waves x 64/(dh/8) positions x 4 slots), per-wave partial outputs and the staged queries
   const int64_t attn_chunk = (int64_t)8 * (64 / (dh / 8)) * 4;
   const int64_t attn_lds = (int64_t)2 * 4 * 8 * 1024 + (int64_t)G * attn_chunk * 4 + (int64_t)8 * G * dh * 4 +
-                           (int64_t)G * dh * 4;
+                           (int64_t)G * dh * 4 + (int64_t)dh * 4;
   int max_q = 0;
   for (int cu = 0; cu < n_cus; ++cu) max_q = std::max(max_q, g.queue_off[cu + 1] - g.queue_off[cu]);
   g.max_queue = max_q;
-  // control block + this CU's task descriptors + the larger of the GEMV and attention working sets
-  g.lds_bytes = 1024 + align_up((int64_t)2 * L * 8, 256) + align_up((int64_t)max_q * (int64_t)sizeof(TaskDesc), 256) +
-                align_up(std::max(gemv_lds, attn_lds), 256);
+  // control block + pool pointers + the touch-ahead sink (1 KB per wave) + this CU's task descriptors
+  // + the larger of the GEMV and attention working sets
+  g.lds_bytes = 1024 + align_up((int64_t)2 * L * 8, 256) + TOUCH_SINK_BYTES +
+                align_up((int64_t)max_q * (int64_t)sizeof(TaskDesc), 256) + align_up(std::max(gemv_lds, attn_lds), 256);
   if (g.lds_bytes > 160 * 1024) return "working set exceeds 160 KB of LDS";
   return "";
 }

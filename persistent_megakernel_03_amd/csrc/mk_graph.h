@@ -57,7 +57,10 @@ struct EventDesc {
 struct ScratchLayout {
   int64_t tasks, queue_off, queue_idx, events, sig_slots, geoms, rope;
   int64_t flags, counters, err;
-  int64_t x, q, o, h, part, amax, tokbuf, tokout, pools;
+  // tagged activations (64-bit words: value bits | step epoch << 32), one buffer per layer
+  int64_t xt, qt, kvt, ot, ht;
+  int64_t tagged_begin, tagged_end;  // byte range holding all tagged buffers
+  int64_t part, amax, tokbuf, tokout, pools;
   int64_t total;
 };
 
@@ -106,10 +109,13 @@ struct KernelParams {
   uint16_t* const* vpool;
   const int32_t* page_table;  // [max_seqs][max_blocks]
   int32_t* ctx_lens;          // [max_seqs]
-  float* x;                   // [max_seqs][d] residual stream
-  float* q;                   // [max_seqs][hq*dh] rotated queries
-  float* o;                   // [max_seqs][hq*dh] attention output
-  float* h;                   // [max_seqs][f] SwiGLU output
+  // Activations handed from CU to CU within a step, as tagged 64-bit words (value bits in the low
+  // half, the step epoch in the high half), one buffer per layer so every word is written once per step.
+  uint64_t* xt;               // [L][2][max_seqs][d] residual stream after O-proj (0) and after down-proj (1)
+  uint64_t* qt;               // [L][max_seqs][hq*dh] rotated queries
+  uint64_t* kvt;              // [L][max_seqs][2][hk][dh/2] the current position's key and value (bf16 pairs)
+  uint64_t* ot;               // [L][max_seqs][hq*dh] attention output
+  uint64_t* ht;               // [L][max_seqs][f] SwiGLU output
   float* part;                // [max_seqs][hq][splits][dh + 2] attention partials (m, l, o[dh])
   float* logits;              // [max_seqs][V]
   uint64_t* amax;             // [max_seqs][n_lm_parts] packed argmax keys
@@ -122,7 +128,11 @@ struct KernelParams {
   uint32_t watchdog_ticks;    // s_memrealtime ticks (100 MHz) a wait may spin before the kernel aborts
   int32_t max_queue;          // longest per-CU queue (its descriptors are staged in LDS)
   TraceRec* trace;            // per-task timestamps of the last step, or nullptr
+  int32_t touch;              // 1: warm the caches with upcoming weights at task boundaries
 };
+
+// LDS bytes that receive the cache-warming loads (their data is never read): 1 KB per wave.
+constexpr int TOUCH_SINK_BYTES = 8 * 1024;
 
 // Arguments of the weight re-layout kernel: one stage's tasks [task0, task0 + ntasks), whose
 // tiles are contiguous in the packed buffer.

@@ -82,6 +82,7 @@ struct Ctl {
   uint32_t flag;
   uint32_t aborted;
   uint64_t kred[NW];
+  uint64_t t_ready;         // trace: when the running task's inputs were all present
 };
 
 __device__ __forceinline__ float block_sum(float v, Ctl* ctl) {
@@ -103,6 +104,98 @@ __device__ void raise_error(const KernelParams& p, uint32_t code, uint32_t a, ui
     stc(&p.err[E_INFO0], a);
     stc(&p.err[E_INFO1], b);
   }
+}
+
+// ----------------------------------------------------------------------------- tagged activations
+// Values that one CU hands to another within a step travel as 64-bit words: the fp32 bits (or a
+// packed bf16 pair) in the low half and the step epoch in the high half, written by one
+// single-copy-atomic store. A consumer polls the words it needs until each carries the current
+// epoch. The data is thus its own ready signal: a producer neither waits for its stores to complete
+// nor sets a flag afterwards, and a consumer needs no second round trip to fetch the data after
+// seeing a flag. With cross-XCD round trips near a microsecond and every layer crossing five
+// dependency boundaries, those two round trips are most of a boundary's cost. Each buffer holds one
+// layer, so every word is written exactly once per step and the epoch alone names its version.
+__device__ __forceinline__ void st_tag(uint64_t* p, uint32_t bits, uint32_t ep) { stc(p, ((uint64_t)ep << 32) | bits); }
+__device__ __forceinline__ void st_tagf(uint64_t* p, float v, uint32_t ep) { st_tag(p, __float_as_uint(v), ep); }
+
+__device__ __forceinline__ uint64_t* xt_at(const KernelParams& p, int l, int which, int s) {
+  return p.xt + (((size_t)l * 2 + which) * p.max_seqs + s) * p.d;
+}
+__device__ __forceinline__ uint64_t* qt_at(const KernelParams& p, int l, int s) {
+  return p.qt + ((size_t)l * p.max_seqs + s) * p.hq * p.dh;
+}
+__device__ __forceinline__ uint64_t* ot_at(const KernelParams& p, int l, int s) {
+  return p.ot + ((size_t)l * p.max_seqs + s) * p.hq * p.dh;
+}
+__device__ __forceinline__ uint64_t* ht_at(const KernelParams& p, int l, int s) {
+  return p.ht + ((size_t)l * p.max_seqs + s) * p.f;
+}
+__device__ __forceinline__ uint64_t* kvt_at(const KernelParams& p, int l, int s, int kv, int grp) {
+  return p.kvt + ((((size_t)l * p.max_seqs + s) * 2 + kv) * p.hk + grp) * (p.dh / 2);
+}
+
+// Coherent 64-bit load through a buffer resource. The lane's byte offset sits in one VGPR and the
+// word's offset in an SGPR, so polling K words per lane costs no per-word address registers. The
+// volatile bit keeps the compiler from hoisting re-loads out of a poll loop; such loads also bypass
+// the caches that are not coherent across XCDs.
+typedef unsigned v2u __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t tag_rsrc(const uint64_t* base) {
+  return __builtin_amdgcn_make_buffer_rsrc((void*)base, (short)0, 0x7FFFFFFF, 0x00020000);
+}
+__device__ __forceinline__ uint64_t ld_tag(__amdgpu_buffer_rsrc_t r, int voff, int soff) {
+  const v2u v = __builtin_amdgcn_raw_buffer_load_b64(r, voff, soff, (int)((1u << 31) | 16u));
+  return ((uint64_t)v.y << 32) | v.x;
+}
+__device__ __forceinline__ uint32_t first_words(int n) { return n >= 32 ? ~0u : n <= 0 ? 0u : (1u << n) - 1u; }
+
+// Polls this thread's tagged words k (bit k of `pending`, k < K); word k sits at byte base + voff(k)
+// + soff(k), soff uniform across the wave. sink(k, bits) receives a word's low half once the word
+// carries the epoch. Each pass issues the loads of all words still stale before checking any. A wave
+// stops when all its lanes are done, when the kernel is aborting, or when the watchdog expires (which
+// raises the timeout, naming `what`, and aborts the kernel).
+template <int K, typename Voff, typename Soff, typename Sink>
+__device__ __forceinline__ void poll_tagged(const KernelParams& p, const uint64_t* base, Voff voff, Soff soff,
+                                            uint32_t pending, uint32_t what, Sink sink) {
+  const __amdgpu_buffer_rsrc_t r = tag_rsrc(base);
+  const uint64_t t0 = __builtin_amdgcn_s_memrealtime();
+  while (true) {
+    uint64_t w[K];
+#pragma unroll
+    for (int k = 0; k < K; ++k)
+      if ((pending >> k) & 1u) w[k] = ld_tag(r, voff(k), soff(k));
+#pragma unroll
+    for (int k = 0; k < K; ++k) {
+      if (((pending >> k) & 1u) && (uint32_t)(w[k] >> 32) == p.epoch) {
+        sink(k, (uint32_t)w[k]);
+        pending &= ~(1u << k);
+      }
+    }
+    if (!__any(pending != 0u)) break;
+    if (ldc(&p.err[E_ABORT])) break;
+    if (__builtin_amdgcn_s_memrealtime() - t0 > p.watchdog_ticks) {
+      if ((threadIdx.x & 63) == 0) {
+        raise_error(p, ERR_TIMEOUT, what, p.epoch);
+        stc(&p.err[E_ABORT], 1u);
+      }
+      break;
+    }
+    __builtin_amdgcn_s_sleep(1);
+  }
+}
+
+// A whole vector src[0, n): wave w polls the contiguous words [w * chunk, (w + 1) * chunk), chunk =
+// n / 8 rounded up to 64, lane l taking words l, l + 64, ..., so each load is one coalesced 512-byte
+// row and the word offsets fit the instruction's immediate (with one SGPR per 4 KB).
+__device__ __forceinline__ int poll_chunk(int n) { return ((n + NW * 64 - 1) / (NW * 64)) * 64; }
+__device__ __forceinline__ int poll_index(int n, int k) {
+  return (int)(threadIdx.x >> 6) * poll_chunk(n) + (int)(threadIdx.x & 63) + 64 * k;
+}
+template <int K, typename Sink>
+__device__ __forceinline__ void poll_vector(const KernelParams& p, const uint64_t* src, int n, uint32_t what, Sink sink) {
+  const int i0 = poll_index(n, 0);
+  const int cnt = min(poll_chunk(n) / 64, (n - i0 + 63) / 64);
+  poll_tagged<K>(p, src, [&](int k) { return i0 * 8 + (k & 7) * 512; }, [](int k) { return (k >> 3) * 4096; },
+                 first_words(cnt), what, sink);
 }
 
 // ----------------------------------------------------------------------------- events
@@ -285,9 +378,40 @@ __device__ __forceinline__ void attn_stage_chunk(const KernelParams& p, const Ta
   }
 }
 
+// Cache warming. The register batches hold only the first 2 * UB units of a wave's run, and a task
+// boundary (waiting for the slowest producer, then for the flag to travel) can leave HBM idle for
+// longer than those take to arrive. So after the register batches each wave also loads the next TB
+// units that follow in its queue (the rest of the next task's run, then the start of the following
+// GEMV task's run) into a sink in LDS that nothing reads. The loads need no registers; they bring
+// the lines into L2 and the memory-side cache, from which the GEMV later streams them faster than
+// from HBM. Their number is fixed, so that the compiler's wait counts for the register batches stay
+// exact; with warming off they re-read the first unit of the weights (a cache hit).
+constexpr int TB = 16;
+
+__device__ __forceinline__ WaveRun dummy_run(const KernelParams& p) {
+  WaveRun w;
+  w.src = (const v4u*)p.wpacked + (threadIdx.x & 63);
+  w.nunits = 1;
+  w.g0 = 0;
+  return w;
+}
+
+__device__ __forceinline__ void touch_ahead(const WaveRun& w1, const WaveRun& w2, unsigned char* sink) {
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  __attribute__((address_space(3))) void* d = (__attribute__((address_space(3))) void*)(sink + wave * 1024);
+  const int end1 = max(w1.nunits, 2 * UB);
+#pragma unroll
+  for (int k = 0; k < TB; ++k) {
+    const int i = 2 * UB + k;
+    const v4u* a = (i < w1.nunits) ? w1.src + (size_t)i * 64 : w2.src + (size_t)min(i - end1, w2.nunits - 1) * 64;
+    __builtin_amdgcn_global_load_lds((const void*)a, d, 16, 0, 0);
+  }
+}
+
 template <int DH>
-__device__ __forceinline__ void prefetch_next(const KernelParams& p, const TaskDesc& tn, bool has_next, WPipe& wp,
-                                              const Ctl* ctl, uint16_t* const* pools, float* lds) {
+__device__ __forceinline__ void prefetch_next(const KernelParams& p, const TaskDesc& tn, bool has_next,
+                                              const TaskDesc* tnn, WPipe& wp, const Ctl* ctl, uint16_t* const* pools,
+                                              float* lds, unsigned char* sink) {
   if (has_next && tn.type == T_ATTN) {  // the split's first chunk of cached keys and values, into LDS
     const AttnRange r = attn_range(p, tn, ctl);
     attn_stage_chunk<DH>(p, tn, r.p0, min(r.p1, r.pos), pools, lds);
@@ -296,12 +420,15 @@ __device__ __forceinline__ void prefetch_next(const KernelParams& p, const TaskD
   WaveRun w;
   w.nunits = 0;
   if (has_next && is_gemv(tn.type)) w = wave_run(p, tn, ctl->geoms[tn.geom]);
-  if (w.nunits <= 0) {  // nothing to stream: re-read the first unit of the weights (valid, cached)
-    w.src = (const v4u*)p.wpacked + (threadIdx.x & 63);
-    w.nunits = 1;
-  }
+  if (w.nunits <= 0) w = dummy_run(p);  // nothing to stream: re-read the first unit (valid, cached)
   load_batch(wp.A, w, 0);
   load_batch(wp.B, w, UB);
+  WaveRun w1 = w, w2;
+  w2.nunits = 0;
+  if (tnn != nullptr && is_gemv(tnn->type)) w2 = wave_run(p, *tnn, ctl->geoms[tnn->geom]);
+  if (w2.nunits <= 0) w2 = dummy_run(p);
+  if (!p.touch) w1 = w2 = dummy_run(p);
+  touch_ahead(w1, w2, sink);
 }
 
 __device__ __forceinline__ void gemv_tile(const KernelParams& p, const TaskDesc& t, const GemvGeom gm, const float* xs, float* ys,
@@ -348,30 +475,44 @@ __device__ __forceinline__ void gemv_tile(const KernelParams& p, const TaskDesc&
   }
 }
 
-// xs (two-plane layout, `padded` = 8 * pieces elements) = RMSNorm(src) * gain, zero past d.
-// src is the residual stream (fp32, coherent loads) or, for the first layer, the token's
-// embedding row (bf16).
-__device__ __forceinline__ void rmsnorm_to_lds(const KernelParams& p, const float* xsrc, const uint16_t* esrc, const uint16_t* gain,
-                               int d, int padded, float* xs, Ctl* ctl) {
-  const int np = padded >> 3;
+// xs (two-plane layout, `padded` = 8 * pieces elements) = RMSNorm(x) * gain, zero past d. x is the
+// tagged residual stream, or, for the first layer, the token's embedding row (bf16). The sum of
+// squares runs over the staged values in a fixed order, so it does not depend on arrival order.
+__device__ __forceinline__ void rmsnorm_to_lds(const KernelParams& p, const uint64_t* xsrc, const uint16_t* esrc,
+                                               const uint16_t* gain, int d, int padded, float* xs, Ctl* ctl,
+                                               uint32_t what) {
+  const int np = padded >> 3, tid = threadIdx.x;
+  if (esrc) {
+    for (int i = tid; i < d; i += NT) xs[xs_index(i, np)] = bf2f(esrc[i]);
+  } else {
+    // word i0 + 64k lands at xs_index(i0) + 32k (64 elements are 8 whole pieces)
+    float* xd = xs + xs_index(poll_index(d, 0), np);
+    poll_vector<16>(p, xsrc, d, what, [&](int k, uint32_t b) { xd[32 * k] = __uint_as_float(b); });
+  }
+  for (int i = d + tid; i < padded; i += NT) xs[xs_index(i, np)] = 0.f;
+  bar();
   float ss = 0.f;
-  for (int i = threadIdx.x; i < padded; i += NT) {
-    const float v = (i < d) ? (esrc ? bf2f(esrc[i]) : ldc(&xsrc[i])) : 0.f;
-    xs[xs_index(i, np)] = v;
+  for (int i = tid; i < d; i += NT) {
+    const float v = xs[xs_index(i, np)];
     ss += v * v;
   }
   ss = block_sum(ss, ctl);
   const float r = 1.0f / sqrtf(ss / (float)d + p.eps);
-  for (int i = threadIdx.x; i < d; i += NT) {  // each thread rescales the entries it wrote
+  for (int i = tid; i < d; i += NT) {
     const int k = xs_index(i, np);
     xs[k] = xs[k] * r * bf2f(gain[i]);
   }
   bar();
 }
 
-__device__ __forceinline__ void load_vec_to_lds(const float* src, int n, int padded, float* xs) {
-  const int np = padded >> 3;
-  for (int i = threadIdx.x; i < padded; i += NT) xs[xs_index(i, np)] = (i < n) ? ldc(&src[i]) : 0.f;
+// xs (two-plane layout) = the tagged vector src[0, n), zero up to `padded`.
+template <int K>
+__device__ __forceinline__ void load_tagged_to_lds(const KernelParams& p, const uint64_t* src, int n, int padded,
+                                                   float* xs, uint32_t what) {
+  const int np = padded >> 3, tid = threadIdx.x;
+  float* xd = xs + xs_index(poll_index(n, 0), np);  // word i0 + 64k lands at xs_index(i0) + 32k
+  poll_vector<K>(p, src, n, what, [&](int k, uint32_t b) { xd[32 * k] = __uint_as_float(b); });
+  for (int i = n + tid; i < padded; i += NT) xs[xs_index(i, np)] = 0.f;
   bar();
 }
 
@@ -437,20 +578,26 @@ __device__ __forceinline__ void task_qkv(const KernelParams& p, const TaskDesc& 
   const int s = 0;
   const int l = t.layer;
   const int G = p.hq / p.hk, dh = p.dh, Rg = (G + 2) * dh;
+  // An out-of-range position is reported and the row is not appended, but q, k and v are still
+  // written (at position 0's rotation) so that no consumer waits for them.
   const int pos = checked_pos(p, ctl, s);
-  const int nsets = pos < 0 ? 0 : (t.row1 - t.row0) >> 2;
+  const int posc = pos < 0 ? 0 : pos;
+  const int nsets = (t.row1 - t.row0) >> 2;
+  const uint32_t ep = p.epoch;
   QkvSet pre;
-  if ((int)threadIdx.x < nsets) pre = qkv_set_consts(p, l, t.row0 + 4 * threadIdx.x, pos, s);
+  if ((int)threadIdx.x < nsets) pre = qkv_set_consts(p, l, t.row0 + 4 * threadIdx.x, posc, s);
   const uint16_t* esrc = nullptr;
   if (l == 0) esrc = p.embed + (size_t)token_of(p, s) * p.d;
-  rmsnorm_to_lds(p, p.x + (size_t)s * p.d, esrc, layer_norm_gain(p, l, 0), p.d, padded, xs, ctl);
+  rmsnorm_to_lds(p, l > 0 ? xt_at(p, l - 1, 1, s) : nullptr, esrc, layer_norm_gain(p, l, 0), p.d, padded, xs, ctl,
+                 (uint32_t)t.wait_ev);
+  if (p.trace && threadIdx.x == 0) ctl->t_ready = __builtin_amdgcn_s_memrealtime();
   gemv_tile(p, t, gm, xs, ys, wp);
   bar();
   for (int m = threadIdx.x; m < nsets; m += NT) {
     const int r = t.row0 + 4 * m;
     const int grp = r / Rg, within = r % Rg, slot = within / dh, jh = within % dh;
     const int i0 = jh >> 1;  // even dim index; the set holds dims i0, i0 + dh/2, i0 + 1, i0 + 1 + dh/2
-    const QkvSet c = (m == (int)threadIdx.x) ? pre : qkv_set_consts(p, l, r, pos, s);
+    const QkvSet c = (m == (int)threadIdx.x) ? pre : qkv_set_consts(p, l, r, posc, s);
     float y0 = ys[4 * m] + c.b0, y1 = ys[4 * m + 1] + c.b1, y2 = ys[4 * m + 2] + c.b2, y3 = ys[4 * m + 3] + c.b3;
     if (slot <= G) {  // rotate q and k: pair (i0, i0 + dh/2) and pair (i0 + 1, i0 + 1 + dh/2)
       const float a0 = y0 * c.cs0.x - y1 * c.cs0.y, b0 = y1 * c.cs0.x + y0 * c.cs0.y;
@@ -458,21 +605,27 @@ __device__ __forceinline__ void task_qkv(const KernelParams& p, const TaskDesc& 
       y0 = a0; y1 = b0; y2 = a1; y3 = b1;
     }
     if (slot < G) {
-      float* q = p.q + (size_t)s * p.hq * dh + (size_t)(grp * G + slot) * dh;
-      stc(&q[i0], y0);
-      stc(&q[i0 + dh / 2], y1);
-      stc(&q[i0 + 1], y2);
-      stc(&q[i0 + 1 + dh / 2], y3);
+      uint64_t* q = qt_at(p, l, s) + (size_t)(grp * G + slot) * dh;
+      st_tagf(&q[i0], y0, ep);
+      st_tagf(&q[i0 + dh / 2], y1, ep);
+      st_tagf(&q[i0 + 1], y2, ep);
+      st_tagf(&q[i0 + 1 + dh / 2], y3, ep);
     } else {
+      // the rounded key/value pairs go to the cache and, tagged, to this step's attention
+      const uint32_t w0 = f2bf(y0) | (f2bf(y2) << 16), w1 = f2bf(y1) | (f2bf(y3) << 16);
+      uint64_t* kv = kvt_at(p, l, s, slot == G ? 0 : 1, grp);
+      st_tag(&kv[i0 >> 1], w0, ep);
+      st_tag(&kv[(i0 + dh / 2) >> 1], w1, ep);
       const int blk = c.blk;
       if (blk < 0 || blk >= p.num_blocks) {
         raise_error(p, ERR_PAGE, (uint32_t)s, (uint32_t)blk);
         continue;
       }
+      if (pos < 0) continue;
       uint16_t* pool = pools[(slot == G ? 0 : p.n_layers) + l];
       uint32_t* row = (uint32_t*)(pool + (((size_t)blk * p.hk + grp) * 16 + (pos & 15)) * dh);
-      stc(&row[i0 >> 1], f2bf(y0) | (f2bf(y2) << 16));
-      stc(&row[(i0 + dh / 2) >> 1], f2bf(y1) | (f2bf(y3) << 16));
+      stc(&row[i0 >> 1], w0);
+      stc(&row[(i0 + dh / 2) >> 1], w1);
     }
   }
 }
@@ -489,17 +642,6 @@ __device__ __forceinline__ void task_qkv(const KernelParams& p, const TaskDesc& 
 // softmax of "Hạt nhân là gì và tại sao mọi người lại viết hạt nhân mới"). The partial
 // (m, l, unnormalised o) goes to `part`. The split that finishes last merges all partials by
 // log-sum-exp and publishes the group's slot.
-// Coherent read of this lane's 16 bytes of the current position's row (written in this step).
-__device__ __forceinline__ v4u ldc_row(const uint16_t* rp) {
-  const uint32_t* r32 = (const uint32_t*)rp;
-  v4u v;
-  v.x = ldc(&r32[0]);
-  v.y = ldc(&r32[1]);
-  v.z = ldc(&r32[2]);
-  v.w = ldc(&r32[3]);
-  return v;
-}
-
 template <int DH, int GMAX>
 __device__ __forceinline__ void task_attn(const KernelParams& p, const TaskDesc& t, float* lds, Ctl* ctl,
                                           uint16_t* const* pools) {
@@ -517,19 +659,43 @@ __device__ __forceinline__ void task_attn(const KernelParams& p, const TaskDesc&
   float* scores = (float*)(vb + ASLOTS * NW * 64);  // [G][CHUNK]
   float* obuf = scores + G * CHUNK;                  // [NW][G][DH]
   float* qs = obuf + NW * G * DH;                    // [G][2][DH/2]: dims 8c..8c+3 at 4c, 8c+4..8c+7 at DH/2 + 4c
+  uint32_t* kvc = (uint32_t*)(qs + G * DH);          // the current position's key (DH/2 words) then value row
   const int splits = p.splits;
   float* part = p.part + ((size_t)s * p.hq) * splits * (DH + 2);
   const uint16_t* kpool = pools[t.layer];
   const uint16_t* vpool = pools[p.n_layers + t.layer];
   const float scale = 1.0f / sqrtf((float)DH);
 
+  const int tid = threadIdx.x;
+  const uint32_t what = (uint32_t)t.wait_ev;
   wait_stores();  // this wave's staged rows (issued before the wait) have landed in LDS
   // the group's queries, staged in LDS (two planes per head, so lanes reading consecutive
   // 8-dim pieces read consecutive 16-byte words)
-  for (int i = threadIdx.x; i < G * DH; i += NT) {
-    const int h = i / DH, d = i % DH, pc = d >> 3, e = d & 7;
-    qs[h * DH + (e < 4 ? 0 : DH / 2) + pc * 4 + (e & 3)] = active ? ldc(&p.q[(size_t)s * p.hq * DH + (size_t)(h0 + h) * DH + d]) : 0.f;
+  auto q_slot = [&](int i) -> float& {
+    const int h = i / DH, d = i % DH, e = d & 7;
+    return qs[h * DH + (e < 4 ? 0 : DH / 2) + (d >> 3) * 4 + (e & 3)];
+  };
+  // One poll for the group's queries (words k < KQ of each thread, laid out as a vector poll) and
+  // the current position's key and value rows (words KQ and KQ + 1 of the first DH/2 threads).
+  constexpr int KQ = (GMAX * DH + NW * 64 - 1) / (NW * 64);
+  if (active) {
+    const uint64_t* qsrc = qt_at(p, t.layer, s) + (size_t)h0 * DH;
+    const int nq = G * DH, iq = poll_index(nq, 0);
+    const int dk = (int)((const char*)kvt_at(p, t.layer, s, 0, grp) - (const char*)qsrc);  // bytes, > 0
+    const int dv = dk + p.hk * (DH / 2) * 8;
+    uint32_t pend = first_words(min(poll_chunk(nq) / 64, (nq - iq + 63) / 64));
+    if (tid < DH / 2) pend |= 3u << KQ;
+    poll_tagged<KQ + 2>(
+        p, qsrc, [&](int k) { return k < KQ ? iq * 8 + k * 512 : tid * 8; },
+        [&](int k) { return k < KQ ? 0 : k == KQ ? dk : dv; }, pend, what, [&](int k, uint32_t b) {
+          if (k < KQ) q_slot(iq + 64 * k) = __uint_as_float(b);
+          else kvc[(k - KQ) * (DH / 2) + tid] = b;
+        });
+  } else {
+    for (int i = tid; i < G * DH; i += NT) q_slot(i) = 0.f;
   }
+  bar();
+  if (p.trace && tid == 0) ctl->t_ready = __builtin_amdgcn_s_memrealtime();
   float oacc[GMAX][8];
 #pragma unroll
   for (int h = 0; h < GMAX; ++h)
@@ -547,17 +713,12 @@ __device__ __forceinline__ void task_attn(const KernelParams& p, const TaskDesc&
       attn_stage_chunk<DH>(p, t, cs, old_end, pools, lds);
       wait_stores();
     }
-    // the current position's key and value come from this step: coherent loads into its slot
+    // the current position's key and value come from this step (polled above) into their slot
     if (pos >= cs && pos < ce) {
       const int idx = pos - cs, ic = idx / (NW * PPW), wc = (idx / PPW) % NW, pc = idx % PPW;
-      if (wave == wc && pg == pc) {
-        const size_t row = 0;
-        (void)row;
-        int b = p.page_table[(size_t)s * p.max_blocks + (pos >> 4)];
-        if (b < 0 || b >= p.num_blocks) b = 0;  // already reported when the row was appended
-        const size_t off = (((size_t)b * p.hk + grp) * 16 + (pos & 15)) * DH + c * 8;
-        kb[(ic * NW + wc) * 64 + lane] = ldc_row(kpool + off);
-        vb[(ic * NW + wc) * 64 + lane] = ldc_row(vpool + off);
+      if (wave == wc && pg == pc) {  // lane c's 8 dims are words 4c..4c+3 of each row
+        kb[(ic * NW + wc) * 64 + lane] = *(const v4u*)(kvc + 4 * c);
+        vb[(ic * NW + wc) * 64 + lane] = *(const v4u*)(kvc + DH / 2 + 4 * c);
       }
     }
     bar();  // queries staged; patched rows visible
@@ -665,10 +826,13 @@ __device__ __forceinline__ void task_attn(const KernelParams& p, const TaskDesc&
     ctl->flag = (old + 1 == p.epoch * (uint32_t)splits) ? 1u : 0u;
   }
   bar();
-  if (!ctl->flag) return;  // only the last split merges and publishes
-  if (active) {
-    // log-sum-exp merge; each split's three loads are independent of the previous split's values
-    for (int i = threadIdx.x; i < G * DH; i += NT) {
+  if (!ctl->flag) return;  // only the last split merges
+  // log-sum-exp merge; each split's three loads are independent of the previous split's values.
+  // The group's output is written (tagged) even for an inactive sequence, as zeros.
+  uint64_t* od = ot_at(p, t.layer, s) + (size_t)h0 * DH;
+  for (int i = threadIdx.x; i < G * DH; i += NT) {
+    float v = 0.f;
+    if (active) {
       const int h = i / DH, dd = i % DH;
       const float* ph = part + (size_t)(h0 + h) * splits * (DH + 2);
       float M = -INFINITY, Lsum = 0.f, acc = 0.f;
@@ -691,31 +855,65 @@ __device__ __forceinline__ void task_attn(const KernelParams& p, const TaskDesc&
           M = mn;
         }
       }
-      stc(&p.o[(size_t)s * p.hq * DH + (size_t)(h0 + h) * DH + dd], acc / Lsum);
+      v = acc / Lsum;
     }
+    st_tagf(&od[i], v, p.epoch);
   }
 }
 
 // ----------------------------------------------------------------------------- O / down projection
+// x_out[r] = x_in[r] + (W . v)[r] for the task's rows. O-proj: v = attention output, x_in = x after
+// the previous layer's down-proj (the embedding row for the first layer). Down-proj: v = SwiGLU
+// output, x_in = x after this layer's O-proj. The residual words are loaded before the input vector
+// is polled; they were written a stage before the vector, so they are nearly always current by then,
+// and a stale one is polled again afterwards.
 __device__ __forceinline__ void task_residual_gemv(const KernelParams& p, const TaskDesc& t, float* lds, Ctl* ctl,
-                                                   int geom, const float* in, int n_in, WPipe& wp) {
-  const GemvGeom gm = ctl->geoms[geom];
+                                                   WPipe& wp) {
+  const bool is_o = t.type == T_OPROJ;
+  const GemvGeom gm = ctl->geoms[is_o ? G_O : G_D];
   const int padded = gm.S * gm.lpr * 8;
   float* xs = lds;
   float* ys = lds + padded;
-  const int s = 0;
-  const bool from_embed = (t.type == T_OPROJ && t.layer == 0);
+  const int s = 0, l = t.layer, tid = threadIdx.x;
+  const uint32_t what = (uint32_t)t.wait_ev;
+  const bool from_embed = is_o && l == 0;
   const uint16_t* erow = from_embed ? p.embed + (size_t)token_of(p, s) * p.d : nullptr;
-  // the residual rows are loaded together with the input vector, ahead of the GEMV
-  const int r_pre = t.row0 + threadIdx.x;
-  float resid_pre = 0.f;
-  if (r_pre < t.row1) resid_pre = from_embed ? bf2f(erow[r_pre]) : ldc(&p.x[(size_t)s * p.d + r_pre]);
-  load_vec_to_lds(in + (size_t)s * n_in, n_in, padded, xs);
+  const uint64_t* rsrc = is_o ? xt_at(p, l > 0 ? l - 1 : 0, 1, s) : xt_at(p, l, 0, s);
+  float res[4] = {0.f, 0.f, 0.f, 0.f};
+  // the residual words, loaded unconditionally (clamped to the task's last row) ahead of the poll
+  const int nrows = t.row1 - t.row0;
+  uint64_t rw[4];
+  const __amdgpu_buffer_rsrc_t rr = tag_rsrc(rsrc + t.row0);
+#pragma unroll
+  for (int k = 0; k < 4; ++k) rw[k] = ld_tag(rr, min(tid + k * NT, nrows - 1) * 8, 0);
+  if (from_embed) {
+#pragma unroll
+    for (int k = 0; k < 4; ++k)
+      if (tid + k * NT < nrows) res[k] = bf2f(erow[t.row0 + tid + k * NT]);
+  }
+  if (is_o) load_tagged_to_lds<16>(p, ot_at(p, l, s), p.hq * p.dh, padded, xs, what);
+  else load_tagged_to_lds<32>(p, ht_at(p, l, s), p.f, padded, xs, what);
+  if (!from_embed) {
+    uint32_t stale = 0;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      if (t.row0 + tid + k * NT < t.row1) {
+        if ((uint32_t)(rw[k] >> 32) == p.epoch) res[k] = __uint_as_float((uint32_t)rw[k]);
+        else stale |= 1u << k;
+      }
+    }
+    if (__any(stale != 0u))
+      poll_tagged<4>(p, rsrc + t.row0, [&](int k) { return (tid + k * NT) * 8; }, [](int) { return 0; }, stale, what,
+                     [&](int k, uint32_t b) { res[k] = __uint_as_float(b); });
+  }
+  if (p.trace && tid == 0) ctl->t_ready = __builtin_amdgcn_s_memrealtime();
   gemv_tile(p, t, gm, xs, ys, wp);
   bar();
-  for (int r = r_pre; r < t.row1; r += NT) {
-    const float resid = (r == r_pre) ? resid_pre : from_embed ? bf2f(erow[r]) : ldc(&p.x[(size_t)s * p.d + r]);
-    stc(&p.x[(size_t)s * p.d + r], resid + ys[r - t.row0]);
+  uint64_t* dst = xt_at(p, l, is_o ? 0 : 1, s);
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    const int r = t.row0 + tid + k * NT;
+    if (r < t.row1) st_tagf(&dst[r], res[k] + ys[r - t.row0], p.epoch);
   }
 }
 
@@ -726,14 +924,17 @@ __device__ __forceinline__ void task_gateup(const KernelParams& p, const TaskDes
   float* xs = lds;
   float* ys = lds + padded;
   const int s = 0;
-  rmsnorm_to_lds(p, p.x + (size_t)s * p.d, nullptr, layer_norm_gain(p, t.layer, 1), p.d, padded, xs, ctl);
+  rmsnorm_to_lds(p, xt_at(p, t.layer, 0, s), nullptr, layer_norm_gain(p, t.layer, 1), p.d, padded, xs, ctl,
+                 (uint32_t)t.wait_ev);
+  if (p.trace && threadIdx.x == 0) ctl->t_ready = __builtin_amdgcn_s_memrealtime();
   gemv_tile(p, t, gm, xs, ys, wp);
   bar();
   const int npairs = (t.row1 - t.row0) >> 1;
+  uint64_t* hd = ht_at(p, t.layer, s) + (t.row0 >> 1);
   for (int m = threadIdx.x; m < npairs; m += NT) {
     const float a = ys[2 * m], b = ys[2 * m + 1];
     const float silu = a / (1.0f + expf(-a));
-    stc(&p.h[(size_t)s * p.f + (t.row0 >> 1) + m], silu * b);
+    st_tagf(&hd[m], silu * b, p.epoch);
   }
 }
 
@@ -766,7 +967,9 @@ __device__ __forceinline__ void task_lmhead(const KernelParams& p, const TaskDes
   float* xs = lds;
   float* ys = lds + padded;
   const int s = 0;
-  rmsnorm_to_lds(p, p.x + (size_t)s * p.d, nullptr, p.norms + (size_t)p.n_layers * 2 * p.d, p.d, padded, xs, ctl);
+  rmsnorm_to_lds(p, xt_at(p, p.n_layers - 1, 1, s), nullptr, p.norms + (size_t)p.n_layers * 2 * p.d, p.d, padded, xs,
+                 ctl, (uint32_t)t.wait_ev);
+  if (p.trace && threadIdx.x == 0) ctl->t_ready = __builtin_amdgcn_s_memrealtime();
   gemv_tile(p, t, gm, xs, ys, wp);
   bar();
   uint64_t best = 0;
@@ -803,11 +1006,12 @@ __global__ __launch_bounds__(NT, 1) void mk_megakernel(KernelParams p) {
   extern __shared__ __attribute__((aligned(16))) unsigned char lds_raw[];
   static_assert(sizeof(Ctl) <= 1024, "control block fits its 1 KB");
   Ctl* ctl = (Ctl*)lds_raw;
-  // LDS: control block | per-layer K/V pool pointers | this CU's queue | working set
+  // LDS: control block | per-layer K/V pool pointers | cache-warming sink | this CU's queue | working set
   uint16_t** pools = (uint16_t**)(lds_raw + 1024);
   const size_t pools_bytes = ((size_t)2 * p.n_layers * sizeof(void*) + 255) & ~size_t(255);
-  TaskDesc* tq = (TaskDesc*)(lds_raw + 1024 + pools_bytes);
-  float* lds = (float*)(lds_raw + 1024 + pools_bytes + (((size_t)p.max_queue * sizeof(TaskDesc) + 255) & ~size_t(255)));
+  unsigned char* sink = lds_raw + 1024 + pools_bytes;
+  TaskDesc* tq = (TaskDesc*)(sink + TOUCH_SINK_BYTES);
+  float* lds = (float*)((unsigned char*)tq + (((size_t)p.max_queue * sizeof(TaskDesc) + 255) & ~size_t(255)));
   const int cu = blockIdx.x;
   const int q0 = p.queue_off[cu], q1 = p.queue_off[cu + 1];
   if (threadIdx.x < G_COUNT * (int)(sizeof(GemvGeom) / 4))
@@ -828,7 +1032,7 @@ __global__ __launch_bounds__(NT, 1) void mk_megakernel(KernelParams p) {
   WPipe wp;
   int ti_next = q0 < q1 ? p.queue_idx[q0] : 0;
   TaskDesc tn = tq[0];
-  prefetch_next<DH>(p, tn, q0 < q1, wp, ctl, pools, lds);
+  prefetch_next<DH>(p, tn, q0 < q1, q0 + 1 < q1 ? &tq[1] : nullptr, wp, ctl, pools, lds, sink);
   for (int qi = q0; qi < q1; ++qi) {
     const int ti = ti_next;
     const TaskDesc t = tn;
@@ -836,40 +1040,39 @@ __global__ __launch_bounds__(NT, 1) void mk_megakernel(KernelParams p) {
       tn = tq[qi + 1 - q0];
       ti_next = p.trace ? p.queue_idx[qi + 1] : 0;
     }
-    const int my_sig = (int)threadIdx.x < t.sig_n ? p.sig_slots[t.sig_off + threadIdx.x] : -1;
-    uint64_t t_queue = 0, t_ready = 0;
-    if (p.trace && threadIdx.x == 0) t_queue = __builtin_amdgcn_s_memrealtime();
-    bool aborted = false;
-    if (t.wait_ev >= 0) {
-      wait_event(p, t, ctl);
-      aborted = ctl->aborted != 0;
+    // Only the LM head's partial maxima travel under flags (the argmax task waits for them); every
+    // other input is a tagged activation that its consumer polls for inside the task.
+    const int my_sig = (t.type == T_LMHEAD && (int)threadIdx.x < t.sig_n) ? p.sig_slots[t.sig_off + threadIdx.x] : -1;
+    uint64_t t_queue = 0;
+    if (p.trace && threadIdx.x == 0) {
+      t_queue = __builtin_amdgcn_s_memrealtime();
+      ctl->t_ready = t_queue;
     }
-    if (p.trace && threadIdx.x == 0) t_ready = __builtin_amdgcn_s_memrealtime();
-    bool pub = true;  // publish this task's flag slots (attention: only the split that merged)
-    if (!aborted) {  // when aborted: publish without computing, so no other CU waits forever
-      switch (t.type) {
-        case T_QKV: task_qkv(p, t, lds, ctl, wp, pools); break;
-        case T_ATTN:
-          task_attn<DH, GMAX>(p, t, lds, ctl, pools);
-          pub = ctl->flag != 0;
-          break;
-        case T_OPROJ: task_residual_gemv(p, t, lds, ctl, G_O, p.o, p.hq * p.dh, wp); break;
-        case T_GATEUP: task_gateup(p, t, lds, ctl, wp); break;
-        case T_DOWN: task_residual_gemv(p, t, lds, ctl, G_D, p.h, p.f, wp); break;
-        case T_LMHEAD: task_lmhead(p, t, lds, ctl, wp); break;
-        case T_ARGMAX: task_argmax(p, t, ctl); break;
-        default: break;
-      }
+    switch (t.type) {
+      case T_QKV: task_qkv(p, t, lds, ctl, wp, pools); break;
+      case T_ATTN: task_attn<DH, GMAX>(p, t, lds, ctl, pools); break;
+      case T_OPROJ:
+      case T_DOWN: task_residual_gemv(p, t, lds, ctl, wp); break;
+      case T_GATEUP: task_gateup(p, t, lds, ctl, wp); break;
+      case T_LMHEAD: task_lmhead(p, t, lds, ctl, wp); break;
+      case T_ARGMAX:
+        if (t.wait_ev >= 0) wait_event(p, t, ctl);
+        if (p.trace && threadIdx.x == 0) ctl->t_ready = __builtin_amdgcn_s_memrealtime();
+        if (t.wait_ev < 0 || !ctl->aborted) task_argmax(p, t, ctl);
+        break;
+      default: break;
     }
-    wait_stores();
+    // The LM head's stores must be complete before its flags go out; other tasks' consumers check
+    // the tags themselves.
+    if (t.type == T_LMHEAD) wait_stores();
     bar();
     // Publish, then start streaming the next task's weights before waiting for its inputs.
-    if (pub) publish(p, my_sig);
-    prefetch_next<DH>(p, tn, qi + 1 < q1, wp, ctl, pools, lds);
+    publish(p, my_sig);
+    prefetch_next<DH>(p, tn, qi + 1 < q1, qi + 2 < q1 ? &tq[qi + 2 - q0] : nullptr, wp, ctl, pools, lds, sink);
     if (p.trace && threadIdx.x == 0) {
       TraceRec r;
       r.t_queue = t_queue;
-      r.t_ready = t_ready;
+      r.t_ready = ctl->t_ready;
       r.t_done = __builtin_amdgcn_s_memrealtime();
       r.cu = (uint16_t)cu;
       r.type = (uint8_t)t.type;
