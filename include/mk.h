@@ -175,7 +175,7 @@ mk_status mk_set_trace(mk_ctx* ctx, void* d_buf, size_t bytes);
  *     Returns MK_OK if every task ran with its inputs complete and no buffer
  *     was overwritten while a pending reader needed it. */
 typedef struct {
-  int64_t n_tasks, n_events, n_flag_slots, n_counters, max_queue_len;
+  int64_t n_tasks, n_events, n_flag_slots, n_attn_groups, max_queue_len;
   int64_t weight_bytes, lds_bytes;
   uint64_t hash;
 } mk_graph_info;

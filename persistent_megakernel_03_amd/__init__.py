@@ -45,7 +45,7 @@ class mk_tensor(ctypes.Structure):
 
 class mk_graph_info(ctypes.Structure):
     _fields_ = [("n_tasks", ctypes.c_int64), ("n_events", ctypes.c_int64), ("n_flag_slots", ctypes.c_int64),
-                ("n_counters", ctypes.c_int64), ("max_queue_len", ctypes.c_int64), ("weight_bytes", ctypes.c_int64),
+                ("n_attn_groups", ctypes.c_int64), ("max_queue_len", ctypes.c_int64), ("weight_bytes", ctypes.c_int64),
                 ("lds_bytes", ctypes.c_int64), ("hash", ctypes.c_uint64)]
 
 

@@ -38,7 +38,6 @@ struct mk_ctx {
   float* d_logits = nullptr;
   uint32_t epoch = 0;
   uint32_t watchdog_ticks = 200000000u;  // 2 s at 100 MHz
-  int32_t touch = 0;                      // cache warming at task boundaries (MK_TOUCH=0 turns it off)
   TraceRec* d_trace = nullptr;
 };
 
@@ -83,7 +82,6 @@ mk_status build(const mk_model_config* cfg, int n_cus, mk_ctx** out) {
     const long us = std::atol(w);
     if (us > 0 && us < 40000000L) c->watchdog_ticks = (uint32_t)(us * 100L);
   }
-  if (const char* t = std::getenv("MK_TOUCH")) c->touch = std::atoi(t) != 0;  // off by default: it delayed the waits
   *out = c;
   return MK_OK;
 }
@@ -104,7 +102,7 @@ mk_status read_error_word(mk_ctx* c, hipStream_t st) {
   HIPCHK(hipStreamSynchronize(st));
   HIPCHK(hipMemcpy(e, c->d_scratch + c->g.sl.err, sizeof(e), hipMemcpyDeviceToHost));
   if (e[E_CODE] == ERR_NONE) return MK_OK;
-  // clear the word; after a timeout the flags and counters are inconsistent, so reset them too
+  // clear the word; after a timeout the flags are inconsistent, so reset them too
   HIPCHK(hipMemset(c->d_scratch + c->g.sl.err, 0, E_COUNT * 4));
   std::string what;
   mk_status s = MK_ERR_DEVICE_FAULT;
@@ -117,7 +115,6 @@ mk_status read_error_word(mk_ctx* c, hipStream_t st) {
   }
   if (e[E_ABORT] || s == MK_ERR_DEVICE_TIMEOUT) {
     HIPCHK(hipMemset(c->d_scratch + c->g.sl.flags, 0, (size_t)c->g.n_flag_slots * 4));
-    HIPCHK(hipMemset(c->d_scratch + c->g.sl.counters, 0, (size_t)c->g.n_counters * 4));
     // epochs restart at 1, so tags of the aborted steps must not survive
     HIPCHK(hipMemset(c->d_scratch + c->g.sl.tagged_begin, 0, (size_t)(c->g.sl.tagged_end - c->g.sl.tagged_begin)));
     HIPCHK(hipDeviceSynchronize());
@@ -139,7 +136,6 @@ KernelParams make_params(mk_ctx* c) {
   p.geoms = (const GemvGeom*)(S + g.sl.geoms);
   p.rope = (const float*)(S + g.sl.rope);
   p.flags = (uint32_t*)(S + g.sl.flags);
-  p.counters = (uint32_t*)(S + g.sl.counters);
   p.err = (uint32_t*)(S + g.sl.err);
   p.wpacked = c->d_weights;
   p.embed = (const uint16_t*)(c->d_weights + g.wl.embed);
@@ -154,7 +150,7 @@ KernelParams make_params(mk_ctx* c) {
   p.kvt = (uint64_t*)(S + g.sl.kvt);
   p.ot = (uint64_t*)(S + g.sl.ot);
   p.ht = (uint64_t*)(S + g.sl.ht);
-  p.part = (float*)(S + g.sl.part);
+  p.pt = (uint64_t*)(S + g.sl.pt);
   p.logits = c->d_logits;
   p.amax = (uint64_t*)(S + g.sl.amax);
   p.n_layers = m.n_layers;
@@ -173,7 +169,6 @@ KernelParams make_params(mk_ctx* c) {
   p.n_lm_parts = g.n_lm_parts;
   p.max_pos = g.max_pos;
   p.watchdog_ticks = c->watchdog_ticks;
-  p.touch = c->touch;
   p.max_queue = g.max_queue;
   p.trace = c->d_trace;
   return p;
@@ -264,7 +259,6 @@ mk_status mk_bind_memory(mk_ctx* c, void* d_weights, void* const* d_k_pools, voi
   pools.insert(pools.end(), c->vpools.begin(), c->vpools.end());
   HIPCHK(up(g.sl.pools, pools.data(), pools.size() * 8));
   HIPCHK(hipMemset(S + g.sl.flags, 0, (size_t)g.n_flag_slots * 4));
-  HIPCHK(hipMemset(S + g.sl.counters, 0, (size_t)std::max(g.n_counters, 1) * 4));
   HIPCHK(hipMemset(S + g.sl.err, 0, E_COUNT * 4));
   HIPCHK(hipMemset(S + g.sl.tagged_begin, 0, (size_t)(g.sl.tagged_end - g.sl.tagged_begin)));
   HIPCHK(hipDeviceSynchronize());
@@ -431,7 +425,7 @@ mk_status mk_graph_stats(const mk_ctx* c, mk_graph_info* out) {
   out->n_tasks = (int64_t)g.tasks.size();
   out->n_events = (int64_t)g.events.size();
   out->n_flag_slots = g.n_flag_slots;
-  out->n_counters = g.n_counters;
+  out->n_attn_groups = g.n_attn_groups;
   int64_t mq = 0;
   for (int i = 0; i < g.n_cus; ++i) mq = std::max<int64_t>(mq, g.queue_off[i + 1] - g.queue_off[i]);
   out->max_queue_len = mq;

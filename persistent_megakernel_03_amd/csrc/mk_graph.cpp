@@ -88,18 +88,22 @@ struct Builder {
     const GemvGeom& q = g.geoms[geom];
     return (int64_t)((rows + q.rg - 1) / q.rg) * q.S * 1024;
   }
-  // A GEMV stage: one task per CU with a non-empty row range.
-  std::vector<int> gemv_stage(int type, int layer, int geom, int N, int A, int wait_ev) {
-    std::vector<int> ids;
-    auto rs = distribute(N, A, g.n_cus);
-    for (int cu = 0; cu < g.n_cus; ++cu) {
-      if (rs[cu].r1 <= rs[cu].r0) continue;
+  // A GEMV stage: one task per CU with a non-empty row range, over the CUs not marked in `skip`.
+  std::vector<int> gemv_stage(int type, int layer, int geom, int N, int A, int wait_ev,
+                              const std::vector<char>* skip = nullptr) {
+    std::vector<int> ids, cus;
+    for (int cu = 0; cu < g.n_cus; ++cu)
+      if (!skip || !(*skip)[cu]) cus.push_back(cu);
+    auto rs = distribute(N, A, (int)cus.size());
+    for (size_t k = 0; k < cus.size(); ++k) {
+      const int cu = cus[k];
+      if (rs[k].r1 <= rs[k].r0) continue;
       TaskDesc t{};
       t.type = type;
       t.layer = layer;
       t.wait_ev = wait_ev;
-      t.row0 = rs[cu].r0;
-      t.row1 = rs[cu].r1;
+      t.row0 = rs[k].r0;
+      t.row1 = rs[k].r1;
       t.geom = geom;
       t.wofs = packed;
       packed += tile_bytes(geom, t.row1 - t.row0);
@@ -205,6 +209,9 @@ std::string build_graph(const mk_model_config& c, int n_cus, HostGraph& g) {
     }
     // ---- attention splits; the last split of each (seq, kv head) merges and signals
     const int ev_att = b.new_event(S * hk);
+    // CUs running attention get no O-projection task in the same layer when they are few: their
+    // register pipelines sit idle through attention, while the other CUs hold their O tiles there.
+    std::vector<char> attn_cu(n_cus, 0);
     {
       const int n_attn = S * hk * g.splits;
       int k = 0;
@@ -220,6 +227,7 @@ std::string build_graph(const mk_model_config& c, int n_cus, HostGraph& g) {
             t.a2 = j;
             t.a3 = (l * S + s) * hk + grp;
             const int cu = (int)((int64_t)k * n_cus / n_attn);
+            attn_cu[cu] = 1;
             const int id = b.add_task(t, cu);
             b.task_sig[id].push_back({ev_att, s * hk + grp});
             b.acc(id, S_Q, (int64_t)s * qd + (int64_t)grp * G * dh, (int64_t)s * qd + (int64_t)(grp + 1) * G * dh, 0);
@@ -231,10 +239,11 @@ std::string build_graph(const mk_model_config& c, int n_cus, HostGraph& g) {
               b.cacc(id, S_PART, ((int64_t)s * hq + h) * g.splits, ((int64_t)s * hq + h + 1) * g.splits, 0);
             b.cacc(id, S_O, (int64_t)s * qd + (int64_t)grp * G * dh, (int64_t)s * qd + (int64_t)(grp + 1) * G * dh, 1);
           }
-      g.n_counters = std::max(g.n_counters, (l + 1) * S * hk);
+      g.n_attn_groups = std::max(g.n_attn_groups, (l + 1) * S * hk);
     }
     // ---- O projection + residual
-    auto op = b.gemv_stage(T_OPROJ, l, G_O, d, g.geoms[G_O].rg, ev_att);
+    const bool few_attn = (int)std::count(attn_cu.begin(), attn_cu.end(), 1) * 4 <= n_cus;
+    auto op = b.gemv_stage(T_OPROJ, l, G_O, d, g.geoms[G_O].rg, ev_att, few_attn ? &attn_cu : nullptr);
     const int ev_o = b.new_event((int)op.size());
     for (size_t i = 0; i < op.size(); ++i) {
       const int t = op[i];
@@ -355,7 +364,6 @@ std::string build_graph(const mk_model_config& c, int n_cus, HostGraph& g) {
   g.sl.geoms = take((int64_t)G_COUNT * sizeof(GemvGeom));
   g.sl.rope = take((int64_t)g.max_pos * (dh / 2) * 8);
   g.sl.flags = take((int64_t)g.n_flag_slots * 4);
-  g.sl.counters = take((int64_t)g.n_counters * 4);
   g.sl.err = take((int64_t)E_COUNT * 4);
   g.sl.tagged_begin = o;
   g.sl.xt = take((int64_t)L * 2 * S * d * 8);
@@ -363,8 +371,8 @@ std::string build_graph(const mk_model_config& c, int n_cus, HostGraph& g) {
   g.sl.kvt = take((int64_t)L * S * 2 * hk * (dh / 2) * 8);
   g.sl.ot = take((int64_t)L * S * qd * 8);
   g.sl.ht = take((int64_t)L * S * f * 8);
+  g.sl.pt = take((int64_t)L * S * hq * g.splits * (dh + 2) * 8);
   g.sl.tagged_end = o;
-  g.sl.part = take((int64_t)S * hq * g.splits * (dh + 2) * 4);
   g.sl.amax = take((int64_t)S * g.n_lm_parts * 8);
   g.sl.tokbuf = take((int64_t)std::max(g.max_pos, 64) * 4);
   g.sl.tokout = take(64 * 4);
@@ -385,10 +393,10 @@ std::string build_graph(const mk_model_config& c, int n_cus, HostGraph& g) {
   int max_q = 0;
   for (int cu = 0; cu < n_cus; ++cu) max_q = std::max(max_q, g.queue_off[cu + 1] - g.queue_off[cu]);
   g.max_queue = max_q;
-  // control block + pool pointers + the touch-ahead sink (1 KB per wave) + this CU's task descriptors
-  // + the larger of the GEMV and attention working sets
-  g.lds_bytes = 1024 + align_up((int64_t)2 * L * 8, 256) + TOUCH_SINK_BYTES +
-                align_up((int64_t)max_q * (int64_t)sizeof(TaskDesc), 256) + align_up(std::max(gemv_lds, attn_lds), 256);
+  // control block + pool pointers + this CU's task descriptors + the larger of the GEMV and
+  // attention working sets
+  g.lds_bytes = 1024 + align_up((int64_t)2 * L * 8, 256) + align_up((int64_t)max_q * (int64_t)sizeof(TaskDesc), 256) +
+                align_up(std::max(gemv_lds, attn_lds), 256);
   if (g.lds_bytes > 160 * 1024) return "working set exceeds 160 KB of LDS";
   return "";
 }
@@ -470,11 +478,11 @@ uint64_t sm_next(uint64_t& s) {
 
 std::string simulate_graph(const HostGraph& g, uint64_t seed, int n_steps) {
   const int nt = (int)g.tasks.size();
-  // Static writer/reader lists per element (a writer of an ATTN merge is attributed to the
-  // group's last split in global order).
+  // Static writer/reader lists per element. An attention group's merge is performed by its last
+  // split (in global order), which polls the other splits' partials: it cannot finish before they do.
   std::vector<int> comb_pos(nt, -1);
   {
-    std::vector<int> last_of_group(g.n_counters, -1);
+    std::vector<int> last_of_group(g.n_attn_groups, -1);
     for (int t = 0; t < nt; ++t)
       if (g.tasks[t].type == T_ATTN) last_of_group[g.tasks[t].a3] = t;
     for (int t = 0; t < nt; ++t)
@@ -505,7 +513,8 @@ std::string simulate_graph(const HostGraph& g, uint64_t seed, int n_steps) {
   // Dynamic state.
   std::vector<std::vector<int64_t>> ver(S_COUNT);  // step * nt + writer position, or -1
   for (int b = 0; b < S_COUNT; ++b) ver[b].assign(g.sym_size[b], -1);
-  std::vector<uint32_t> flags(g.n_flag_slots, 0), counters(g.n_counters, 0);
+  std::vector<uint32_t> flags(g.n_flag_slots, 0);
+  std::vector<int> group_ended(g.n_attn_groups, 0);
   uint64_t rng = seed;
   for (int step = 0; step < n_steps; ++step) {
     const uint32_t epoch = (uint32_t)step + 1;
@@ -563,7 +572,12 @@ std::string simulate_graph(const HostGraph& g, uint64_t seed, int n_steps) {
     while (done < nt) {
       cand.clear();
       for (int cu = 0; cu < g.n_cus; ++cu) {
-        if (running[cu] >= 0) cand.push_back(cu);
+        if (running[cu] >= 0) {
+          // a merging split ends only after the other splits of its group have ended
+          const int t = running[cu];
+          if (comb_pos[t] == t && group_ended[g.tasks[t].a3] < g.splits - 1) continue;
+          cand.push_back(cu);
+        }
         else if (qpos[cu] < g.queue_off[cu + 1] && ready(g.queue_idx[qpos[cu]])) cand.push_back(cu);
       }
       if (cand.empty()) return "deadlock at step " + std::to_string(step) + " after " + std::to_string(done) + " tasks";
@@ -582,10 +596,13 @@ std::string simulate_graph(const HostGraph& g, uint64_t seed, int n_steps) {
         ended[t] = 1;
         ++done;
         if (td.type == T_ATTN) {
-          if (++counters[td.a3] == epoch * (uint32_t)g.splits) {
-            if (!check_reads(g.comb_acc[t], comb_pos[t], true, err)) return err;
-            if (!apply_writes(g.comb_acc[t], comb_pos[t], err)) return err;
+          if (comb_pos[t] == t) {
+            if (!check_reads(g.comb_acc[t], t, true, err)) return err;
+            if (!apply_writes(g.comb_acc[t], t, err)) return err;
             for (int i = 0; i < td.sig_n; ++i) flags[g.sig_slots[td.sig_off + i]] = epoch;
+            group_ended[td.a3] = 0;
+          } else {
+            ++group_ended[td.a3];
           }
         } else {
           for (int i = 0; i < td.sig_n; ++i) flags[g.sig_slots[td.sig_off + i]] = epoch;

@@ -56,11 +56,11 @@ struct EventDesc {
 // Byte offsets of the regions inside the caller's scratch buffer.
 struct ScratchLayout {
   int64_t tasks, queue_off, queue_idx, events, sig_slots, geoms, rope;
-  int64_t flags, counters, err;
+  int64_t flags, err;
   // tagged activations (64-bit words: value bits | step epoch << 32), one buffer per layer
-  int64_t xt, qt, kvt, ot, ht;
+  int64_t xt, qt, kvt, ot, ht, pt;
   int64_t tagged_begin, tagged_end;  // byte range holding all tagged buffers
-  int64_t part, amax, tokbuf, tokout, pools;
+  int64_t amax, tokbuf, tokout, pools;
   int64_t total;
 };
 
@@ -99,7 +99,6 @@ struct KernelParams {
   const GemvGeom* geoms;
   const float* rope;          // [max_pos][dh/2][2] (cos, sin)
   uint32_t* flags;
-  uint32_t* counters;
   uint32_t* err;
   const uint8_t* wpacked;     // packed tiles
   const uint16_t* embed;      // natural embedding [V, d]
@@ -116,7 +115,7 @@ struct KernelParams {
   uint64_t* kvt;              // [L][max_seqs][2][hk][dh/2] the current position's key and value (bf16 pairs)
   uint64_t* ot;               // [L][max_seqs][hq*dh] attention output
   uint64_t* ht;               // [L][max_seqs][f] SwiGLU output
-  float* part;                // [max_seqs][hq][splits][dh + 2] attention partials (m, l, o[dh])
+  uint64_t* pt;               // [L][max_seqs][hq][splits][dh + 2] attention partials (m, l, unnormalised o)
   float* logits;              // [max_seqs][V]
   uint64_t* amax;             // [max_seqs][n_lm_parts] packed argmax keys
   const int32_t* tokens_in;   // [max_seqs]
@@ -128,11 +127,7 @@ struct KernelParams {
   uint32_t watchdog_ticks;    // s_memrealtime ticks (100 MHz) a wait may spin before the kernel aborts
   int32_t max_queue;          // longest per-CU queue (its descriptors are staged in LDS)
   TraceRec* trace;            // per-task timestamps of the last step, or nullptr
-  int32_t touch;              // 1: warm the caches with upcoming weights at task boundaries
 };
-
-// LDS bytes that receive the cache-warming loads (their data is never read): 1 KB per wave.
-constexpr int TOUCH_SINK_BYTES = 8 * 1024;
 
 // Arguments of the weight re-layout kernel: one stage's tasks [task0, task0 + ntasks), whose
 // tiles are contiguous in the packed buffer.

@@ -25,7 +25,7 @@ struct HostGraph {
   int n_cus = 0;
   int splits = 1;
   int max_pos = 0;
-  int n_counters = 0;
+  int n_attn_groups = 0;  // (layer, sequence, KV head) groups whose attention splits are merged
   int n_lm_parts = 0;
   int max_queue = 0;
   int64_t lds_bytes = 0;

@@ -31,7 +31,7 @@ typedef float v4f __attribute__((ext_vector_type(4)));
 
 constexpr int NT = 512;     // threads per workgroup
 constexpr int NW = NT / 64; // waves per workgroup
-constexpr int UB = 8;       // 1 KB units per load batch per wave (two batches in flight)
+constexpr int NSLOT = 16;   // 1 KB weight units in flight per wave (16 KB), one register slot each
 
 // ----------------------------------------------------------------------------- helpers
 __device__ __forceinline__ float ldc(const float* p) { return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT); }
@@ -51,7 +51,12 @@ __device__ __forceinline__ uint32_t f2bf(float f) {
   return u >> 16;
 }
 
-__device__ __forceinline__ void wait_stores() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+// Wait until this wave's vector memory operations (loads, stores, LDS DMA) have completed. Issued
+// through the builtin (s_waitcnt with vmcnt 0 and the other counters at their maximum: 0x0F70 on
+// gfx9-family encodings) rather than inline assembly, so that the compiler's own wait insertion
+// knows the counter is drained afterwards; otherwise it treats LDS DMA as possibly pending and
+// guards later LDS accesses with full waits.
+__device__ __forceinline__ void wait_stores() { __builtin_amdgcn_s_waitcnt(0x0F70); }
 
 // Workgroup barrier that orders LDS only. __syncthreads() also carries a workgroup release fence,
 // which waits for every outstanding global load (vmcnt(0)) and would stall the weight prefetch
@@ -79,7 +84,6 @@ struct Ctl {
   int32_t ctx[16];          // context lengths of the first 16 sequences, read once per launch
   float red[NW * 8];
   float m_run[16], l_run[16], scale[16];
-  uint32_t flag;
   uint32_t aborted;
   uint64_t kred[NW];
   uint64_t t_ready;         // trace: when the running task's inputs were all present
@@ -238,8 +242,7 @@ __device__ __forceinline__ void publish(const KernelParams& p, int my_sig) {
 // ----------------------------------------------------------------------------- GEMV tile
 // ys[r] = sum_k W[row0 + r][k] * xs[k] for the task's rows. Row groups are split evenly over
 // the 8 waves. Each wave streams its contiguous run of 1 KB units with nontemporal dwordx4
-// loads, two batches of UB units in flight. The xs entries past K are zero, and so are the
-// padded weights.
+// loads, NSLOT units in flight. The xs entries past K are zero, and so are the padded weights.
 // The GEMV input vector sits in LDS as two planes: plane A holds elements 8p..8p+3 of every
 // 16-byte weight piece p at A[4p..4p+3], plane B holds 8p+4..8p+7 at B[4p..4p+3]. Lanes that
 // read consecutive pieces then read consecutive 16-byte words of each plane, free of bank
@@ -262,14 +265,13 @@ __device__ __forceinline__ void unit_fma(const v4u w, const float* xa, const flo
   acc1 = fmaf(bf_hi(w.w), b.w, acc1);
 }
 
-// Register pipeline of one wave's weight stream: two batches of UB units. The batches of the
-// NEXT task are loaded before that task's event is satisfied: weights do not depend on
-// activations, so the HBM stream keeps running across the dependency wait. The pipeline is
-// refilled unconditionally at the end of every task (a cached dummy unit when the next task is
-// not a GEMV), so the registers flow straight from the loads into the next GEMV without copies
-// (a copy would have to wait for the loads to land).
+// Register pipeline of one wave's weight stream: NSLOT slots of one unit each. A task's first
+// NSLOT units are loaded before the task polls for its inputs: weights do not depend on
+// activations, so the HBM stream keeps running across the dependency wait. The registers flow
+// straight from the loads into the GEMV without copies (a copy would have to wait for the loads
+// to land).
 struct WPipe {
-  v4u A[UB], B[UB];
+  v4u R[NSLOT];
 };
 
 struct WaveRun {
@@ -292,10 +294,9 @@ __device__ __forceinline__ WaveRun wave_run(const KernelParams& p, const TaskDes
 }
 
 // Loads are unconditional (units past the run re-read its last unit, a cache hit, and are never
-// consumed), so the in-order wait counter is exact: a batch is waited for only when consumed.
-__device__ __forceinline__ void load_batch(v4u (&R)[UB], const WaveRun& w, int i0) {
-#pragma unroll
-  for (int j = 0; j < UB; ++j) R[j] = __builtin_nontemporal_load(w.src + (size_t)min(i0 + j, w.nunits - 1) * 64);
+// consumed), so the in-order wait counter is exact: a slot is waited for only when consumed.
+__device__ __forceinline__ v4u load_unit(const WaveRun& w, int i) {
+  return __builtin_nontemporal_load(w.src + (size_t)min(i, w.nunits - 1) * 64);
 }
 
 __device__ __forceinline__ bool is_gemv(int type) {
@@ -378,16 +379,6 @@ __device__ __forceinline__ void attn_stage_chunk(const KernelParams& p, const Ta
   }
 }
 
-// Cache warming. The register batches hold only the first 2 * UB units of a wave's run, and a task
-// boundary (waiting for the slowest producer, then for the flag to travel) can leave HBM idle for
-// longer than those take to arrive. So after the register batches each wave also loads the next TB
-// units that follow in its queue (the rest of the next task's run, then the start of the following
-// GEMV task's run) into a sink in LDS that nothing reads. The loads need no registers; they bring
-// the lines into L2 and the memory-side cache, from which the GEMV later streams them faster than
-// from HBM. Their number is fixed, so that the compiler's wait counts for the register batches stay
-// exact; with warming off they re-read the first unit of the weights (a cache hit).
-constexpr int TB = 16;
-
 __device__ __forceinline__ WaveRun dummy_run(const KernelParams& p) {
   WaveRun w;
   w.src = (const v4u*)p.wpacked + (threadIdx.x & 63);
@@ -396,39 +387,14 @@ __device__ __forceinline__ WaveRun dummy_run(const KernelParams& p) {
   return w;
 }
 
-__device__ __forceinline__ void touch_ahead(const WaveRun& w1, const WaveRun& w2, unsigned char* sink) {
-  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  __attribute__((address_space(3))) void* d = (__attribute__((address_space(3))) void*)(sink + wave * 1024);
-  const int end1 = max(w1.nunits, 2 * UB);
-#pragma unroll
-  for (int k = 0; k < TB; ++k) {
-    const int i = 2 * UB + k;
-    const v4u* a = (i < w1.nunits) ? w1.src + (size_t)i * 64 : w2.src + (size_t)min(i - end1, w2.nunits - 1) * 64;
-    __builtin_amdgcn_global_load_lds((const void*)a, d, 16, 0, 0);
-  }
-}
-
+// An attention split's first chunk of cached keys and values, staged into LDS before the split polls
+// for its queries ("MPK: A Compiler and Runtime for Mega-Kernelizing Tensor Programs", analogy 4:
+// a task's inputs load while the previous one runs).
 template <int DH>
-__device__ __forceinline__ void prefetch_next(const KernelParams& p, const TaskDesc& tn, bool has_next,
-                                              const TaskDesc* tnn, WPipe& wp, const Ctl* ctl, uint16_t* const* pools,
-                                              float* lds, unsigned char* sink) {
-  if (has_next && tn.type == T_ATTN) {  // the split's first chunk of cached keys and values, into LDS
-    const AttnRange r = attn_range(p, tn, ctl);
-    attn_stage_chunk<DH>(p, tn, r.p0, min(r.p1, r.pos), pools, lds);
-    return;
-  }
-  WaveRun w;
-  w.nunits = 0;
-  if (has_next && is_gemv(tn.type)) w = wave_run(p, tn, ctl->geoms[tn.geom]);
-  if (w.nunits <= 0) w = dummy_run(p);  // nothing to stream: re-read the first unit (valid, cached)
-  load_batch(wp.A, w, 0);
-  load_batch(wp.B, w, UB);
-  WaveRun w1 = w, w2;
-  w2.nunits = 0;
-  if (tnn != nullptr && is_gemv(tnn->type)) w2 = wave_run(p, *tnn, ctl->geoms[tnn->geom]);
-  if (w2.nunits <= 0) w2 = dummy_run(p);
-  if (!p.touch) w1 = w2 = dummy_run(p);
-  touch_ahead(w1, w2, sink);
+__device__ __forceinline__ void attn_prefetch(const KernelParams& p, const TaskDesc& t, const Ctl* ctl,
+                                              uint16_t* const* pools, float* lds) {
+  const AttnRange r = attn_range(p, t, ctl);
+  attn_stage_chunk<DH>(p, t, r.p0, min(r.p1, r.pos), pools, lds);
 }
 
 __device__ __forceinline__ void gemv_tile(const KernelParams& p, const TaskDesc& t, const GemvGeom gm, const float* xs, float* ys,
@@ -445,75 +411,36 @@ __device__ __forceinline__ void gemv_tile(const KernelParams& p, const TaskDesc&
   int g = w.g0, ug = 0;
   float acc0 = 0.f, acc1 = 0.f;
 
-  auto consume = [&](v4u(&R)[UB], int i0) {
+  auto unit = [&](const v4u& wv) {
+    unit_fma(wv, xa + ug * lpr * 4, xb + ug * lpr * 4, acc0, acc1);
+    if (++ug == S) {
+      float acc = acc0 + acc1;
 #pragma unroll
-    for (int j = 0; j < UB; ++j) {
-      if (i0 + j < nunits) {
-        unit_fma(R[j], xa + ug * lpr * 4, xb + ug * lpr * 4, acc0, acc1);
-        if (++ug == S) {
-          float acc = acc0 + acc1;
-          for (int off = lpr >> 1; off >= 1; off >>= 1) acc += __shfl_xor(acc, off);
-          const int r = g * gm.rg + rin;
-          if (sub == 0 && r < rows) ys[r] = acc;
-          acc0 = 0.f;
-          acc1 = 0.f;
-          ug = 0;
-          ++g;
-        }
-      }
+      for (int off = 32; off >= 1; off >>= 1)  // fixed trip count (lpr <= 64) keeps the wait analysis exact
+        if (off < lpr) acc += __shfl_xor(acc, off);
+      const int r = g * gm.rg + rin;
+      if (sub == 0 && r < rows) ys[r] = acc;
+      acc0 = 0.f;
+      acc1 = 0.f;
+      ug = 0;
+      ++g;
     }
   };
-  // wp holds this task's first two batches (loaded by prefetch_next)
-  consume(wp.A, 0);
-  load_batch(wp.A, w, 2 * UB);
-  consume(wp.B, UB);
-  for (int i0 = 2 * UB; i0 < nunits; i0 += 2 * UB) {
-    load_batch(wp.B, w, i0 + UB);
-    consume(wp.A, i0);
-    load_batch(wp.A, w, i0 + 2 * UB);
-    consume(wp.B, i0 + UB);
+  // Slot j holds unit i0 + j. Each slot is refilled with unit i0 + j + NSLOT as soon as it has been
+  // consumed, so NSLOT - 1 loads stay in flight while a unit is processed. Refills past the run
+  // re-read its last unit (a cache hit). A scheduling barrier after each slot keeps each refill
+  // after its slot's use. The compiler still waits for most of a round's loads at the round's start
+  // (the first fill is not kept in slot order), so about one round of loads is in flight per wave;
+  // measured on the 8B decode, this streams slightly faster than a strict slot-by-slot pipeline
+  // with 16 loads always in flight: the HBM stream is already saturated.
+  for (int i0 = 0; i0 < nunits; i0 += NSLOT) {
+#pragma unroll
+    for (int j = 0; j < NSLOT; ++j) {
+      if (i0 + j < nunits) unit(wp.R[j]);
+      wp.R[j] = load_unit(w, i0 + j + NSLOT);
+      __builtin_amdgcn_sched_barrier(0);
+    }
   }
-}
-
-// xs (two-plane layout, `padded` = 8 * pieces elements) = RMSNorm(x) * gain, zero past d. x is the
-// tagged residual stream, or, for the first layer, the token's embedding row (bf16). The sum of
-// squares runs over the staged values in a fixed order, so it does not depend on arrival order.
-__device__ __forceinline__ void rmsnorm_to_lds(const KernelParams& p, const uint64_t* xsrc, const uint16_t* esrc,
-                                               const uint16_t* gain, int d, int padded, float* xs, Ctl* ctl,
-                                               uint32_t what) {
-  const int np = padded >> 3, tid = threadIdx.x;
-  if (esrc) {
-    for (int i = tid; i < d; i += NT) xs[xs_index(i, np)] = bf2f(esrc[i]);
-  } else {
-    // word i0 + 64k lands at xs_index(i0) + 32k (64 elements are 8 whole pieces)
-    float* xd = xs + xs_index(poll_index(d, 0), np);
-    poll_vector<16>(p, xsrc, d, what, [&](int k, uint32_t b) { xd[32 * k] = __uint_as_float(b); });
-  }
-  for (int i = d + tid; i < padded; i += NT) xs[xs_index(i, np)] = 0.f;
-  bar();
-  float ss = 0.f;
-  for (int i = tid; i < d; i += NT) {
-    const float v = xs[xs_index(i, np)];
-    ss += v * v;
-  }
-  ss = block_sum(ss, ctl);
-  const float r = 1.0f / sqrtf(ss / (float)d + p.eps);
-  for (int i = tid; i < d; i += NT) {
-    const int k = xs_index(i, np);
-    xs[k] = xs[k] * r * bf2f(gain[i]);
-  }
-  bar();
-}
-
-// xs (two-plane layout) = the tagged vector src[0, n), zero up to `padded`.
-template <int K>
-__device__ __forceinline__ void load_tagged_to_lds(const KernelParams& p, const uint64_t* src, int n, int padded,
-                                                   float* xs, uint32_t what) {
-  const int np = padded >> 3, tid = threadIdx.x;
-  float* xd = xs + xs_index(poll_index(n, 0), np);  // word i0 + 64k lands at xs_index(i0) + 32k
-  poll_vector<K>(p, src, n, what, [&](int k, uint32_t b) { xd[32 * k] = __uint_as_float(b); });
-  for (int i = n + tid; i < padded; i += NT) xs[xs_index(i, np)] = 0.f;
-  bar();
 }
 
 __device__ __forceinline__ int token_of(const KernelParams& p, int s) {
@@ -569,79 +496,17 @@ __device__ __forceinline__ QkvSet qkv_set_consts(const KernelParams& p, int l, i
   return c;
 }
 
-__device__ __forceinline__ void task_qkv(const KernelParams& p, const TaskDesc& t, float* lds, Ctl* ctl, WPipe& wp,
-                                         uint16_t* const* pools) {
-  const GemvGeom gm = ctl->geoms[G_QKV];
-  const int padded = gm.S * gm.lpr * 8;
-  float* xs = lds;
-  float* ys = lds + padded;
-  const int s = 0;
-  const int l = t.layer;
-  const int G = p.hq / p.hk, dh = p.dh, Rg = (G + 2) * dh;
-  // An out-of-range position is reported and the row is not appended, but q, k and v are still
-  // written (at position 0's rotation) so that no consumer waits for them.
-  const int pos = checked_pos(p, ctl, s);
-  const int posc = pos < 0 ? 0 : pos;
-  const int nsets = (t.row1 - t.row0) >> 2;
-  const uint32_t ep = p.epoch;
-  QkvSet pre;
-  if ((int)threadIdx.x < nsets) pre = qkv_set_consts(p, l, t.row0 + 4 * threadIdx.x, posc, s);
-  const uint16_t* esrc = nullptr;
-  if (l == 0) esrc = p.embed + (size_t)token_of(p, s) * p.d;
-  rmsnorm_to_lds(p, l > 0 ? xt_at(p, l - 1, 1, s) : nullptr, esrc, layer_norm_gain(p, l, 0), p.d, padded, xs, ctl,
-                 (uint32_t)t.wait_ev);
-  if (p.trace && threadIdx.x == 0) ctl->t_ready = __builtin_amdgcn_s_memrealtime();
-  gemv_tile(p, t, gm, xs, ys, wp);
-  bar();
-  for (int m = threadIdx.x; m < nsets; m += NT) {
-    const int r = t.row0 + 4 * m;
-    const int grp = r / Rg, within = r % Rg, slot = within / dh, jh = within % dh;
-    const int i0 = jh >> 1;  // even dim index; the set holds dims i0, i0 + dh/2, i0 + 1, i0 + 1 + dh/2
-    const QkvSet c = (m == (int)threadIdx.x) ? pre : qkv_set_consts(p, l, r, posc, s);
-    float y0 = ys[4 * m] + c.b0, y1 = ys[4 * m + 1] + c.b1, y2 = ys[4 * m + 2] + c.b2, y3 = ys[4 * m + 3] + c.b3;
-    if (slot <= G) {  // rotate q and k: pair (i0, i0 + dh/2) and pair (i0 + 1, i0 + 1 + dh/2)
-      const float a0 = y0 * c.cs0.x - y1 * c.cs0.y, b0 = y1 * c.cs0.x + y0 * c.cs0.y;
-      const float a1 = y2 * c.cs1.x - y3 * c.cs1.y, b1 = y3 * c.cs1.x + y2 * c.cs1.y;
-      y0 = a0; y1 = b0; y2 = a1; y3 = b1;
-    }
-    if (slot < G) {
-      uint64_t* q = qt_at(p, l, s) + (size_t)(grp * G + slot) * dh;
-      st_tagf(&q[i0], y0, ep);
-      st_tagf(&q[i0 + dh / 2], y1, ep);
-      st_tagf(&q[i0 + 1], y2, ep);
-      st_tagf(&q[i0 + 1 + dh / 2], y3, ep);
-    } else {
-      // the rounded key/value pairs go to the cache and, tagged, to this step's attention
-      const uint32_t w0 = f2bf(y0) | (f2bf(y2) << 16), w1 = f2bf(y1) | (f2bf(y3) << 16);
-      uint64_t* kv = kvt_at(p, l, s, slot == G ? 0 : 1, grp);
-      st_tag(&kv[i0 >> 1], w0, ep);
-      st_tag(&kv[(i0 + dh / 2) >> 1], w1, ep);
-      const int blk = c.blk;
-      if (blk < 0 || blk >= p.num_blocks) {
-        raise_error(p, ERR_PAGE, (uint32_t)s, (uint32_t)blk);
-        continue;
-      }
-      if (pos < 0) continue;
-      uint16_t* pool = pools[(slot == G ? 0 : p.n_layers) + l];
-      uint32_t* row = (uint32_t*)(pool + (((size_t)blk * p.hk + grp) * 16 + (pos & 15)) * dh);
-      stc(&row[i0 >> 1], w0);
-      stc(&row[(i0 + dh / 2) >> 1], w1);
-    }
-  }
-}
-
 // ----------------------------------------------------------------------------- attention
 // One split of grouped-query attention for (seq, kv head): a contiguous range of cache blocks.
-// The G query heads that share the KV head read each key and value row once ([SL] slide 28).
-// Keys and values of earlier positions do not change during a step. The worker loads the
-// split's first chunk of them (K into the pipeline's A registers, V into B) while the previous
-// task finishes, before this task waits for its queries ("MPK: A Compiler and Runtime for
-// Mega-Kernelizing Tensor Programs", analogy 4: inputs load while the previous task runs).
-// After the wait, only q and the current position's key and value are fetched. Softmax runs
-// online across chunks. The running max and sum rescale the output ([SL] slide 13; the online
-// softmax of "Hạt nhân là gì và tại sao mọi người lại viết hạt nhân mới"). The partial
-// (m, l, unnormalised o) goes to `part`. The split that finishes last merges all partials by
-// log-sum-exp and publishes the group's slot.
+// The G query heads that share the KV head read each key and value row once ("LLM高速化勉強会資料", slide 28).
+// Keys and values of earlier positions do not change during a step. The worker stages the
+// split's first chunk of them into LDS while the previous task finishes, before this task polls
+// for its queries ("MPK: A Compiler and Runtime for Mega-Kernelizing Tensor Programs", analogy 4:
+// inputs load while the previous task runs). Then only q and the current position's key and
+// value are fetched, in one poll. Softmax runs online across chunks. The running max and sum
+// rescale the output ("LLM高速化勉強会資料", slide 13; the online softmax of "Hạt nhân là gì và tại sao mọi người
+// lại viết hạt nhân mới"). Each split's partial (m, l, unnormalised o) goes out as tagged words;
+// the group's last split polls for the others' and merges them by log-sum-exp into o.
 template <int DH, int GMAX>
 __device__ __forceinline__ void task_attn(const KernelParams& p, const TaskDesc& t, float* lds, Ctl* ctl,
                                           uint16_t* const* pools) {
@@ -661,9 +526,6 @@ __device__ __forceinline__ void task_attn(const KernelParams& p, const TaskDesc&
   float* qs = obuf + NW * G * DH;                    // [G][2][DH/2]: dims 8c..8c+3 at 4c, 8c+4..8c+7 at DH/2 + 4c
   uint32_t* kvc = (uint32_t*)(qs + G * DH);          // the current position's key (DH/2 words) then value row
   const int splits = p.splits;
-  float* part = p.part + ((size_t)s * p.hq) * splits * (DH + 2);
-  const uint16_t* kpool = pools[t.layer];
-  const uint16_t* vpool = pools[p.n_layers + t.layer];
   const float scale = 1.0f / sqrtf((float)DH);
 
   const int tid = threadIdx.x;
@@ -806,139 +668,98 @@ __device__ __forceinline__ void task_attn(const KernelParams& p, const TaskDesc&
       for (int e = 0; e < 8; ++e) obuf[(wave * G + h) * DH + c * 8 + e] = oacc[h][e];
     }
   bar();
-  if (active) {
-    for (int i = threadIdx.x; i < G * DH; i += NT) {
+  // The split's partial (m, l and the unnormalised o of each of its G heads) goes out tagged, except
+  // from the merging split (the last), which keeps its own in registers and polls for the others'.
+  const bool merger = (j == splits - 1);
+  const uint32_t ep = p.epoch;
+  uint64_t* pgrp = p.pt + ((((size_t)t.layer * p.max_seqs + s) * p.hq + h0) * splits) * (DH + 2);  // [G][splits][DH+2]
+  constexpr int EPT = (GMAX * DH + NT - 1) / NT;  // output elements per thread
+  float own[EPT];
+  int eh[EPT];
+#pragma unroll
+  for (int e = 0; e < EPT; ++e) {
+    const int i = tid + e * NT;
+    own[e] = 0.f;
+    eh[e] = 0;
+    if (i < G * DH) {
       const int h = i / DH, dd = i % DH;
       float v = 0.f;
       for (int w = 0; w < NW; ++w) v += obuf[(w * G + h) * DH + dd];
-      stc(&part[((size_t)(h0 + h) * splits + j) * (DH + 2) + 2 + dd], v);
-    }
-    if (threadIdx.x < G) {
-      stc(&part[((size_t)(h0 + threadIdx.x) * splits + j) * (DH + 2) + 0], ctl->m_run[threadIdx.x]);
-      stc(&part[((size_t)(h0 + threadIdx.x) * splits + j) * (DH + 2) + 1], ctl->l_run[threadIdx.x]);
+      own[e] = v;
+      eh[e] = h;
+      if (active && !merger) st_tagf(&pgrp[((size_t)h * splits + j) * (DH + 2) + 2 + dd], v, ep);
     }
   }
-  // arrive; the last split of the group merges
-  wait_stores();
-  bar();
-  if (threadIdx.x == 0) {
-    const uint32_t old = __hip_atomic_fetch_add(&p.counters[t.a3], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    ctl->flag = (old + 1 == p.epoch * (uint32_t)splits) ? 1u : 0u;
+  if (active && !merger && tid < G) {
+    st_tagf(&pgrp[((size_t)tid * splits + j) * (DH + 2) + 0], ctl->m_run[tid], ep);
+    st_tagf(&pgrp[((size_t)tid * splits + j) * (DH + 2) + 1], ctl->l_run[tid], ep);
   }
-  bar();
-  if (!ctl->flag) return;  // only the last split merges
-  // log-sum-exp merge; each split's three loads are independent of the previous split's values.
-  // The group's output is written (tagged) even for an inactive sequence, as zeros.
+  if (!merger) return;
+  // Log-sum-exp merge in split order, R splits per poll round (3 words per split and element:
+  // m, l and o[dd]). The group's output is written (tagged) even for an inactive sequence, as zeros.
+  constexpr int R = 8 / EPT;
+  float M[EPT], Ls[EPT], A[EPT];
+#pragma unroll
+  for (int e = 0; e < EPT; ++e) {
+    M[e] = -INFINITY;
+    Ls[e] = 0.f;
+    A[e] = 0.f;
+  }
+  if (active) {
+    int hb[EPT], ob[EPT];  // byte offsets of the element's head row: m at +0, l at +8, o[dd] at +(2 + dd) 8
+#pragma unroll
+    for (int e = 0; e < EPT; ++e) {
+      const int i = min(tid + e * NT, G * DH - 1);
+      hb[e] = (i / DH) * splits * (DH + 2) * 8;
+      ob[e] = hb[e] + (2 + i % DH) * 8;
+    }
+    for (int j0 = 0; j0 < splits; j0 += R) {
+      uint32_t pend = 0;
+#pragma unroll
+      for (int e = 0; e < EPT; ++e)
+#pragma unroll
+        for (int r = 0; r < R; ++r)
+          if (tid + e * NT < G * DH && j0 + r < splits && j0 + r != j) pend |= 7u << ((e * R + r) * 3);
+      float mv[EPT][R], lv[EPT][R], ov[EPT][R];
+      poll_tagged<3 * R * EPT>(
+          p, pgrp,
+          [&](int k) {
+            const int e = k / (3 * R), c3 = k % 3;
+            return c3 == 2 ? ob[e] : hb[e] + c3 * 8;
+          },
+          [&](int k) { return (j0 + (k / 3) % R) * (DH + 2) * 8; }, pend, what,
+          [&](int k, uint32_t b) {
+            const int e = k / (3 * R), r = (k / 3) % R, c3 = k % 3;
+            const float f = __uint_as_float(b);
+            if (c3 == 0) mv[e][r] = f;
+            else if (c3 == 1) lv[e][r] = f;
+            else ov[e][r] = f;
+          });
+#pragma unroll
+      for (int e = 0; e < EPT; ++e)
+#pragma unroll
+        for (int r = 0; r < R; ++r) {
+          const int jj = j0 + r;
+          if (tid + e * NT >= G * DH || jj >= splits) continue;
+          const float mk = jj == j ? ctl->m_run[eh[e]] : mv[e][r];
+          const float lk = jj == j ? ctl->l_run[eh[e]] : lv[e][r];
+          const float ok = jj == j ? own[e] : ov[e][r];
+          if (mk == -INFINITY) continue;
+          const float mn = fmaxf(M[e], mk);
+          const float a = (M[e] == -INFINITY) ? 0.f : expf(M[e] - mn), b = expf(mk - mn);
+          Ls[e] = Ls[e] * a + lk * b;
+          A[e] = A[e] * a + ok * b;
+          M[e] = mn;
+        }
+    }
+  }
   uint64_t* od = ot_at(p, t.layer, s) + (size_t)h0 * DH;
-  for (int i = threadIdx.x; i < G * DH; i += NT) {
-    float v = 0.f;
-    if (active) {
-      const int h = i / DH, dd = i % DH;
-      const float* ph = part + (size_t)(h0 + h) * splits * (DH + 2);
-      float M = -INFINITY, Lsum = 0.f, acc = 0.f;
-      for (int k0 = 0; k0 < splits; k0 += 4) {
-        float mk[4], lk[4], ok[4];
 #pragma unroll
-        for (int u = 0; u < 4; ++u) {
-          const int k = min(k0 + u, splits - 1);
-          mk[u] = ldc(&ph[k * (DH + 2)]);
-          lk[u] = ldc(&ph[k * (DH + 2) + 1]);
-          ok[u] = ldc(&ph[k * (DH + 2) + 2 + dd]);
-        }
-#pragma unroll
-        for (int u = 0; u < 4; ++u) {
-          if (k0 + u >= splits || mk[u] == -INFINITY) continue;
-          const float mn = fmaxf(M, mk[u]);
-          const float a = (M == -INFINITY) ? 0.f : expf(M - mn), b = expf(mk[u] - mn);
-          Lsum = Lsum * a + lk[u] * b;
-          acc = acc * a + ok[u] * b;
-          M = mn;
-        }
-      }
-      v = acc / Lsum;
-    }
-    st_tagf(&od[i], v, p.epoch);
-  }
+  for (int e = 0; e < EPT; ++e)
+    if (tid + e * NT < G * DH) st_tagf(&od[tid + e * NT], active ? A[e] / Ls[e] : 0.f, ep);
 }
 
-// ----------------------------------------------------------------------------- O / down projection
-// x_out[r] = x_in[r] + (W . v)[r] for the task's rows. O-proj: v = attention output, x_in = x after
-// the previous layer's down-proj (the embedding row for the first layer). Down-proj: v = SwiGLU
-// output, x_in = x after this layer's O-proj. The residual words are loaded before the input vector
-// is polled; they were written a stage before the vector, so they are nearly always current by then,
-// and a stale one is polled again afterwards.
-__device__ __forceinline__ void task_residual_gemv(const KernelParams& p, const TaskDesc& t, float* lds, Ctl* ctl,
-                                                   WPipe& wp) {
-  const bool is_o = t.type == T_OPROJ;
-  const GemvGeom gm = ctl->geoms[is_o ? G_O : G_D];
-  const int padded = gm.S * gm.lpr * 8;
-  float* xs = lds;
-  float* ys = lds + padded;
-  const int s = 0, l = t.layer, tid = threadIdx.x;
-  const uint32_t what = (uint32_t)t.wait_ev;
-  const bool from_embed = is_o && l == 0;
-  const uint16_t* erow = from_embed ? p.embed + (size_t)token_of(p, s) * p.d : nullptr;
-  const uint64_t* rsrc = is_o ? xt_at(p, l > 0 ? l - 1 : 0, 1, s) : xt_at(p, l, 0, s);
-  float res[4] = {0.f, 0.f, 0.f, 0.f};
-  // the residual words, loaded unconditionally (clamped to the task's last row) ahead of the poll
-  const int nrows = t.row1 - t.row0;
-  uint64_t rw[4];
-  const __amdgpu_buffer_rsrc_t rr = tag_rsrc(rsrc + t.row0);
-#pragma unroll
-  for (int k = 0; k < 4; ++k) rw[k] = ld_tag(rr, min(tid + k * NT, nrows - 1) * 8, 0);
-  if (from_embed) {
-#pragma unroll
-    for (int k = 0; k < 4; ++k)
-      if (tid + k * NT < nrows) res[k] = bf2f(erow[t.row0 + tid + k * NT]);
-  }
-  if (is_o) load_tagged_to_lds<16>(p, ot_at(p, l, s), p.hq * p.dh, padded, xs, what);
-  else load_tagged_to_lds<32>(p, ht_at(p, l, s), p.f, padded, xs, what);
-  if (!from_embed) {
-    uint32_t stale = 0;
-#pragma unroll
-    for (int k = 0; k < 4; ++k) {
-      if (t.row0 + tid + k * NT < t.row1) {
-        if ((uint32_t)(rw[k] >> 32) == p.epoch) res[k] = __uint_as_float((uint32_t)rw[k]);
-        else stale |= 1u << k;
-      }
-    }
-    if (__any(stale != 0u))
-      poll_tagged<4>(p, rsrc + t.row0, [&](int k) { return (tid + k * NT) * 8; }, [](int) { return 0; }, stale, what,
-                     [&](int k, uint32_t b) { res[k] = __uint_as_float(b); });
-  }
-  if (p.trace && tid == 0) ctl->t_ready = __builtin_amdgcn_s_memrealtime();
-  gemv_tile(p, t, gm, xs, ys, wp);
-  bar();
-  uint64_t* dst = xt_at(p, l, is_o ? 0 : 1, s);
-#pragma unroll
-  for (int k = 0; k < 4; ++k) {
-    const int r = t.row0 + tid + k * NT;
-    if (r < t.row1) st_tagf(&dst[r], res[k] + ys[r - t.row0], p.epoch);
-  }
-}
-
-// ----------------------------------------------------------------------------- gate/up + SwiGLU
-__device__ __forceinline__ void task_gateup(const KernelParams& p, const TaskDesc& t, float* lds, Ctl* ctl, WPipe& wp) {
-  const GemvGeom gm = ctl->geoms[G_GU];
-  const int padded = gm.S * gm.lpr * 8;
-  float* xs = lds;
-  float* ys = lds + padded;
-  const int s = 0;
-  rmsnorm_to_lds(p, xt_at(p, t.layer, 0, s), nullptr, layer_norm_gain(p, t.layer, 1), p.d, padded, xs, ctl,
-                 (uint32_t)t.wait_ev);
-  if (p.trace && threadIdx.x == 0) ctl->t_ready = __builtin_amdgcn_s_memrealtime();
-  gemv_tile(p, t, gm, xs, ys, wp);
-  bar();
-  const int npairs = (t.row1 - t.row0) >> 1;
-  uint64_t* hd = ht_at(p, t.layer, s) + (t.row0 >> 1);
-  for (int m = threadIdx.x; m < npairs; m += NT) {
-    const float a = ys[2 * m], b = ys[2 * m + 1];
-    const float silu = a / (1.0f + expf(-a));
-    st_tagf(&hd[m], silu * b, p.epoch);
-  }
-}
-
-// ----------------------------------------------------------------------------- LM head + argmax
+// ----------------------------------------------------------------------------- argmax keys
 // Order-preserving key: larger float -> larger key; on equal values the lower index wins.
 __device__ __forceinline__ uint64_t argmax_key(float v, int idx) {
   uint32_t u = __float_as_uint(v);
@@ -961,26 +782,213 @@ __device__ __forceinline__ uint64_t block_max_u64(uint64_t k, Ctl* ctl) {
   return m;
 }
 
-__device__ __forceinline__ void task_lmhead(const KernelParams& p, const TaskDesc& t, float* lds, Ctl* ctl, WPipe& wp) {
-  const GemvGeom gm = ctl->geoms[G_LM];
-  const int padded = gm.S * gm.lpr * 8;
+// ----------------------------------------------------------------------------- GEMV tasks
+// Every GEMV task runs one code path: stage the input vector into LDS (polled tagged words, or the
+// token's embedding row), RMS-normalise it where the operator starts with a norm, stream the weight
+// tile against it, then apply the operator's epilogue:
+//   QKV      x (after the previous layer) -> RMSNorm -> rows of q, k, v -> bias, RoPE, KV append
+//   O-proj   attention output -> x after O = x + W o
+//   gate/up  x after O -> RMSNorm -> interleaved gate/up rows -> SwiGLU
+//   down     SwiGLU output -> x after down = x + W h
+//   LM head  final x -> RMSNorm -> logits and the tile's argmax key
+// One shared path keeps the instruction footprint small. The kernel's code is larger than the
+// instruction cache, and code that a CU runs once per layer is otherwise fetched anew each time.
+__device__ __forceinline__ void gemv_task(const KernelParams& p, const TaskDesc& t, float* lds, Ctl* ctl, WPipe& wp,
+                                          uint16_t* const* pools) {
+  const int type = t.type, l = t.layer, s = 0, tid = threadIdx.x;
+  const uint32_t ep = p.epoch, what = (uint32_t)t.wait_ev;
+  const GemvGeom gm = ctl->geoms[t.geom];
+  const int padded = gm.S * gm.lpr * 8, np = padded >> 3;
   float* xs = lds;
   float* ys = lds + padded;
-  const int s = 0;
-  rmsnorm_to_lds(p, xt_at(p, p.n_layers - 1, 1, s), nullptr, p.norms + (size_t)p.n_layers * 2 * p.d, p.d, padded, xs,
-                 ctl, (uint32_t)t.wait_ev);
-  if (p.trace && threadIdx.x == 0) ctl->t_ready = __builtin_amdgcn_s_memrealtime();
+  const bool norm = type == T_QKV || type == T_GATEUP || type == T_LMHEAD;
+  const bool resid = type == T_OPROJ || type == T_DOWN;
+  const int n = type == T_OPROJ ? p.hq * p.dh : type == T_DOWN ? p.f : p.d;
+  const uint64_t* src = type == T_QKV      ? xt_at(p, l > 0 ? l - 1 : 0, 1, s)
+                        : type == T_GATEUP ? xt_at(p, l, 0, s)
+                        : type == T_LMHEAD ? xt_at(p, p.n_layers - 1, 1, s)
+                        : type == T_OPROJ  ? ot_at(p, l, s)
+                                           : ht_at(p, l, s);
+  const bool in_embed = type == T_QKV && l == 0;     // the first QKV reads the embedding row
+  const bool res_embed = type == T_OPROJ && l == 0;  // the first O-proj adds to it
+  const uint16_t* erow = (in_embed || res_embed) ? p.embed + (size_t)token_of(p, s) * p.d : nullptr;
+
+  // Everything the task loads before its GEMV is issued ahead of the weight stream: the wait counter
+  // of vector memory completes in order, so a load issued after the stream's first NSLOT units per
+  // wave could not be used before they had all arrived. In order: the first pass of the input poll,
+  // the RMSNorm gains, the residual words; then the weight units; then the QKV epilogue constants,
+  // which are needed only after the GEMV.
+  // Input words: thread t polls words i0 + 64k (see poll_vector), landing at xs_index(i0) + 32k.
+  const __amdgpu_buffer_rsrc_t rin = tag_rsrc(src);
+  const int i0 = poll_index(n, 0);
+  uint32_t pending = in_embed ? 0u : first_words(min(poll_chunk(n) / 64, (n - i0 + 63) / 64));
+  uint64_t w1[32];
+#pragma unroll
+  for (int k = 0; k < 32; ++k)
+    if ((pending >> k) & 1u) w1[k] = ld_tag(rin, i0 * 8 + (k & 7) * 512, (k >> 3) * 4096);
+  // Gains: thread t scales elements [8t, 8t + 8) and [4096 + 8t, 4096 + 8t + 8) (n <= 8192).
+  const uint16_t* gain = type == T_QKV      ? layer_norm_gain(p, l, 0)
+                         : type == T_GATEUP ? layer_norm_gain(p, l, 1)
+                                            : p.norms + (size_t)p.n_layers * 2 * p.d;
+  v4u gq[2];
+  if (norm) {
+#pragma unroll
+    for (int c = 0; c < 2; ++c) gq[c] = *(const v4u*)(gain + min(8 * tid + 4096 * c, n - 8));
+  }
+  // O-proj and down: the residual words, clamped to the task's last row. They were written a stage
+  // before the input vector, so they are nearly always current once it is; a stale one is polled
+  // again below.
+  const uint64_t* rsrc = type == T_OPROJ ? xt_at(p, l > 0 ? l - 1 : 0, 1, s) : xt_at(p, l, 0, s);
+  const int nrows = t.row1 - t.row0;
+  uint64_t rw[4] = {0, 0, 0, 0};
+  if (resid && !res_embed) {
+    const __amdgpu_buffer_rsrc_t rr = tag_rsrc(rsrc + t.row0);
+#pragma unroll
+    for (int k = 0; k < 4; ++k) rw[k] = ld_tag(rr, min(tid + k * NT, nrows - 1) * 8, 0);
+  }
+  {  // the wave's first NSLOT weight units
+    WaveRun w = wave_run(p, t, gm);
+    if (w.nunits <= 0) w = dummy_run(p);
+#pragma unroll
+    for (int j = 0; j < NSLOT; ++j) wp.R[j] = load_unit(w, j);
+  }
+  // QKV: the rotary, bias and page-table constants of the thread's 4-row set. An out-of-range
+  // position is reported and the row is not appended, but q, k and v are still written (at
+  // position 0's rotation) so that no consumer waits for them.
+  const int nsets = nrows >> 2;
+  int pos = 0;
+  QkvSet pre;
+  if (type == T_QKV) {
+    pos = checked_pos(p, ctl, s);
+    if (tid < nsets) pre = qkv_set_consts(p, l, t.row0 + 4 * tid, pos < 0 ? 0 : pos, s);
+  }
+
+  // the input vector, two-plane layout in LDS, zero past n
+  float* xd = xs + xs_index(i0, np);
+  if (in_embed) {
+    for (int i = tid; i < n; i += NT) xs[xs_index(i, np)] = bf2f(erow[i]);
+  } else {
+#pragma unroll
+    for (int k = 0; k < 32; ++k) {
+      if (((pending >> k) & 1u) && (uint32_t)(w1[k] >> 32) == ep) {
+        xd[32 * k] = __uint_as_float((uint32_t)w1[k]);
+        pending &= ~(1u << k);
+      }
+    }
+    if (__any(pending != 0u))
+      poll_tagged<32>(p, src, [&](int k) { return i0 * 8 + (k & 7) * 512; }, [](int k) { return (k >> 3) * 4096; },
+                      pending, what, [&](int k, uint32_t b) { xd[32 * k] = __uint_as_float(b); });
+  }
+  for (int i = n + tid; i < padded; i += NT) xs[xs_index(i, np)] = 0.f;
+  bar();
+  if (norm) {  // the sum of squares runs over the staged values in a fixed order
+    float ss = 0.f;
+    for (int i = tid; i < n; i += NT) {
+      const float v = xs[xs_index(i, np)];
+      ss += v * v;
+    }
+    ss = block_sum(ss, ctl);
+    const float r = 1.0f / sqrtf(ss / (float)n + p.eps);
+#pragma unroll
+    for (int c = 0; c < 2; ++c) {
+      const int pc = tid + 512 * c;  // piece: elements 8 pc .. 8 pc + 7
+      if (8 * pc < n) {
+        v4f* pa = (v4f*)(xs + 4 * pc);
+        v4f* pb = (v4f*)(xs + 4 * np + 4 * pc);
+        v4f a = *pa, b = *pb;
+        const v4u g = gq[c];
+        a.x = a.x * r * bf_lo(g.x); a.y = a.y * r * bf_hi(g.x); a.z = a.z * r * bf_lo(g.y); a.w = a.w * r * bf_hi(g.y);
+        b.x = b.x * r * bf_lo(g.z); b.y = b.y * r * bf_hi(g.z); b.z = b.z * r * bf_lo(g.w); b.w = b.w * r * bf_hi(g.w);
+        *pa = a;
+        *pb = b;
+      }
+    }
+    bar();
+  }
+  float res[4] = {0.f, 0.f, 0.f, 0.f};
+  if (resid) {
+    uint32_t stale = 0;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const int r = tid + k * NT;
+      if (r < nrows) {
+        if (res_embed) res[k] = bf2f(erow[t.row0 + r]);
+        else if ((uint32_t)(rw[k] >> 32) == ep) res[k] = __uint_as_float((uint32_t)rw[k]);
+        else stale |= 1u << k;
+      }
+    }
+    if (__any(stale != 0u))
+      poll_tagged<4>(p, rsrc + t.row0, [&](int k) { return (tid + k * NT) * 8; }, [](int) { return 0; }, stale, what,
+                     [&](int k, uint32_t b) { res[k] = __uint_as_float(b); });
+  }
+  if (p.trace && tid == 0) ctl->t_ready = __builtin_amdgcn_s_memrealtime();
+
   gemv_tile(p, t, gm, xs, ys, wp);
   bar();
-  uint64_t best = 0;
-  for (int r = t.row0 + threadIdx.x; r < t.row1; r += NT) {
-    const float v = ys[r - t.row0];
-    p.logits[(size_t)s * p.vocab + r] = v;
-    const uint64_t k = argmax_key(v, r);
-    best = k > best ? k : best;
+
+  if (type == T_QKV) {
+    const int G = p.hq / p.hk, dh = p.dh, Rg = (G + 2) * dh;
+    for (int m = tid; m < nsets; m += NT) {
+      const int r = t.row0 + 4 * m;
+      const int grp = r / Rg, within = r % Rg, slot = within / dh, jh = within % dh;
+      const int i0 = jh >> 1;  // even dim index; the set holds dims i0, i0 + dh/2, i0 + 1, i0 + 1 + dh/2
+      const QkvSet c = (m == tid) ? pre : qkv_set_consts(p, l, r, pos < 0 ? 0 : pos, s);
+      float y0 = ys[4 * m] + c.b0, y1 = ys[4 * m + 1] + c.b1, y2 = ys[4 * m + 2] + c.b2, y3 = ys[4 * m + 3] + c.b3;
+      if (slot <= G) {  // rotate q and k: pair (i0, i0 + dh/2) and pair (i0 + 1, i0 + 1 + dh/2)
+        const float a0 = y0 * c.cs0.x - y1 * c.cs0.y, b0 = y1 * c.cs0.x + y0 * c.cs0.y;
+        const float a1 = y2 * c.cs1.x - y3 * c.cs1.y, b1 = y3 * c.cs1.x + y2 * c.cs1.y;
+        y0 = a0; y1 = b0; y2 = a1; y3 = b1;
+      }
+      if (slot < G) {
+        uint64_t* q = qt_at(p, l, s) + (size_t)(grp * G + slot) * dh;
+        st_tagf(&q[i0], y0, ep);
+        st_tagf(&q[i0 + dh / 2], y1, ep);
+        st_tagf(&q[i0 + 1], y2, ep);
+        st_tagf(&q[i0 + 1 + dh / 2], y3, ep);
+      } else {
+        // the rounded key/value pairs go to the cache and, tagged, to this step's attention
+        const uint32_t w0 = f2bf(y0) | (f2bf(y2) << 16), w1 = f2bf(y1) | (f2bf(y3) << 16);
+        uint64_t* kv = kvt_at(p, l, s, slot == G ? 0 : 1, grp);
+        st_tag(&kv[i0 >> 1], w0, ep);
+        st_tag(&kv[(i0 + dh / 2) >> 1], w1, ep);
+        const int blk = c.blk;
+        if (blk < 0 || blk >= p.num_blocks) {
+          raise_error(p, ERR_PAGE, (uint32_t)s, (uint32_t)blk);
+          continue;
+        }
+        if (pos < 0) continue;
+        uint16_t* pool = pools[(slot == G ? 0 : p.n_layers) + l];
+        uint32_t* row = (uint32_t*)(pool + (((size_t)blk * p.hk + grp) * 16 + (pos & 15)) * dh);
+        stc(&row[i0 >> 1], w0);
+        stc(&row[(i0 + dh / 2) >> 1], w1);
+      }
+    }
+  } else if (resid) {
+    uint64_t* dst = xt_at(p, l, type == T_OPROJ ? 0 : 1, s);
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const int r = t.row0 + tid + k * NT;
+      if (r < t.row1) st_tagf(&dst[r], res[k] + ys[r - t.row0], ep);
+    }
+  } else if (type == T_GATEUP) {
+    const int npairs = nrows >> 1;
+    uint64_t* hd = ht_at(p, l, s) + (t.row0 >> 1);
+    for (int m = tid; m < npairs; m += NT) {
+      const float a = ys[2 * m], b = ys[2 * m + 1];
+      const float silu = a / (1.0f + expf(-a));
+      st_tagf(&hd[m], silu * b, ep);
+    }
+  } else {  // LM head
+    uint64_t best = 0;
+    for (int r = t.row0 + tid; r < t.row1; r += NT) {
+      const float v = ys[r - t.row0];
+      p.logits[(size_t)s * p.vocab + r] = v;
+      const uint64_t k = argmax_key(v, r);
+      best = k > best ? k : best;
+    }
+    best = block_max_u64(best, ctl);
+    if (tid == 0) stc(&p.amax[(size_t)s * p.n_lm_parts + t.a0], best);
   }
-  best = block_max_u64(best, ctl);
-  if (threadIdx.x == 0) stc(&p.amax[(size_t)s * p.n_lm_parts + t.a0], best);
 }
 
 __device__ __forceinline__ void task_argmax(const KernelParams& p, const TaskDesc& t, Ctl* ctl) {
@@ -1006,11 +1014,10 @@ __global__ __launch_bounds__(NT, 1) void mk_megakernel(KernelParams p) {
   extern __shared__ __attribute__((aligned(16))) unsigned char lds_raw[];
   static_assert(sizeof(Ctl) <= 1024, "control block fits its 1 KB");
   Ctl* ctl = (Ctl*)lds_raw;
-  // LDS: control block | per-layer K/V pool pointers | cache-warming sink | this CU's queue | working set
+  // LDS: control block | per-layer K/V pool pointers | this CU's queue | working set
   uint16_t** pools = (uint16_t**)(lds_raw + 1024);
   const size_t pools_bytes = ((size_t)2 * p.n_layers * sizeof(void*) + 255) & ~size_t(255);
-  unsigned char* sink = lds_raw + 1024 + pools_bytes;
-  TaskDesc* tq = (TaskDesc*)(sink + TOUCH_SINK_BYTES);
+  TaskDesc* tq = (TaskDesc*)(lds_raw + 1024 + pools_bytes);
   float* lds = (float*)((unsigned char*)tq + (((size_t)p.max_queue * sizeof(TaskDesc) + 255) & ~size_t(255)));
   const int cu = blockIdx.x;
   const int q0 = p.queue_off[cu], q1 = p.queue_off[cu + 1];
@@ -1030,16 +1037,8 @@ __global__ __launch_bounds__(NT, 1) void mk_megakernel(KernelParams p) {
   }
   bar();
   WPipe wp;
-  int ti_next = q0 < q1 ? p.queue_idx[q0] : 0;
-  TaskDesc tn = tq[0];
-  prefetch_next<DH>(p, tn, q0 < q1, q0 + 1 < q1 ? &tq[1] : nullptr, wp, ctl, pools, lds, sink);
   for (int qi = q0; qi < q1; ++qi) {
-    const int ti = ti_next;
-    const TaskDesc t = tn;
-    if (qi + 1 < q1) {
-      tn = tq[qi + 1 - q0];
-      ti_next = p.trace ? p.queue_idx[qi + 1] : 0;
-    }
+    const TaskDesc t = tq[qi - q0];
     // Only the LM head's partial maxima travel under flags (the argmax task waits for them); every
     // other input is a tagged activation that its consumer polls for inside the task.
     const int my_sig = (t.type == T_LMHEAD && (int)threadIdx.x < t.sig_n) ? p.sig_slots[t.sig_off + threadIdx.x] : -1;
@@ -1048,27 +1047,25 @@ __global__ __launch_bounds__(NT, 1) void mk_megakernel(KernelParams p) {
       t_queue = __builtin_amdgcn_s_memrealtime();
       ctl->t_ready = t_queue;
     }
-    switch (t.type) {
-      case T_QKV: task_qkv(p, t, lds, ctl, wp, pools); break;
-      case T_ATTN: task_attn<DH, GMAX>(p, t, lds, ctl, pools); break;
-      case T_OPROJ:
-      case T_DOWN: task_residual_gemv(p, t, lds, ctl, wp); break;
-      case T_GATEUP: task_gateup(p, t, lds, ctl, wp); break;
-      case T_LMHEAD: task_lmhead(p, t, lds, ctl, wp); break;
-      case T_ARGMAX:
-        if (t.wait_ev >= 0) wait_event(p, t, ctl);
-        if (p.trace && threadIdx.x == 0) ctl->t_ready = __builtin_amdgcn_s_memrealtime();
-        if (t.wait_ev < 0 || !ctl->aborted) task_argmax(p, t, ctl);
-        break;
-      default: break;
+    // Each task starts its own input streams before it polls for its inputs (they do not depend on
+    // them): an attention split stages its first keys and values, a GEMV its first weight units.
+    // The staging is issued inside the attention branch, so the compiler's wait insertion never sees
+    // an LDS DMA that might be pending on the GEMV path.
+    if (t.type == T_ATTN) {
+      attn_prefetch<DH>(p, t, ctl, pools, lds);
+      task_attn<DH, GMAX>(p, t, lds, ctl, pools);
+    } else if (t.type == T_ARGMAX) {
+      if (t.wait_ev >= 0) wait_event(p, t, ctl);
+      if (p.trace && threadIdx.x == 0) ctl->t_ready = __builtin_amdgcn_s_memrealtime();
+      if (t.wait_ev < 0 || !ctl->aborted) task_argmax(p, t, ctl);
+    } else {
+      gemv_task(p, t, lds, ctl, wp, pools);
     }
     // The LM head's stores must be complete before its flags go out; other tasks' consumers check
     // the tags themselves.
     if (t.type == T_LMHEAD) wait_stores();
     bar();
-    // Publish, then start streaming the next task's weights before waiting for its inputs.
     publish(p, my_sig);
-    prefetch_next<DH>(p, tn, qi + 1 < q1, qi + 2 < q1 ? &tq[qi + 2 - q0] : nullptr, wp, ctl, pools, lds, sink);
     if (p.trace && threadIdx.x == 0) {
       TraceRec r;
       r.t_queue = t_queue;
@@ -1078,7 +1075,7 @@ __global__ __launch_bounds__(NT, 1) void mk_megakernel(KernelParams p) {
       r.type = (uint8_t)t.type;
       r.layer = (uint8_t)t.layer;
       r.epoch = p.epoch;
-      p.trace[ti] = r;
+      p.trace[p.queue_idx[qi]] = r;
     }
   }
 }
