@@ -18,7 +18,7 @@
 
 namespace mk {
 hipError_t launch_megakernel(const KernelParams& p, int grid, size_t lds_bytes, hipStream_t stream);
-hipError_t megakernel_occupancy(int* blocks_per_cu, size_t lds_bytes, int dh, int hq, int hk);
+hipError_t megakernel_occupancy(int* blocks_per_cu, size_t lds_bytes, int dh, int hq, int hk, bool batched);
 hipError_t launch_repack(const RepackArgs& a, int64_t units, hipStream_t stream);
 hipError_t launch_repack_bias(const uint16_t* bq, const uint16_t* bk, const uint16_t* bv, int G, int dh, int nrows,
                               uint16_t* out, hipStream_t stream);
@@ -151,6 +151,7 @@ KernelParams make_params(mk_ctx* c) {
   p.ot = (uint64_t*)(S + g.sl.ot);
   p.ht = (uint64_t*)(S + g.sl.ht);
   p.pt = (uint64_t*)(S + g.sl.pt);
+  p.bpt = (uint64_t*)(S + g.sl.bpt);
   p.logits = c->d_logits;
   p.amax = (uint64_t*)(S + g.sl.amax);
   p.n_layers = m.n_layers;
@@ -202,7 +203,8 @@ mk_status mk_create(const mk_model_config* cfg, int device, mk_ctx** out) {
   (*out)->device = device;
   DeviceGuard dg(device);
   int blocks = 0;
-  if (megakernel_occupancy(&blocks, (size_t)(*out)->g.lds_bytes, cfg->head_dim, cfg->n_q_heads, cfg->n_kv_heads) !=
+  if (megakernel_occupancy(&blocks, (size_t)(*out)->g.lds_bytes, cfg->head_dim, cfg->n_q_heads, cfg->n_kv_heads,
+                           cfg->max_seqs > 1) !=
           hipSuccess ||
       blocks < 1) {
     mk_destroy(*out);
@@ -341,7 +343,7 @@ mk_status mk_load_weights(mk_ctx* c, const mk_tensor* ts, int n, void* stream) {
       default: break;
     }
     const TaskDesc& last = g.tasks[t1 - 1];
-    const int64_t bytes = last.wofs + (int64_t)((last.row1 - last.row0 + r.gm.rg - 1) / r.gm.rg) * r.gm.S * 1024 - a.wofs;
+    const int64_t bytes = last.wofs + task_tile_bytes(r.gm, last) - a.wofs;
     HIPCHK(launch_repack(r, bytes / 1024, st));
     t0 = t1;
   }

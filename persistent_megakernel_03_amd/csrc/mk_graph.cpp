@@ -12,6 +12,8 @@
 // one CU. The tasks of one operator stage are spread evenly, one per CU, so
 // every CU streams an equal share of each weight matrix.
 #include <algorithm>
+#include <climits>
+#include <cstdlib>
 #include <cstring>
 #include <numeric>
 #include <string>
@@ -40,6 +42,17 @@ GemvGeom choose_geom(int K) {
   return g;
 }
 
+GemvGeom choose_geom_batched(int K) {
+  GemvGeom g{};
+  g.K = K;
+  g.P = K / 8;
+  g.lpr = 4;
+  g.rg = 16;
+  g.S = (K + 511) / 512 * 16;
+  g.mfma = 1;
+  return g;
+}
+
 namespace {
 
 struct Range { int r0, r1; };
@@ -54,6 +67,49 @@ std::vector<Range> distribute(int N, int A, int n) {
     out[c].r1 = (int)std::min<int64_t>(N, u1 * A);
   }
   return out;
+}
+
+// Column split of a batched GEMV stage: kS splits of nu units (32 columns each) per row tile.
+struct KSplit {
+  int kS, nu, tiles;
+};
+constexpr int kMaxTileGroups = 48;  // 16-row groups of one batched tile: their partial sums stay in LDS
+
+// Per-CU bytes of a batched stage for each candidate split count, and the cheapest. A CU streams its
+// weight tile (rows x its columns) and reads its columns of every sequence's input as tagged 64-bit
+// words from the coherent level (16 sequences x 8 B per column). Splitting the columns cuts that
+// input traffic kS-fold but adds an exchange: each split writes its partial sums of the tile and
+// reads back kS partials of its own share, plus one more cross-CU round trip (charged as 40 KB).
+// With one split and more than 32 units, the task streams its columns in blocks of 16 units.
+KSplit choose_ksplit(int N, int K, int n_cus, int max_split) {
+  const int nu_tot = (K + 31) / 32;
+  const int64_t units16 = (N + 15) / 16;
+  KSplit best{0, 0, 0};
+  int64_t best_cost = INT64_MAX;
+  for (int kS = 1; kS <= std::min({nu_tot, n_cus, max_split}); ++kS) {
+    int nu = (nu_tot + kS - 1) / kS;
+    if ((nu_tot + nu - 1) / nu != kS) continue;  // the last split would be empty
+    if (kS > 1 && nu > 32) continue;               // a split's columns fit one LDS block
+    if (nu > 32) nu = (int)align_up(nu, 16);
+    // one split: as many row tiles as CUs, or more (several per CU) when tiles would outgrow the LDS;
+    // with a column split, one task per CU and stage (its splits wait for each other)
+    const int64_t tiles = kS == 1 ? std::max<int64_t>(n_cus, (units16 + kMaxTileGroups - 1) / kMaxTileGroups) : n_cus / kS;
+    const int64_t R = (units16 + tiles - 1) / tiles;
+    if (R > kMaxTileGroups) continue;
+    if (kS > 1) {  // every split must own rows: each non-empty tile needs at least kS row quads
+      int min_q = INT_MAX;
+      for (const Range& r : distribute(N, 16, (int)tiles))
+        if (r.r1 > r.r0) min_q = std::min(min_q, (r.r1 - r.r0 + 3) / 4);
+      if (min_q < kS) continue;
+    }
+    const int64_t per_cu = (tiles + n_cus - 1) / n_cus;  // tasks per CU and stage
+    const int64_t cost = per_cu * (R * nu * 1024 + (int64_t)4096 * nu) + (kS > 1 ? 4096 * R + 40000 : 0);
+    if (cost < best_cost) {
+      best_cost = cost;
+      best = KSplit{kS, nu, (int)tiles};
+    }
+  }
+  return best;
 }
 
 struct Builder {
@@ -74,6 +130,8 @@ struct Builder {
     g.tasks.push_back(t);
     g.acc.emplace_back();
     g.comb_acc.emplace_back();
+    g.task_group.push_back(-1);
+    g.task_comb.push_back(0);
     task_cu.push_back(cu);
     task_sig.emplace_back();
     return (int)g.tasks.size() - 1;
@@ -130,7 +188,7 @@ std::string build_graph(const mk_model_config& c, int n_cus, HostGraph& g) {
   // a workgroup polls each tagged activation vector with at most 16 (d, hq*dh) or 32 (d_ffn) words per thread
   if (c.d_model > 8192 || c.n_q_heads * c.head_dim > 8192 || c.d_ffn > 16384) return "model too wide for the activation polls";
   if (c.block_size != 16) return "block_size must be 16";
-  if (c.max_seqs != 1) return "this build runs batch-1 graphs (max_seqs == 1)";
+  if (c.max_seqs < 1 || c.max_seqs > 16) return "max_seqs must be 1..16 (one 16-row MFMA tile of sequences)";
   if (c.max_blocks_per_seq < 1 || c.num_blocks < 1) return "empty KV cache";
   if (!(c.rms_eps >= 0.f) || !(c.rope_theta > 0.f)) return "bad rms_eps or rope_theta";
   if (c.attn_splits < 0 || c.attn_splits > 64) return "attn_splits out of range";
@@ -150,11 +208,13 @@ std::string build_graph(const mk_model_config& c, int n_cus, HostGraph& g) {
     sp = std::min(sp, std::max(1, 2 * n_cus / (S * hk)));
     g.splits = std::max(1, sp);
   }
-  g.geoms[G_QKV] = choose_geom(d);
-  g.geoms[G_O] = choose_geom(qd);
-  g.geoms[G_GU] = choose_geom(d);
-  g.geoms[G_D] = choose_geom(f);
-  g.geoms[G_LM] = choose_geom(d);
+  // one sequence: row-per-lanes GEMV tiles; several: 16-row MFMA tiles (the GEMV becomes a skinny GEMM)
+  auto geom = S > 1 ? choose_geom_batched : choose_geom;
+  g.geoms[G_QKV] = geom(d);
+  g.geoms[G_O] = geom(qd);
+  g.geoms[G_GU] = geom(d);
+  g.geoms[G_D] = geom(f);
+  g.geoms[G_LM] = geom(d);
 
   g.sym_size[S_X] = (int64_t)S * d;
   g.sym_size[S_Q] = (int64_t)S * qd;
@@ -167,45 +227,150 @@ std::string build_graph(const mk_model_config& c, int n_cus, HostGraph& g) {
   g.sym_size[S_TOKOUT] = S;
 
   Builder b(g, c);
-  int ev_x = -1;  // event "residual stream ready for this layer" (none before layer 0)
-  int max_task_rows = 0;
-  std::vector<int> down_ids;
-  for (int l = 0; l < L; ++l) {
-    // ---- QKV: RMSNorm + GEMV + bias + RoPE + KV append
-    const int aq = lcm_i(4, g.geoms[G_QKV].rg);
-    auto qkv = b.gemv_stage(T_QKV, l, G_QKV, Nqkv, aq, ev_x);
-    std::vector<int> ev_qkv(hk);
-    std::vector<int> nprod(hk, 0);
-    for (int t : qkv) {
-      const TaskDesc& td = g.tasks[t];
-      for (int grp = td.row0 / Rg; grp <= (td.row1 - 1) / Rg; ++grp) b.task_sig[t].push_back({-1 - grp, nprod[grp]++});
+  // Batched stages also split the columns over CUs. MK_BATCHED_MAX_KSPLIT caps the number of column
+  // splits (1 = row tiles only, whose columns then stream in 512-column blocks).
+  int max_ksplit = 1 << 20;
+  if (const char* e = std::getenv("MK_BATCHED_MAX_KSPLIT")) max_ksplit = std::max(1, std::atoi(e));
+  int64_t bpt_words = 0;
+  int64_t bpart_slots = 0;
+  std::string err;
+
+  // Reads of columns [c0, c1) of every sequence's GEMV input.
+  auto in_acc = [&](int t, int type, int l, int64_t c0, int64_t c1) {
+    for (int s = 0; s < S; ++s) {
+      if (type == T_QKV) {
+        if (l > 0) b.acc(t, S_X, (int64_t)s * d + c0, (int64_t)s * d + c1, 0);
+      } else if (type == T_OPROJ) {
+        b.acc(t, S_O, (int64_t)s * qd + c0, (int64_t)s * qd + c1, 0);
+      } else if (type == T_DOWN) {
+        b.acc(t, S_H, (int64_t)s * f + c0, (int64_t)s * f + c1, 0);
+      } else {
+        b.acc(t, S_X, (int64_t)s * d + c0, (int64_t)s * d + c1, 0);
+      }
     }
-    for (int grp = 0; grp < hk; ++grp) ev_qkv[grp] = b.new_event(nprod[grp]);
-    for (int t : qkv) {
-      for (auto& s : b.task_sig[t]) s.first = ev_qkv[-1 - s.first];
-      const TaskDesc& td = g.tasks[t];
-      max_task_rows = std::max(max_task_rows, td.row1 - td.row0);
-      for (int s = 0; s < S; ++s) {
-        if (l > 0) b.acc(t, S_X, (int64_t)s * d, (int64_t)(s + 1) * d, 0);
-        b.acc(t, S_CTX, s, s + 1, 0);
+  };
+  // Output rows [r0, r1) of every sequence, with the residual rows and context lengths the epilogue
+  // reads, in the task's first phase or (comb) its second.
+  auto out_acc = [&](int t, int type, int l, int r0, int r1, bool comb) {
+    auto A = [&](int buf, int64_t lo, int64_t hi, int w) {
+      if (comb) b.cacc(t, buf, lo, hi, w);
+      else b.acc(t, buf, lo, hi, w);
+    };
+    for (int s = 0; s < S; ++s) {
+      if (type == T_QKV) {
+        A(S_CTX, s, s + 1, 0);
         // packed rows -> written q / k / v elements (pairs [a/2, b/2) and their + dh/2 partners)
-        for (int r = td.row0; r < td.row1;) {
+        for (int r = r0; r < r1;) {
           const int grp = r / Rg, within = r % Rg, slot = within / dh;
-          const int hs = grp * Rg + slot * dh;                       // packed start of this head
-          const int e = std::min(td.row1, hs + dh);
+          const int hs = grp * Rg + slot * dh;  // packed start of this head
+          const int e = std::min(r1, hs + dh);
           const int p0 = (r - hs) / 2, p1 = (e - hs) / 2;
           if (slot < G) {
             const int64_t base = (int64_t)s * qd + (int64_t)(grp * G + slot) * dh;
-            b.acc(t, S_Q, base + p0, base + p1, 1);
-            b.acc(t, S_Q, base + p0 + dh / 2, base + p1 + dh / 2, 1);
+            A(S_Q, base + p0, base + p1, 1);
+            A(S_Q, base + p0 + dh / 2, base + p1 + dh / 2, 1);
           } else {
             const int64_t base = (((int64_t)l * S + s) * hk + grp) * 2 * dh + (slot == G ? 0 : dh);
-            b.acc(t, S_KVCUR, base + p0, base + p1, 1);
-            b.acc(t, S_KVCUR, base + p0 + dh / 2, base + p1 + dh / 2, 1);
+            A(S_KVCUR, base + p0, base + p1, 1);
+            A(S_KVCUR, base + p0 + dh / 2, base + p1 + dh / 2, 1);
           }
           r = e;
         }
+      } else if (type == T_OPROJ || type == T_DOWN) {
+        if (type == T_DOWN || l > 0) A(S_X, (int64_t)s * d + r0, (int64_t)s * d + r1, 0);
+        A(S_X, (int64_t)s * d + r0, (int64_t)s * d + r1, 1);
+      } else if (type == T_GATEUP) {
+        A(S_H, (int64_t)s * f + r0 / 2, (int64_t)s * f + r1 / 2, 1);
+      } else {
+        A(S_LOGITS, (int64_t)s * V + r0, (int64_t)s * V + r1, 1);
       }
+    }
+  };
+  struct StageTask {
+    int id, r0, r1;  // task and the output rows it writes
+    bool comb;       // written in its second phase
+  };
+  // One GEMV stage. One sequence: one task per CU with a row tile. Several: row tiles of 16-row
+  // groups, each split by columns over kS CUs; each split then sums the kS partials of its share of
+  // the tile's rows (a quarter-row-group granularity) and applies the epilogue to it.
+  auto stage = [&](int type, int l, int geom, int N, int K, int align, int wait_ev,
+                   const std::vector<char>* skip) -> std::vector<StageTask> {
+    std::vector<StageTask> out;
+    if (S == 1) {
+      for (int id : b.gemv_stage(type, l, geom, N, align, wait_ev, skip)) {
+        in_acc(id, type, l, 0, K);
+        out.push_back({id, g.tasks[id].row0, g.tasks[id].row1, false});
+      }
+      return out;
+    }
+    const KSplit ks = choose_ksplit(N, K, n_cus, max_ksplit);
+    if (!ks.kS) {
+      err = "no column split of a batched GEMV stage fits the LDS";
+      return out;
+    }
+    const int nu_tot = (K + 31) / 32, tiles = ks.tiles;
+    const auto rs = distribute(N, 16, tiles);
+    for (int k = 0; k < tiles; ++k) {
+      if (rs[k].r1 <= rs[k].r0) continue;
+      const int rows = rs[k].r1 - rs[k].r0, R = (rows + 15) / 16, Q = (rows + 3) / 4;
+      if (Q < ks.kS) {
+        err = "a batched tile has fewer row quads than column splits";
+        return out;
+      }
+      g.max_tile_groups = std::max(g.max_tile_groups, R);
+      int grp = -1;
+      const int64_t pofs = bpt_words, slot0 = bpart_slots;
+      if (ks.kS > 1) {
+        bpt_words += (int64_t)ks.kS * (R * 256 + 64);
+        bpart_slots += ks.kS;
+        grp = (int)g.group_size.size();
+        g.group_size.push_back(ks.kS);
+      }
+      for (int j = 0; j < ks.kS; ++j) {
+        TaskDesc t{};
+        t.type = type;
+        t.layer = l;
+        t.wait_ev = wait_ev;
+        t.row0 = rs[k].r0;
+        t.row1 = rs[k].r1;
+        t.geom = geom;
+        t.wofs = b.packed;
+        const int kb0 = j * ks.nu, nuj = ks.kS == 1 ? ks.nu : std::min(ks.nu, nu_tot - kb0);
+        t.a1 = (int32_t)pofs;
+        t.a2 = kb0 | (nuj << 16);
+        t.a3 = j | (ks.kS << 8);
+        b.packed += (int64_t)R * nuj * 1024;
+        const int id = b.add_task(t, (k * ks.kS + j) % n_cus);
+        g.task_group[id] = grp;
+        g.task_comb[id] = ks.kS > 1;
+        in_acc(id, type, l, 32LL * kb0, std::min<int64_t>(K, 32LL * (kb0 + nuj)));
+        if (ks.kS > 1) {
+          b.acc(id, S_BPART, slot0 + j, slot0 + j + 1, 1);
+          b.cacc(id, S_BPART, slot0, slot0 + ks.kS, 0);
+        }
+        const int r0 = rs[k].r0 + 4 * (Q * j / ks.kS), r1 = std::min(rs[k].r1, rs[k].r0 + 4 * (Q * (j + 1) / ks.kS));
+        out.push_back({id, r0, r1, ks.kS > 1});
+      }
+    }
+    return out;
+  };
+
+  int ev_x = -1;  // event "residual stream ready for this layer" (none before layer 0)
+  int max_task_rows = 0;
+  for (int l = 0; l < L; ++l) {
+    // ---- QKV: RMSNorm + GEMV + bias + RoPE + KV append
+    auto qkv = stage(T_QKV, l, G_QKV, Nqkv, d, lcm_i(4, g.geoms[G_QKV].rg), ev_x, nullptr);
+    if (!err.empty()) return err;
+    std::vector<int> ev_qkv(hk);
+    std::vector<int> nprod(hk, 0);
+    for (const StageTask& st : qkv)
+      for (int grp = st.r0 / Rg; st.r1 > st.r0 && grp <= (st.r1 - 1) / Rg; ++grp)
+        b.task_sig[st.id].push_back({-1 - grp, nprod[grp]++});
+    for (int grp = 0; grp < hk; ++grp) ev_qkv[grp] = b.new_event(nprod[grp]);
+    for (const StageTask& st : qkv) {
+      for (auto& sg : b.task_sig[st.id]) sg.first = ev_qkv[-1 - sg.first];
+      max_task_rows = std::max(max_task_rows, g.tasks[st.id].row1 - g.tasks[st.id].row0);
+      out_acc(st.id, T_QKV, l, st.r0, st.r1, st.comb);
     }
     // ---- attention splits; the last split of each (seq, kv head) merges and signals
     const int ev_att = b.new_event(S * hk);
@@ -216,7 +381,9 @@ std::string build_graph(const mk_model_config& c, int n_cus, HostGraph& g) {
       const int n_attn = S * hk * g.splits;
       int k = 0;
       for (int s = 0; s < S; ++s)
-        for (int grp = 0; grp < hk; ++grp)
+        for (int grp = 0; grp < hk; ++grp) {
+          const int agrp = (int)g.group_size.size();
+          g.group_size.push_back(g.splits);
           for (int j = 0; j < g.splits; ++j, ++k) {
             TaskDesc t{};
             t.type = T_ATTN;
@@ -229,6 +396,8 @@ std::string build_graph(const mk_model_config& c, int n_cus, HostGraph& g) {
             const int cu = (int)((int64_t)k * n_cus / n_attn);
             attn_cu[cu] = 1;
             const int id = b.add_task(t, cu);
+            g.task_group[id] = agrp;
+            g.task_comb[id] = j == g.splits - 1;
             b.task_sig[id].push_back({ev_att, s * hk + grp});
             b.acc(id, S_Q, (int64_t)s * qd + (int64_t)grp * G * dh, (int64_t)s * qd + (int64_t)(grp + 1) * G * dh, 0);
             b.acc(id, S_KVCUR, (((int64_t)l * S + s) * hk + grp) * 2 * dh, (((int64_t)l * S + s) * hk + grp + 1) * 2 * dh, 0);
@@ -239,66 +408,54 @@ std::string build_graph(const mk_model_config& c, int n_cus, HostGraph& g) {
               b.cacc(id, S_PART, ((int64_t)s * hq + h) * g.splits, ((int64_t)s * hq + h + 1) * g.splits, 0);
             b.cacc(id, S_O, (int64_t)s * qd + (int64_t)grp * G * dh, (int64_t)s * qd + (int64_t)(grp + 1) * G * dh, 1);
           }
+        }
       g.n_attn_groups = std::max(g.n_attn_groups, (l + 1) * S * hk);
     }
     // ---- O projection + residual
     const bool few_attn = (int)std::count(attn_cu.begin(), attn_cu.end(), 1) * 4 <= n_cus;
-    auto op = b.gemv_stage(T_OPROJ, l, G_O, d, g.geoms[G_O].rg, ev_att, few_attn ? &attn_cu : nullptr);
+    auto op = stage(T_OPROJ, l, G_O, d, qd, g.geoms[G_O].rg, ev_att, few_attn ? &attn_cu : nullptr);
+    if (!err.empty()) return err;
     const int ev_o = b.new_event((int)op.size());
     for (size_t i = 0; i < op.size(); ++i) {
-      const int t = op[i];
-      const TaskDesc& td = g.tasks[t];
-      max_task_rows = std::max(max_task_rows, td.row1 - td.row0);
-      b.task_sig[t].push_back({ev_o, (int)i});
-      for (int s = 0; s < S; ++s) {
-        b.acc(t, S_O, (int64_t)s * qd, (int64_t)(s + 1) * qd, 0);
-        if (l > 0) b.acc(t, S_X, (int64_t)s * d + td.row0, (int64_t)s * d + td.row1, 0);
-        b.acc(t, S_X, (int64_t)s * d + td.row0, (int64_t)s * d + td.row1, 1);
-      }
+      max_task_rows = std::max(max_task_rows, g.tasks[op[i].id].row1 - g.tasks[op[i].id].row0);
+      b.task_sig[op[i].id].push_back({ev_o, (int)i});
+      out_acc(op[i].id, T_OPROJ, l, op[i].r0, op[i].r1, op[i].comb);
     }
     // ---- RMSNorm + gate/up + SwiGLU
-    auto gu = b.gemv_stage(T_GATEUP, l, G_GU, 2 * f, lcm_i(2, g.geoms[G_GU].rg), ev_o);
+    auto gu = stage(T_GATEUP, l, G_GU, 2 * f, d, lcm_i(2, g.geoms[G_GU].rg), ev_o, nullptr);
+    if (!err.empty()) return err;
     const int ev_gu = b.new_event((int)gu.size());
     for (size_t i = 0; i < gu.size(); ++i) {
-      const int t = gu[i];
-      const TaskDesc& td = g.tasks[t];
-      max_task_rows = std::max(max_task_rows, td.row1 - td.row0);
-      b.task_sig[t].push_back({ev_gu, (int)i});
-      for (int s = 0; s < S; ++s) {
-        b.acc(t, S_X, (int64_t)s * d, (int64_t)(s + 1) * d, 0);
-        b.acc(t, S_H, (int64_t)s * f + td.row0 / 2, (int64_t)s * f + td.row1 / 2, 1);
-      }
+      max_task_rows = std::max(max_task_rows, g.tasks[gu[i].id].row1 - g.tasks[gu[i].id].row0);
+      b.task_sig[gu[i].id].push_back({ev_gu, (int)i});
+      out_acc(gu[i].id, T_GATEUP, l, gu[i].r0, gu[i].r1, gu[i].comb);
     }
     // ---- down projection + residual
-    auto dn = b.gemv_stage(T_DOWN, l, G_D, d, g.geoms[G_D].rg, ev_gu);
+    auto dn = stage(T_DOWN, l, G_D, d, f, g.geoms[G_D].rg, ev_gu, nullptr);
+    if (!err.empty()) return err;
     ev_x = b.new_event((int)dn.size());
     for (size_t i = 0; i < dn.size(); ++i) {
-      const int t = dn[i];
-      const TaskDesc& td = g.tasks[t];
-      max_task_rows = std::max(max_task_rows, td.row1 - td.row0);
-      b.task_sig[t].push_back({ev_x, (int)i});
-      for (int s = 0; s < S; ++s) {
-        b.acc(t, S_H, (int64_t)s * f, (int64_t)(s + 1) * f, 0);
-        b.acc(t, S_X, (int64_t)s * d + td.row0, (int64_t)s * d + td.row1, 0);
-        b.acc(t, S_X, (int64_t)s * d + td.row0, (int64_t)s * d + td.row1, 1);
-      }
+      max_task_rows = std::max(max_task_rows, g.tasks[dn[i].id].row1 - g.tasks[dn[i].id].row0);
+      b.task_sig[dn[i].id].push_back({ev_x, (int)i});
+      out_acc(dn[i].id, T_DOWN, l, dn[i].r0, dn[i].r1, dn[i].comb);
     }
   }
-  // ---- final RMSNorm + LM head + partial argmax
-  auto lm = b.gemv_stage(T_LMHEAD, L, G_LM, V, g.geoms[G_LM].rg, ev_x);
+  // ---- final RMSNorm + LM head + partial argmax (one part per task)
+  auto lm = stage(T_LMHEAD, L, G_LM, V, d, g.geoms[G_LM].rg, ev_x, nullptr);
+  if (!err.empty()) return err;
   g.n_lm_parts = (int)lm.size();
   g.sym_size[S_AMAX] = (int64_t)S * g.n_lm_parts;
   const int ev_lm = b.new_event((int)lm.size());
   for (size_t i = 0; i < lm.size(); ++i) {
-    const int t = lm[i];
-    TaskDesc& td = g.tasks[t];
-    td.a0 = (int)i;
-    max_task_rows = std::max(max_task_rows, td.row1 - td.row0);
+    const int t = lm[i].id;
+    g.tasks[t].a0 = (int)i;
+    max_task_rows = std::max(max_task_rows, g.tasks[t].row1 - g.tasks[t].row0);
     b.task_sig[t].push_back({ev_lm, (int)i});
+    out_acc(t, T_LMHEAD, L, lm[i].r0, lm[i].r1, lm[i].comb);
     for (int s = 0; s < S; ++s) {
-      b.acc(t, S_X, (int64_t)s * d, (int64_t)(s + 1) * d, 0);
-      b.acc(t, S_LOGITS, (int64_t)s * V + td.row0, (int64_t)s * V + td.row1, 1);
-      b.acc(t, S_AMAX, (int64_t)s * g.n_lm_parts + (int64_t)i, (int64_t)s * g.n_lm_parts + (int64_t)i + 1, 1);
+      const int64_t e = (int64_t)s * g.n_lm_parts + (int64_t)i;
+      if (lm[i].comb) b.cacc(t, S_AMAX, e, e + 1, 1);
+      else b.acc(t, S_AMAX, e, e + 1, 1);
     }
   }
   // ---- argmax per sequence
@@ -314,6 +471,7 @@ std::string build_graph(const mk_model_config& c, int n_cus, HostGraph& g) {
     b.acc(id, S_CTX, s, s + 1, 1);
     b.acc(id, S_TOKOUT, s, s + 1, 1);
   }
+  g.sym_size[S_BPART] = bpart_slots;
 
   // ---- events -> contiguous flag slots; task signal lists -> absolute slots
   g.events.resize(b.ev_producers.size());
@@ -335,7 +493,7 @@ std::string build_graph(const mk_model_config& c, int n_cus, HostGraph& g) {
   }
   // the O and down tasks keep their residual rows in registers: at most 4 per thread of 512
   for (const TaskDesc& td : g.tasks)
-    if ((td.type == T_OPROJ || td.type == T_DOWN) && td.row1 - td.row0 > 4 * 512) return "residual task too tall";
+    if (S == 1 && (td.type == T_OPROJ || td.type == T_DOWN) && td.row1 - td.row0 > 4 * 512) return "residual task too tall";
   // ---- per-CU queues in global order
   g.queue_off.assign(n_cus + 1, 0);
   for (int32_t cu : b.task_cu) g.queue_off[cu + 1]++;
@@ -372,6 +530,7 @@ std::string build_graph(const mk_model_config& c, int n_cus, HostGraph& g) {
   g.sl.ot = take((int64_t)L * S * qd * 8);
   g.sl.ht = take((int64_t)L * S * f * 8);
   g.sl.pt = take((int64_t)L * S * hq * g.splits * (dh + 2) * 8);
+  g.sl.bpt = take(bpt_words * 8);
   g.sl.tagged_end = o;
   g.sl.amax = take((int64_t)S * g.n_lm_parts * 8);
   g.sl.tokbuf = take((int64_t)std::max(g.max_pos, 64) * 4);
@@ -382,7 +541,10 @@ std::string build_graph(const mk_model_config& c, int n_cus, HostGraph& g) {
   // ---- LDS: padded GEMV input vector + per-row results, or the attention working set
   int64_t xs = 0;
   for (int i = 0; i < G_COUNT; ++i) xs = std::max<int64_t>(xs, (int64_t)g.geoms[i].S * g.geoms[i].lpr * 8);
-  const int64_t gemv_lds = xs * 4 + (int64_t)align_up(max_task_rows, 64) * 4 * S + 1024;
+  int64_t gemv_lds = xs * 4 + (int64_t)align_up(max_task_rows, 64) * 4 * S + 1024;
+  if (S > 1)  // batched: the input columns as MFMA fragments (32 units x 64 lanes x 32 B), the tile's
+              // partial sums (1 KB per 16-row group), two edge tiles per wave, per-sequence scalars
+    gemv_lds = 32 * 64 * 32 + (int64_t)g.max_tile_groups * 1024 + 8 * 2 * 1024 + 256;
   // attention: scores of one register chunk (8 waves x 64/(dh/8) positions x 8 slots), per-wave
   // partial outputs and the staged queries
   // attention: K and V staging (4 slots x 8 waves x 1 KB each), the scores of one chunk
@@ -457,7 +619,12 @@ std::string validate_graph(const HostGraph& g) {
     const GemvGeom& q = g.geoms[td.geom];
     if (td.row1 <= td.row0) return "empty GEMV task";
     if (td.wofs != end) return "GEMV tiles not contiguous in stage order";
-    end += (int64_t)((td.row1 - td.row0 + q.rg - 1) / q.rg) * q.S * 1024;
+    if (q.mfma) {  // a batched split: its columns lie inside K, and a several-block task has whole blocks
+      const int kb0 = td.a2 & 0xFFFF, nu = td.a2 >> 16, kS = td.a3 >> 8;
+      if (nu < 1 || 32 * kb0 >= q.K || (kS > 1 && nu > 32) || (nu > 32 && nu % 16)) return "bad batched column split";
+      if ((td.row1 - td.row0 + 15) / 16 > g.max_tile_groups) return "batched tile taller than its LDS";
+    }
+    end += task_tile_bytes(q, td);
     if (td.type == T_QKV && (td.row0 % 4 || td.row1 % 4)) return "QKV task not aligned to RoPE pair sets";
     if (td.type == T_GATEUP && (td.row0 % 2 || td.row1 % 2)) return "gate/up task splits a pair";
   }
@@ -478,16 +645,8 @@ uint64_t sm_next(uint64_t& s) {
 
 std::string simulate_graph(const HostGraph& g, uint64_t seed, int n_steps) {
   const int nt = (int)g.tasks.size();
-  // Static writer/reader lists per element. An attention group's merge is performed by its last
-  // split (in global order), which polls the other splits' partials: it cannot finish before they do.
-  std::vector<int> comb_pos(nt, -1);
-  {
-    std::vector<int> last_of_group(g.n_attn_groups, -1);
-    for (int t = 0; t < nt; ++t)
-      if (g.tasks[t].type == T_ATTN) last_of_group[g.tasks[t].a3] = t;
-    for (int t = 0; t < nt; ++t)
-      if (g.tasks[t].type == T_ATTN) comb_pos[t] = last_of_group[g.tasks[t].a3];
-  }
+  const int ng = (int)g.group_size.size();
+  // Static writer/reader lists per element; a task's second-phase accesses count at its position.
   std::vector<std::vector<std::vector<int>>> writers(S_COUNT), readers(S_COUNT);
   for (int b = 0; b < S_COUNT; ++b) {
     writers[b].resize(g.sym_size[b]);
@@ -501,9 +660,9 @@ std::string simulate_graph(const HostGraph& g, uint64_t seed, int n_steps) {
   for (int t = 0; t < nt; ++t) {
     for (const Access& a : g.acc[t])
       if (!add(a, t)) return "access out of symbolic range";
-    if (comb_pos[t] == t)
+    if (g.task_comb[t])
       for (const Access& a : g.comb_acc[t])
-        if (!add(a, t)) return "merge access out of symbolic range";
+        if (!add(a, t)) return "second-phase access out of symbolic range";
   }
   for (int b = 0; b < S_COUNT; ++b)
     for (auto& v : writers[b]) {
@@ -514,17 +673,20 @@ std::string simulate_graph(const HostGraph& g, uint64_t seed, int n_steps) {
   std::vector<std::vector<int64_t>> ver(S_COUNT);  // step * nt + writer position, or -1
   for (int b = 0; b < S_COUNT; ++b) ver[b].assign(g.sym_size[b], -1);
   std::vector<uint32_t> flags(g.n_flag_slots, 0);
-  std::vector<int> group_ended(g.n_attn_groups, 0);
   uint64_t rng = seed;
   for (int step = 0; step < n_steps; ++step) {
     const uint32_t epoch = (uint32_t)step + 1;
-    std::vector<char> ended(nt, 0), started(nt, 0);
+    std::vector<char> ended(nt, 0), phase(nt, 0);  // phase 1: first phase running, 2: waiting for its group
+    std::vector<int> group_done(ng, 0);            // tasks of the group past their first phase
     std::vector<int> qpos(g.n_cus), running(g.n_cus, -1);
     for (int cu = 0; cu < g.n_cus; ++cu) qpos[cu] = g.queue_off[cu];
     // Expected version of element e for a reader at global position pos: the last writer before
-    // pos in this step (at or before pos for a merge, which runs after its own split's write).
+    // pos in this step (at or before pos in a second phase, which runs after the task's own first
+    // phase). A batched tile's partials are read from every split of its group, earlier or later in
+    // the global order: they must all be this step's.
     auto expected = [&](int b, int64_t e, int pos, bool inclusive) -> int64_t {
       const auto& w = writers[b][e];
+      if (b == S_BPART) return w.size() == 1 ? (int64_t)step * nt + w[0] : -2;
       auto it = inclusive ? std::upper_bound(w.begin(), w.end(), pos) : std::lower_bound(w.begin(), w.end(), pos);
       if (it != w.begin()) return (int64_t)step * nt + *(it - 1);
       if (!w.empty() && step > 0) return (int64_t)(step - 1) * nt + w.back();
@@ -549,8 +711,9 @@ std::string simulate_graph(const HostGraph& g, uint64_t seed, int n_steps) {
           const auto& w = writers[a.buf][e];
           auto it = std::lower_bound(w.begin(), w.end(), pos);
           const int prev = it != w.begin() ? *(it - 1) : -1;
+          // (a tile's partials are written once per step and read only within it)
           for (int r : readers[a.buf][e])
-            if (r > prev && r < pos && !ended[r]) {
+            if (a.buf != S_BPART && r > prev && r < pos && !ended[r]) {
               err = "task " + std::to_string(pos) + " overwrote buffer " + std::to_string(a.buf) + " element " +
                     std::to_string(e) + " while task " + std::to_string(r) + " still needed it";
               return false;
@@ -567,18 +730,25 @@ std::string simulate_graph(const HostGraph& g, uint64_t seed, int n_steps) {
         if (flags[s] < epoch) return false;
       return true;
     };
+    auto finish = [&](int t) {  // a group's tasks without a second phase leave publishing to those with one
+      ended[t] = 1;
+      if (g.task_group[t] >= 0 && !g.task_comb[t]) return;
+      const TaskDesc& td = g.tasks[t];
+      for (int i = 0; i < td.sig_n; ++i) flags[g.sig_slots[td.sig_off + i]] = epoch;
+    };
     int done = 0;
     std::vector<int> cand;
     while (done < nt) {
       cand.clear();
       for (int cu = 0; cu < g.n_cus; ++cu) {
         if (running[cu] >= 0) {
-          // a merging split ends only after the other splits of its group have ended
           const int t = running[cu];
-          if (comb_pos[t] == t && group_ended[g.tasks[t].a3] < g.splits - 1) continue;
+          // a second phase waits until every task of its group has finished its first phase
+          if (phase[t] == 2 && group_done[g.task_group[t]] < g.group_size[g.task_group[t]]) continue;
+          cand.push_back(cu);
+        } else if (qpos[cu] < g.queue_off[cu + 1] && ready(g.queue_idx[qpos[cu]])) {
           cand.push_back(cu);
         }
-        else if (qpos[cu] < g.queue_off[cu + 1] && ready(g.queue_idx[qpos[cu]])) cand.push_back(cu);
       }
       if (cand.empty()) return "deadlock at step " + std::to_string(step) + " after " + std::to_string(done) + " tasks";
       const int cu = cand[sm_next(rng) % cand.size()];
@@ -586,27 +756,27 @@ std::string simulate_graph(const HostGraph& g, uint64_t seed, int n_steps) {
       if (running[cu] < 0) {
         const int t = g.queue_idx[qpos[cu]++];
         if (!check_reads(g.acc[t], t, false, err)) return err;
-        started[t] = 1;
+        phase[t] = 1;
         running[cu] = t;
+      } else if (phase[running[cu]] == 1) {
+        const int t = running[cu];
+        if (!apply_writes(g.acc[t], t, err)) return err;
+        if (g.task_group[t] >= 0) ++group_done[g.task_group[t]];
+        if (g.task_comb[t]) {
+          phase[t] = 2;
+        } else {
+          running[cu] = -1;
+          finish(t);
+          ++done;
+        }
       } else {
         const int t = running[cu];
         running[cu] = -1;
-        const TaskDesc& td = g.tasks[t];
-        if (!apply_writes(g.acc[t], t, err)) return err;
-        ended[t] = 1;
+        // an attention merge reads its own split's partial, written in its first phase
+        if (!check_reads(g.comb_acc[t], t, g.tasks[t].type == T_ATTN, err)) return err;
+        if (!apply_writes(g.comb_acc[t], t, err)) return err;
+        finish(t);
         ++done;
-        if (td.type == T_ATTN) {
-          if (comb_pos[t] == t) {
-            if (!check_reads(g.comb_acc[t], t, true, err)) return err;
-            if (!apply_writes(g.comb_acc[t], t, err)) return err;
-            for (int i = 0; i < td.sig_n; ++i) flags[g.sig_slots[td.sig_off + i]] = epoch;
-            group_ended[td.a3] = 0;
-          } else {
-            ++group_ended[td.a3];
-          }
-        } else {
-          for (int i = 0; i < td.sig_n; ++i) flags[g.sig_slots[td.sig_off + i]] = epoch;
-        }
       }
     }
   }

@@ -25,13 +25,19 @@ enum TaskType : int32_t {
   T_ARGMAX = 7,  // argmax over the LM-head partials, token out, context length + 1
 };
 
-// Geometry of one GEMV operand in the packed (streaming) layout. A row of K
-// bf16 values is P = K/8 pieces of 16 bytes. A "unit" is 1 KB: 64 lanes x 16 B.
-// Rows go in groups of RG = 64/LPR rows. A group is S units. In unit u of a
-// group, lane l holds piece u*LPR + l%LPR of row l/LPR. Pieces past P are zero.
+// Geometry of one GEMV operand in the packed (streaming) layout. A row of K bf16 values is
+// P = K/8 pieces of 16 bytes. A "unit" is 1 KB: 64 lanes x 16 B.
+//  mfma == 0 (one sequence): rows go in groups of rg = 64/lpr rows; a group is S units. In unit u
+//    of a group, lane l holds piece u*lpr + l%lpr of row l/lpr.
+//  mfma == 1 (batched): rows go in groups of 16; unit u of a group covers columns [32u, 32u + 32)
+//    and lane l holds piece 4u + l/16 of row l%16: the row operand of one 16x16x32 bf16 MFMA.
+//    A task streams only the units of its own column range (see TaskDesc); S is the number of
+//    units that cover K.
+// Pieces past P are zero.
 struct GemvGeom {
   int32_t K, P, lpr, rg, S;
-  int32_t pad[3];
+  int32_t mfma;
+  int32_t pad[2];
 };
 enum GeomIndex : int32_t { G_QKV = 0, G_O = 1, G_GU = 2, G_D = 3, G_LM = 4, G_COUNT = 5 };
 
@@ -44,7 +50,12 @@ struct TaskDesc {       // 64 bytes; read with scalar loads
   int32_t row0, row1;   // GEMV: packed output rows [row0, row1)
   int32_t geom;         // GEMV: GeomIndex
   int64_t wofs;         // GEMV: byte offset of the tile in the packed weights
-  int32_t a0, a1, a2, a3;  // ATTN: seq, kv head, split, counter | LMHEAD: part index | ARGMAX: seq
+  // ATTN: seq, kv head, split, group | ARGMAX: a0 = seq | LMHEAD: a0 = part index.
+  // Batched GEMV (several sequences): the tile's rows are split over kS tasks by columns.
+  //   a1 = word offset of the tile's partial sums in KernelParams::bpt (kS > 1),
+  //   a2 = first column unit | units << 16 (units of 32 columns),
+  //   a3 = split index | kS << 8.
+  int32_t a0, a1, a2, a3;
   int32_t wait_slot0, wait_nslots;  // the wait event's flag slots (copied from events[wait_ev])
 };
 static_assert(sizeof(TaskDesc) == 64, "TaskDesc is 64 bytes");
@@ -59,6 +70,7 @@ struct ScratchLayout {
   int64_t flags, err;
   // tagged activations (64-bit words: value bits | step epoch << 32), one buffer per layer
   int64_t xt, qt, kvt, ot, ht, pt;
+  int64_t bpt;                       // batched GEMV: per-tile partial sums of each column split
   int64_t tagged_begin, tagged_end;  // byte range holding all tagged buffers
   int64_t amax, tokbuf, tokout, pools;
   int64_t total;
@@ -116,6 +128,8 @@ struct KernelParams {
   uint64_t* ot;               // [L][max_seqs][hq*dh] attention output
   uint64_t* ht;               // [L][max_seqs][f] SwiGLU output
   uint64_t* pt;               // [L][max_seqs][hq][splits][dh + 2] attention partials (m, l, unnormalised o)
+  uint64_t* bpt;              // batched GEMV tiles: [split][16-row group][64 lanes][4] partial sums + 64 words
+                              // (sums of squares per sequence), one block per tile (see TaskDesc)
   float* logits;              // [max_seqs][V]
   uint64_t* amax;             // [max_seqs][n_lm_parts] packed argmax keys
   const int32_t* tokens_in;   // [max_seqs]

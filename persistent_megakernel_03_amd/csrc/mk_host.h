@@ -12,7 +12,8 @@
 namespace mk {
 
 // Symbolic buffers for the validator/simulator (element granularity).
-enum SymBuf : int32_t { S_X, S_Q, S_KVCUR, S_PART, S_O, S_H, S_LOGITS, S_AMAX, S_CTX, S_TOKOUT, S_COUNT };
+// S_BPART has one element per column split of a batched GEMV tile (the split's whole partial block).
+enum SymBuf : int32_t { S_X, S_Q, S_KVCUR, S_PART, S_O, S_H, S_LOGITS, S_AMAX, S_CTX, S_TOKOUT, S_BPART, S_COUNT };
 
 struct Access {
   int32_t buf;
@@ -32,7 +33,15 @@ struct HostGraph {
   GemvGeom geoms[G_COUNT]{};
   std::vector<TaskDesc> tasks;               // global topological order
   std::vector<std::vector<Access>> acc;      // per task
-  std::vector<std::vector<Access>> comb_acc; // ATTN tasks: accesses of the merge the last split performs
+  std::vector<std::vector<Access>> comb_acc; // accesses of a task's second phase (below)
+  // Split groups: the attention splits of one (layer, sequence, KV head), or the column splits of
+  // one batched GEMV tile. A task with a second phase (task_comb) runs it only after every task of
+  // its group has finished its first phase: the last attention split merges the group's partials;
+  // every split of a batched tile sums the group's partials for its share of the rows.
+  std::vector<int32_t> task_group;           // per task: group index or -1
+  std::vector<char> task_comb;               // per task: has a second phase
+  std::vector<int32_t> group_size;           // per group
+  int max_tile_groups = 0;                   // batched: most 16-row groups in one tile
   std::vector<int32_t> queue_off, queue_idx;
   std::vector<EventDesc> events;
   std::vector<int32_t> sig_slots;
@@ -48,6 +57,13 @@ std::string validate_graph(const HostGraph& g);
 std::string simulate_graph(const HostGraph& g, uint64_t seed, int n_steps);
 uint64_t graph_hash(const HostGraph& g);
 GemvGeom choose_geom(int K);
+GemvGeom choose_geom_batched(int K);
+
+// Bytes of a GEMV task's packed tile.
+inline int64_t task_tile_bytes(const GemvGeom& q, const TaskDesc& t) {
+  if (q.mfma) return (int64_t)((t.row1 - t.row0 + 15) / 16) * (t.a2 >> 16) * 1024;
+  return (int64_t)((t.row1 - t.row0 + q.rg - 1) / q.rg) * q.S * 1024;
+}
 
 // Packed-row bookkeeping shared with the weight re-layout.
 // QKV rows are grouped per KV head g: the G query heads of g, then k head g, then v head g.

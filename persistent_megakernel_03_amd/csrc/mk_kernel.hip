@@ -187,6 +187,37 @@ __device__ __forceinline__ void poll_tagged(const KernelParams& p, const uint64_
   }
 }
 
+// Finishes a poll whose first loads are already in w (bit k of `pending`: word k issued, not yet
+// seen current): checks the words, and re-issues reload(k) for those still stale, reusing w, with the
+// same abort and watchdog rules as poll_tagged.
+template <int K, typename Reload, typename Sink>
+__device__ __forceinline__ void poll_finish(const KernelParams& p, uint64_t (&w)[K], uint32_t pending, uint32_t what,
+                                            Reload reload, Sink sink) {
+  const uint64_t t0 = __builtin_amdgcn_s_memrealtime();
+  while (true) {
+#pragma unroll
+    for (int k = 0; k < K; ++k) {
+      if (((pending >> k) & 1u) && (uint32_t)(w[k] >> 32) == p.epoch) {
+        sink(k, (uint32_t)w[k]);
+        pending &= ~(1u << k);
+      }
+    }
+    if (!__any(pending != 0u)) break;
+    if (ldc(&p.err[E_ABORT])) break;
+    if (__builtin_amdgcn_s_memrealtime() - t0 > p.watchdog_ticks) {
+      if ((threadIdx.x & 63) == 0) {
+        raise_error(p, ERR_TIMEOUT, what, p.epoch);
+        stc(&p.err[E_ABORT], 1u);
+      }
+      break;
+    }
+    __builtin_amdgcn_s_sleep(1);
+#pragma unroll
+    for (int k = 0; k < K; ++k)
+      if ((pending >> k) & 1u) w[k] = reload(k);
+  }
+}
+
 // A whole vector src[0, n): wave w polls the contiguous words [w * chunk, (w + 1) * chunk), chunk =
 // n / 8 rounded up to 64, lane l taking words l, l + 64, ..., so each load is one coalesced 512-byte
 // row and the word offsets fit the instruction's immediate (with one SGPR per 4 KB).
@@ -494,6 +525,49 @@ __device__ __forceinline__ QkvSet qkv_set_consts(const KernelParams& p, int l, i
   }
   if (slot >= G) c.blk = p.page_table[(size_t)s * p.max_blocks + pos / 16];
   return c;
+}
+
+// The epilogue of one 4-row set of packed QKV rows (r = its first row) for sequence s: bias, the
+// rotation of q and k, then the stores. The rotated query goes to the tagged query buffer; the key or
+// value pairs, rounded to bf16, go to the tagged current-row buffer and to the cache at position pos.
+// An out-of-range position (pos < 0) skips the append; a bad block is reported and skipped.
+__device__ __forceinline__ void qkv_store_set(const KernelParams& p, int l, int s, int r, float y0, float y1, float y2,
+                                              float y3, const QkvSet& c, int pos, uint16_t* const* pools, uint32_t ep) {
+  const int G = p.hq / p.hk, dh = p.dh, Rg = (G + 2) * dh;
+  const int grp = r / Rg, within = r % Rg, slot = within / dh, jh = within % dh;
+  const int i0 = jh >> 1;  // even dim index; the set holds dims i0, i0 + dh/2, i0 + 1, i0 + 1 + dh/2
+  y0 += c.b0;
+  y1 += c.b1;
+  y2 += c.b2;
+  y3 += c.b3;
+  if (slot <= G) {  // rotate q and k: pair (i0, i0 + dh/2) and pair (i0 + 1, i0 + 1 + dh/2)
+    const float a0 = y0 * c.cs0.x - y1 * c.cs0.y, b0 = y1 * c.cs0.x + y0 * c.cs0.y;
+    const float a1 = y2 * c.cs1.x - y3 * c.cs1.y, b1 = y3 * c.cs1.x + y2 * c.cs1.y;
+    y0 = a0; y1 = b0; y2 = a1; y3 = b1;
+  }
+  if (slot < G) {
+    uint64_t* q = qt_at(p, l, s) + (size_t)(grp * G + slot) * dh;
+    st_tagf(&q[i0], y0, ep);
+    st_tagf(&q[i0 + dh / 2], y1, ep);
+    st_tagf(&q[i0 + 1], y2, ep);
+    st_tagf(&q[i0 + 1 + dh / 2], y3, ep);
+  } else {
+    // the rounded key/value pairs go to the cache and, tagged, to this step's attention
+    const uint32_t w0 = f2bf(y0) | (f2bf(y2) << 16), w1 = f2bf(y1) | (f2bf(y3) << 16);
+    uint64_t* kv = kvt_at(p, l, s, slot == G ? 0 : 1, grp);
+    st_tag(&kv[i0 >> 1], w0, ep);
+    st_tag(&kv[(i0 + dh / 2) >> 1], w1, ep);
+    const int blk = c.blk;
+    if (blk < 0 || blk >= p.num_blocks) {
+      raise_error(p, ERR_PAGE, (uint32_t)s, (uint32_t)blk);
+      return;
+    }
+    if (pos < 0) return;
+    uint16_t* pool = pools[(slot == G ? 0 : p.n_layers) + l];
+    uint32_t* row = (uint32_t*)(pool + (((size_t)blk * p.hk + grp) * 16 + (pos & 15)) * dh);
+    stc(&row[i0 >> 1], w0);
+    stc(&row[(i0 + dh / 2) >> 1], w1);
+  }
 }
 
 // ----------------------------------------------------------------------------- attention
@@ -927,41 +1001,10 @@ __device__ __forceinline__ void gemv_task(const KernelParams& p, const TaskDesc&
   bar();
 
   if (type == T_QKV) {
-    const int G = p.hq / p.hk, dh = p.dh, Rg = (G + 2) * dh;
     for (int m = tid; m < nsets; m += NT) {
       const int r = t.row0 + 4 * m;
-      const int grp = r / Rg, within = r % Rg, slot = within / dh, jh = within % dh;
-      const int i0 = jh >> 1;  // even dim index; the set holds dims i0, i0 + dh/2, i0 + 1, i0 + 1 + dh/2
       const QkvSet c = (m == tid) ? pre : qkv_set_consts(p, l, r, pos < 0 ? 0 : pos, s);
-      float y0 = ys[4 * m] + c.b0, y1 = ys[4 * m + 1] + c.b1, y2 = ys[4 * m + 2] + c.b2, y3 = ys[4 * m + 3] + c.b3;
-      if (slot <= G) {  // rotate q and k: pair (i0, i0 + dh/2) and pair (i0 + 1, i0 + 1 + dh/2)
-        const float a0 = y0 * c.cs0.x - y1 * c.cs0.y, b0 = y1 * c.cs0.x + y0 * c.cs0.y;
-        const float a1 = y2 * c.cs1.x - y3 * c.cs1.y, b1 = y3 * c.cs1.x + y2 * c.cs1.y;
-        y0 = a0; y1 = b0; y2 = a1; y3 = b1;
-      }
-      if (slot < G) {
-        uint64_t* q = qt_at(p, l, s) + (size_t)(grp * G + slot) * dh;
-        st_tagf(&q[i0], y0, ep);
-        st_tagf(&q[i0 + dh / 2], y1, ep);
-        st_tagf(&q[i0 + 1], y2, ep);
-        st_tagf(&q[i0 + 1 + dh / 2], y3, ep);
-      } else {
-        // the rounded key/value pairs go to the cache and, tagged, to this step's attention
-        const uint32_t w0 = f2bf(y0) | (f2bf(y2) << 16), w1 = f2bf(y1) | (f2bf(y3) << 16);
-        uint64_t* kv = kvt_at(p, l, s, slot == G ? 0 : 1, grp);
-        st_tag(&kv[i0 >> 1], w0, ep);
-        st_tag(&kv[(i0 + dh / 2) >> 1], w1, ep);
-        const int blk = c.blk;
-        if (blk < 0 || blk >= p.num_blocks) {
-          raise_error(p, ERR_PAGE, (uint32_t)s, (uint32_t)blk);
-          continue;
-        }
-        if (pos < 0) continue;
-        uint16_t* pool = pools[(slot == G ? 0 : p.n_layers) + l];
-        uint32_t* row = (uint32_t*)(pool + (((size_t)blk * p.hk + grp) * 16 + (pos & 15)) * dh);
-        stc(&row[i0 >> 1], w0);
-        stc(&row[(i0 + dh / 2) >> 1], w1);
-      }
+      qkv_store_set(p, l, s, r, ys[4 * m], ys[4 * m + 1], ys[4 * m + 2], ys[4 * m + 3], c, pos, pools, ep);
     }
   } else if (resid) {
     uint64_t* dst = xt_at(p, l, type == T_OPROJ ? 0 : 1, s);
@@ -991,6 +1034,376 @@ __device__ __forceinline__ void gemv_task(const KernelParams& p, const TaskDesc&
   }
 }
 
+// ----------------------------------------------------------------------------- batched GEMM tiles
+// With several sequences each GEMV becomes a skinny GEMM, Y[rows][seqs] = W[rows][K] X[seqs][K]^T,
+// 16 sequences wide, and runs on v_mfma_f32_16x16x32_bf16. A packed weight unit is the 16x32 row
+// operand as it comes from memory; the inputs form the 32x16 column operand. Each fp32 input is split
+// into a bf16 high part and a bf16 remainder and every unit takes two MFMAs, so the products carry
+// about 16 significant bits of each input and accumulate in fp32.
+//
+// A task covers a tile of rows and a range of 32-column units. Its input columns are staged in LDS as
+// MFMA fragments (unit u, lane l: 8 columns of sequence l % 16, high parts then remainders), one block
+// of at most 32 units at a time (16 when a task streams several blocks). Each wave streams an even
+// share of the block's (row group, unit) items; a 16x16 accumulator runs along a row group's units and
+// goes to LDS at the group's end. Groups that straddle two waves are summed in wave order afterwards,
+// so the result does not depend on timing. When a tile's columns are split over kS tasks, each writes
+// its partial sums as tagged words; each then sums the kS partials (in split order) of its share of
+// the tile's row quads and applies the epilogue to that share. RMSNorm enters as a per-sequence scale
+// of the sums, W (g * x) / rms(x), with the sums of squares exchanged along with the partials.
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+
+__device__ __forceinline__ v4f mfma_bf16(const v4u a, const v4u b, const v4f c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a), __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
+}
+
+// Token and position of sequence s; any thread may report a bad one (the first report is kept).
+__device__ __forceinline__ int token_any(const KernelParams& p, int s) {
+  int tok = p.tokens_in[s];
+  if (tok < 0 || tok >= p.vocab) {
+    raise_error(p, ERR_TOKEN, (uint32_t)s, (uint32_t)tok);
+    tok = 0;
+  }
+  return tok;
+}
+__device__ __forceinline__ int pos_any(const KernelParams& p, const Ctl* ctl, int s) {
+  const int pos = ctl->ctx[s];
+  if (pos < 0 || pos >= p.max_pos) {
+    raise_error(p, ERR_CTX, (uint32_t)s, (uint32_t)pos);
+    return -1;
+  }
+  return pos;
+}
+
+__device__ __forceinline__ void gemv_task_b(const KernelParams& p, const TaskDesc& t, float* lds, Ctl* ctl,
+                                            uint16_t* const* pools) {
+  WPipe wp;  // task-local: no weight loads are carried into the next task
+  const int type = t.type, l = t.layer, tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const uint32_t ep = p.epoch, what = (uint32_t)t.wait_ev;
+  const int nact = min(p.n_active, p.max_seqs);
+  const int rows = t.row1 - t.row0, R = (rows + 15) >> 4, Q = (rows + 3) >> 2;
+  const int kb0 = t.a2 & 0xFFFF, nu = t.a2 >> 16, js = t.a3 & 0xFF, kS = t.a3 >> 8;
+  const bool multi = nu > 32;  // one column split streaming several 16-unit blocks
+  const int ub = multi ? 16 : nu, nb = multi ? nu >> 4 : 1;
+  const bool norm = type == T_QKV || type == T_GATEUP || type == T_LMHEAD;
+  const bool resid = type == T_OPROJ || type == T_DOWN;
+  const int K = type == T_OPROJ ? p.hq * p.dh : type == T_DOWN ? p.f : p.d;
+  // sequence s's input vector is src + s * K (one buffer per layer)
+  const uint64_t* src = type == T_QKV      ? xt_at(p, l > 0 ? l - 1 : 0, 1, 0)
+                        : type == T_GATEUP ? xt_at(p, l, 0, 0)
+                        : type == T_LMHEAD ? xt_at(p, p.n_layers - 1, 1, 0)
+                        : type == T_OPROJ  ? ot_at(p, l, 0)
+                                           : ht_at(p, l, 0);
+  const bool in_embed = type == T_QKV && l == 0;
+  const uint16_t* gain = type == T_QKV      ? layer_norm_gain(p, l, 0)
+                         : type == T_GATEUP ? layer_norm_gain(p, l, 1)
+                                            : p.norms + (size_t)p.n_layers * 2 * p.d;
+
+  uint32_t* afrag = (uint32_t*)lds;  // [unit][64 lanes][4 dwords high | 4 dwords low]: 2 KB per unit, 64 KB
+  float* T = lds + 16384;            // [R][64 lanes][4]: the tile's sums, one 16x16 MFMA tile per row group
+  float* E = T + R * 256;            // [NW][2][64][4]: each wave's partial first and last row groups
+  float* ssl = E + NW * 2 * 256;     // [16] sums of squares of this task's columns, per sequence
+  float* rsq = ssl + 16;             // [16] per-sequence scale of the sums (1 / rms, or 1)
+  unsigned long long* kseq = (unsigned long long*)(rsq + 16);  // [16] LM head: best argmax key per sequence
+  if (tid < 16) kseq[tid] = 0ull;
+
+  // Input staging. Thread (wave w, lane) holds sequences 2w and 2w + 1, columns 64 c + lane of the
+  // block (c < 16): each load is a coalesced 512-byte row of one sequence's tagged words. The loads are
+  // unconditional and bounded by their buffer's size (out-of-range loads return zero), so all of them
+  // issue together; only the words of active sequences inside K are polled. `ln` is the lane index
+  // made opaque per task, so that per-lane offsets are not hoisted out of the task loop and held in
+  // registers across every task.
+  int ln = lane;
+  asm volatile("" : "+v"(ln));
+  const int s0 = 2 * wave;
+  float ss[2] = {0.f, 0.f};
+  uint64_t xw[32];  // the words in flight; once current, their low halves are the inputs
+  uint32_t gq[16];
+  uint32_t xpend = 0, xvalid = 0;
+  const __amdgpu_buffer_rsrc_t rx = __builtin_amdgcn_make_buffer_rsrc((void*)src, (short)0, p.max_seqs * K * 8, 0x00020000);
+  const __amdgpu_buffer_rsrc_t rgain = __builtin_amdgcn_make_buffer_rsrc((void*)gain, (short)0, K * 2, 0x00020000);
+  auto x_word = [&](int b, int kw) {
+    const int c0 = 32 * (kb0 + b * ub), c = kw & 15;
+    return ld_tag(rx, ln * 8 + (c & 7) * 512, ((s0 + (kw >> 4)) * K + c0) * 8 + (c >> 3) * 4096);
+  };
+  auto x_issue = [&](int b) {
+    const int c0 = 32 * (kb0 + b * ub), ncol = 32 * min(ub, nu - b * ub);
+    xvalid = 0;
+#pragma unroll
+    for (int kw = 0; kw < 32; ++kw) {
+      const int h = kw >> 4, c = kw & 15;
+      if (s0 + h < nact && 64 * c + ln < ncol && c0 + 64 * c + ln < K) xvalid |= 1u << kw;
+    }
+    if (in_embed) {  // the first layer's input: the tokens' embedding rows, as current words
+      xpend = 0;
+      for (int h = 0; h < 2; ++h) {
+        const int tk = s0 + h < nact ? token_any(p, s0 + h) : 0;
+        const __amdgpu_buffer_rsrc_t re =
+            __builtin_amdgcn_make_buffer_rsrc((void*)(p.embed + (size_t)tk * p.d), (short)0, p.d * 2, 0x00020000);
+#pragma unroll
+        for (int c = 0; c < 16; ++c)
+          xw[16 * h + c] = (uint64_t)__builtin_amdgcn_raw_buffer_load_b16(re, ln * 2, (c0 + 64 * c) * 2, 0) << 16;
+      }
+    } else {
+      xpend = xvalid;
+#pragma unroll
+      for (int kw = 0; kw < 32; ++kw) xw[kw] = x_word(b, kw);
+    }
+    if (norm) {
+#pragma unroll
+      for (int c = 0; c < 16; ++c) gq[c] = __builtin_amdgcn_raw_buffer_load_b16(rgain, ln * 2, (c0 + 64 * c) * 2, 0);
+    }
+  };
+  auto x_finish = [&](int b) {
+    const int ncol = 32 * min(ub, nu - b * ub);
+    poll_finish<32>(p, xw, xpend, what, [&](int kw) { return x_word(b, kw); }, [](int, uint32_t) {});
+    // Fragments: sequence s, column col -> unit col / 32, lane s + 16 ((col % 32) / 8), element col % 8.
+    // Lane pairs swap halves so each lane stores one dword: the even lane two high parts, the odd lane
+    // two remainders. With col = 64 c + lane, word kw lands at dword 1024 c + 8 h past the lane's base.
+    uint32_t* al = afrag + (multi ? (b & 1) * 8192 : 0) +
+                   ((ln >> 5) * 64 + s0 + 16 * ((ln & 31) >> 3)) * 8 + (ln & 1) * 4 + ((ln & 7) >> 1);
+#pragma unroll
+    for (int kw = 0; kw < 32; ++kw) {
+      const int h = kw >> 4, c = kw & 15;
+      const float x = ((xvalid >> kw) & 1u) ? __uint_as_float((uint32_t)xw[kw]) : 0.f;
+      ss[h] = fmaf(x, x, ss[h]);
+      const float v = norm ? x * bf2f((uint16_t)gq[c]) : x;
+      const uint32_t hi = f2bf(v), lo = f2bf(v - bf2f((uint16_t)hi));
+      const uint32_t other = (uint32_t)__shfl_xor((int)((ln & 1) ? hi : lo), 1);
+      const uint32_t word = (ln & 1) ? (other | (lo << 16)) : (hi | (other << 16));
+      if (64 * c + ln < ncol) al[1024 * c + 8 * h] = word;
+    }
+  };
+
+  // This wave's items of each block: (row group, unit) pairs [ia, ib) in that order. Several blocks:
+  // whole row groups per wave, so that a round of NSLOT units is one group's block.
+  int ia, ib;
+  if (multi) {
+    ia = 16 * (R * wave / NW);
+    ib = 16 * (R * (wave + 1) / NW);
+  } else {
+    ia = R * nu * wave / NW;
+    ib = R * nu * (wave + 1) / NW;
+  }
+  const int cnt = ib - ia, rpb = (cnt + NSLOT - 1) / NSLOT, nrounds = nb * rpb;
+  const v4u* wbase = (const v4u*)(p.wpacked + t.wofs) + lane;
+  auto round_base = [&](int r) -> int {  // packed unit of slot 0 of round r
+    if (!multi) return ia + NSLOT * r;
+    const int b = r / rpb, rr = r - b * rpb;
+    return (ia / 16 + rr) * nu + 16 * b;
+  };
+  const int last_unit = max(0, multi ? (ib / 16) * nu - 1 : ib - 1);
+  auto load_w = [&](int a) { return __builtin_nontemporal_load(wbase + (size_t)min(a, last_unit) * 64); };
+
+  x_issue(0);
+  {  // the wave's first NSLOT weight units stream while the inputs arrive
+    const int a0 = cnt > 0 ? round_base(0) : 0;
+#pragma unroll
+    for (int j = 0; j < NSLOT; ++j) wp.R[j] = load_w(a0 + j);
+  }
+  x_finish(0);
+  bar();
+  if (p.trace && tid == 0) ctl->t_ready = __builtin_amdgcn_s_memrealtime();
+
+  auto flush = [&](int g, int b, v4f v) {
+    v4f* dst;
+    if (multi) {
+      dst = (v4f*)T + g * 64 + lane;
+      if (b > 0) v += *dst;
+    } else {
+      const bool whole = g * ub >= ia && (g + 1) * ub <= ib;
+      dst = whole ? (v4f*)T + g * 64 + lane : (v4f*)E + (wave * 2 + (g == ia / ub ? 0 : 1)) * 64 + lane;
+    }
+    *dst = v;
+  };
+  const v4f zero = {0.f, 0.f, 0.f, 0.f};
+  for (int b = 0; b < nb; ++b) {
+    if (b > 0) {
+      x_issue(b);
+      x_finish(b);
+      bar();
+    }
+    const uint32_t* ab = afrag + (multi ? (b & 1) * 8192 : 0);
+    int g = ia / ub, u = ia % ub;
+    v4f cur = zero;
+    for (int rr = 0; rr < rpb; ++rr) {
+      const int r = b * rpb + rr;
+      // refills of the last round re-read one unit: nothing past the stream is fetched
+      const int nbase = r + 1 < nrounds ? round_base(r + 1) : last_unit;
+#pragma unroll
+      for (int j = 0; j < NSLOT; ++j) {
+        if (NSLOT * rr + j < cnt) {
+          const v4u* a = (const v4u*)(ab + (u * 64 + lane) * 8);
+          const v4u ahi = a[0], alo = a[1];
+          cur = mfma_bf16(wp.R[j], ahi, cur);
+          cur = mfma_bf16(wp.R[j], alo, cur);
+          if (++u == ub) {
+            flush(g, b, cur);
+            cur = zero;
+            u = 0;
+            ++g;
+          }
+        }
+        wp.R[j] = load_w(nbase + j);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    }
+    if (u != 0 && cnt > 0) flush(g, b, cur);  // the wave's items end inside a row group
+  }
+  {
+    const float sa = wave_sum(ss[0]), sb = wave_sum(ss[1]);
+    if (lane == 0) {
+      ssl[s0] = sa;
+      ssl[s0 + 1] = sb;
+    }
+  }
+  bar();
+  if (!multi) {  // row groups shared by two waves: their partials, in wave order
+    const int per = R * nu;
+    for (int e = tid; e < R * 256; e += NT) {
+      const int g = e >> 8;
+      float acc = 0.f;
+      bool edge = false;
+      for (int w = 0; w < NW; ++w) {
+        const int a = per * w / NW, z = per * (w + 1) / NW;
+        if (a == z || a >= (g + 1) * nu || z <= g * nu) continue;
+        if (a <= g * nu && z >= (g + 1) * nu) break;  // one wave holds the whole group
+        acc += E[(w * 2 + (g == a / nu ? 0 : 1)) * 256 + (e & 255)];
+        edge = true;
+      }
+      if (edge) T[e] = acc;
+    }
+    bar();
+  }
+
+  // This task's share of the tile: row quads [qa, qb) (all of them without a column split). The sums
+  // of quad q for sequence s sit at word ((q / 4) * 64 + s + 16 (q % 4)) * 4 of a tile: rows 4q .. 4q+3.
+  const int qa = Q * js / kS, qb = Q * (js + 1) / kS;
+  const int npairs = (qb - qa) * nact;
+  if (kS > 1) {
+    uint64_t* bp = p.bpt + t.a1;
+    const int SW = R * 256 + 64;  // words of one split's block: the tile, then the sums of squares
+    for (int e = tid; e < R * 256; e += NT) {
+      const int le = (e >> 2) & 63, q = 4 * (e >> 8) + (le >> 4);  // lane and quad of word e
+      if ((le & 15) < nact && (q < qa || q >= qb)) st_tagf(&bp[(size_t)js * SW + e], T[e], ep);
+    }
+    if (norm && tid < nact) st_tagf(&bp[(size_t)js * SW + R * 256 + tid], ssl[tid], ep);
+    // tpp threads per (quad, sequence) pair, each summing the splits congruent to it, in order
+    int tpp = 1;
+    while (2 * tpp <= kS && npairs * 2 * tpp <= NT) tpp *= 2;
+    const int sub = tid % tpp;
+    float* scr = (float*)afrag;  // the fragments are no longer needed
+    for (int pb = 0; pb < npairs; pb += NT / tpp) {
+      const int pair = pb + tid / tpp;
+      const bool act = pair < npairs;
+      const int q = qa + (act ? pair / nact : 0), s = act ? pair % nact : 0;
+      const int eo = ((q >> 2) * 64 + s + 16 * (q & 3)) * 4;
+      float y0 = 0.f, y1 = 0.f, y2 = 0.f, y3 = 0.f, sq = 0.f;
+      for (int jb = sub; jb < kS; jb += 6 * tpp) {  // up to 6 splits per poll round
+        uint32_t pend = 0;
+#pragma unroll
+        for (int i = 0; i < 6; ++i) {
+          const int jj = jb + i * tpp;
+          if (act && jj < kS && jj != js) pend |= (norm ? 0x1Fu : 0xFu) << (5 * i);
+        }
+        float v[30];
+        poll_tagged<30>(
+            p, bp,
+            [&](int k) {
+              const int i = k / 5, c = k % 5;
+              return ((jb + i * tpp) * SW + (c < 4 ? eo + c : R * 256 + s)) * 8;
+            },
+            [](int) { return 0; }, pend, what, [&](int k, uint32_t bits) { v[k] = __uint_as_float(bits); });
+#pragma unroll
+        for (int i = 0; i < 6; ++i) {
+          const int jj = jb + i * tpp;
+          if (!act || jj >= kS) continue;
+          if (jj == js) {
+            y0 += T[eo];
+            y1 += T[eo + 1];
+            y2 += T[eo + 2];
+            y3 += T[eo + 3];
+            sq += ssl[s];
+          } else {
+            y0 += v[5 * i];
+            y1 += v[5 * i + 1];
+            y2 += v[5 * i + 2];
+            y3 += v[5 * i + 3];
+            if (norm) sq += v[5 * i + 4];
+          }
+        }
+      }
+      scr[tid * 5 + 0] = y0;
+      scr[tid * 5 + 1] = y1;
+      scr[tid * 5 + 2] = y2;
+      scr[tid * 5 + 3] = y3;
+      scr[tid * 5 + 4] = sq;
+      bar();
+      if (act && sub == 0) {
+        float z[5] = {0.f, 0.f, 0.f, 0.f, 0.f};
+        for (int k = 0; k < tpp; ++k)
+#pragma unroll
+          for (int c = 0; c < 5; ++c) z[c] += scr[(tid + k) * 5 + c];
+        T[eo] = z[0];
+        T[eo + 1] = z[1];
+        T[eo + 2] = z[2];
+        T[eo + 3] = z[3];
+        if (q == qa) rsq[s] = norm ? 1.0f / sqrtf(z[4] / (float)K + p.eps) : 1.f;
+      }
+      bar();
+    }
+  } else {
+    if (tid < 16) rsq[tid] = norm ? 1.0f / sqrtf(ssl[tid] / (float)K + p.eps) : 1.f;
+    bar();
+  }
+
+  // the epilogue of each (quad, sequence) of the share
+  for (int pr = tid; pr < npairs; pr += NT) {
+    const int q = qa + pr / nact, s = pr % nact;
+    const int eo = ((q >> 2) * 64 + s + 16 * (q & 3)) * 4;
+    const float sc = rsq[s];
+    const float y[4] = {T[eo] * sc, T[eo + 1] * sc, T[eo + 2] * sc, T[eo + 3] * sc};
+    const int r0 = t.row0 + 4 * q, nr = min(4, t.row1 - r0);
+    if (type == T_QKV) {
+      const int pos = pos_any(p, ctl, s);
+      const QkvSet c = qkv_set_consts(p, l, r0, pos < 0 ? 0 : pos, s);
+      qkv_store_set(p, l, s, r0, y[0], y[1], y[2], y[3], c, pos, pools, ep);
+    } else if (resid) {
+      float xo[4] = {0.f, 0.f, 0.f, 0.f};
+      if (type == T_OPROJ && l == 0) {
+        const uint16_t* er = p.embed + (size_t)token_any(p, s) * p.d;
+        for (int r = 0; r < nr; ++r) xo[r] = bf2f(er[r0 + r]);
+      } else {
+        const uint64_t* rb = type == T_OPROJ ? xt_at(p, l - 1, 1, 0) : xt_at(p, l, 0, 0);
+        poll_tagged<4>(p, rb, [&](int k) { return (s * p.d + r0 + k) * 8; }, [](int) { return 0; }, first_words(nr), what,
+                       [&](int k, uint32_t bits) { xo[k] = __uint_as_float(bits); });
+      }
+      uint64_t* dst = xt_at(p, l, type == T_OPROJ ? 0 : 1, s) + r0;
+#pragma unroll
+      for (int r = 0; r < 4; ++r)
+        if (r < nr) st_tagf(&dst[r], xo[r] + y[r], ep);
+    } else if (type == T_GATEUP) {
+      uint64_t* hd = ht_at(p, l, s) + (r0 >> 1);
+      st_tagf(&hd[0], y[0] / (1.0f + expf(-y[0])) * y[1], ep);
+      if (nr > 2) st_tagf(&hd[1], y[2] / (1.0f + expf(-y[2])) * y[3], ep);
+    } else {  // LM head
+      unsigned long long best = 0;
+#pragma unroll
+      for (int r = 0; r < 4; ++r)
+        if (r < nr) {
+          p.logits[(size_t)s * p.vocab + r0 + r] = y[r];
+          const unsigned long long k = argmax_key(y[r], r0 + r);
+          best = k > best ? k : best;
+        }
+      atomicMax(&kseq[s], best);
+    }
+  }
+  if (type == T_LMHEAD) {
+    bar();
+    if (tid < nact) stc(&p.amax[(size_t)tid * p.n_lm_parts + t.a0], (uint64_t)kseq[tid]);
+  }
+}
+
 __device__ __forceinline__ void task_argmax(const KernelParams& p, const TaskDesc& t, Ctl* ctl) {
   const int s = t.a0;
   uint64_t best = 0;
@@ -1009,7 +1422,7 @@ __device__ __forceinline__ void task_argmax(const KernelParams& p, const TaskDes
 // One instantiation per (head dim, query heads per KV head rounded up to 2, 4 or 8): the
 // attention tile keeps GMAX x 8 query values and accumulators per lane in registers, and a
 // kernel's register budget is set by its largest path.
-template <int DH, int GMAX>
+template <int DH, int GMAX, bool BATCHED>
 __global__ __launch_bounds__(NT, 1) void mk_megakernel(KernelParams p) {
   extern __shared__ __attribute__((aligned(16))) unsigned char lds_raw[];
   static_assert(sizeof(Ctl) <= 1024, "control block fits its 1 KB");
@@ -1058,6 +1471,8 @@ __global__ __launch_bounds__(NT, 1) void mk_megakernel(KernelParams p) {
       if (t.wait_ev >= 0) wait_event(p, t, ctl);
       if (p.trace && threadIdx.x == 0) ctl->t_ready = __builtin_amdgcn_s_memrealtime();
       if (t.wait_ev < 0 || !ctl->aborted) task_argmax(p, t, ctl);
+    } else if constexpr (BATCHED) {
+      gemv_task_b(p, t, lds, ctl, pools);
     } else {
       gemv_task(p, t, lds, ctl, wp, pools);
     }
@@ -1094,10 +1509,12 @@ extern "C" __global__ __launch_bounds__(64) void mk_repack(RepackArgs a) {
   }
   const TaskDesc t = a.tasks[lo];
   const int64_t u = (byte - t.wofs) / 1024;
-  const int gi = (int)(u / a.gm.S), ui = (int)(u % a.gm.S);
+  // one sequence: groups of S units; batched: groups of the task's own units, from its first column unit
+  const int gs = a.gm.mfma ? (t.a2 >> 16) : a.gm.S, uoff = a.gm.mfma ? (t.a2 & 0xFFFF) : 0;
+  const int gi = (int)(u / gs), ui = (int)(u % gs) + uoff;
   const int lane = threadIdx.x;
-  const int rl = gi * a.gm.rg + lane / a.gm.lpr;
-  const int piece = ui * a.gm.lpr + (lane & (a.gm.lpr - 1));
+  const int rl = gi * a.gm.rg + (a.gm.mfma ? lane % 16 : lane / a.gm.lpr);
+  const int piece = ui * a.gm.lpr + (a.gm.mfma ? lane / 16 : (lane & (a.gm.lpr - 1)));
   v4u v = {0u, 0u, 0u, 0u};
   if (rl < t.row1 - t.row0 && piece < a.gm.P) {
     const int pr = t.row0 + rl;
@@ -1134,21 +1551,26 @@ extern "C" __global__ __launch_bounds__(256) void mk_repack_bias(const uint16_t*
 }
 
 // ----------------------------------------------------------------------------- host-side launchers
-static const void* megakernel_for(int dh, int hq, int hk) {
-  const int g = hq / hk;
-  if (dh == 128) return g <= 2 ? (const void*)mk_megakernel<128, 2> : g <= 4 ? (const void*)mk_megakernel<128, 4> : (const void*)mk_megakernel<128, 8>;
-  return g <= 2 ? (const void*)mk_megakernel<64, 2> : g <= 4 ? (const void*)mk_megakernel<64, 4> : (const void*)mk_megakernel<64, 8>;
+template <bool B>
+static const void* megakernel_for_t(int dh, int g) {
+  if (dh == 128)
+    return g <= 2 ? (const void*)mk_megakernel<128, 2, B> : g <= 4 ? (const void*)mk_megakernel<128, 4, B> : (const void*)mk_megakernel<128, 8, B>;
+  return g <= 2 ? (const void*)mk_megakernel<64, 2, B> : g <= 4 ? (const void*)mk_megakernel<64, 4, B> : (const void*)mk_megakernel<64, 8, B>;
+}
+// One sequence: GEMV tiles on the vector units. Several: the batched instantiation (MFMA tiles).
+static const void* megakernel_for(int dh, int hq, int hk, bool batched) {
+  return batched ? megakernel_for_t<true>(dh, hq / hk) : megakernel_for_t<false>(dh, hq / hk);
 }
 
 hipError_t launch_megakernel(const KernelParams& p, int grid, size_t lds_bytes, hipStream_t stream) {
   KernelParams copy = p;
   void* args[] = {(void*)&copy};
-  return hipLaunchCooperativeKernel(megakernel_for(p.dh, p.hq, p.hk), dim3(grid), dim3(NT), args, (unsigned)lds_bytes,
-                                    stream);
+  return hipLaunchCooperativeKernel(megakernel_for(p.dh, p.hq, p.hk, p.max_seqs > 1), dim3(grid), dim3(NT), args,
+                                    (unsigned)lds_bytes, stream);
 }
 
-hipError_t megakernel_occupancy(int* blocks_per_cu, size_t lds_bytes, int dh, int hq, int hk) {
-  return hipOccupancyMaxActiveBlocksPerMultiprocessor(blocks_per_cu, megakernel_for(dh, hq, hk), NT, lds_bytes);
+hipError_t megakernel_occupancy(int* blocks_per_cu, size_t lds_bytes, int dh, int hq, int hk, bool batched) {
+  return hipOccupancyMaxActiveBlocksPerMultiprocessor(blocks_per_cu, megakernel_for(dh, hq, hk, batched), NT, lds_bytes);
 }
 
 hipError_t launch_repack(const RepackArgs& a, int64_t units, hipStream_t stream) {

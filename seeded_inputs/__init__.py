@@ -71,6 +71,9 @@ class Workload:
 TINY = ModelShape("tiny", 2, 256, 4, 2, 64, 688, 4096, 1e-5, 1e4, False, False)
 QWEN05B = ModelShape("qwen0.5b", 24, 896, 14, 2, 64, 4864, 151936, 1e-6, 1e6, True, True)
 LLAMA8B = ModelShape("llama8b", 32, 4096, 32, 8, 128, 14336, 128256, 1e-5, 5e5, False, False)
+# A two-layer shape between tiny and 8B (8B head geometry, GQA 4:1), for batched-decode tests at a size
+# the oracle runs in seconds.
+MID = ModelShape("mid", 2, 2048, 16, 4, 128, 5632, 16384, 1e-5, 5e5, False, False)
 
 WORKLOADS = {
     "tiny": Workload("tiny", TINY, 1, prompt_len=16, steps=32),
@@ -78,6 +81,9 @@ WORKLOADS = {
     "llama8b": Workload("llama8b", LLAMA8B, 1, prompt_len=39, steps=512),
     "llama8b_long": Workload("llama8b_long", LLAMA8B, 1, steps=64, prefill_ctx=32768, paging="permuted"),
     "llama8b_b16": Workload("llama8b_b16", LLAMA8B, 16, steps=128, ctx_range=(512, 8192), paging="permuted"),
+    # small batched workloads with the same structure (per-sequence contexts, permuted pages)
+    "tiny_b4": Workload("tiny_b4", TINY, 4, steps=8, ctx_range=(5, 60), paging="permuted"),
+    "mid_b16": Workload("mid_b16", MID, 16, steps=4, ctx_range=(16, 300), paging="permuted"),
 }
 
 

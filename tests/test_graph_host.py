@@ -144,3 +144,69 @@ def test_host_context_refuses_device_calls(L):
         assert mk.mk_status_str(-5) == "MK_ERR_DEVICE_TIMEOUT"
     finally:
         mk.mk_destroy(ctx)
+
+
+# --------------------------------------------------------------------------- batched graphs
+def batched_cfg(shape, n_seqs, blocks_per_seq, splits=0):
+    return mk.make_config(shape, max_seqs=n_seqs, max_blocks_per_seq=blocks_per_seq,
+                          num_blocks=n_seqs * blocks_per_seq, attn_splits=splits)
+
+
+@pytest.fixture
+def ksplit_cap(monkeypatch):
+    """Sets MK_BATCHED_MAX_KSPLIT (read when a graph is built) for the test's duration."""
+    def set_cap(v):
+        if v is None:
+            monkeypatch.delenv("MK_BATCHED_MAX_KSPLIT", raising=False)
+        else:
+            monkeypatch.setenv("MK_BATCHED_MAX_KSPLIT", str(v))
+    return set_cap
+
+
+@pytest.mark.parametrize("shape,n_seqs,n_cus,cap", [
+    (si.TINY, 4, 256, None), (si.TINY, 4, 7, None), (si.TINY, 16, 64, None), (si.TINY, 2, 3, None),
+    (si.MID, 16, 256, None), (si.MID, 16, 256, 1), (si.MID, 3, 40, 2)])
+def test_batched_graph_interleavings(L, ksplit_cap, shape, n_seqs, n_cus, cap):
+    ksplit_cap(cap)
+    ctx = mk.mk_create_host(batched_cfg(shape, n_seqs, 4), n_cus)
+    try:
+        mk.mk_graph_validate(ctx)
+        assert mk.mk_graph_stats(ctx).lds_bytes <= 160 * 1024
+        for seed in range(3):
+            mk.mk_graph_simulate(ctx, seed, 2)
+    finally:
+        mk.mk_destroy(ctx)
+
+
+def test_batched_8b_graph(L, ksplit_cap):
+    # the 16-sequence 8B decode: contexts up to 8192 + 128 steps, 16-token blocks
+    ksplit_cap(None)
+    nb = (8192 + 128 + 15) // 16
+    ctx = mk.mk_create_host(batched_cfg(si.LLAMA8B, 16, nb), 256)
+    try:
+        mk.mk_graph_validate(ctx)
+        info = mk.mk_graph_stats(ctx)
+        assert info.lds_bytes <= 160 * 1024
+        m = si.LLAMA8B
+        gemv = (m.n_layers * (6144 * 4096 + 4096 * 4096 + 3 * 14336 * 4096) + m.vocab * 4096) * 2
+        assert info.weight_bytes == gemv   # every row tile is whole 16-row groups of whole 32-column units
+        # the batched graph differs from the one-sequence graph of the same shape
+        one = mk.mk_create_host(cfg_for(m, nb, nb), 256)
+        assert mk.mk_graph_stats(one).hash != info.hash
+        mk.mk_destroy(one)
+    finally:
+        mk.mk_destroy(ctx)
+
+
+def test_batched_weights_cover_every_column_once(L, ksplit_cap):
+    # the packed size equals rows x columns, each padded to its tile: no column is streamed twice
+    for cap in (None, 1, 3):
+        ksplit_cap(cap)
+        ctx = mk.mk_create_host(batched_cfg(si.MID, 16, 4), 256)
+        m = si.MID
+        gemv = (m.n_layers * ((m.n_q_heads + 2 * m.n_kv_heads) * m.head_dim * m.d_model
+                              + m.d_model * m.n_q_heads * m.head_dim + 3 * m.d_ffn * m.d_model)
+                + m.vocab * m.d_model) * 2
+        w = mk.mk_graph_stats(ctx).weight_bytes
+        assert gemv <= w <= gemv * 1.1, (cap, w, gemv)
+        mk.mk_destroy(ctx)
