@@ -49,6 +49,122 @@ def cpu_baseline(shape, weights, prompt, seconds):
                       "from host memory each step)" % (len(times), len(times) - 1)}
 
 
+def cpu_baseline_batched(wl, weights, seconds):
+    """The oracle on this host's cores over a bounded sample of a batched workload: sequence 0 alone,
+    its KV cache pre-filled as in the workload, decode steps at its context length."""
+    import oracle as orc
+    m = wl.model
+    cores = len(os.sched_getaffinity(0))
+    orc.set_threads(cores)
+    ctx0 = int(si_mod().context_lengths(wl)[0])
+    om = orc.OracleModel(m, weights, 1, ctx0 + 4)
+    for l in range(m.n_layers):
+        om.set_kv(l, 0, 0, si_mod().kv_fill(wl, l, 0, ctx0, "k"), si_mod().kv_fill(wl, l, 0, ctx0, "v"))
+    tok = int(si_mod().first_tokens(wl)[0])
+    times = []
+    t_all = time.perf_counter()
+    for i in range(4):
+        t0 = time.perf_counter()
+        tok, _ = om.step(0, tok, ctx0 + i)
+        times.append(time.perf_counter() - t0)
+        if time.perf_counter() - t_all > seconds and len(times) >= 2:
+            break
+    om.close()
+    ms = 1e3 * sum(times) / len(times)
+    return {"value": ms, "unit": "ms/token", "tokens_per_s": 1e3 / ms, "cores": orc.threads(), "kind": "oracle",
+            "sample": "%d decode steps of sequence 0 alone (context %d, fp64 oracle, weights streamed from host "
+                      "memory each step)" % (len(times), ctx0)}
+
+
+def si_mod():
+    import seeded_inputs as si
+    return si
+
+
+def bench_batched(args, wl):
+    """Batched decode: all sequences of the workload in every step, each from its own KV cache
+    pre-filled to its context length (seeded N(0, 1) bf16 values, keys taken as rotated), pages
+    permuted. A step's algorithmic bytes are the weights once plus every sequence's KV rows."""
+    import numpy as np
+    import torch
+    import persistent_megakernel_03_amd as mk
+    from persistent_megakernel_03_amd import roofline as rf
+    si = si_mod()
+    m = wl.model
+    n = wl.n_seqs
+    K, W = min(args.steps, wl.steps), args.warmup
+    ctx = si.context_lengths(wl).astype(np.int64)
+    cap = ctx + max(K, W)
+    table, nblocks = si.block_tables(wl, cap)
+    t0 = time.time()
+    weights = si.gen_weights(m)
+    log("weights generated in %.1fs" % (time.time() - t0))
+    cfg = mk.make_config(m, max_seqs=n, max_blocks_per_seq=table.shape[1], num_blocks=nblocks)
+    dec = mk.Decoder(cfg, 0)
+    dec.load_weights(weights)
+    dec.set_page_table(table)
+    # cache contents do not change the work; fill them on the device from a seeded generator
+    g = torch.Generator(device=dec.dev)
+    g.manual_seed(1234)
+    for pool in dec.k_pools + dec.v_pools:
+        pool.copy_(torch.randn(pool.numel(), generator=g, device=dec.dev).to(torch.bfloat16).view(torch.int16))
+    first = torch.as_tensor(si.first_tokens(wl), dtype=torch.int32, device=dec.dev)
+    dec.set_ctx_lens(ctx)
+    dec.tokens[:n].copy_(first)
+    for _ in range(W):
+        dec.step(dec.tokens, n)
+    dec.sync_check()
+    dec.set_ctx_lens(ctx)
+    dec.tokens[:n].copy_(first)
+    stream = torch.cuda.current_stream(dec.dev)
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize(dec.dev)
+    ev0.record(stream)
+    for _ in range(K):
+        dec.step(dec.tokens, n)
+    ev1.record(stream)
+    torch.cuda.synchronize(dec.dev)
+    ms = ev0.elapsed_time(ev1) / K
+    dec.sync_check()
+    assert (dec.ctx_lens.cpu().numpy()[:n] == ctx + K).all()
+    bytes_avg = sum(rf.step_bytes(m, list(ctx + i + 1)) for i in range(K)) / K
+    achieved = bytes_avg / (ms * 1e-3) / 1e9
+    log("batched decode (%d sequences): %.4f ms/step, %.1f tok/s, %.1f GB/s (%.1f%% of %.0f GB/s)" %
+        (n, ms, n * 1e3 / ms, achieved, 100 * achieved / rf.MI355X_HBM_PEAK_GBS, rf.MI355X_HBM_PEAK_GBS))
+    dec.close()
+    cpu = None
+    if not args.no_cpu_baseline:
+        t0 = time.time()
+        cpu = cpu_baseline_batched(wl, weights, args.cpu_seconds)
+        log("cpu baseline: %.1f ms/token on %d cores (%.1fs)" % (cpu["value"], cpu["cores"], time.time() - t0))
+    out = {
+        "metric": "decode ms/step (%d sequences, %s-shape bf16); achieved HBM GB/s vs peak" % (n, m.name),
+        "value": round(ms, 5),
+        "unit": "ms/step",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": W,
+        "ms_per_step": round(ms, 5),
+        "tokens_per_s": round(n * 1e3 / ms, 1),
+        "achieved_hbm_gbs": round(achieved, 1),
+        "higher_is_better": False,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "weights_dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": "%s: %d sequences, contexts %d..%d (seeded uniform in [%d, %d]), %d steps"
+                               % (wl.name, n, int(ctx.min()), int(ctx.max()), wl.ctx_range[0], wl.ctx_range[1], K),
+                   "batch": n, "decode_steps": K, "weight_bytes_per_step": rf.weight_bytes_per_token(m),
+                   "kv": "bf16, paged in 16-token blocks, permuted page tables"},
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": rf.MI355X_HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(achieved / rf.MI355X_HBM_PEAK_GBS, 4), "traffic": None,
+                     "bytes_per_launch": int(bytes_avg), "kernel": "mk_megakernel, batched (one launch per step)"},
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(out), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -83,8 +199,11 @@ def main():
 
     wl = si.WORKLOADS[args.workload]
     m = wl.model
-    if wl.n_seqs != 1 or wl.prompt_len == 0:
-        print("bench.py times the batch-1 prompt workloads (tiny, qwen0.5b, llama8b)", file=sys.stderr)
+    if wl.n_seqs > 1:
+        return bench_batched(args, wl)
+    if wl.prompt_len == 0:
+        print("bench.py times the prompt workloads (tiny, qwen0.5b, llama8b) and the batched ones "
+              "(llama8b_b16, mid_b16, tiny_b4)", file=sys.stderr)
         sys.exit(2)
     K, W = args.steps, args.warmup
     P = wl.prompt_len

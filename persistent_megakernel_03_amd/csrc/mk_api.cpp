@@ -171,6 +171,7 @@ KernelParams make_params(mk_ctx* c) {
   p.max_pos = g.max_pos;
   p.watchdog_ticks = c->watchdog_ticks;
   p.max_queue = g.max_queue;
+  p.attn_tasks = g.attn_tasks;
   p.trace = c->d_trace;
   return p;
 }

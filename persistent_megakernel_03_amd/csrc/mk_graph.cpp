@@ -219,7 +219,7 @@ std::string build_graph(const mk_model_config& c, int n_cus, HostGraph& g) {
   g.sym_size[S_X] = (int64_t)S * d;
   g.sym_size[S_Q] = (int64_t)S * qd;
   g.sym_size[S_KVCUR] = (int64_t)L * S * hk * 2 * dh;
-  g.sym_size[S_PART] = (int64_t)S * hq * g.splits;
+  g.sym_size[S_PART] = (int64_t)L * 2 * S * hk * g.splits;
   g.sym_size[S_O] = (int64_t)S * qd;
   g.sym_size[S_H] = (int64_t)S * f;
   g.sym_size[S_LOGITS] = (int64_t)S * V;
@@ -325,6 +325,7 @@ std::string build_graph(const mk_model_config& c, int n_cus, HostGraph& g) {
         bpart_slots += ks.kS;
         grp = (int)g.group_size.size();
         g.group_size.push_back(ks.kS);
+        g.group_ordered.push_back(0);
       }
       for (int j = 0; j < ks.kS; ++j) {
         TaskDesc t{};
@@ -361,55 +362,50 @@ std::string build_graph(const mk_model_config& c, int n_cus, HostGraph& g) {
     // ---- QKV: RMSNorm + GEMV + bias + RoPE + KV append
     auto qkv = stage(T_QKV, l, G_QKV, Nqkv, d, lcm_i(4, g.geoms[G_QKV].rg), ev_x, nullptr);
     if (!err.empty()) return err;
-    std::vector<int> ev_qkv(hk);
-    std::vector<int> nprod(hk, 0);
-    for (const StageTask& st : qkv)
-      for (int grp = st.r0 / Rg; st.r1 > st.r0 && grp <= (st.r1 - 1) / Rg; ++grp)
-        b.task_sig[st.id].push_back({-1 - grp, nprod[grp]++});
-    for (int grp = 0; grp < hk; ++grp) ev_qkv[grp] = b.new_event(nprod[grp]);
-    for (const StageTask& st : qkv) {
-      for (auto& sg : b.task_sig[st.id]) sg.first = ev_qkv[-1 - sg.first];
+    const int ev_qkv = b.new_event((int)qkv.size());
+    for (size_t i = 0; i < qkv.size(); ++i) {
+      const StageTask& st = qkv[i];
+      b.task_sig[st.id].push_back({ev_qkv, (int)i});
       max_task_rows = std::max(max_task_rows, g.tasks[st.id].row1 - g.tasks[st.id].row0);
       out_acc(st.id, T_QKV, l, st.r0, st.r1, st.comb);
     }
-    // ---- attention splits; the last split of each (seq, kv head) merges and signals
-    const int ev_att = b.new_event(S * hk);
+    // ---- attention: T tasks cut the layer's (sequence, KV head) segments of cache blocks evenly at run
+    // time; the task holding a segment's last block merges the others' partials of it. In the symbolic
+    // model the layer's tasks form one group: each may merge any segment, and the last one stands for
+    // the writers of the attention output.
+    const int T = std::min(S * hk * g.splits, n_cus);  // the cut is balanced: one task per CU suffices
+    g.attn_tasks = T;
+    const int ev_att = b.new_event(T);
     // CUs running attention get no O-projection task in the same layer when they are few: their
     // register pipelines sit idle through attention, while the other CUs hold their O tiles there.
     std::vector<char> attn_cu(n_cus, 0);
     {
-      const int n_attn = S * hk * g.splits;
-      int k = 0;
-      for (int s = 0; s < S; ++s)
-        for (int grp = 0; grp < hk; ++grp) {
-          const int agrp = (int)g.group_size.size();
-          g.group_size.push_back(g.splits);
-          for (int j = 0; j < g.splits; ++j, ++k) {
-            TaskDesc t{};
-            t.type = T_ATTN;
-            t.layer = l;
-            t.wait_ev = ev_qkv[grp];
-            t.a0 = s;
-            t.a1 = grp;
-            t.a2 = j;
-            t.a3 = (l * S + s) * hk + grp;
-            const int cu = (int)((int64_t)k * n_cus / n_attn);
-            attn_cu[cu] = 1;
-            const int id = b.add_task(t, cu);
-            g.task_group[id] = agrp;
-            g.task_comb[id] = j == g.splits - 1;
-            b.task_sig[id].push_back({ev_att, s * hk + grp});
-            b.acc(id, S_Q, (int64_t)s * qd + (int64_t)grp * G * dh, (int64_t)s * qd + (int64_t)(grp + 1) * G * dh, 0);
-            b.acc(id, S_KVCUR, (((int64_t)l * S + s) * hk + grp) * 2 * dh, (((int64_t)l * S + s) * hk + grp + 1) * 2 * dh, 0);
-            b.acc(id, S_CTX, s, s + 1, 0);
-            for (int h = grp * G; h < (grp + 1) * G; ++h)
-              b.acc(id, S_PART, ((int64_t)s * hq + h) * g.splits + j, ((int64_t)s * hq + h) * g.splits + j + 1, 1);
-            for (int h = grp * G; h < (grp + 1) * G; ++h)
-              b.cacc(id, S_PART, ((int64_t)s * hq + h) * g.splits, ((int64_t)s * hq + h + 1) * g.splits, 0);
-            b.cacc(id, S_O, (int64_t)s * qd + (int64_t)grp * G * dh, (int64_t)s * qd + (int64_t)(grp + 1) * G * dh, 1);
-          }
-        }
-      g.n_attn_groups = std::max(g.n_attn_groups, (l + 1) * S * hk);
+      const int agrp = (int)g.group_size.size();
+      g.group_size.push_back(T);
+      g.group_ordered.push_back(1);
+      for (int i = 0; i < T; ++i) {
+        TaskDesc t{};
+        t.type = T_ATTN;
+        t.layer = l;
+        t.wait_ev = ev_qkv;
+        t.a2 = i;
+        t.a3 = l * T + i;
+        // at most one task per CU: spread; more: round-major (CU c runs tasks c, c + n_cus, ...), so that
+        // a merging task never waits on a task that is queued behind another merge
+        const int cu = T <= n_cus ? (int)((int64_t)i * n_cus / T) : i % n_cus;
+        attn_cu[cu] = 1;
+        const int id = b.add_task(t, cu);
+        g.task_group[id] = agrp;
+        g.task_comb[id] = 1;
+        b.task_sig[id].push_back({ev_att, i});
+        b.acc(id, S_Q, 0, (int64_t)S * qd, 0);
+        b.acc(id, S_KVCUR, (int64_t)l * S * hk * 2 * dh, (int64_t)(l + 1) * S * hk * 2 * dh, 0);
+        b.acc(id, S_CTX, 0, S, 0);
+        b.acc(id, S_PART, ((int64_t)l * T + i) * 2, ((int64_t)l * T + i + 1) * 2, 1);
+        b.cacc(id, S_PART, (int64_t)l * T * 2, ((int64_t)l * T + i + 1) * 2, 0);  // its own and earlier tasks'
+        if (i == T - 1) b.cacc(id, S_O, 0, (int64_t)S * qd, 1);
+      }
+      g.n_attn_groups = (l + 1) * S * hk;
     }
     // ---- O projection + residual
     const bool few_attn = (int)std::count(attn_cu.begin(), attn_cu.end(), 1) * 4 <= n_cus;
@@ -529,7 +525,7 @@ std::string build_graph(const mk_model_config& c, int n_cus, HostGraph& g) {
   g.sl.kvt = take((int64_t)L * S * 2 * hk * (dh / 2) * 8);
   g.sl.ot = take((int64_t)L * S * qd * 8);
   g.sl.ht = take((int64_t)L * S * f * 8);
-  g.sl.pt = take((int64_t)L * S * hq * g.splits * (dh + 2) * 8);
+  g.sl.pt = take((int64_t)L * g.attn_tasks * 2 * G * (dh + 2) * 8);
   g.sl.bpt = take(bpt_words * 8);
   g.sl.tagged_end = o;
   g.sl.amax = take((int64_t)S * g.n_lm_parts * 8);
@@ -545,13 +541,10 @@ std::string build_graph(const mk_model_config& c, int n_cus, HostGraph& g) {
   if (S > 1)  // batched: the input columns as MFMA fragments (32 units x 64 lanes x 32 B), the tile's
               // partial sums (1 KB per 16-row group), two edge tiles per wave, per-sequence scalars
     gemv_lds = 32 * 64 * 32 + (int64_t)g.max_tile_groups * 1024 + 8 * 2 * 1024 + 256;
-  // attention: scores of one register chunk (8 waves x 64/(dh/8) positions x 8 slots), per-wave
-  // partial outputs and the staged queries
-  // attention: K and V staging (4 slots x 8 waves x 1 KB each), the scores of one chunk
-  // (8 waves x 64/(dh/8) positions x 4 slots), per-wave partial outputs and the staged queries
-  const int64_t attn_chunk = (int64_t)8 * (64 / (dh / 8)) * 4;
-  const int64_t attn_lds = (int64_t)2 * 4 * 8 * 1024 + (int64_t)G * attn_chunk * 4 + (int64_t)8 * G * dh * 4 +
-                           (int64_t)G * dh * 4 + (int64_t)dh * 4;
+  // attention: the staged queries (G rounded up to 2, 4 or 8 heads), the current key and value rows,
+  // each wave's merged (m, l, o) per head
+  const int gmax = G <= 2 ? 2 : G <= 4 ? 4 : 8;
+  const int64_t attn_lds = (int64_t)gmax * dh * 4 + (int64_t)dh * 4 + (int64_t)8 * G * (dh + 2) * 4;
   int max_q = 0;
   for (int cu = 0; cu < n_cus; ++cu) max_q = std::max(max_q, g.queue_off[cu + 1] - g.queue_off[cu]);
   g.max_queue = max_q;
@@ -678,6 +671,19 @@ std::string simulate_graph(const HostGraph& g, uint64_t seed, int n_steps) {
     const uint32_t epoch = (uint32_t)step + 1;
     std::vector<char> ended(nt, 0), phase(nt, 0);  // phase 1: first phase running, 2: waiting for its group
     std::vector<int> group_done(ng, 0);            // tasks of the group past their first phase
+    // members of ordered groups, in global order
+    std::vector<std::vector<int>> members(ng);
+    for (int t = 0; t < nt; ++t)
+      if (g.task_group[t] >= 0 && g.group_ordered[g.task_group[t]]) members[g.task_group[t]].push_back(t);
+    auto group_ready = [&](int t) {
+      const int gi = g.task_group[t];
+      if (!g.group_ordered[gi]) return group_done[gi] >= g.group_size[gi];
+      for (int m : members[gi]) {
+        if (m > t) break;
+        if (phase[m] < 2 && !ended[m]) return false;
+      }
+      return true;
+    };
     std::vector<int> qpos(g.n_cus), running(g.n_cus, -1);
     for (int cu = 0; cu < g.n_cus; ++cu) qpos[cu] = g.queue_off[cu];
     // Expected version of element e for a reader at global position pos: the last writer before
@@ -686,7 +692,7 @@ std::string simulate_graph(const HostGraph& g, uint64_t seed, int n_steps) {
     // the global order: they must all be this step's.
     auto expected = [&](int b, int64_t e, int pos, bool inclusive) -> int64_t {
       const auto& w = writers[b][e];
-      if (b == S_BPART) return w.size() == 1 ? (int64_t)step * nt + w[0] : -2;
+      if (b == S_BPART || b == S_PART) return w.size() == 1 ? (int64_t)step * nt + w[0] : -2;
       auto it = inclusive ? std::upper_bound(w.begin(), w.end(), pos) : std::lower_bound(w.begin(), w.end(), pos);
       if (it != w.begin()) return (int64_t)step * nt + *(it - 1);
       if (!w.empty() && step > 0) return (int64_t)(step - 1) * nt + w.back();
@@ -711,9 +717,9 @@ std::string simulate_graph(const HostGraph& g, uint64_t seed, int n_steps) {
           const auto& w = writers[a.buf][e];
           auto it = std::lower_bound(w.begin(), w.end(), pos);
           const int prev = it != w.begin() ? *(it - 1) : -1;
-          // (a tile's partials are written once per step and read only within it)
+          // (a group's partials are written once per step and read only within it)
           for (int r : readers[a.buf][e])
-            if (a.buf != S_BPART && r > prev && r < pos && !ended[r]) {
+            if (a.buf != S_BPART && a.buf != S_PART && r > prev && r < pos && !ended[r]) {
               err = "task " + std::to_string(pos) + " overwrote buffer " + std::to_string(a.buf) + " element " +
                     std::to_string(e) + " while task " + std::to_string(r) + " still needed it";
               return false;
@@ -744,7 +750,7 @@ std::string simulate_graph(const HostGraph& g, uint64_t seed, int n_steps) {
         if (running[cu] >= 0) {
           const int t = running[cu];
           // a second phase waits until every task of its group has finished its first phase
-          if (phase[t] == 2 && group_done[g.task_group[t]] < g.group_size[g.task_group[t]]) continue;
+          if (phase[t] == 2 && !group_ready(t)) continue;
           cand.push_back(cu);
         } else if (qpos[cu] < g.queue_off[cu + 1] && ready(g.queue_idx[qpos[cu]])) {
           cand.push_back(cu);

@@ -50,7 +50,7 @@ struct TaskDesc {       // 64 bytes; read with scalar loads
   int32_t row0, row1;   // GEMV: packed output rows [row0, row1)
   int32_t geom;         // GEMV: GeomIndex
   int64_t wofs;         // GEMV: byte offset of the tile in the packed weights
-  // ATTN: seq, kv head, split, group | ARGMAX: a0 = seq | LMHEAD: a0 = part index.
+  // ATTN: a2 = task index within its layer, a3 = a unique id | ARGMAX: a0 = seq | LMHEAD: a0 = part.
   // Batched GEMV (several sequences): the tile's rows are split over kS tasks by columns.
   //   a1 = word offset of the tile's partial sums in KernelParams::bpt (kS > 1),
   //   a2 = first column unit | units << 16 (units of 32 columns),
@@ -127,7 +127,7 @@ struct KernelParams {
   uint64_t* kvt;              // [L][max_seqs][2][hk][dh/2] the current position's key and value (bf16 pairs)
   uint64_t* ot;               // [L][max_seqs][hq*dh] attention output
   uint64_t* ht;               // [L][max_seqs][f] SwiGLU output
-  uint64_t* pt;               // [L][max_seqs][hq][splits][dh + 2] attention partials (m, l, unnormalised o)
+  uint64_t* pt;               // [L][attention task][2][G][dh + 2] attention partials (m, l, unnormalised o)
   uint64_t* bpt;              // batched GEMV tiles: [split][16-row group][64 lanes][4] partial sums + 64 words
                               // (sums of squares per sequence), one block per tile (see TaskDesc)
   float* logits;              // [max_seqs][V]
@@ -140,6 +140,7 @@ struct KernelParams {
   uint32_t epoch;
   uint32_t watchdog_ticks;    // s_memrealtime ticks (100 MHz) a wait may spin before the kernel aborts
   int32_t max_queue;          // longest per-CU queue (its descriptors are staged in LDS)
+  int32_t attn_tasks;         // attention tasks per layer (they cut the layer's KV blocks evenly)
   TraceRec* trace;            // per-task timestamps of the last step, or nullptr
 };
 

@@ -26,7 +26,8 @@ struct HostGraph {
   int n_cus = 0;
   int splits = 1;
   int max_pos = 0;
-  int n_attn_groups = 0;  // (layer, sequence, KV head) groups whose attention splits are merged
+  int n_attn_groups = 0;  // (layer, sequence, KV head) segments of attention
+  int attn_tasks = 0;     // attention tasks per layer  // (layer, sequence, KV head) groups whose attention splits are merged
   int n_lm_parts = 0;
   int max_queue = 0;
   int64_t lds_bytes = 0;
@@ -41,6 +42,9 @@ struct HostGraph {
   std::vector<int32_t> task_group;           // per task: group index or -1
   std::vector<char> task_comb;               // per task: has a second phase
   std::vector<int32_t> group_size;           // per group
+  // per group: 1 = a member's second phase waits only for the members before it in the global order
+  // (attention merges read earlier tasks' partials); 0 = for all members (batched column splits)
+  std::vector<char> group_ordered;
   int max_tile_groups = 0;                   // batched: most 16-row groups in one tile
   std::vector<int32_t> queue_off, queue_idx;
   std::vector<EventDesc> events;

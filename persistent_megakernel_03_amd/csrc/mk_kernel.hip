@@ -83,7 +83,9 @@ struct Ctl {
   GemvGeom geoms[G_COUNT];  // copied once per launch
   int32_t ctx[16];          // context lengths of the first 16 sequences, read once per launch
   float red[NW * 8];
-  float m_run[16], l_run[16], scale[16];
+  // attention work of this step: blocks per (sequence, KV head) segment of sequence s (0 when the
+  // sequence is inactive), and the first block of sequence s's segments in the layer's block order
+  int32_t anb[16], aoff[17];
   uint32_t aborted;
   uint64_t kred[NW];
   uint64_t t_ready;         // trace: when the running task's inputs were all present
@@ -334,98 +336,12 @@ __device__ __forceinline__ bool is_gemv(int type) {
   return type == T_QKV || type == T_OPROJ || type == T_GATEUP || type == T_DOWN || type == T_LMHEAD;
 }
 
-// Attention tiling shared by the prefetch and the attention task (see the attention section).
-constexpr int ASLOTS = 4;  // register-free K/V slots per wave per chunk, staged in LDS
-
-template <int DH>
-struct AttnShape {
-  static constexpr int LPP = DH / 8;              // lanes per position (8 dims each)
-  static constexpr int PPW = 64 / LPP;            // positions per wave per slot
-  static constexpr int CHUNK = NW * PPW * ASLOTS; // positions per chunk
-};
-
-struct AttnRange {
-  int p0, p1;  // the split's positions [p0, p1)
-  int pos;     // the current position, or -1 when the sequence is inactive or out of range
-};
-
-__device__ __forceinline__ AttnRange attn_range(const KernelParams& p, const TaskDesc& t, const Ctl* ctl) {
-  AttnRange r;
-  r.p0 = r.p1 = 0;
-  r.pos = -1;
-  const int s = t.a0;
-  if (s >= p.n_active) return r;
-  const int pos = ctl->ctx[s];
-  if (pos < 0 || pos >= p.max_pos) return r;
-  const int n = pos + 1, nb = (n + 15) >> 4, pps = (nb + p.splits - 1) / p.splits;
-  r.p0 = min(n, t.a2 * pps * 16);
-  r.p1 = min(n, (t.a2 + 1) * pps * 16);
-  r.pos = pos;
-  return r;
-}
-
-// LDS staging of one chunk: K rows then V rows, each [ASLOTS][NW][64 lanes] x 16 bytes. Slot i of
-// wave w, lane l holds 8 dims (l % LPP) of position cs + (i * NW + w) * PPW + l / LPP: exactly the
-// layout one wave-wide 16-byte-per-lane load writes, so the cache rows go straight from memory
-// to LDS with global_load_lds (no registers), and each wave later reads back only its own slots.
-template <int DH>
-__device__ __forceinline__ v4u* attn_kbuf(float* lds) { return (v4u*)lds; }
-template <int DH>
-__device__ __forceinline__ v4u* attn_vbuf(float* lds) { return (v4u*)lds + ASLOTS * NW * 64; }
-
-// Issue the loads of positions [cs, min(cs + CHUNK, ce)) of the task's (seq, kv head) into the
-// LDS staging buffers. The chunk's page-table entries are fetched first, all at once, so the
-// row loads issue together; slots past the range load a dummy row (block 0, offset 0).
-template <int DH>
-__device__ __forceinline__ void attn_stage_chunk(const KernelParams& p, const TaskDesc& t, int cs, int ce,
-                                                 uint16_t* const* pools, float* lds) {
-  constexpr int LPP = AttnShape<DH>::LPP, PPW = AttnShape<DH>::PPW;
-  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int lane = threadIdx.x & 63, pg = lane / LPP, c = lane % LPP;
-  const int s = t.a0, grp = t.a1;
-  const uint16_t* kpool = pools[t.layer];
-  const uint16_t* vpool = pools[p.n_layers + t.layer];
-  const int32_t* ptab = p.page_table + (size_t)s * p.max_blocks;
-  int blk[ASLOTS];
-#pragma unroll
-  for (int i = 0; i < ASLOTS; ++i) {
-    const int pp = cs + (i * NW + wave) * PPW + pg;
-    blk[i] = (pp < ce) ? ptab[pp >> 4] : 0;
-  }
-#pragma unroll
-  for (int i = 0; i < ASLOTS; ++i) {
-    const int pp = cs + (i * NW + wave) * PPW + pg;
-    int b = blk[i];
-    if (b < 0 || b >= p.num_blocks) {
-      raise_error(p, ERR_PAGE, (uint32_t)s, (uint32_t)b);
-      b = 0;
-    }
-    const size_t row = (((size_t)b * p.hk + grp) * 16 + (pp < ce ? (pp & 15) : 0)) * DH + c * 8;
-    __attribute__((address_space(3))) void* kd =
-        (__attribute__((address_space(3))) void*)(attn_kbuf<DH>(lds) + (i * NW + wave) * 64);
-    __attribute__((address_space(3))) void* vd =
-        (__attribute__((address_space(3))) void*)(attn_vbuf<DH>(lds) + (i * NW + wave) * 64);
-    __builtin_amdgcn_global_load_lds((const void*)(kpool + row), kd, 16, 0, 0);
-    __builtin_amdgcn_global_load_lds((const void*)(vpool + row), vd, 16, 0, 0);
-  }
-}
-
 __device__ __forceinline__ WaveRun dummy_run(const KernelParams& p) {
   WaveRun w;
   w.src = (const v4u*)p.wpacked + (threadIdx.x & 63);
   w.nunits = 1;
   w.g0 = 0;
   return w;
-}
-
-// An attention split's first chunk of cached keys and values, staged into LDS before the split polls
-// for its queries ("MPK: A Compiler and Runtime for Mega-Kernelizing Tensor Programs", analogy 4:
-// a task's inputs load while the previous one runs).
-template <int DH>
-__device__ __forceinline__ void attn_prefetch(const KernelParams& p, const TaskDesc& t, const Ctl* ctl,
-                                              uint16_t* const* pools, float* lds) {
-  const AttnRange r = attn_range(p, t, ctl);
-  attn_stage_chunk<DH>(p, t, r.p0, min(r.p1, r.pos), pools, lds);
 }
 
 __device__ __forceinline__ void gemv_tile(const KernelParams& p, const TaskDesc& t, const GemvGeom gm, const float* xs, float* ys,
@@ -571,266 +487,408 @@ __device__ __forceinline__ void qkv_store_set(const KernelParams& p, int l, int 
 }
 
 // ----------------------------------------------------------------------------- attention
-// One split of grouped-query attention for (seq, kv head): a contiguous range of cache blocks.
-// The G query heads that share the KV head read each key and value row once ("LLM高速化勉強会資料", slide 28).
-// Keys and values of earlier positions do not change during a step. The worker stages the
-// split's first chunk of them into LDS while the previous task finishes, before this task polls
-// for its queries ("MPK: A Compiler and Runtime for Mega-Kernelizing Tensor Programs", analogy 4:
-// inputs load while the previous task runs). Then only q and the current position's key and
-// value are fetched, in one poll. Softmax runs online across chunks. The running max and sum
-// rescale the output ("LLM高速化勉強会資料", slide 13; the online softmax of "Hạt nhân là gì và tại sao mọi người
-// lại viết hạt nhân mới"). Each split's partial (m, l, unnormalised o) goes out as tagged words;
-// the group's last split polls for the others' and merges them by log-sum-exp into o.
+// Grouped-query decode attention over the paged cache, split across CUs as flash-decoding.
+//
+// Work split. A layer's attention is a set of segments, one per (sequence s, KV head g): the cache
+// blocks 0 .. nb_s - 1 of s, the last one holding the current position. The segments are laid end to
+// end (sequence-major, then KV head) and this concatenation of blocks is cut into T equal ranges, one
+// per attention task, at run time from the context lengths. Every task thus streams about the same
+// number of key and value bytes whatever the mix of context lengths in the batch. The G query heads
+// that share a KV head read each key and value row once ("LLM高速化勉強会資料", slide 28).
+//
+// Within a task's part of a segment, each wave streams its own groups of positions (64 lanes = PPW
+// positions x DH/8 lanes, 8 dimensions per lane) through a register pipeline of keys and values, issued
+// before the task polls for its queries: cached rows do not depend on this step ("MPK: A Compiler and
+// Runtime for Mega-Kernelizing Tensor Programs", analogy 4). Each lane group keeps its own
+// online-softmax state per head: running max, running sum, and the unnormalised output of its 8
+// dimensions, rescaled when the max grows by more than 8 ("LLM高速化勉強会資料", slide 13;
+// the online softmax of "Hạt nhân là gì và tại sao mọi người lại viết hạt nhân mới"). No barrier runs
+// inside the stream. The lane groups of a wave, then the waves of the workgroup (in wave order), are
+// merged by log-sum-exp. The current position's key and value come from this step's tagged words.
+//
+// A segment held whole by one task ends there as o = sum / l. A segment cut between tasks: each task
+// but the last writes its partial (m, l, unnormalised o) as tagged words; the last (the one holding
+// the segment's final block) polls them and merges them in task order.
 template <int DH, int GMAX>
-__device__ __forceinline__ void task_attn(const KernelParams& p, const TaskDesc& t, float* lds, Ctl* ctl,
-                                          uint16_t* const* pools) {
-  constexpr int LPP = AttnShape<DH>::LPP, PPW = AttnShape<DH>::PPW, CHUNK = AttnShape<DH>::CHUNK;
-  const int s = t.a0, grp = t.a1, j = t.a2;
-  const int G = p.hq / p.hk, h0 = grp * G;
-  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int lane = threadIdx.x & 63, pg = lane / LPP, c = lane % LPP;
-  const AttnRange r = attn_range(p, t, ctl);
-  if (s < p.n_active && r.pos < 0 && threadIdx.x == 0) raise_error(p, ERR_CTX, (uint32_t)s, (uint32_t)ctl->ctx[s]);
-  const bool active = r.pos >= 0;
-  const int pos = r.pos;
-  v4u* kb = attn_kbuf<DH>(lds);
-  v4u* vb = attn_vbuf<DH>(lds);
-  float* scores = (float*)(vb + ASLOTS * NW * 64);  // [G][CHUNK]
-  float* obuf = scores + G * CHUNK;                  // [NW][G][DH]
-  float* qs = obuf + NW * G * DH;                    // [G][2][DH/2]: dims 8c..8c+3 at 4c, 8c+4..8c+7 at DH/2 + 4c
-  uint32_t* kvc = (uint32_t*)(qs + G * DH);          // the current position's key (DH/2 words) then value row
-  const int splits = p.splits;
-  const float scale = 1.0f / sqrtf((float)DH);
+struct AttnShape {
+  static constexpr int LPP = DH / 8;         // lanes per position
+  static constexpr int PPW = 64 / LPP;       // positions per wave-wide load
+  static constexpr int EPT = (GMAX * DH + NT - 1) / NT;  // output elements (head, dim) per thread
+};
 
-  const int tid = threadIdx.x;
+// First block of attention task i's range: T tasks cut W blocks evenly.
+__device__ __forceinline__ int attn_lo(int W, int T, int i) { return (int)((int64_t)W * i / T); }
+// The task whose range holds block x: the last i with attn_lo(i) <= x.
+__device__ __forceinline__ int attn_task_of(int W, int T, int x) {
+  return min(T - 1, (int)(((int64_t)(x + 1) * T - 1) / W));
+}
+
+// DPP moves within a row of 16 lanes: swap pairs, swap pairs of pairs, mirror within 8, mirror within 16.
+// Applied in turn, each adds a lane's partner from another group, so LPP consecutive lanes end with the
+// sum over all of them (LPP = 8 uses the first three).
+template <int CTRL>
+__device__ __forceinline__ float dpp_add(float v) {
+  return v + __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), CTRL, 0xF, 0xF, false));
+}
+
+// Scores of one position for every head: s_h = q_h . k, this lane's 8 dimensions summed over the
+// position's lanes. The heads' reductions are interleaved so that each DPP move reads a value written
+// several instructions earlier.
+template <int DH, int GMAX>
+__device__ __forceinline__ void attn_scores(const v4u kv, bool valid, int G, const float (&qr)[GMAX][8], float (&a)[GMAX]) {
+  const float kf[8] = {bf_lo(kv.x), bf_hi(kv.x), bf_lo(kv.y), bf_hi(kv.y), bf_lo(kv.z), bf_hi(kv.z), bf_lo(kv.w), bf_hi(kv.w)};
+#pragma unroll
+  for (int h = 0; h < GMAX; ++h) {
+    a[h] = 0.f;
+    if (h < G) {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) a[h] = fmaf(qr[h][e], kf[e], a[h]);
+    }
+  }
+#pragma unroll
+  for (int h = 0; h < GMAX; ++h) a[h] = dpp_add<0xB1>(a[h]);
+#pragma unroll
+  for (int h = 0; h < GMAX; ++h) a[h] = dpp_add<0x4E>(a[h]);
+#pragma unroll
+  for (int h = 0; h < GMAX; ++h) a[h] = dpp_add<0x141>(a[h]);
+  if (DH == 128) {
+#pragma unroll
+    for (int h = 0; h < GMAX; ++h) a[h] = dpp_add<0x140>(a[h]);
+  }
+#pragma unroll
+  for (int h = 0; h < GMAX; ++h) a[h] = valid ? a[h] : -INFINITY;
+}
+
+// Raises each head's running max to cover mx, rescaling the running sum and output.
+template <int GMAX>
+__device__ __forceinline__ void attn_rescale(int G, const float (&mx)[GMAX], float (&mr)[GMAX], float (&lr)[GMAX],
+                                             float (&orr)[GMAX][8]) {
+#pragma unroll
+  for (int h = 0; h < GMAX; ++h) {
+    if (h >= G) break;
+    const float mn = fmaxf(mr[h], mx[h]), al = __expf(mr[h] - mn);
+    lr[h] *= al;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) orr[h][e] *= al;
+    mr[h] = mn;
+  }
+}
+
+// Adds one position's values with weights exp(s_h - m_h).
+template <int GMAX>
+__device__ __forceinline__ void attn_accum(const v4u vv, int G, const float (&a)[GMAX], const float (&mr)[GMAX],
+                                           float (&lr)[GMAX], float (&orr)[GMAX][8]) {
+  const float vf[8] = {bf_lo(vv.x), bf_hi(vv.x), bf_lo(vv.y), bf_hi(vv.y), bf_lo(vv.z), bf_hi(vv.z), bf_lo(vv.w), bf_hi(vv.w)};
+#pragma unroll
+  for (int h = 0; h < GMAX; ++h) {
+    if (h >= G) break;
+    const float pe = __expf(a[h] - mr[h]);
+    lr[h] += pe;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) orr[h][e] = fmaf(pe, vf[e], orr[h][e]);
+  }
+}
+
+// Attention over positions [c0, c1) of segment (s, grp), c1 <= pos + 1 (pos = the current position).
+// Returns, per output element (head, dim) of this thread, the merged (max, sum, unnormalised output).
+template <int DH, int GMAX, int ANS>
+__device__ __forceinline__ void attn_part(const KernelParams& p, const TaskDesc& t, float* lds, Ctl* ctl,
+                                          uint16_t* const* pools, int s, int grp, int pos, int c0, int c1,
+                                          float (&Mo)[AttnShape<DH, GMAX>::EPT], float (&Lo)[AttnShape<DH, GMAX>::EPT],
+                                          float (&Ao)[AttnShape<DH, GMAX>::EPT]) {
+  using AS = AttnShape<DH, GMAX>;
+  constexpr int LPP = AS::LPP, PPW = AS::PPW, EPT = AS::EPT;
+  // the thread index made opaque per call: per-lane offsets are then computed here rather than hoisted
+  // out of the task loop and held in registers through every other task
+  int tid = threadIdx.x;
+  asm volatile("" : "+v"(tid));
+  const int G = p.hq / p.hk, h0 = grp * G, l = t.layer, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int pg = lane / LPP, c = lane % LPP;
+  float* qs = lds;  // [G][2][DH/2] scaled queries: dims 8c..8c+3 at 4c, 8c+4..8c+7 at DH/2 + 4c
+  uint32_t* kvc = (uint32_t*)(qs + GMAX * DH);  // the current position's key (DH/2 words) then value row
+  float* wbuf = (float*)(kvc + DH);          // [NW][G][DH + 2]: each wave's merged (m, l, o)
   const uint32_t what = (uint32_t)t.wait_ev;
-  wait_stores();  // this wave's staged rows (issued before the wait) have landed in LDS
-  // the group's queries, staged in LDS (two planes per head, so lanes reading consecutive
-  // 8-dim pieces read consecutive 16-byte words)
+  const bool cur = pos >= 0 && c1 == pos + 1;  // the part ends with the current position
+  const int ce = cur ? pos : c1;             // cached positions [c0, ce)
+  const int ngr = ce > c0 ? (ce - c0 + PPW - 1) / PPW : 0;
+  const int nw = ngr > wave ? (ngr - wave + NW - 1) / NW : 0;  // this wave's groups: wave + NW k
+  // Cache rows: this lane's 8 dims of group k's position (clamped to the last cached position), with
+  // nontemporal loads (each row is read once per step). Page entries are clamped into the pool here
+  // and checked once per part after the stream.
+  const uint16_t* kpool = pools[l];
+  const uint16_t* vpool = pools[p.n_layers + l];
+  const int32_t* ptab = p.page_table + (size_t)s * p.max_blocks;
+  auto row_load = [&](const uint16_t* pool, int k) {
+    size_t off = (size_t)c * 8;  // no cached rows: a dummy row, block 0
+    if (nw > 0) {
+      const int p0g = c0 + (wave + NW * min(k, nw - 1)) * PPW;
+      const int b = min(max(ptab[p0g >> 4], 0), p.num_blocks - 1);
+      off = (((size_t)b * p.hk + grp) * 16 + (min(p0g + pg, ce - 1) & 15)) * DH + c * 8;
+    }
+    return __builtin_nontemporal_load((const v4u*)(pool + off));
+  };
+  v4u RK[ANS], RV[ANS];
+#pragma unroll
+  for (int j = 0; j < ANS; ++j) {
+    RK[j] = row_load(kpool, j);
+    RV[j] = row_load(vpool, j);
+  }
+  // the group's queries (a vector poll) and, when the part ends with the current position, its key
+  // and value rows (words KQ and KQ + 1 of the first DH/2 threads), in one poll
   auto q_slot = [&](int i) -> float& {
     const int h = i / DH, d = i % DH, e = d & 7;
     return qs[h * DH + (e < 4 ? 0 : DH / 2) + (d >> 3) * 4 + (e & 3)];
   };
-  // One poll for the group's queries (words k < KQ of each thread, laid out as a vector poll) and
-  // the current position's key and value rows (words KQ and KQ + 1 of the first DH/2 threads).
-  constexpr int KQ = (GMAX * DH + NW * 64 - 1) / (NW * 64);
-  if (active) {
-    const uint64_t* qsrc = qt_at(p, t.layer, s) + (size_t)h0 * DH;
-    const int nq = G * DH, iq = poll_index(nq, 0);
-    const int dk = (int)((const char*)kvt_at(p, t.layer, s, 0, grp) - (const char*)qsrc);  // bytes, > 0
+  {
+    constexpr int KQ = (GMAX * DH + NW * 64 - 1) / (NW * 64);
+    const uint64_t* qsrc = qt_at(p, l, s) + (size_t)h0 * DH;
+    const float qscale = 1.0f / sqrtf((float)DH);  // the scores' 1 / sqrt(dh), folded into the queries
+    const int nq = G * DH, iq = (tid >> 6) * poll_chunk(nq) + (tid & 63);  // poll_index, from the opaque tid
+    const int dk = (int)((const char*)kvt_at(p, l, s, 0, grp) - (const char*)qsrc);  // bytes, > 0
     const int dv = dk + p.hk * (DH / 2) * 8;
     uint32_t pend = first_words(min(poll_chunk(nq) / 64, (nq - iq + 63) / 64));
-    if (tid < DH / 2) pend |= 3u << KQ;
+    if (cur && tid < DH / 2) pend |= 3u << KQ;
     poll_tagged<KQ + 2>(
         p, qsrc, [&](int k) { return k < KQ ? iq * 8 + k * 512 : tid * 8; },
         [&](int k) { return k < KQ ? 0 : k == KQ ? dk : dv; }, pend, what, [&](int k, uint32_t b) {
-          if (k < KQ) q_slot(iq + 64 * k) = __uint_as_float(b);
+          if (k < KQ) q_slot(iq + 64 * k) = __uint_as_float(b) * qscale;
           else kvc[(k - KQ) * (DH / 2) + tid] = b;
         });
-  } else {
-    for (int i = tid; i < G * DH; i += NT) q_slot(i) = 0.f;
   }
   bar();
   if (p.trace && tid == 0) ctl->t_ready = __builtin_amdgcn_s_memrealtime();
-  float oacc[GMAX][8];
+  float mr[GMAX], lr[GMAX], orr[GMAX][8];
 #pragma unroll
-  for (int h = 0; h < GMAX; ++h)
+  for (int h = 0; h < GMAX; ++h) {
+    mr[h] = -1e30f;  // finite: a fully masked position then adds exp(-inf) = 0
+    lr[h] = 0.f;
 #pragma unroll
-    for (int e = 0; e < 8; ++e) oacc[h][e] = 0.f;
-  if (threadIdx.x < 16) {
-    ctl->m_run[threadIdx.x] = -INFINITY;
-    ctl->l_run[threadIdx.x] = 0.f;
+    for (int e = 0; e < 8; ++e) orr[h][e] = 0.f;
   }
-  const int old_end = min(r.p1, pos);  // rows before the current position are staged ahead
-  for (int cs = r.p0; cs < r.p1; cs += CHUNK) {
-    const int ce = min(r.p1, cs + CHUNK);
-    if (cs != r.p0) {
-      bar();  // every wave is done with the previous chunk's scores
-      attn_stage_chunk<DH>(p, t, cs, old_end, pools, lds);
-      wait_stores();
-    }
-    // the current position's key and value come from this step (polled above) into their slot
-    if (pos >= cs && pos < ce) {
-      const int idx = pos - cs, ic = idx / (NW * PPW), wc = (idx / PPW) % NW, pc = idx % PPW;
-      if (wave == wc && pg == pc) {  // lane c's 8 dims are words 4c..4c+3 of each row
-        kb[(ic * NW + wc) * 64 + lane] = *(const v4u*)(kvc + 4 * c);
-        vb[(ic * NW + wc) * 64 + lane] = *(const v4u*)(kvc + DH / 2 + 4 * c);
-      }
-    }
-    bar();  // queries staged; patched rows visible
-    // scores = q . k * scale
+  // this lane's 8 dimensions of each head's scaled query
+  float qr[GMAX][8];
 #pragma unroll
-    for (int i = 0; i < ASLOTS; ++i) {
-      const int pp = cs + (i * NW + wave) * PPW + pg;
-      const v4u kv = kb[(i * NW + wave) * 64 + lane];
-      const float kf[8] = {bf_lo(kv.x), bf_hi(kv.x), bf_lo(kv.y), bf_hi(kv.y), bf_lo(kv.z), bf_hi(kv.z), bf_lo(kv.w), bf_hi(kv.w)};
+  for (int h = 0; h < GMAX; ++h) {
+    const v4f qa = *(const v4f*)(qs + min(h, G - 1) * DH + c * 4);
+    const v4f qb = *(const v4f*)(qs + min(h, G - 1) * DH + DH / 2 + c * 4);
+    qr[h][0] = qa.x; qr[h][1] = qa.y; qr[h][2] = qa.z; qr[h][3] = qa.w;
+    qr[h][4] = qb.x; qr[h][5] = qb.y; qr[h][6] = qb.z; qr[h][7] = qb.w;
+  }
+  // Slot j holds group k0 + j; it is refilled with group k0 + j + ANS once consumed. Refills past the
+  // wave's groups re-read its last group (and weigh 0). The running max moves only when a score passes
+  // it by more than 8: until then exp(s - m) stays below e^8, far inside fp32, and the sums need no
+  // rescaling (the result is the same ratio).
+  for (int k0 = 0; k0 < nw; k0 += ANS) {
 #pragma unroll
-      for (int h = 0; h < GMAX; ++h) {
-        if (h >= G) break;
-        const v4f qa = *(const v4f*)(qs + h * DH + c * 4);
-        const v4f qb = *(const v4f*)(qs + h * DH + DH / 2 + c * 4);
-        float a = 0.f;
-        a = fmaf(qa.x, kf[0], a); a = fmaf(qa.y, kf[1], a); a = fmaf(qa.z, kf[2], a); a = fmaf(qa.w, kf[3], a);
-        a = fmaf(qb.x, kf[4], a); a = fmaf(qb.y, kf[5], a); a = fmaf(qb.z, kf[6], a); a = fmaf(qb.w, kf[7], a);
+    for (int j = 0; j < ANS; ++j) {
+      const int pp = c0 + (wave + NW * (k0 + j)) * PPW + pg;
+      float sc[GMAX];
+      attn_scores<DH, GMAX>(RK[j], k0 + j < nw && pp < ce, G, qr, sc);
+      bool up = false;
 #pragma unroll
-        for (int off = LPP >> 1; off >= 1; off >>= 1) a += __shfl_xor(a, off);
-        if (c == 0 && pp < ce) scores[h * CHUNK + (pp - cs)] = a * scale;
-      }
+      for (int h = 0; h < GMAX; ++h)
+        if (h < G) up = up || sc[h] > mr[h] + 8.f;
+      if (__builtin_expect(__any(up), 0)) attn_rescale<GMAX>(G, sc, mr, lr, orr);
+      attn_accum<GMAX>(RV[j], G, sc, mr, lr, orr);
+      RK[j] = row_load(kpool, k0 + j + ANS);
+      RV[j] = row_load(vpool, k0 + j + ANS);
+      __builtin_amdgcn_sched_barrier(0);
     }
-    bar();
-    // chunk max and running-max update, one wave per head
-    const int nch = ce - cs;
-    for (int h = wave; h < G; h += NW) {
-      float mx = -INFINITY;
-      for (int i = lane; i < nch; i += 64) mx = fmaxf(mx, scores[h * CHUNK + i]);
-      mx = wave_max(mx);
-      const float m_old = ctl->m_run[h];
-      const float m_new = fmaxf(m_old, mx);
-      float sum = 0.f;
-      for (int i = lane; i < nch; i += 64) {
-        const float e = expf(scores[h * CHUNK + i] - m_new);
-        scores[h * CHUNK + i] = e;
-        sum += e;
-      }
-      sum = wave_sum(sum);
-      if (lane == 0) {
-        const float sc = (m_old == -INFINITY) ? 0.f : expf(m_old - m_new);
-        ctl->scale[h] = sc;
-        ctl->l_run[h] = ctl->l_run[h] * sc + sum;
-        ctl->m_run[h] = m_new;
-      }
-    }
-    bar();
+  }
+  // the part's page entries, checked once (the stream clamped them into the pool)
+  for (int bi = (c0 >> 4) + tid; bi < ((ce + 15) >> 4); bi += NT) {
+    const int b = ptab[bi];
+    if (b < 0 || b >= p.num_blocks) raise_error(p, ERR_PAGE, (uint32_t)s, (uint32_t)b);
+  }
+  if (cur && wave == 0) {  // the current position: lane c's 8 dims are words 4c..4c+3 of each row
+    const v4u kq = *(const v4u*)(kvc + 4 * c), vq = *(const v4u*)(kvc + DH / 2 + 4 * c);
+    float sq[GMAX];
+    attn_scores<DH, GMAX>(kq, pg == 0, G, qr, sq);
+    attn_rescale<GMAX>(G, sq, mr, lr, orr);
+    attn_accum<GMAX>(vq, G, sq, mr, lr, orr);
+  }
+  // merge the wave's lane groups, then the waves
+#pragma unroll
+  for (int off = LPP; off < 64; off <<= 1) {
 #pragma unroll
     for (int h = 0; h < GMAX; ++h) {
       if (h >= G) break;
-      const float sc = ctl->scale[h];
+      const float m2 = __shfl_xor(mr[h], off), l2 = __shfl_xor(lr[h], off);
+      const float mx = fmaxf(mr[h], m2), e1 = __expf(mr[h] - mx), e2 = __expf(m2 - mx);
+      lr[h] = lr[h] * e1 + l2 * e2;
 #pragma unroll
-      for (int e = 0; e < 8; ++e) oacc[h][e] *= sc;
+      for (int e = 0; e < 8; ++e) orr[h][e] = orr[h][e] * e1 + __shfl_xor(orr[h][e], off) * e2;
+      mr[h] = mx;
     }
-    // o += p * v
+  }
+  if (pg == 0) {
 #pragma unroll
-    for (int i = 0; i < ASLOTS; ++i) {
-      const int pp = cs + (i * NW + wave) * PPW + pg;
-      if (pp < ce) {
-        const v4u vv = vb[(i * NW + wave) * 64 + lane];
-        const float vf[8] = {bf_lo(vv.x), bf_hi(vv.x), bf_lo(vv.y), bf_hi(vv.y), bf_lo(vv.z), bf_hi(vv.z), bf_lo(vv.w), bf_hi(vv.w)};
+    for (int h = 0; h < GMAX; ++h) {
+      if (h >= G) break;
+      float* wb = wbuf + (wave * G + h) * (DH + 2);
+      if (c == 0) {
+        wb[0] = mr[h];
+        wb[1] = lr[h];
+      }
 #pragma unroll
-        for (int h = 0; h < GMAX; ++h) {
-          if (h >= G) break;
-          const float pw = scores[h * CHUNK + (pp - cs)];
+      for (int e = 0; e < 8; ++e) wb[2 + c * 8 + e] = orr[h][e];
+    }
+  }
+  bar();
 #pragma unroll
-          for (int e = 0; e < 8; ++e) oacc[h][e] = fmaf(pw, vf[e], oacc[h][e]);
+  for (int e = 0; e < EPT; ++e) {
+    const int i = min(tid + e * NT, G * DH - 1), h = i / DH, dd = i % DH;
+    float M = -1e30f;
+    for (int w = 0; w < NW; ++w) M = fmaxf(M, wbuf[(w * G + h) * (DH + 2)]);
+    float L = 0.f, A = 0.f;
+    for (int w = 0; w < NW; ++w) {
+      const float* wb = wbuf + (w * G + h) * (DH + 2);
+      const float f = __expf(wb[0] - M);
+      L = fmaf(wb[1], f, L);
+      A = fmaf(wb[2 + dd], f, A);
+    }
+    Mo[e] = M;
+    Lo[e] = L;
+    Ao[e] = A;
+  }
+}
+
+template <int DH, int GMAX, int ANS>
+__device__ __forceinline__ void task_attn(const KernelParams& p, const TaskDesc& t, float* lds, Ctl* ctl,
+                                          uint16_t* const* pools) {
+  using AS = AttnShape<DH, GMAX>;
+  constexpr int EPT = AS::EPT;
+  int tid = threadIdx.x;
+  asm volatile("" : "+v"(tid));
+  const int T = p.attn_tasks, ti = t.a2, W = ctl->aoff[16];
+  const int G = p.hq / p.hk, l = t.layer;
+  const uint32_t ep = p.epoch, what = (uint32_t)t.wait_ev;
+  const int lo = attn_lo(W, T, ti), hi = attn_lo(W, T, ti + 1);
+  // this task's partial slots: [2][G][DH + 2] words (m, l, unnormalised o)
+  auto part_base = [&](int task, int slot) { return p.pt + (((size_t)l * T + task) * 2 + slot) * G * (DH + 2); };
+  auto seg_start = [&](int x) {  // first block of the segment holding block x
+    int s = 0;
+    while (s < 15 && ctl->aoff[s + 1] <= x) ++s;
+    return ctl->aoff[s] + (x - ctl->aoff[s]) / ctl->anb[s] * ctl->anb[s];
+  };
+  // When the task's last segment goes on past it, that partial is computed and written first: partials
+  // never wait on merges, so a merge waits at most for its writers' streaming, never for a chain of
+  // other merges.
+  const int b_last = hi > lo ? max(lo, seg_start(hi - 1)) : hi;
+  int s_last = 0;
+  while (hi > lo && s_last < 15 && ctl->aoff[s_last + 1] <= hi - 1) ++s_last;
+  const bool last_partial = hi > lo && seg_start(hi - 1) + ctl->anb[s_last] > hi;
+  for (int k = 0, x = last_partial ? b_last : lo; x < hi; ++k) {
+    // the segment holding block x
+    int s = 0;
+    while (s < 15 && ctl->aoff[s + 1] <= x) ++s;
+    const int nb = ctl->anb[s], grp = (x - ctl->aoff[s]) / nb, B = ctl->aoff[s] + grp * nb, E = B + nb;
+    const int xe = min(hi, E);
+    int pos = ctl->ctx[s];
+    const bool ok = pos >= 0 && pos < p.max_pos;
+    if (!ok && tid == 0 && x == B) raise_error(p, ERR_CTX, (uint32_t)s, (uint32_t)pos);
+    const int c0 = ok ? 16 * (x - B) : 0, c1 = ok ? min(16 * (xe - B), pos + 1) : 0;
+    if (!ok) pos = -1;
+    float M[EPT], L[EPT], A[EPT];
+    attn_part<DH, GMAX, ANS>(p, t, lds, ctl, pools, s, grp, pos, c0, c1, M, L, A);
+    if (xe < E) {  // the segment goes on in later tasks: this task's partial
+      uint64_t* pb = part_base(ti, x == lo ? 0 : 1);
+#pragma unroll
+      for (int e = 0; e < EPT; ++e) {
+        const int i = tid + e * NT;
+        if (i < G * DH) {
+          const int h = i / DH, dd = i % DH;
+          if (dd == 0) {
+            st_tagf(&pb[h * (DH + 2)], M[e], ep);
+            st_tagf(&pb[h * (DH + 2) + 1], L[e], ep);
+          }
+          st_tagf(&pb[h * (DH + 2) + 2 + dd], A[e], ep);
         }
       }
-    }
-  }
-  // reduce o over the position groups of each wave, then over waves
+    } else {
+      // This task holds the segment's last block: merge the earlier tasks' partials in task order,
+      // then its own, R tasks per poll round (3 words per task and element: m, l, o[dim]).
+      const int first = attn_task_of(W, T, B);
+      float Mm[EPT], Lm[EPT], Am[EPT];
 #pragma unroll
-  for (int h = 0; h < GMAX; ++h)
+      for (int e = 0; e < EPT; ++e) {
+        Mm[e] = -1e30f;
+        Lm[e] = 0.f;
+        Am[e] = 0.f;
+      }
+      constexpr int R = 8 / EPT;
+      int hb[EPT], ob[EPT];  // byte offsets of the element's head row: m at +0, l at +8, o[dim] at +(2 + dim) 8
 #pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      float v = oacc[h][e];
-      for (int off = LPP; off < 64; off <<= 1) v += __shfl_xor(v, off);
-      oacc[h][e] = v;
-    }
-  if (pg == 0)
-#pragma unroll
-    for (int h = 0; h < GMAX; ++h) {
-      if (h >= G) break;
-#pragma unroll
-      for (int e = 0; e < 8; ++e) obuf[(wave * G + h) * DH + c * 8 + e] = oacc[h][e];
-    }
-  bar();
-  // The split's partial (m, l and the unnormalised o of each of its G heads) goes out tagged, except
-  // from the merging split (the last), which keeps its own in registers and polls for the others'.
-  const bool merger = (j == splits - 1);
-  const uint32_t ep = p.epoch;
-  uint64_t* pgrp = p.pt + ((((size_t)t.layer * p.max_seqs + s) * p.hq + h0) * splits) * (DH + 2);  // [G][splits][DH+2]
-  constexpr int EPT = (GMAX * DH + NT - 1) / NT;  // output elements per thread
-  float own[EPT];
-  int eh[EPT];
-#pragma unroll
-  for (int e = 0; e < EPT; ++e) {
-    const int i = tid + e * NT;
-    own[e] = 0.f;
-    eh[e] = 0;
-    if (i < G * DH) {
-      const int h = i / DH, dd = i % DH;
-      float v = 0.f;
-      for (int w = 0; w < NW; ++w) v += obuf[(w * G + h) * DH + dd];
-      own[e] = v;
-      eh[e] = h;
-      if (active && !merger) st_tagf(&pgrp[((size_t)h * splits + j) * (DH + 2) + 2 + dd], v, ep);
-    }
-  }
-  if (active && !merger && tid < G) {
-    st_tagf(&pgrp[((size_t)tid * splits + j) * (DH + 2) + 0], ctl->m_run[tid], ep);
-    st_tagf(&pgrp[((size_t)tid * splits + j) * (DH + 2) + 1], ctl->l_run[tid], ep);
-  }
-  if (!merger) return;
-  // Log-sum-exp merge in split order, R splits per poll round (3 words per split and element:
-  // m, l and o[dd]). The group's output is written (tagged) even for an inactive sequence, as zeros.
-  constexpr int R = 8 / EPT;
-  float M[EPT], Ls[EPT], A[EPT];
-#pragma unroll
-  for (int e = 0; e < EPT; ++e) {
-    M[e] = -INFINITY;
-    Ls[e] = 0.f;
-    A[e] = 0.f;
-  }
-  if (active) {
-    int hb[EPT], ob[EPT];  // byte offsets of the element's head row: m at +0, l at +8, o[dd] at +(2 + dd) 8
-#pragma unroll
-    for (int e = 0; e < EPT; ++e) {
-      const int i = min(tid + e * NT, G * DH - 1);
-      hb[e] = (i / DH) * splits * (DH + 2) * 8;
-      ob[e] = hb[e] + (2 + i % DH) * 8;
-    }
-    for (int j0 = 0; j0 < splits; j0 += R) {
-      uint32_t pend = 0;
-#pragma unroll
-      for (int e = 0; e < EPT; ++e)
-#pragma unroll
-        for (int r = 0; r < R; ++r)
-          if (tid + e * NT < G * DH && j0 + r < splits && j0 + r != j) pend |= 7u << ((e * R + r) * 3);
-      float mv[EPT][R], lv[EPT][R], ov[EPT][R];
-      poll_tagged<3 * R * EPT>(
-          p, pgrp,
-          [&](int k) {
-            const int e = k / (3 * R), c3 = k % 3;
-            return c3 == 2 ? ob[e] : hb[e] + c3 * 8;
-          },
-          [&](int k) { return (j0 + (k / 3) % R) * (DH + 2) * 8; }, pend, what,
-          [&](int k, uint32_t b) {
-            const int e = k / (3 * R), r = (k / 3) % R, c3 = k % 3;
-            const float f = __uint_as_float(b);
-            if (c3 == 0) mv[e][r] = f;
-            else if (c3 == 1) lv[e][r] = f;
-            else ov[e][r] = f;
-          });
-#pragma unroll
-      for (int e = 0; e < EPT; ++e)
+      for (int e = 0; e < EPT; ++e) {
+        const int i = min(tid + e * NT, G * DH - 1);
+        hb[e] = (i / DH) * (DH + 2) * 8;
+        ob[e] = hb[e] + (2 + i % DH) * 8;
+      }
+      for (int j0 = first; j0 < ti; j0 += R) {
+        uint32_t pend = 0;
 #pragma unroll
         for (int r = 0; r < R; ++r) {
-          const int jj = j0 + r;
-          if (tid + e * NT >= G * DH || jj >= splits) continue;
-          const float mk = jj == j ? ctl->m_run[eh[e]] : mv[e][r];
-          const float lk = jj == j ? ctl->l_run[eh[e]] : lv[e][r];
-          const float ok = jj == j ? own[e] : ov[e][r];
-          if (mk == -INFINITY) continue;
-          const float mn = fmaxf(M[e], mk);
-          const float a = (M[e] == -INFINITY) ? 0.f : expf(M[e] - mn), b = expf(mk - mn);
-          Ls[e] = Ls[e] * a + lk * b;
-          A[e] = A[e] * a + ok * b;
-          M[e] = mn;
+          const int j = j0 + r;
+          const bool live = j < ti && attn_lo(W, T, j) < attn_lo(W, T, j + 1);  // empty tasks wrote nothing
+#pragma unroll
+          for (int e = 0; e < EPT; ++e)
+            if (live && tid + e * NT < G * DH) pend |= 7u << ((e * R + r) * 3);
         }
+        float mv[EPT][R], lv[EPT][R], ov[EPT][R];
+        poll_tagged<3 * R * EPT>(
+            p, part_base(0, 0),
+            [&](int k) {
+              const int e = k / (3 * R), c3 = k % 3;
+              return c3 == 2 ? ob[e] : hb[e] + c3 * 8;
+            },
+            [&](int k) {
+              const int j = j0 + (k / 3) % R;
+              const int slot = (j == first && attn_lo(W, T, first) < B) ? 1 : 0;
+              return (int)((part_base(min(j, T - 1), slot) - part_base(0, 0)) * 8);
+            },
+            pend, what,
+            [&](int k, uint32_t b) {
+              const int e = k / (3 * R), r = (k / 3) % R, c3 = k % 3;
+              const float f = __uint_as_float(b);
+              if (c3 == 0) mv[e][r] = f;
+              else if (c3 == 1) lv[e][r] = f;
+              else ov[e][r] = f;
+            });
+#pragma unroll
+        for (int e = 0; e < EPT; ++e)
+#pragma unroll
+          for (int r = 0; r < R; ++r) {
+            const int j = j0 + r;
+            if (!(j < ti && attn_lo(W, T, j) < attn_lo(W, T, j + 1)) || tid + e * NT >= G * DH) continue;
+            const float mn = fmaxf(Mm[e], mv[e][r]);
+            const float a = __expf(Mm[e] - mn), b = __expf(mv[e][r] - mn);
+            Lm[e] = Lm[e] * a + lv[e][r] * b;
+            Am[e] = Am[e] * a + ov[e][r] * b;
+            Mm[e] = mn;
+          }
+      }
+      uint64_t* od = ot_at(p, l, s) + (size_t)grp * G * DH;
+#pragma unroll
+      for (int e = 0; e < EPT; ++e) {
+        const int i = tid + e * NT;
+        if (i >= G * DH) continue;
+        const float mn = fmaxf(Mm[e], M[e]);
+        const float a = __expf(Mm[e] - mn), b = __expf(M[e] - mn);
+        const float Lt = Lm[e] * a + L[e] * b, At = Am[e] * a + A[e] * b;
+        st_tagf(&od[i], ok ? At / Lt : 0.f, ep);
+      }
+    }
+    bar();  // the next part reuses the LDS staging
+    // after the leading partial, go back to the start of the range; stop before the partial's blocks
+    if (last_partial && k == 0) {
+      if (b_last == lo) break;
+      x = lo;
+    } else {
+      x = xe;
+      if (last_partial && x >= b_last) break;
     }
   }
-  uint64_t* od = ot_at(p, t.layer, s) + (size_t)h0 * DH;
-#pragma unroll
-  for (int e = 0; e < EPT; ++e)
-    if (tid + e * NT < G * DH) st_tagf(&od[tid + e * NT], active ? A[e] / Ls[e] : 0.f, ep);
 }
 
 // ----------------------------------------------------------------------------- argmax keys
@@ -1077,7 +1135,11 @@ __device__ __forceinline__ int pos_any(const KernelParams& p, const Ctl* ctl, in
 __device__ __forceinline__ void gemv_task_b(const KernelParams& p, const TaskDesc& t, float* lds, Ctl* ctl,
                                             uint16_t* const* pools) {
   WPipe wp;  // task-local: no weight loads are carried into the next task
-  const int type = t.type, l = t.layer, tid = threadIdx.x, lane = tid & 63;
+  // The thread index made opaque per task: per-lane offsets are computed here rather than hoisted out of
+  // the task loop and held in registers through every other task.
+  int tid = threadIdx.x;
+  asm volatile("" : "+v"(tid));
+  const int type = t.type, l = t.layer, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const uint32_t ep = p.epoch, what = (uint32_t)t.wait_ev;
   const int nact = min(p.n_active, p.max_seqs);
@@ -1110,11 +1172,8 @@ __device__ __forceinline__ void gemv_task_b(const KernelParams& p, const TaskDes
   // Input staging. Thread (wave w, lane) holds sequences 2w and 2w + 1, columns 64 c + lane of the
   // block (c < 16): each load is a coalesced 512-byte row of one sequence's tagged words. The loads are
   // unconditional and bounded by their buffer's size (out-of-range loads return zero), so all of them
-  // issue together; only the words of active sequences inside K are polled. `ln` is the lane index
-  // made opaque per task, so that per-lane offsets are not hoisted out of the task loop and held in
-  // registers across every task.
-  int ln = lane;
-  asm volatile("" : "+v"(ln));
+  // issue together; only the words of active sequences inside K are polled.
+  const int ln = lane;
   const int s0 = 2 * wave;
   float ss[2] = {0.f, 0.f};
   uint64_t xw[32];  // the words in flight; once current, their low halves are the inputs
@@ -1441,12 +1500,25 @@ __global__ __launch_bounds__(NT, 1) void mk_megakernel(KernelParams p) {
     pools[p.n_layers + i] = p.vpool[i];
   }
   // context lengths change only at the end of the step (the argmax task), after every reader
-  if (threadIdx.x < 16) ctl->ctx[threadIdx.x] = (int)threadIdx.x < p.max_seqs ? p.ctx_lens[threadIdx.x] : 0;
+  if (threadIdx.x < 16) {
+    const int s = threadIdx.x;
+    const int pos = s < p.max_seqs ? p.ctx_lens[s] : 0;
+    ctl->ctx[s] = pos;
+    // an active sequence attends to blocks 0 .. pos / 16 (one block when its position is out of range:
+    // the task holding it reports the error and writes zeros)
+    ctl->anb[s] = s < min(p.n_active, p.max_seqs) ? ((pos >= 0 && pos < p.max_pos) ? (pos >> 4) + 1 : 1) : 0;
+  }
   // Stage the queue's descriptors in LDS: a task switch then costs an LDS read instead of two
   // dependent scalar loads from memory on the path between one task's publish and the next wait.
   for (int i = threadIdx.x; i < (q1 - q0) * 16; i += NT) {
     const int k = i >> 4, w = i & 15;
     ((int32_t*)&tq[k])[w] = ((const int32_t*)&p.tasks[p.queue_idx[q0 + k]])[w];
+  }
+  bar();
+  if (threadIdx.x < 17) {  // first block of sequence s's segments: hk segments per earlier sequence
+    int o = 0;
+    for (int s = 0; s < (int)threadIdx.x; ++s) o += ctl->anb[s];
+    ctl->aoff[threadIdx.x] = o * p.hk;
   }
   bar();
   WPipe wp;
@@ -1461,12 +1533,11 @@ __global__ __launch_bounds__(NT, 1) void mk_megakernel(KernelParams p) {
       ctl->t_ready = t_queue;
     }
     // Each task starts its own input streams before it polls for its inputs (they do not depend on
-    // them): an attention split stages its first keys and values, a GEMV its first weight units.
-    // The staging is issued inside the attention branch, so the compiler's wait insertion never sees
-    // an LDS DMA that might be pending on the GEMV path.
+    // them): an attention task its first keys and values, a GEMV its first weight units.
     if (t.type == T_ATTN) {
-      attn_prefetch<DH>(p, t, ctl, pools, lds);
-      task_attn<DH, GMAX>(p, t, lds, ctl, pools);
+      // position groups in flight per wave: more for batches (long streams), fewer for one sequence
+      // and for many heads per KV head (register budget)
+      task_attn<DH, GMAX, (GMAX > 4 || !BATCHED) ? 4 : 8>(p, t, lds, ctl, pools);
     } else if (t.type == T_ARGMAX) {
       if (t.wait_ev >= 0) wait_event(p, t, ctl);
       if (p.trace && threadIdx.x == 0) ctl->t_ready = __builtin_amdgcn_s_memrealtime();
