@@ -619,11 +619,22 @@ __device__ __forceinline__ void attn_part(const KernelParams& p, const TaskDesc&
   const uint16_t* kpool = pools[l];
   const uint16_t* vpool = pools[p.n_layers + l];
   const int32_t* ptab = p.page_table + (size_t)s * p.max_blocks;
+  // The page entries of the wave's groups pbase .. pbase + 63 sit one per lane (lane i: group pbase + i),
+  // loaded a window at a time; a group's entry is then a lane read, not a memory load inside the stream
+  // (a load there would make the in-order wait drain every key and value load in flight).
+  int pbase = 0, pent = 0;
+  auto load_pages = [&](int base) {
+    pbase = base;
+    const int k = min(base + lane, max(nw - 1, 0));
+    pent = nw > 0 ? min(max(ptab[(c0 + (wave + NW * k) * PPW) >> 4], 0), p.num_blocks - 1) : 0;
+  };
+  load_pages(0);
   auto row_load = [&](const uint16_t* pool, int k) {
     size_t off = (size_t)c * 8;  // no cached rows: a dummy row, block 0
     if (nw > 0) {
-      const int p0g = c0 + (wave + NW * min(k, nw - 1)) * PPW;
-      const int b = min(max(ptab[p0g >> 4], 0), p.num_blocks - 1);
+      const int kk = min(k, nw - 1);
+      const int p0g = c0 + (wave + NW * kk) * PPW;
+      const int b = __builtin_amdgcn_readlane(pent, kk - pbase);
       off = (((size_t)b * p.hk + grp) * 16 + (min(p0g + pg, ce - 1) & 15)) * DH + c * 8;
     }
     return __builtin_nontemporal_load((const v4u*)(pool + off));
@@ -675,11 +686,12 @@ __device__ __forceinline__ void attn_part(const KernelParams& p, const TaskDesc&
     qr[h][0] = qa.x; qr[h][1] = qa.y; qr[h][2] = qa.z; qr[h][3] = qa.w;
     qr[h][4] = qb.x; qr[h][5] = qb.y; qr[h][6] = qb.z; qr[h][7] = qb.w;
   }
-  // Slot j holds group k0 + j; it is refilled with group k0 + j + ANS once consumed. Refills past the
-  // wave's groups re-read its last group (and weigh 0). The running max moves only when a score passes
+  // Slot j holds group k0 + j; it is refilled with group k0 + j + ANS once consumed. Slots past the
+  // wave's groups weigh 0. The running max moves only when a score passes
   // it by more than 8: until then exp(s - m) stays below e^8, far inside fp32, and the sums need no
   // rescaling (the result is the same ratio).
   for (int k0 = 0; k0 < nw; k0 += ANS) {
+    if (k0 + 2 * ANS > pbase + 64) load_pages(k0);  // this round's refills need groups up to k0 + 2 ANS - 1
 #pragma unroll
     for (int j = 0; j < ANS; ++j) {
       const int pp = c0 + (wave + NW * (k0 + j)) * PPW + pg;
@@ -691,8 +703,10 @@ __device__ __forceinline__ void attn_part(const KernelParams& p, const TaskDesc&
         if (h < G) up = up || sc[h] > mr[h] + 8.f;
       if (__builtin_expect(__any(up), 0)) attn_rescale<GMAX>(G, sc, mr, lr, orr);
       attn_accum<GMAX>(RV[j], G, sc, mr, lr, orr);
-      RK[j] = row_load(kpool, k0 + j + ANS);
-      RV[j] = row_load(vpool, k0 + j + ANS);
+      if (k0 + j + ANS < nw) {  // no loads past the wave's groups: nothing is left in flight
+        RK[j] = row_load(kpool, k0 + j + ANS);
+        RV[j] = row_load(vpool, k0 + j + ANS);
+      }
       __builtin_amdgcn_sched_barrier(0);
     }
   }
@@ -761,7 +775,7 @@ __device__ __forceinline__ void task_attn(const KernelParams& p, const TaskDesc&
   constexpr int EPT = AS::EPT;
   int tid = threadIdx.x;
   asm volatile("" : "+v"(tid));
-  const int T = p.attn_tasks, ti = t.a2, W = ctl->aoff[16];
+  const int T = p.attn_tasks, ti = t.a2, W = __builtin_amdgcn_readfirstlane(ctl->aoff[16]);
   const int G = p.hq / p.hk, l = t.layer;
   const uint32_t ep = p.epoch, what = (uint32_t)t.wait_ev;
   const int lo = attn_lo(W, T, ti), hi = attn_lo(W, T, ti + 1);
@@ -770,7 +784,7 @@ __device__ __forceinline__ void task_attn(const KernelParams& p, const TaskDesc&
   auto seg_start = [&](int x) {  // first block of the segment holding block x
     int s = 0;
     while (s < 15 && ctl->aoff[s + 1] <= x) ++s;
-    return ctl->aoff[s] + (x - ctl->aoff[s]) / ctl->anb[s] * ctl->anb[s];
+    return __builtin_amdgcn_readfirstlane(ctl->aoff[s] + (x - ctl->aoff[s]) / ctl->anb[s] * ctl->anb[s]);
   };
   // When the task's last segment goes on past it, that partial is computed and written first: partials
   // never wait on merges, so a merge waits at most for its writers' streaming, never for a chain of
@@ -778,14 +792,17 @@ __device__ __forceinline__ void task_attn(const KernelParams& p, const TaskDesc&
   const int b_last = hi > lo ? max(lo, seg_start(hi - 1)) : hi;
   int s_last = 0;
   while (hi > lo && s_last < 15 && ctl->aoff[s_last + 1] <= hi - 1) ++s_last;
-  const bool last_partial = hi > lo && seg_start(hi - 1) + ctl->anb[s_last] > hi;
+  const bool last_partial = hi > lo && seg_start(hi - 1) + __builtin_amdgcn_readfirstlane(ctl->anb[s_last]) > hi;
   for (int k = 0, x = last_partial ? b_last : lo; x < hi; ++k) {
-    // the segment holding block x
+    // the segment holding block x (values read from LDS are made explicitly wave-uniform, so that the
+    // page-table reads that depend on them are scalar loads)
     int s = 0;
     while (s < 15 && ctl->aoff[s + 1] <= x) ++s;
-    const int nb = ctl->anb[s], grp = (x - ctl->aoff[s]) / nb, B = ctl->aoff[s] + grp * nb, E = B + nb;
+    s = __builtin_amdgcn_readfirstlane(s);
+    const int nb = __builtin_amdgcn_readfirstlane(ctl->anb[s]), a0 = __builtin_amdgcn_readfirstlane(ctl->aoff[s]);
+    const int grp = (x - a0) / nb, B = a0 + grp * nb, E = B + nb;
     const int xe = min(hi, E);
-    int pos = ctl->ctx[s];
+    int pos = __builtin_amdgcn_readfirstlane(ctl->ctx[s]);
     const bool ok = pos >= 0 && pos < p.max_pos;
     if (!ok && tid == 0 && x == B) raise_error(p, ERR_CTX, (uint32_t)s, (uint32_t)pos);
     const int c0 = ok ? 16 * (x - B) : 0, c1 = ok ? min(16 * (xe - B), pos + 1) : 0;
