@@ -173,6 +173,7 @@ def main():
     ap.add_argument("--workload", default="llama8b")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--staged-steps", type=int, default=64, help="steps of the stage-sliced comparison run")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 1 GiB device-to-device copy 5 times (to scale HBM byte counters)")
     args = ap.parse_args()
@@ -245,6 +246,35 @@ def main():
     achieved = bytes_avg / (ms * 1e-3) / 1e9
     log("decode: %.4f ms/token, %.1f tok/s, %.1f GB/s (%.1f%% of %.0f GB/s)" %
         (ms, 1e3 / ms, achieved, 100 * achieved / rf.MI355X_HBM_PEAK_GBS, rf.MI355X_HBM_PEAK_GBS))
+    # The same steps as one dispatch per dependency stage (same kernel and graph): the stop-and-go
+    # execution the single launch replaces. Its extra time per token is the pass-to-pass cost removed.
+    n_stages = int(mk.mk_graph_stats(dec.ctx).n_stages)
+    Ks = min(K, args.staged_steps)
+    dec.set_ctx_lens([P])
+    tokens.copy_(g0)
+    torch.cuda.synchronize(dec.dev)
+    ev0.record(stream)
+    for _ in range(Ks):
+        dec.step_staged(tokens)
+    ev1.record(stream)
+    torch.cuda.synchronize(dec.dev)
+    ms_staged = ev0.elapsed_time(ev1) / Ks
+    dec.sync_check()
+    ms_fused_same = None
+    if Ks < K:  # the one-launch time over the same positions
+        dec.set_ctx_lens([P])
+        tokens.copy_(g0)
+        torch.cuda.synchronize(dec.dev)
+        ev0.record(stream)
+        for _ in range(Ks):
+            dec.step(tokens)
+        ev1.record(stream)
+        torch.cuda.synchronize(dec.dev)
+        ms_fused_same = ev0.elapsed_time(ev1) / Ks
+    else:
+        ms_fused_same = ms
+    log("staged: %.4f ms/token in %d dispatches (one launch: %.4f ms/token over the same %d steps)" %
+        (ms_staged, n_stages, ms_fused_same, Ks))
     dec.close()
 
     traffic = None
@@ -283,6 +313,12 @@ def main():
                      "traffic_unit": "HBM bytes/launch (FETCH_SIZE + WRITE_SIZE, copy-calibrated)",
                      "bytes_per_launch": int(bytes_avg), "kernel": "mk_megakernel (one launch per decode step)"},
         "cpu_baseline": cpu,
+        "pass_to_pass": {"stage_sliced_ms_per_token": round(ms_staged, 5), "dispatches_per_token": n_stages,
+                         "one_launch_ms_per_token": round(ms_fused_same, 5), "steps": Ks,
+                         "removed_ms_per_token": round(ms_staged - ms_fused_same, 5),
+                         "removed_us_per_boundary": round(1e3 * (ms_staged - ms_fused_same) / max(1, n_stages - 1), 3),
+                         "what": "the same kernel and task graph launched once per dependency stage (stop-and-go) "
+                                 "vs once per step"},
     }
     print(json.dumps(out), flush=True)
 

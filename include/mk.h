@@ -135,6 +135,17 @@ mk_status mk_load_weights(mk_ctx* ctx, const mk_tensor* ts, int n, void* stream)
  * synchronisation. n_seqs must be at most max_seqs. */
 mk_status mk_decode_step(mk_ctx* ctx, const int32_t* d_tokens_in, int n_seqs, int32_t* d_tokens_out, void* stream);
 
+/* The same decode step as mk_decode_step, launched as one kernel dispatch per dependency stage
+ * (QKV, attention, O projection, gate/up and down of each layer, then the LM head and the argmax):
+ * the same kernel, task graph and arithmetic, so the results are identical. Each dispatch runs only
+ * its stage's tasks, so a stage starts only after the previous one has fully drained. This is the
+ * operator-by-operator execution the persistent kernel replaces ("LLMs in einen MegaKernel
+ * kompilieren", the stop-and-go execution of kernel-per-operator frameworks); it exists to measure
+ * the pass-to-pass gaps that the single launch removes. Asynchronous, same arguments and errors as
+ * mk_decode_step; mk_graph_info.n_stages dispatches per step. */
+mk_status mk_decode_step_staged(mk_ctx* ctx, const int32_t* d_tokens_in, int n_seqs, int32_t* d_tokens_out,
+                                void* stream);
+
 /* Prefill by repeated decode steps: the n_tokens host tokens h_tokens run
  * through the step one position at a time, for sequence `seq` only. When
  * d_token_out is not NULL, it receives the greedy token after the last
@@ -178,6 +189,7 @@ typedef struct {
   int64_t n_tasks, n_events, n_flag_slots, n_attn_groups, max_queue_len;
   int64_t weight_bytes, lds_bytes;
   uint64_t hash;
+  int64_t n_stages; /* dependency stages: the dispatches of mk_decode_step_staged */
 } mk_graph_info;
 mk_status mk_graph_stats(const mk_ctx* ctx, mk_graph_info* out);
 mk_status mk_graph_validate(const mk_ctx* ctx);

@@ -46,11 +46,11 @@ class mk_tensor(ctypes.Structure):
 class mk_graph_info(ctypes.Structure):
     _fields_ = [("n_tasks", ctypes.c_int64), ("n_events", ctypes.c_int64), ("n_flag_slots", ctypes.c_int64),
                 ("n_attn_groups", ctypes.c_int64), ("max_queue_len", ctypes.c_int64), ("weight_bytes", ctypes.c_int64),
-                ("lds_bytes", ctypes.c_int64), ("hash", ctypes.c_uint64)]
+                ("lds_bytes", ctypes.c_int64), ("hash", ctypes.c_uint64), ("n_stages", ctypes.c_int64)]
 
 
 EXPORTS = ["mk_create", "mk_create_host", "mk_workspace_size", "mk_bind_memory", "mk_load_weights", "mk_decode_step",
-           "mk_prefill", "mk_read_logits", "mk_sync_check", "mk_graph_stats", "mk_graph_validate",
+           "mk_decode_step_staged", "mk_prefill", "mk_read_logits", "mk_sync_check", "mk_graph_stats", "mk_graph_validate",
            "mk_graph_simulate", "mk_set_trace", "mk_destroy", "mk_status_str", "mk_last_error"]
 
 
@@ -83,6 +83,7 @@ def lib():
             "mk_bind_memory": [vp, vp, ctypes.POINTER(vp), ctypes.POINTER(vp), vp, vp, vp, vp],
             "mk_load_weights": [vp, ctypes.POINTER(mk_tensor), ctypes.c_int, vp],
             "mk_decode_step": [vp, vp, ctypes.c_int, vp, vp],
+            "mk_decode_step_staged": [vp, vp, ctypes.c_int, vp, vp],
             "mk_prefill": [vp, ctypes.c_int, ctypes.POINTER(i32), ctypes.c_int, vp, vp],
             "mk_read_logits": [vp, ctypes.c_int, ctypes.POINTER(ctypes.c_float), sz, vp],
             "mk_sync_check": [vp, vp],
@@ -159,6 +160,10 @@ def mk_load_weights(ctx, named: dict, stream=None):
 
 def mk_decode_step(ctx, tokens_in, n_seqs, tokens_out, stream=None):
     _check(lib().mk_decode_step(ctx, _vp(tokens_in), n_seqs, _vp(tokens_out), _vp(stream)))
+
+
+def mk_decode_step_staged(ctx, tokens_in, n_seqs, tokens_out, stream=None):
+    _check(lib().mk_decode_step_staged(ctx, _vp(tokens_in), n_seqs, _vp(tokens_out), _vp(stream)))
 
 
 def mk_prefill(ctx, seq, tokens, token_out=None, stream=None):
@@ -267,6 +272,11 @@ class Decoder:
     def step(self, tokens_in, n_seqs=1, tokens_out=None):
         mk_decode_step(self.ctx, tokens_in, n_seqs, tokens_out if tokens_out is not None else tokens_in,
                        self.stream_ptr())
+
+    def step_staged(self, tokens_in, n_seqs=1, tokens_out=None):
+        """The same step as one kernel dispatch per dependency stage (to measure pass-to-pass gaps)."""
+        mk_decode_step_staged(self.ctx, tokens_in, n_seqs, tokens_out if tokens_out is not None else tokens_in,
+                              self.stream_ptr())
 
     def read_logits(self, seq=0):
         return mk_read_logits(self.ctx, seq, self.cfg.vocab, self.stream_ptr())

@@ -176,13 +176,29 @@ KernelParams make_params(mk_ctx* c) {
   return p;
 }
 
-mk_status launch_step(mk_ctx* c, const int32_t* tin, int n_active, int32_t* tout, hipStream_t st) {
+// One decode step: one launch over the whole task graph, or (staged) one launch per dependency
+// stage, in order, each running only that stage's tasks with the same kernel and step epoch.
+mk_status launch_step(mk_ctx* c, const int32_t* tin, int n_active, int32_t* tout, hipStream_t st, bool staged = false) {
   KernelParams p = make_params(c);
   p.tokens_in = tin;
   p.tokens_out = tout;
   p.n_active = n_active;
   p.epoch = ++c->epoch;
-  HIPCHK(launch_megakernel(p, c->g.n_cus, (size_t)c->g.lds_bytes, st));
+  if (!staged) {
+    p.task_lo = 0;
+    p.task_hi = (int32_t)c->g.tasks.size();
+    HIPCHK(launch_megakernel(p, c->g.n_cus, (size_t)c->g.lds_bytes, st));
+    return MK_OK;
+  }
+  const auto& t = c->g.tasks;
+  for (size_t a = 0; a < t.size();) {
+    size_t b = a + 1;
+    while (b < t.size() && t[b].type == t[a].type && t[b].layer == t[a].layer) ++b;
+    p.task_lo = (int32_t)a;
+    p.task_hi = (int32_t)b;
+    HIPCHK(launch_megakernel(p, c->g.n_cus, (size_t)c->g.lds_bytes, st));
+    a = b;
+  }
   return MK_OK;
 }
 }  // namespace
@@ -371,6 +387,14 @@ mk_status mk_decode_step(mk_ctx* c, const int32_t* d_tokens_in, int n_seqs, int3
   return launch_step(c, d_tokens_in, n_seqs, d_tokens_out, (hipStream_t)stream);
 }
 
+mk_status mk_decode_step_staged(mk_ctx* c, const int32_t* d_tokens_in, int n_seqs, int32_t* d_tokens_out, void* stream) {
+  if (!c || !d_tokens_in || !d_tokens_out) return fail(MK_ERR_INVALID_ARG, "null argument");
+  if (!c->bound || !c->loaded) return fail(MK_ERR_STATE, "bind memory and load weights before decoding");
+  if (n_seqs < 1 || n_seqs > c->g.cfg.max_seqs) return fail(MK_ERR_INVALID_ARG, "n_seqs out of range");
+  DeviceGuard dg(c->device);
+  return launch_step(c, d_tokens_in, n_seqs, d_tokens_out, (hipStream_t)stream, true);
+}
+
 mk_status mk_prefill(mk_ctx* c, int seq, const int32_t* h_tokens, int n_tokens, int32_t* d_token_out, void* stream) {
   if (!c || (!h_tokens && n_tokens > 0) || n_tokens < 0) return fail(MK_ERR_INVALID_ARG, "null argument");
   if (!c->bound || !c->loaded) return fail(MK_ERR_STATE, "bind memory and load weights before prefill");
@@ -435,6 +459,10 @@ mk_status mk_graph_stats(const mk_ctx* c, mk_graph_info* out) {
   out->weight_bytes = g.wl.packed_bytes;
   out->lds_bytes = g.lds_bytes;
   out->hash = graph_hash(g);
+  int64_t stages = 0;
+  for (size_t a = 0; a < g.tasks.size(); ++a)
+    if (a == 0 || g.tasks[a].type != g.tasks[a - 1].type || g.tasks[a].layer != g.tasks[a - 1].layer) ++stages;
+  out->n_stages = stages;
   return MK_OK;
 }
 

@@ -375,6 +375,8 @@ std::string build_graph(const mk_model_config& c, int n_cus, HostGraph& g) {
     // the writers of the attention output.
     const int T = std::min(S * hk * g.splits, n_cus);  // the cut is balanced: one task per CU suffices
     g.attn_tasks = T;
+    // the device cuts the step's blocks with 32-bit products (blocks x tasks)
+    if ((int64_t)S * hk * c.max_blocks_per_seq * T >= ((int64_t)1 << 32)) return "too many KV blocks x attention tasks";
     const int ev_att = b.new_event(T);
     // CUs running attention get no O-projection task in the same layer when they are few: their
     // register pipelines sit idle through attention, while the other CUs hold their O tiles there.
@@ -548,10 +550,10 @@ std::string build_graph(const mk_model_config& c, int n_cus, HostGraph& g) {
   int max_q = 0;
   for (int cu = 0; cu < n_cus; ++cu) max_q = std::max(max_q, g.queue_off[cu + 1] - g.queue_off[cu]);
   g.max_queue = max_q;
-  // control block + pool pointers + this CU's task descriptors + the larger of the GEMV and
-  // attention working sets
+  // control block + pool pointers + this CU's task descriptors + the attention tasks' first blocks +
+  // the larger of the GEMV and attention working sets
   g.lds_bytes = 1024 + align_up((int64_t)2 * L * 8, 256) + align_up((int64_t)max_q * (int64_t)sizeof(TaskDesc), 256) +
-                align_up(std::max(gemv_lds, attn_lds), 256);
+                align_up((int64_t)(g.attn_tasks + 1) * 4, 256) + align_up(std::max(gemv_lds, attn_lds), 256);
   if (g.lds_bytes > 160 * 1024) return "working set exceeds 160 KB of LDS";
   return "";
 }

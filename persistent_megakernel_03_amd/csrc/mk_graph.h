@@ -141,6 +141,7 @@ struct KernelParams {
   uint32_t watchdog_ticks;    // s_memrealtime ticks (100 MHz) a wait may spin before the kernel aborts
   int32_t max_queue;          // longest per-CU queue (its descriptors are staged in LDS)
   int32_t attn_tasks;         // attention tasks per layer (they cut the layer's KV blocks evenly)
+  int32_t task_lo, task_hi;   // this launch runs the tasks [task_lo, task_hi) of the global order
   TraceRec* trace;            // per-task timestamps of the last step, or nullptr
 };
 

@@ -517,10 +517,11 @@ struct AttnShape {
 };
 
 // First block of attention task i's range: T tasks cut W blocks evenly.
-__device__ __forceinline__ int attn_lo(int W, int T, int i) { return (int)((int64_t)W * i / T); }
-// The task whose range holds block x: the last i with attn_lo(i) <= x.
+// (W * i / T for i = 0..T is tabulated in LDS once per launch: alo[i].)
+__device__ __forceinline__ int attn_lo_of(int W, int T, int i) { return (int)((uint32_t)W * (uint32_t)i / (uint32_t)T); }
+// The task whose range holds block x: the last i with alo[i] <= x.
 __device__ __forceinline__ int attn_task_of(int W, int T, int x) {
-  return min(T - 1, (int)(((int64_t)(x + 1) * T - 1) / W));
+  return min(T - 1, (int)(((uint32_t)(x + 1) * (uint32_t)T - 1u) / (uint32_t)W));
 }
 
 // DPP moves within a row of 16 lanes: swap pairs, swap pairs of pairs, mirror within 8, mirror within 16.
@@ -770,7 +771,7 @@ __device__ __forceinline__ void attn_part(const KernelParams& p, const TaskDesc&
 
 template <int DH, int GMAX, int ANS>
 __device__ __forceinline__ void task_attn(const KernelParams& p, const TaskDesc& t, float* lds, Ctl* ctl,
-                                          uint16_t* const* pools) {
+                                          uint16_t* const* pools, const int32_t* alo) {
   using AS = AttnShape<DH, GMAX>;
   constexpr int EPT = AS::EPT;
   int tid = threadIdx.x;
@@ -778,7 +779,7 @@ __device__ __forceinline__ void task_attn(const KernelParams& p, const TaskDesc&
   const int T = p.attn_tasks, ti = t.a2, W = __builtin_amdgcn_readfirstlane(ctl->aoff[16]);
   const int G = p.hq / p.hk, l = t.layer;
   const uint32_t ep = p.epoch, what = (uint32_t)t.wait_ev;
-  const int lo = attn_lo(W, T, ti), hi = attn_lo(W, T, ti + 1);
+  const int lo = __builtin_amdgcn_readfirstlane(alo[ti]), hi = __builtin_amdgcn_readfirstlane(alo[ti + 1]);
   // this task's partial slots: [2][G][DH + 2] words (m, l, unnormalised o)
   auto part_base = [&](int task, int slot) { return p.pt + (((size_t)l * T + task) * 2 + slot) * G * (DH + 2); };
   auto seg_start = [&](int x) {  // first block of the segment holding block x
@@ -842,16 +843,23 @@ __device__ __forceinline__ void task_attn(const KernelParams& p, const TaskDesc&
         hb[e] = (i / DH) * (DH + 2) * 8;
         ob[e] = hb[e] + (2 + i % DH) * 8;
       }
+      // the first contributing task holds the segment as its last part (slot 1) when it starts before it
+      const int slot_first = __builtin_amdgcn_readfirstlane(alo[first]) < B ? 1 : 0;
+      const int task_words = 2 * G * (DH + 2);
       for (int j0 = first; j0 < ti; j0 += R) {
-        uint32_t pend = 0;
+        uint32_t live = 0;  // bit r: task j0 + r contributes (tasks with empty ranges wrote nothing)
 #pragma unroll
         for (int r = 0; r < R; ++r) {
           const int j = j0 + r;
-          const bool live = j < ti && attn_lo(W, T, j) < attn_lo(W, T, j + 1);  // empty tasks wrote nothing
+          if (j < ti && alo[min(j, T - 1)] < alo[min(j, T - 1) + 1]) live |= 1u << r;
+        }
+        live = __builtin_amdgcn_readfirstlane(live);
+        uint32_t pend = 0;
+#pragma unroll
+        for (int r = 0; r < R; ++r)
 #pragma unroll
           for (int e = 0; e < EPT; ++e)
-            if (live && tid + e * NT < G * DH) pend |= 7u << ((e * R + r) * 3);
-        }
+            if (((live >> r) & 1u) && tid + e * NT < G * DH) pend |= 7u << ((e * R + r) * 3);
         float mv[EPT][R], lv[EPT][R], ov[EPT][R];
         poll_tagged<3 * R * EPT>(
             p, part_base(0, 0),
@@ -861,8 +869,7 @@ __device__ __forceinline__ void task_attn(const KernelParams& p, const TaskDesc&
             },
             [&](int k) {
               const int j = j0 + (k / 3) % R;
-              const int slot = (j == first && attn_lo(W, T, first) < B) ? 1 : 0;
-              return (int)((part_base(min(j, T - 1), slot) - part_base(0, 0)) * 8);
+              return ((j - first) * task_words + (first * task_words + (j == first ? slot_first : 0) * G * (DH + 2))) * 8;
             },
             pend, what,
             [&](int k, uint32_t b) {
@@ -876,8 +883,7 @@ __device__ __forceinline__ void task_attn(const KernelParams& p, const TaskDesc&
         for (int e = 0; e < EPT; ++e)
 #pragma unroll
           for (int r = 0; r < R; ++r) {
-            const int j = j0 + r;
-            if (!(j < ti && attn_lo(W, T, j) < attn_lo(W, T, j + 1)) || tid + e * NT >= G * DH) continue;
+            if (!((live >> r) & 1u) || tid + e * NT >= G * DH) continue;
             const float mn = fmaxf(Mm[e], mv[e][r]);
             const float a = __expf(Mm[e] - mn), b = __expf(mv[e][r] - mn);
             Lm[e] = Lm[e] * a + lv[e][r] * b;
@@ -1507,9 +1513,15 @@ __global__ __launch_bounds__(NT, 1) void mk_megakernel(KernelParams p) {
   uint16_t** pools = (uint16_t**)(lds_raw + 1024);
   const size_t pools_bytes = ((size_t)2 * p.n_layers * sizeof(void*) + 255) & ~size_t(255);
   TaskDesc* tq = (TaskDesc*)(lds_raw + 1024 + pools_bytes);
-  float* lds = (float*)((unsigned char*)tq + (((size_t)p.max_queue * sizeof(TaskDesc) + 255) & ~size_t(255)));
+  // the attention tasks' first blocks for this step (W * i / T, i = 0..T), then the working set
+  int32_t* alo = (int32_t*)((unsigned char*)tq + (((size_t)p.max_queue * sizeof(TaskDesc) + 255) & ~size_t(255)));
+  float* lds = (float*)((unsigned char*)alo + (((size_t)(p.attn_tasks + 1) * 4 + 255) & ~size_t(255)));
   const int cu = blockIdx.x;
-  const int q0 = p.queue_off[cu], q1 = p.queue_off[cu + 1];
+  // This launch runs the tasks of global order [task_lo, task_hi) (the whole step, or one dependency
+  // stage in a stage-sliced launch): the contiguous part of this CU's queue inside that range.
+  int q0 = p.queue_off[cu], q1 = p.queue_off[cu + 1];
+  while (q0 < q1 && p.queue_idx[q0] < p.task_lo) ++q0;
+  while (q1 > q0 && p.queue_idx[q1 - 1] >= p.task_hi) --q1;
   if (threadIdx.x < G_COUNT * (int)(sizeof(GemvGeom) / 4))
     ((int32_t*)ctl->geoms)[threadIdx.x] = ((const int32_t*)p.geoms)[threadIdx.x];
   for (int i = threadIdx.x; i < p.n_layers; i += NT) {
@@ -1538,6 +1550,8 @@ __global__ __launch_bounds__(NT, 1) void mk_megakernel(KernelParams p) {
     ctl->aoff[threadIdx.x] = o * p.hk;
   }
   bar();
+  for (int i = threadIdx.x; i <= p.attn_tasks; i += NT) alo[i] = attn_lo_of(ctl->aoff[16], p.attn_tasks, i);
+  bar();
   WPipe wp;
   for (int qi = q0; qi < q1; ++qi) {
     const TaskDesc t = tq[qi - q0];
@@ -1554,7 +1568,7 @@ __global__ __launch_bounds__(NT, 1) void mk_megakernel(KernelParams p) {
     if (t.type == T_ATTN) {
       // position groups in flight per wave: more for batches (long streams), fewer for one sequence
       // and for many heads per KV head (register budget)
-      task_attn<DH, GMAX, (GMAX > 4 || !BATCHED) ? 4 : 8>(p, t, lds, ctl, pools);
+      task_attn<DH, GMAX, (GMAX > 4 || !BATCHED) ? 4 : 8>(p, t, lds, ctl, pools, alo);
     } else if (t.type == T_ARGMAX) {
       if (t.wait_ev >= 0) wait_event(p, t, ctl);
       if (p.trace && threadIdx.x == 0) ctl->t_ready = __builtin_amdgcn_s_memrealtime();

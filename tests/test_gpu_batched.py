@@ -91,3 +91,29 @@ def test_llama8b_sixteen_sequences():
     # configuration the benchmark times
     log("case: llama8b_b16 full size, 16 sequences, 1 step")
     run_batched(si.WORKLOADS["llama8b_b16"], 1)
+
+
+def test_mid_staged_launch_matches_fused():
+    # batched: one dispatch per dependency stage gives the same logits and tokens, bit for bit
+    import torch
+    wl = si.WORKLOADS["mid_b16"]
+    log("case: mid_b16 staged launch vs one launch")
+    a, om, ctx, table, w = prefilled_case(wl, 2)
+    om.close()
+    b, om2, _, _, _ = prefilled_case(wl, 2)
+    om2.close()
+    n = wl.n_seqs
+    toks = torch.as_tensor(si.first_tokens(wl), dtype=torch.int32)
+    for i in range(2):
+        a.tokens[:n] = toks
+        b.tokens[:n] = toks
+        oa = torch.zeros(n, dtype=torch.int32, device=a.dev)
+        ob = torch.zeros(n, dtype=torch.int32, device=b.dev)
+        a.step(a.tokens, n, oa)
+        b.step_staged(b.tokens, n, ob)
+        for s in range(n):
+            assert np.array_equal(a.read_logits(s), b.read_logits(s)), "step %d seq %d" % (i, s)
+        assert torch.equal(oa, ob)
+        toks = oa.cpu()
+    a.close()
+    b.close()

@@ -236,3 +236,27 @@ def test_llama8b_long_context_paged():
     assert max(rels) <= REL_L2_BAR
     assert int(dec.ctx_lens.item()) == int(ctx[0]) + n
     dec.close()
+
+
+def test_staged_launch_matches_fused(tiny):
+    # the same step as one dispatch per dependency stage: identical logits and tokens, bit for bit
+    import torch
+    w, prompt, wl = tiny
+    log("case: tiny staged launch vs one launch")
+    a, _ = make_gpu(si.TINY, w, 64)
+    b, _ = make_gpu(si.TINY, w, 64)
+    tok = int(prompt[0])
+    for i in range(12):
+        a.tokens[0] = tok
+        b.tokens[0] = tok
+        oa = torch.zeros(1, dtype=torch.int32, device=a.dev)
+        ob = torch.zeros(1, dtype=torch.int32, device=b.dev)
+        a.step(a.tokens, 1, oa)
+        b.step_staged(b.tokens, 1, ob)
+        la, lb = a.read_logits(0), b.read_logits(0)
+        assert np.array_equal(la, lb), "step %d: staged logits differ" % i
+        assert int(oa.item()) == int(ob.item())
+        tok = int(prompt[i + 1]) if i + 1 < len(prompt) else int(oa.item())
+    assert int(a.ctx_lens.item()) == int(b.ctx_lens.item()) == 12
+    a.close()
+    b.close()
