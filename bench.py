@@ -137,6 +137,9 @@ def bench_batched(args, wl):
         t0 = time.time()
         cpu = cpu_baseline_batched(wl, weights, args.cpu_seconds)
         log("cpu baseline: %.1f ms/token on %d cores (%.1fs)" % (cpu["value"], cpu["cores"], time.time() - t0))
+    traffic = None
+    if wl.name == "llama8b_b16":
+        traffic = rf.profiled_traffic(os.path.join(ROOT, "profiles", "mk_megakernel_llama8b_b16_decode.md"))
     out = {
         "metric": "decode ms/step (%d sequences, %s-shape bf16); achieved HBM GB/s vs peak" % (n, m.name),
         "value": round(ms, 5),
@@ -158,7 +161,8 @@ def bench_batched(args, wl):
                    "batch": n, "decode_steps": K, "weight_bytes_per_step": rf.weight_bytes_per_token(m),
                    "kv": "bf16, paged in 16-token blocks, permuted page tables"},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": rf.MI355X_HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": round(achieved / rf.MI355X_HBM_PEAK_GBS, 4), "traffic": None,
+                     "frac": round(achieved / rf.MI355X_HBM_PEAK_GBS, 4), "traffic": traffic,
+                     "traffic_unit": "HBM bytes/launch (FETCH_SIZE + WRITE_SIZE, copy-calibrated)",
                      "bytes_per_launch": int(bytes_avg), "kernel": "mk_megakernel, batched (one launch per step)"},
         "cpu_baseline": cpu,
     }
@@ -173,7 +177,7 @@ def main():
     ap.add_argument("--workload", default="llama8b")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--staged-steps", type=int, default=64, help="steps of the stage-sliced comparison run")
+    ap.add_argument("--staged-steps", type=int, default=64, help="steps of the stage-sliced comparison run (0: skip it)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 1 GiB device-to-device copy 5 times (to scale HBM byte counters)")
     args = ap.parse_args()
@@ -250,31 +254,38 @@ def main():
     # execution the single launch replaces. Its extra time per token is the pass-to-pass cost removed.
     n_stages = int(mk.mk_graph_stats(dec.ctx).n_stages)
     Ks = min(K, args.staged_steps)
-    dec.set_ctx_lens([P])
-    tokens.copy_(g0)
-    torch.cuda.synchronize(dec.dev)
-    ev0.record(stream)
-    for _ in range(Ks):
-        dec.step_staged(tokens)
-    ev1.record(stream)
-    torch.cuda.synchronize(dec.dev)
-    ms_staged = ev0.elapsed_time(ev1) / Ks
-    dec.sync_check()
-    ms_fused_same = None
-    if Ks < K:  # the one-launch time over the same positions
+    pass_to_pass = None
+    if Ks > 0:
         dec.set_ctx_lens([P])
         tokens.copy_(g0)
         torch.cuda.synchronize(dec.dev)
         ev0.record(stream)
         for _ in range(Ks):
-            dec.step(tokens)
+            dec.step_staged(tokens)
         ev1.record(stream)
         torch.cuda.synchronize(dec.dev)
-        ms_fused_same = ev0.elapsed_time(ev1) / Ks
-    else:
-        ms_fused_same = ms
-    log("staged: %.4f ms/token in %d dispatches (one launch: %.4f ms/token over the same %d steps)" %
-        (ms_staged, n_stages, ms_fused_same, Ks))
+        ms_staged = ev0.elapsed_time(ev1) / Ks
+        dec.sync_check()
+        if Ks < K:  # the one-launch time over the same positions
+            dec.set_ctx_lens([P])
+            tokens.copy_(g0)
+            torch.cuda.synchronize(dec.dev)
+            ev0.record(stream)
+            for _ in range(Ks):
+                dec.step(tokens)
+            ev1.record(stream)
+            torch.cuda.synchronize(dec.dev)
+            ms_fused_same = ev0.elapsed_time(ev1) / Ks
+        else:
+            ms_fused_same = ms
+        log("staged: %.4f ms/token in %d dispatches (one launch: %.4f ms/token over the same %d steps)" %
+            (ms_staged, n_stages, ms_fused_same, Ks))
+        pass_to_pass = {"stage_sliced_ms_per_token": round(ms_staged, 5), "dispatches_per_token": n_stages,
+                        "one_launch_ms_per_token": round(ms_fused_same, 5), "steps": Ks,
+                        "removed_ms_per_token": round(ms_staged - ms_fused_same, 5),
+                        "removed_us_per_boundary": round(1e3 * (ms_staged - ms_fused_same) / max(1, n_stages - 1), 3),
+                        "what": "the same kernel and task graph launched once per dependency stage (stop-and-go) "
+                                "vs once per step"}
     dec.close()
 
     traffic = None
@@ -313,12 +324,7 @@ def main():
                      "traffic_unit": "HBM bytes/launch (FETCH_SIZE + WRITE_SIZE, copy-calibrated)",
                      "bytes_per_launch": int(bytes_avg), "kernel": "mk_megakernel (one launch per decode step)"},
         "cpu_baseline": cpu,
-        "pass_to_pass": {"stage_sliced_ms_per_token": round(ms_staged, 5), "dispatches_per_token": n_stages,
-                         "one_launch_ms_per_token": round(ms_fused_same, 5), "steps": Ks,
-                         "removed_ms_per_token": round(ms_staged - ms_fused_same, 5),
-                         "removed_us_per_boundary": round(1e3 * (ms_staged - ms_fused_same) / max(1, n_stages - 1), 3),
-                         "what": "the same kernel and task graph launched once per dependency stage (stop-and-go) "
-                                 "vs once per step"},
+        "pass_to_pass": pass_to_pass,
     }
     print(json.dumps(out), flush=True)
 
