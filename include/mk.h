@@ -162,15 +162,16 @@ mk_status mk_read_logits(mk_ctx* ctx, int seq, float* h_dst, size_t n, void* str
 /* Synchronise `stream` and report the device error word (MK_OK if clear). */
 mk_status mk_sync_check(mk_ctx* ctx, void* stream);
 
-/* Task tracing. With a device buffer of at least n_tasks * 32 bytes (n_tasks from
+/* Task tracing. With a device buffer of at least n_tasks * 40 bytes (n_tasks from
  * mk_graph_stats), every later step writes one record per task, indexed by the task's
- * position in the global order. A record is {uint64 t_queue, t_ready, t_done; uint16 cu;
- * uint8 type; uint8 layer; uint32 epoch}: the times (100 MHz device real-time counter) when
- * the CU reached the task, when its input event was satisfied and when it published its
- * outputs; the CU; the task type (1 QKV, 2 attention, 3 O projection, 4 gate/up, 5 down,
+ * position in the global order. A record is {uint64 t_queue, t_ready, t_streamed, t_done;
+ * uint16 cu; uint8 type; uint8 layer; uint32 epoch}: the times (100 MHz device real-time
+ * counter) when the CU reached the task, when its inputs were all present, when its own
+ * streaming ended (a GEMV's weights, before the epilogue; attention's cache rows and its
+ * in-task merge, before partials are written or merged) and when it published its outputs; the CU; the task type (1 QKV, 2 attention, 3 O projection, 4 gate/up, 5 down,
  * 6 LM head, 7 argmax); its layer (n_layers for the LM head and argmax, mod 256). Each step overwrites
  * the records. d_buf == NULL turns tracing off. The buffer stays the caller's.
- * Errors: MK_ERR_INVALID_ARG (too small or not 32-byte aligned). */
+ * Errors: MK_ERR_INVALID_ARG (too small or not 8-byte aligned). */
 mk_status mk_set_trace(mk_ctx* ctx, void* d_buf, size_t bytes);
 
 /* Graph inspection (host only, no GPU needed).

@@ -286,15 +286,15 @@ class Decoder:
 
     def enable_trace(self):
         n = mk_graph_stats(self.ctx).n_tasks
-        self.trace_buf = self.torch.zeros(n * 32, dtype=self.torch.uint8, device=self.dev)
-        mk_set_trace(self.ctx, self.trace_buf, n * 32)
+        self.trace_buf = self.torch.zeros(n * 40, dtype=self.torch.uint8, device=self.dev)
+        mk_set_trace(self.ctx, self.trace_buf, n * 40)
 
     def read_trace(self):
-        """Per-task records of the last step: structured numpy array (t_queue, t_ready, t_done, cu, type,
-        layer, epoch), indexed by the task's position in the global order."""
+        """Per-task records of the last step: structured numpy array (t_queue, t_ready, t_streamed, t_done,
+        cu, type, layer, epoch), indexed by the task's position in the global order."""
         import numpy as np
         self.torch.cuda.synchronize(self.dev)
-        dt = np.dtype([("t_queue", "<u8"), ("t_ready", "<u8"), ("t_done", "<u8"), ("cu", "<u2"), ("type", "u1"),
+        dt = np.dtype([("t_queue", "<u8"), ("t_ready", "<u8"), ("t_streamed", "<u8"), ("t_done", "<u8"), ("cu", "<u2"), ("type", "u1"),
                        ("layer", "u1"), ("epoch", "<u4")])
         return self.trace_buf.cpu().numpy().view(dt)
 

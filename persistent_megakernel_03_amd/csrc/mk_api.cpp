@@ -441,7 +441,7 @@ mk_status mk_set_trace(mk_ctx* c, void* d_buf, size_t bytes) {
     return MK_OK;
   }
   if (bytes < c->g.tasks.size() * sizeof(TraceRec)) return fail(MK_ERR_INVALID_ARG, "trace buffer too small");
-  if (((uintptr_t)d_buf & 31) != 0) return fail(MK_ERR_INVALID_ARG, "trace buffer must be 32-byte aligned");
+  if (((uintptr_t)d_buf & 7) != 0) return fail(MK_ERR_INVALID_ARG, "trace buffer must be 8-byte aligned");
   c->d_trace = (TraceRec*)d_buf;
   return MK_OK;
 }

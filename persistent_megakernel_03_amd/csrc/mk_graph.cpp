@@ -554,7 +554,7 @@ std::string build_graph(const mk_model_config& c, int n_cus, HostGraph& g) {
   // the larger of the GEMV and attention working sets
   g.lds_bytes = 1024 + align_up((int64_t)2 * L * 8, 256) + align_up((int64_t)max_q * (int64_t)sizeof(TaskDesc), 256) +
                 align_up((int64_t)(g.attn_tasks + 1) * 4, 256) + align_up(std::max(gemv_lds, attn_lds), 256);
-  if (g.lds_bytes > 160 * 1024) return "working set exceeds 160 KB of LDS";
+  if (g.lds_bytes + (S == 1 ? kStageBytes : 0) > 160 * 1024) return "working set exceeds 160 KB of LDS";
   return "";
 }
 
@@ -624,7 +624,7 @@ std::string validate_graph(const HostGraph& g) {
     if (td.type == T_GATEUP && (td.row0 % 2 || td.row1 % 2)) return "gate/up task splits a pair";
   }
   if (end > g.wl.packed_bytes) return "tiles exceed the packed weights";
-  if (g.lds_bytes > 160 * 1024) return "LDS over budget";
+  if (g.lds_bytes + (g.cfg.max_seqs == 1 ? kStageBytes : 0) > 160 * 1024) return "LDS over budget";
   return "";
 }
 

@@ -25,6 +25,12 @@ enum TaskType : int32_t {
   T_ARGMAX = 7,  // argmax over the LM-head partials, token out, context length + 1
 };
 
+// One sequence: 1 KB weight units per wave that a GEMV task stages in LDS (by DMA) on top of the
+// units it holds in registers, all issued before the task waits for its input. The stage is a
+// static LDS array of 8 waves x kStageUnits KB beside the dynamic working set.
+constexpr int kStageUnits = 10;
+constexpr int kStageBytes = 8 * kStageUnits * 1024;
+
 // Geometry of one GEMV operand in the packed (streaming) layout. A row of K bf16 values is
 // P = K/8 pieces of 16 bytes. A "unit" is 1 KB: 64 lanes x 16 B.
 //  mfma == 0 (one sequence): rows go in groups of rg = 64/lpr rows; a group is S units. In unit u
@@ -92,14 +98,15 @@ enum ErrCode : uint32_t { ERR_NONE = 0, ERR_TOKEN = 1, ERR_PAGE = 2, ERR_TIMEOUT
 // One task's timestamps (s_memrealtime, 100 MHz), written when tracing is on.
 struct TraceRec {
   uint64_t t_queue;   // the CU reached the task in its queue
-  uint64_t t_ready;   // its input event was satisfied
+  uint64_t t_ready;   // its inputs were all present
+  uint64_t t_streamed;  // its own streaming ended: GEMV before the epilogue, attention before the partials
   uint64_t t_done;    // its outputs were published
   uint16_t cu;
   uint8_t type;       // TaskType
   uint8_t layer;      // layer index (n_layers for the LM head and argmax), mod 256
   uint32_t epoch;
 };
-static_assert(sizeof(TraceRec) == 32, "TraceRec is 32 bytes");
+static_assert(sizeof(TraceRec) == 40, "TraceRec is 40 bytes");
 
 // Everything the megakernel reads, passed by value.
 struct KernelParams {

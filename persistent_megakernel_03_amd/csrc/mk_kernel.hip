@@ -67,11 +67,53 @@ __device__ __forceinline__ void bar() {
   asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
 }
 
-__device__ __forceinline__ float wave_sum(float v) {
-#pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off);
+// DPP moves within a row of 16 lanes: swap pairs, swap pairs of pairs, mirror within 8, mirror within 16.
+// Applied in turn, each adds a lane's partner from another group, so LPP consecutive lanes end with the
+// sum over all of them (LPP = 8 uses the first three).
+template <int CTRL>
+__device__ __forceinline__ float dpp_add(float v) {
+  return v + __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), CTRL, 0xF, 0xF, false));
+}
+
+// The two values of a lane pair {l, l ^ OFF}, in the same order on both lanes: (lower lane's,
+// upper lane's). Distances 16 and 32 swap rows or halves of the wave in one VALU instruction.
+template <int OFF>
+__device__ __forceinline__ void lane_pair(float v, float& lo, float& hi) {
+  if constexpr (OFF == 16 || OFF == 32) {
+    const uint32_t b = __float_as_uint(v);
+    const auto r = OFF == 16 ? __builtin_amdgcn_permlane16_swap(b, b, false, false)
+                             : __builtin_amdgcn_permlane32_swap(b, b, false, false);
+    lo = __uint_as_float(r[0]);
+    hi = __uint_as_float(r[1]);
+  } else {
+    const float o = __shfl_xor(v, OFF);
+    const bool upper = (threadIdx.x & OFF) != 0;
+    lo = upper ? o : v;
+    hi = upper ? v : o;
+  }
+}
+
+// Sum over aligned groups of n lanes (n a power of two up to 64), the same bits on every lane of a
+// group: four DPP steps within rows of 16 lanes, then row and half-wave swaps.
+__device__ __forceinline__ float lanes_sum(float v, int n) {
+  if (n >= 2) v = dpp_add<0xB1>(v);
+  if (n >= 4) v = dpp_add<0x4E>(v);
+  if (n >= 8) v = dpp_add<0x141>(v);
+  if (n >= 16) v = dpp_add<0x140>(v);
+  if (n >= 32) {
+    float a, b;
+    lane_pair<16>(v, a, b);
+    v = a + b;
+  }
+  if (n >= 64) {
+    float a, b;
+    lane_pair<32>(v, a, b);
+    v = a + b;
+  }
   return v;
 }
+
+__device__ __forceinline__ float wave_sum(float v) { return lanes_sum(v, 64); }
 __device__ __forceinline__ float wave_max(float v) {
 #pragma unroll
   for (int off = 32; off >= 1; off >>= 1) v = fmaxf(v, __shfl_xor(v, off));
@@ -89,6 +131,7 @@ struct Ctl {
   uint32_t aborted;
   uint64_t kred[NW];
   uint64_t t_ready;         // trace: when the running task's inputs were all present
+  uint64_t t_streamed;      // trace: when its own streaming ended
 };
 
 __device__ __forceinline__ float block_sum(float v, Ctl* ctl) {
@@ -344,12 +387,27 @@ __device__ __forceinline__ WaveRun dummy_run(const KernelParams& p) {
   return w;
 }
 
+// The LDS stage of each wave: kStageUnits units that follow its first NSLOT register units.
+__shared__ v4u g_stage[NW][kStageUnits][64];
+
+// Issues the DMA of units NSLOT .. NSLOT + kStageUnits - 1 of the wave's run into its stage (only
+// units the run has). Each lane's 16 bytes land at lane * 16 of the unit's 1 KB slot.
+__device__ __forceinline__ void stage_units(const WaveRun& w) {
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+#pragma unroll
+  for (int j = 0; j < kStageUnits; ++j)
+    if (NSLOT + j < w.nunits)
+      __builtin_amdgcn_global_load_lds((const void*)(w.src + (size_t)(NSLOT + j) * 64),
+                                       (__attribute__((address_space(3))) void*)&g_stage[wave][j][0], 16, 0, 2);
+}
+
 __device__ __forceinline__ void gemv_tile(const KernelParams& p, const TaskDesc& t, const GemvGeom gm, const float* xs, float* ys,
                           WPipe& wp) {
   const WaveRun w = wave_run(p, t, gm);
   const int nunits = w.nunits;
   if (nunits <= 0) return;
   const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int rows = t.row1 - t.row0;
   const int S = gm.S, lpr = gm.lpr;
   const int sub = lane & (lpr - 1), rin = lane / lpr;
@@ -361,10 +419,7 @@ __device__ __forceinline__ void gemv_tile(const KernelParams& p, const TaskDesc&
   auto unit = [&](const v4u& wv) {
     unit_fma(wv, xa + ug * lpr * 4, xb + ug * lpr * 4, acc0, acc1);
     if (++ug == S) {
-      float acc = acc0 + acc1;
-#pragma unroll
-      for (int off = 32; off >= 1; off >>= 1)  // fixed trip count (lpr <= 64) keeps the wait analysis exact
-        if (off < lpr) acc += __shfl_xor(acc, off);
+      const float acc = lanes_sum(acc0 + acc1, lpr);
       const int r = g * gm.rg + rin;
       if (sub == 0 && r < rows) ys[r] = acc;
       acc0 = 0.f;
@@ -373,14 +428,31 @@ __device__ __forceinline__ void gemv_tile(const KernelParams& p, const TaskDesc&
       ++g;
     }
   };
-  // Slot j holds unit i0 + j. Each slot is refilled with unit i0 + j + NSLOT as soon as it has been
-  // consumed, so NSLOT - 1 loads stay in flight while a unit is processed. Refills past the run
-  // re-read its last unit (a cache hit). A scheduling barrier after each slot keeps each refill
+  // Units in run order: 0 .. NSLOT - 1 from the registers, the next kStageUnits from the LDS stage,
+  // then the rest through the registers again. Slot j holds unit i0 + j of its round and is refilled
+  // with the unit NSLOT further on as soon as it has been consumed (the first round's refills skip
+  // the staged units), so NSLOT - 1 loads stay in flight while a unit is processed. Refills past the
+  // run re-read its last unit (a cache hit). A scheduling barrier after each slot keeps each refill
   // after its slot's use. The compiler still waits for most of a round's loads at the round's start
   // (the first fill is not kept in slot order), so about one round of loads is in flight per wave;
   // measured on the 8B decode, this streams slightly faster than a strict slot-by-slot pipeline
   // with 16 loads always in flight: the HBM stream is already saturated.
-  for (int i0 = 0; i0 < nunits; i0 += NSLOT) {
+#pragma unroll
+  for (int j = 0; j < NSLOT; ++j) {
+    if (j < nunits) unit(wp.R[j]);
+    wp.R[j] = load_unit(w, j + NSLOT + kStageUnits);
+    __builtin_amdgcn_sched_barrier(0);
+  }
+  if (nunits > NSLOT) {
+    // The stage's DMA was issued before the first round's NSLOT refills and nothing else is younger,
+    // and the counter completes in order: once at most NSLOT loads are outstanding, it has landed.
+    // (The compiler does not track the DMA's writes to LDS, so the wait is explicit.)
+    asm volatile("s_waitcnt vmcnt(%0)" ::"n"(NSLOT) : "memory");
+#pragma unroll
+    for (int j = 0; j < kStageUnits; ++j)
+      if (NSLOT + j < nunits) unit(g_stage[wave][j][lane]);
+  }
+  for (int i0 = NSLOT + kStageUnits; i0 < nunits; i0 += NSLOT) {
 #pragma unroll
     for (int j = 0; j < NSLOT; ++j) {
       if (i0 + j < nunits) unit(wp.R[j]);
@@ -524,14 +596,6 @@ __device__ __forceinline__ int attn_task_of(int W, int T, int x) {
   return min(T - 1, (int)(((uint32_t)(x + 1) * (uint32_t)T - 1u) / (uint32_t)W));
 }
 
-// DPP moves within a row of 16 lanes: swap pairs, swap pairs of pairs, mirror within 8, mirror within 16.
-// Applied in turn, each adds a lane's partner from another group, so LPP consecutive lanes end with the
-// sum over all of them (LPP = 8 uses the first three).
-template <int CTRL>
-__device__ __forceinline__ float dpp_add(float v) {
-  return v + __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), CTRL, 0xF, 0xF, false));
-}
-
 // Scores of one position for every head: s_h = q_h . k, this lane's 8 dimensions summed over the
 // position's lanes. The heads' reductions are interleaved so that each DPP move reads a value written
 // several instructions earlier.
@@ -592,6 +656,34 @@ __device__ __forceinline__ void attn_accum(const v4u vv, int G, const float (&a)
 
 // Attention over positions [c0, c1) of segment (s, grp), c1 <= pos + 1 (pos = the current position).
 // Returns, per output element (head, dim) of this thread, the merged (max, sum, unnormalised output).
+// Log-sum-exp merge of the wave's lane groups (LPP lanes hold one position group's state): every
+// lane ends with the merge over the 64 / LPP groups, the same bits on every lane.
+template <int OFF, int GMAX>
+__device__ __forceinline__ void attn_merge_level(int G, float (&mr)[GMAX], float (&lr)[GMAX], float (&orr)[GMAX][8]) {
+#pragma unroll
+  for (int h = 0; h < GMAX; ++h) {
+    if (h >= G) break;
+    float ma, mb, la, lb;
+    lane_pair<OFF>(mr[h], ma, mb);
+    lane_pair<OFF>(lr[h], la, lb);
+    const float mx = fmaxf(ma, mb), ea = __expf(ma - mx), eb = __expf(mb - mx);
+    lr[h] = fmaf(la, ea, lb * eb);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      float oa, ob;
+      lane_pair<OFF>(orr[h][e], oa, ob);
+      orr[h][e] = fmaf(oa, ea, ob * eb);
+    }
+    mr[h] = mx;
+  }
+}
+template <int LPP, int GMAX>
+__device__ __forceinline__ void attn_lane_merge(int G, float (&mr)[GMAX], float (&lr)[GMAX], float (&orr)[GMAX][8]) {
+  if constexpr (LPP <= 8) attn_merge_level<8, GMAX>(G, mr, lr, orr);
+  if constexpr (LPP <= 16) attn_merge_level<16, GMAX>(G, mr, lr, orr);
+  attn_merge_level<32, GMAX>(G, mr, lr, orr);
+}
+
 template <int DH, int GMAX, int ANS>
 __device__ __forceinline__ void attn_part(const KernelParams& p, const TaskDesc& t, float* lds, Ctl* ctl,
                                           uint16_t* const* pools, int s, int grp, int pos, int c0, int c1,
@@ -624,10 +716,14 @@ __device__ __forceinline__ void attn_part(const KernelParams& p, const TaskDesc&
   // loaded a window at a time; a group's entry is then a lane read, not a memory load inside the stream
   // (a load there would make the in-order wait drain every key and value load in flight).
   int pbase = 0, pent = 0;
+  // Every cached block of the part holds the first position of some group, so checking the entries as
+  // they are loaded covers the part; a bad entry is reported and clamped into the pool.
   auto load_pages = [&](int base) {
     pbase = base;
     const int k = min(base + lane, max(nw - 1, 0));
-    pent = nw > 0 ? min(max(ptab[(c0 + (wave + NW * k) * PPW) >> 4], 0), p.num_blocks - 1) : 0;
+    const int raw = nw > 0 ? ptab[(c0 + (wave + NW * k) * PPW) >> 4] : 0;
+    if (raw < 0 || raw >= p.num_blocks) raise_error(p, ERR_PAGE, (uint32_t)s, (uint32_t)raw);
+    pent = min(max(raw, 0), p.num_blocks - 1);
   };
   load_pages(0);
   auto row_load = [&](const uint16_t* pool, int k) {
@@ -695,9 +791,10 @@ __device__ __forceinline__ void attn_part(const KernelParams& p, const TaskDesc&
     if (k0 + 2 * ANS > pbase + 64) load_pages(k0);  // this round's refills need groups up to k0 + 2 ANS - 1
 #pragma unroll
     for (int j = 0; j < ANS; ++j) {
+      if (k0 + j >= nw) break;  // wave-uniform: the slots past the wave's groups hold nothing
       const int pp = c0 + (wave + NW * (k0 + j)) * PPW + pg;
       float sc[GMAX];
-      attn_scores<DH, GMAX>(RK[j], k0 + j < nw && pp < ce, G, qr, sc);
+      attn_scores<DH, GMAX>(RK[j], pp < ce, G, qr, sc);
       bool up = false;
 #pragma unroll
       for (int h = 0; h < GMAX; ++h)
@@ -711,11 +808,6 @@ __device__ __forceinline__ void attn_part(const KernelParams& p, const TaskDesc&
       __builtin_amdgcn_sched_barrier(0);
     }
   }
-  // the part's page entries, checked once (the stream clamped them into the pool)
-  for (int bi = (c0 >> 4) + tid; bi < ((ce + 15) >> 4); bi += NT) {
-    const int b = ptab[bi];
-    if (b < 0 || b >= p.num_blocks) raise_error(p, ERR_PAGE, (uint32_t)s, (uint32_t)b);
-  }
   if (cur && wave == 0) {  // the current position: lane c's 8 dims are words 4c..4c+3 of each row
     const v4u kq = *(const v4u*)(kvc + 4 * c), vq = *(const v4u*)(kvc + DH / 2 + 4 * c);
     float sq[GMAX];
@@ -724,19 +816,7 @@ __device__ __forceinline__ void attn_part(const KernelParams& p, const TaskDesc&
     attn_accum<GMAX>(vq, G, sq, mr, lr, orr);
   }
   // merge the wave's lane groups, then the waves
-#pragma unroll
-  for (int off = LPP; off < 64; off <<= 1) {
-#pragma unroll
-    for (int h = 0; h < GMAX; ++h) {
-      if (h >= G) break;
-      const float m2 = __shfl_xor(mr[h], off), l2 = __shfl_xor(lr[h], off);
-      const float mx = fmaxf(mr[h], m2), e1 = __expf(mr[h] - mx), e2 = __expf(m2 - mx);
-      lr[h] = lr[h] * e1 + l2 * e2;
-#pragma unroll
-      for (int e = 0; e < 8; ++e) orr[h][e] = orr[h][e] * e1 + __shfl_xor(orr[h][e], off) * e2;
-      mr[h] = mx;
-    }
-  }
+  attn_lane_merge<LPP, GMAX>(G, mr, lr, orr);
   if (pg == 0) {
 #pragma unroll
     for (int h = 0; h < GMAX; ++h) {
@@ -810,6 +890,7 @@ __device__ __forceinline__ void task_attn(const KernelParams& p, const TaskDesc&
     if (!ok) pos = -1;
     float M[EPT], L[EPT], A[EPT];
     attn_part<DH, GMAX, ANS>(p, t, lds, ctl, pools, s, grp, pos, c0, c1, M, L, A);
+    if (p.trace && tid == 0) ctl->t_streamed = __builtin_amdgcn_s_memrealtime();
     if (xe < E) {  // the segment goes on in later tasks: this task's partial
       uint64_t* pb = part_base(ti, x == lo ? 0 : 1);
 #pragma unroll
@@ -1001,11 +1082,12 @@ __device__ __forceinline__ void gemv_task(const KernelParams& p, const TaskDesc&
 #pragma unroll
     for (int k = 0; k < 4; ++k) rw[k] = ld_tag(rr, min(tid + k * NT, nrows - 1) * 8, 0);
   }
-  {  // the wave's first NSLOT weight units
+  {  // the wave's first NSLOT weight units, and the next kStageUnits into its LDS stage
     WaveRun w = wave_run(p, t, gm);
     if (w.nunits <= 0) w = dummy_run(p);
 #pragma unroll
     for (int j = 0; j < NSLOT; ++j) wp.R[j] = load_unit(w, j);
+    stage_units(w);
   }
   // QKV: the rotary, bias and page-table constants of the thread's 4-row set. An out-of-range
   // position is reported and the row is not appended, but q, k and v are still written (at
@@ -1080,6 +1162,7 @@ __device__ __forceinline__ void gemv_task(const KernelParams& p, const TaskDesc&
 
   gemv_tile(p, t, gm, xs, ys, wp);
   bar();
+  if (p.trace && tid == 0) ctl->t_streamed = __builtin_amdgcn_s_memrealtime();
 
   if (type == T_QKV) {
     for (int m = tid; m < nsets; m += NT) {
@@ -1340,6 +1423,7 @@ __device__ __forceinline__ void gemv_task_b(const KernelParams& p, const TaskDes
     }
   }
   bar();
+  if (p.trace && tid == 0) ctl->t_streamed = __builtin_amdgcn_s_memrealtime();
   if (!multi) {  // row groups shared by two waves: their partials, in wave order
     const int per = R * nu;
     for (int e = tid; e < R * 256; e += NT) {
@@ -1562,6 +1646,7 @@ __global__ __launch_bounds__(NT, 1) void mk_megakernel(KernelParams p) {
     if (p.trace && threadIdx.x == 0) {
       t_queue = __builtin_amdgcn_s_memrealtime();
       ctl->t_ready = t_queue;
+      ctl->t_streamed = t_queue;
     }
     // Each task starts its own input streams before it polls for its inputs (they do not depend on
     // them): an attention task its first keys and values, a GEMV its first weight units.
@@ -1587,6 +1672,7 @@ __global__ __launch_bounds__(NT, 1) void mk_megakernel(KernelParams p) {
       TraceRec r;
       r.t_queue = t_queue;
       r.t_ready = ctl->t_ready;
+      r.t_streamed = ctl->t_streamed;
       r.t_done = __builtin_amdgcn_s_memrealtime();
       r.cu = (uint16_t)cu;
       r.type = (uint8_t)t.type;
