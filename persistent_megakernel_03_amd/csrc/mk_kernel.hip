@@ -391,14 +391,23 @@ __device__ __forceinline__ WaveRun dummy_run(const KernelParams& p) {
 __shared__ v4u g_stage[NW][kStageUnits][64];
 
 // Issues the DMA of units NSLOT .. NSLOT + kStageUnits - 1 of the wave's run into its stage (only
-// units the run has). Each lane's 16 bytes land at lane * 16 of the unit's 1 KB slot.
+// units the run has). Each lane's 16 bytes land at lane * 16 of the unit's 1 KB slot, at the LDS
+// address in M0. The DMA is written as inline assembly and issued before any other load of the task:
+// the compiler then neither sees a DMA in flight (with one, it drains the whole counter before any
+// LDS access it cannot prove separate) nor miscounts the waits of later loads, all of which are
+// younger. Its completion is waited for explicitly where the stage is read. No register receives
+// data, so nothing is left to be overwritten in flight.
 __device__ __forceinline__ void stage_units(const WaveRun& w) {
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
 #pragma unroll
   for (int j = 0; j < kStageUnits; ++j)
-    if (NSLOT + j < w.nunits)
-      __builtin_amdgcn_global_load_lds((const void*)(w.src + (size_t)(NSLOT + j) * 64),
-                                       (__attribute__((address_space(3))) void*)&g_stage[wave][j][0], 16, 0, 2);
+    if (NSLOT + j < w.nunits) {
+      const uint32_t dst = (uint32_t)(size_t)(__attribute__((address_space(3))) void*)&g_stage[wave][j][0];
+      asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off nt"
+                   :
+                   : "v"(w.src + (size_t)(NSLOT + j) * 64), "s"(dst)
+                   : "memory", "m0");
+    }
 }
 
 __device__ __forceinline__ void gemv_tile(const KernelParams& p, const TaskDesc& t, const GemvGeom gm, const float* xs, float* ys,
@@ -444,9 +453,9 @@ __device__ __forceinline__ void gemv_tile(const KernelParams& p, const TaskDesc&
     __builtin_amdgcn_sched_barrier(0);
   }
   if (nunits > NSLOT) {
-    // The stage's DMA was issued before the first round's NSLOT refills and nothing else is younger,
-    // and the counter completes in order: once at most NSLOT loads are outstanding, it has landed.
-    // (The compiler does not track the DMA's writes to LDS, so the wait is explicit.)
+    // The stage's DMA was issued before every other load of the task, the first round's NSLOT refills
+    // are the youngest, and the counter completes in order: once at most NSLOT loads are outstanding,
+    // it has landed. (The compiler does not know of the DMA, so the wait is explicit.)
     asm volatile("s_waitcnt vmcnt(%0)" ::"n"(NSLOT) : "memory");
 #pragma unroll
     for (int j = 0; j < kStageUnits; ++j)
@@ -1055,6 +1064,10 @@ __device__ __forceinline__ void gemv_task(const KernelParams& p, const TaskDesc&
   // the RMSNorm gains, the residual words; then the weight units; then the QKV epilogue constants,
   // which are needed only after the GEMV.
   // Input words: thread t polls words i0 + 64k (see poll_vector), landing at xs_index(i0) + 32k.
+  // The LDS stage's DMA goes out first, ahead of every other load of the task (see stage_units).
+  WaveRun wrun = wave_run(p, t, gm);
+  if (wrun.nunits <= 0) wrun = dummy_run(p);
+  stage_units(wrun);
   const __amdgpu_buffer_rsrc_t rin = tag_rsrc(src);
   const int i0 = poll_index(n, 0);
   uint32_t pending = in_embed ? 0u : first_words(min(poll_chunk(n) / 64, (n - i0 + 63) / 64));
@@ -1082,13 +1095,9 @@ __device__ __forceinline__ void gemv_task(const KernelParams& p, const TaskDesc&
 #pragma unroll
     for (int k = 0; k < 4; ++k) rw[k] = ld_tag(rr, min(tid + k * NT, nrows - 1) * 8, 0);
   }
-  {  // the wave's first NSLOT weight units, and the next kStageUnits into its LDS stage
-    WaveRun w = wave_run(p, t, gm);
-    if (w.nunits <= 0) w = dummy_run(p);
+  // the wave's first NSLOT weight units
 #pragma unroll
-    for (int j = 0; j < NSLOT; ++j) wp.R[j] = load_unit(w, j);
-    stage_units(w);
-  }
+  for (int j = 0; j < NSLOT; ++j) wp.R[j] = load_unit(wrun, j);
   // QKV: the rotary, bias and page-table constants of the thread's 4-row set. An out-of-range
   // position is reported and the row is not appended, but q, k and v are still written (at
   // position 0's rotation) so that no consumer waits for them.
