@@ -61,13 +61,18 @@ typedef struct mk_ctx mk_ctx; /* opaque, owned by the library */
  *   - max_blocks_per_seq: columns of the page table.
  *   - num_blocks: blocks in each layer's K pool and in each layer's V pool.
  *   - attn_splits: KV splits per (sequence, KV head). 0 = chosen from
- *     max_blocks_per_seq. */
+ *     max_blocks_per_seq. The layer's attention tasks are at most
+ *     max_seqs * n_kv_heads * attn_splits (and at most one per compute unit).
+ *   - attn_min_blocks: each step cuts its cache blocks over at most
+ *     ceil(blocks / attn_min_blocks) of those tasks (fewer tasks, fewer
+ *     merges); 0 = 1, every task gets blocks once there are enough. */
 typedef struct {
   int32_t n_layers, d_model, n_q_heads, n_kv_heads, head_dim, d_ffn, vocab;
   float rms_eps, rope_theta;
   int32_t tied_embeddings, qkv_bias;
   int32_t max_seqs, block_size, max_blocks_per_seq, num_blocks;
   int32_t attn_splits;
+  int32_t attn_min_blocks;
 } mk_model_config;
 
 /* One weight tensor for mk_load_weights.

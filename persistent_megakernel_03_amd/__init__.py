@@ -36,7 +36,7 @@ class mk_model_config(ctypes.Structure):
                 ("vocab", ctypes.c_int32), ("rms_eps", ctypes.c_float), ("rope_theta", ctypes.c_float),
                 ("tied_embeddings", ctypes.c_int32), ("qkv_bias", ctypes.c_int32), ("max_seqs", ctypes.c_int32),
                 ("block_size", ctypes.c_int32), ("max_blocks_per_seq", ctypes.c_int32), ("num_blocks", ctypes.c_int32),
-                ("attn_splits", ctypes.c_int32)]
+                ("attn_splits", ctypes.c_int32), ("attn_min_blocks", ctypes.c_int32)]
 
 
 class mk_tensor(ctypes.Structure):
@@ -214,12 +214,13 @@ def mk_last_error() -> str:
 
 
 # ------------------------------------------------------------------- convenience
-def make_config(shape, max_seqs=1, max_blocks_per_seq=64, num_blocks=64, attn_splits=0, block_size=16):
+def make_config(shape, max_seqs=1, max_blocks_per_seq=64, num_blocks=64, attn_splits=0, block_size=16,
+                attn_min_blocks=0):
     """mk_model_config from any object with the model-shape attributes."""
     return mk_model_config(shape.n_layers, shape.d_model, shape.n_q_heads, shape.n_kv_heads, shape.head_dim,
                            shape.d_ffn, shape.vocab, float(shape.rms_eps), float(shape.rope_theta),
                            int(bool(shape.tied_embeddings)), int(bool(shape.qkv_bias)), max_seqs, block_size,
-                           max_blocks_per_seq, num_blocks, attn_splits)
+                           max_blocks_per_seq, num_blocks, attn_splits, attn_min_blocks)
 
 
 class Decoder:

@@ -172,6 +172,7 @@ KernelParams make_params(mk_ctx* c) {
   p.watchdog_ticks = c->watchdog_ticks;
   p.max_queue = g.max_queue;
   p.attn_tasks = g.attn_tasks;
+  p.attn_min_blocks = g.cfg.attn_min_blocks > 0 ? g.cfg.attn_min_blocks : kAttnMinBlocks;
   p.trace = c->d_trace;
   return p;
 }

@@ -192,6 +192,7 @@ std::string build_graph(const mk_model_config& c, int n_cus, HostGraph& g) {
   if (c.max_blocks_per_seq < 1 || c.num_blocks < 1) return "empty KV cache";
   if (!(c.rms_eps >= 0.f) || !(c.rope_theta > 0.f)) return "bad rms_eps or rope_theta";
   if (c.attn_splits < 0 || c.attn_splits > 64) return "attn_splits out of range";
+  if (c.attn_min_blocks < 0 || c.attn_min_blocks > (1 << 20)) return "attn_min_blocks out of range";
   g.cfg = c;
   g.n_cus = n_cus;
   g.max_pos = c.max_blocks_per_seq * c.block_size;

@@ -29,6 +29,11 @@ enum TaskType : int32_t {
 // units it holds in registers, all issued before the task waits for its input. The stage is a
 // static LDS array of 8 waves x kStageUnits KB beside the dynamic working set.
 constexpr int kStageUnits = 10;
+
+// Attention: by default the layer's cache blocks are cut over at most one task per kAttnMinBlocks
+// blocks. With 1, every attention task gets blocks once there are as many blocks as tasks: on
+// MI355X the extra merges cost less than fewer, longer tasks.
+constexpr int kAttnMinBlocks = 1;
 constexpr int kStageBytes = 8 * kStageUnits * 1024;
 
 // Geometry of one GEMV operand in the packed (streaming) layout. A row of K bf16 values is
@@ -149,6 +154,8 @@ struct KernelParams {
   int32_t max_queue;          // longest per-CU queue (its descriptors are staged in LDS)
   int32_t attn_tasks;         // attention tasks per layer (they cut the layer's KV blocks evenly)
   int32_t task_lo, task_hi;   // this launch runs the tasks [task_lo, task_hi) of the global order
+  int32_t attn_min_blocks;    // cache blocks per attention task at least (fewer tasks get blocks)
+  int32_t pad_;
   TraceRec* trace;            // per-task timestamps of the last step, or nullptr
 };
 

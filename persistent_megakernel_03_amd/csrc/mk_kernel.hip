@@ -128,6 +128,7 @@ struct Ctl {
   // attention work of this step: blocks per (sequence, KV head) segment of sequence s (0 when the
   // sequence is inactive), and the first block of sequence s's segments in the layer's block order
   int32_t anb[16], aoff[17];
+  int32_t ate;  // attention tasks that get blocks this step (the rest are empty)
   uint32_t aborted;
   uint64_t kred[NW];
   uint64_t t_ready;         // trace: when the running task's inputs were all present
@@ -598,7 +599,8 @@ struct AttnShape {
 };
 
 // First block of attention task i's range: T tasks cut W blocks evenly.
-// (W * i / T for i = 0..T is tabulated in LDS once per launch: alo[i].)
+// (W * i / T for i = 0..T is tabulated in LDS once per launch: alo[i]; tasks past the T used this
+// step start at W.)
 __device__ __forceinline__ int attn_lo_of(int W, int T, int i) { return (int)((uint32_t)W * (uint32_t)i / (uint32_t)T); }
 // The task whose range holds block x: the last i with alo[i] <= x.
 __device__ __forceinline__ int attn_task_of(int W, int T, int x) {
@@ -917,7 +919,7 @@ __device__ __forceinline__ void task_attn(const KernelParams& p, const TaskDesc&
     } else {
       // This task holds the segment's last block: merge the earlier tasks' partials in task order,
       // then its own, R tasks per poll round (3 words per task and element: m, l, o[dim]).
-      const int first = attn_task_of(W, T, B);
+      const int first = attn_task_of(W, __builtin_amdgcn_readfirstlane(ctl->ate), B);
       float Mm[EPT], Lm[EPT], Am[EPT];
 #pragma unroll
       for (int e = 0; e < EPT; ++e) {
@@ -1643,7 +1645,11 @@ __global__ __launch_bounds__(NT, 1) void mk_megakernel(KernelParams p) {
     ctl->aoff[threadIdx.x] = o * p.hk;
   }
   bar();
-  for (int i = threadIdx.x; i <= p.attn_tasks; i += NT) alo[i] = attn_lo_of(ctl->aoff[16], p.attn_tasks, i);
+  {
+    const int W = ctl->aoff[16], te = min(p.attn_tasks, max(1, (W + p.attn_min_blocks - 1) / p.attn_min_blocks));
+    for (int i = threadIdx.x; i <= p.attn_tasks; i += NT) alo[i] = attn_lo_of(W, te, min(i, te));
+    if (threadIdx.x == 0) ctl->ate = te;
+  }
   bar();
   WPipe wp;
   for (int qi = q0; qi < q1; ++qi) {

@@ -28,11 +28,12 @@ def capacity_blocks(n_positions: int, block_size: int = 16) -> int:
     return (n_positions + block_size - 1) // block_size
 
 
-def make_gpu(shape, weights, n_positions, paging="identity", attn_splits=0, device=0, seed_ns=None):
+def make_gpu(shape, weights, n_positions, paging="identity", attn_splits=0, device=0, seed_ns=None, attn_min_blocks=0):
     """A Decoder with a one-sequence cache of n_positions, weights loaded, ctx 0."""
     import persistent_megakernel_03_amd as mk
     nb = capacity_blocks(n_positions)
-    cfg = mk.make_config(shape, max_seqs=1, max_blocks_per_seq=nb, num_blocks=nb, attn_splits=attn_splits)
+    cfg = mk.make_config(shape, max_seqs=1, max_blocks_per_seq=nb, num_blocks=nb, attn_splits=attn_splits,
+                         attn_min_blocks=attn_min_blocks)
     dec = mk.Decoder(cfg, device)
     dec.load_weights(weights)
     if paging == "permuted":
@@ -55,7 +56,7 @@ def gpu_step(dec, token: int):
 
 
 def teacher_forced(shape, weights, prompt, n_decode, paging="identity", attn_splits=0, oracle_model=None,
-                   n_positions=None, f32_reference=True):
+                   n_positions=None, f32_reference=True, attn_min_blocks=0):
     """Run prompt + n_decode steps on both sides; the oracle's greedy token is fed to both.
 
     Returns a dict with per-step rel-L2, device tokens, oracle tokens, device-argmax agreement
@@ -65,7 +66,7 @@ def teacher_forced(shape, weights, prompt, n_decode, paging="identity", attn_spl
     n_positions = n_positions or total
     orm = oracle_model or orc.OracleModel(shape, weights, 1, n_positions)
     o32 = orc.OracleModel(shape, weights, 1, n_positions, precision="f32") if f32_reference else None
-    dec, table = make_gpu(shape, weights, n_positions, paging, attn_splits)
+    dec, table = make_gpu(shape, weights, n_positions, paging, attn_splits, attn_min_blocks=attn_min_blocks)
     rels, rels32, dev_tok, orc_tok, self_argmax, gaps = [], [], [], [], [], []
     tok = int(prompt[0])
     for i in range(total):

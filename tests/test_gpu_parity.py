@@ -92,9 +92,11 @@ def test_tiny_permuted_pages_bit_identical(tiny):
 
 @pytest.mark.parametrize("splits", [1, 2, 3])
 def test_tiny_split_counts(tiny, splits):
+    # one cache block per task at least: the tiny contexts then split each KV head's blocks over
+    # several tasks, and the last of them merges the others' partials
     w, prompt, wl = tiny
     log("case: tiny attn_splits", splits)
-    res = teacher_forced(si.TINY, w, prompt, 8, attn_splits=splits, paging="permuted")
+    res = teacher_forced(si.TINY, w, prompt, 8, attn_splits=splits, paging="permuted", attn_min_blocks=1)
     check(res, "tiny splits=%d" % splits)
     res["dec"].close()
 

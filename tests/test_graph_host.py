@@ -125,6 +125,11 @@ def test_rejects_bad_configs(L):
     with pytest.raises(mk.MKError) as e:
         mk.mk_create_host(cfg_for(si.TINY, 4, 4), 0)
     assert e.value.status == -2
+    c = cfg_for(si.TINY, 4, 4)
+    c.attn_min_blocks = -1
+    with pytest.raises(mk.MKError) as e:
+        mk.mk_create_host(c, 256)
+    assert e.value.status == -2
 
 
 def test_host_context_refuses_device_calls(L):
