@@ -397,17 +397,19 @@ __shared__ v4u g_stage[NW][kStageUnits][64];
 // the compiler then neither sees a DMA in flight (with one, it drains the whole counter before any
 // LDS access it cannot prove separate) nor miscounts the waits of later loads, all of which are
 // younger. Its completion is waited for explicitly where the stage is read. No register receives
-// data, so nothing is left to be overwritten in flight.
+// data, so nothing is left to be overwritten in flight; M0 (the LDS address) is restored after issue.
 __device__ __forceinline__ void stage_units(const WaveRun& w) {
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
 #pragma unroll
   for (int j = 0; j < kStageUnits; ++j)
     if (NSLOT + j < w.nunits) {
       const uint32_t dst = (uint32_t)(size_t)(__attribute__((address_space(3))) void*)&g_stage[wave][j][0];
-      asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off nt"
-                   :
+      uint32_t keep;  // M0 is the compiler's: it is saved and restored around the DMA
+      asm volatile("s_mov_b32 %0, m0\n\ts_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, off nt\n\t"
+                   "s_nop 4\n\ts_mov_b32 m0, %0"
+                   : "=&s"(keep)
                    : "v"(w.src + (size_t)(NSLOT + j) * 64), "s"(dst)
-                   : "memory", "m0");
+                   : "memory");
     }
 }
 
