@@ -413,8 +413,9 @@ __device__ __forceinline__ void stage_units(const WaveRun& w) {
     }
 }
 
+// restage: once this task has read its own staged units, the stage receives those of run `next`.
 __device__ __forceinline__ void gemv_tile(const KernelParams& p, const TaskDesc& t, const GemvGeom gm, const float* xs, float* ys,
-                          WPipe& wp) {
+                          WPipe& wp, bool restage, const WaveRun next) {
   const WaveRun w = wave_run(p, t, gm);
   const int nunits = w.nunits;
   if (nunits <= 0) return;
@@ -463,6 +464,10 @@ __device__ __forceinline__ void gemv_tile(const KernelParams& p, const TaskDesc&
 #pragma unroll
     for (int j = 0; j < kStageUnits; ++j)
       if (NSLOT + j < nunits) unit(g_stage[wave][j][lane]);
+  }
+  if (restage) {  // the stage's reads have returned before the DMA may overwrite it
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+    stage_units(next);
   }
   for (int i0 = NSLOT + kStageUnits; i0 < nunits; i0 += NSLOT) {
 #pragma unroll
@@ -1042,8 +1047,10 @@ __device__ __forceinline__ uint64_t block_max_u64(uint64_t k, Ctl* ctl) {
 //   LM head  final x -> RMSNorm -> logits and the tile's argmax key
 // One shared path keeps the instruction footprint small. The kernel's code is larger than the
 // instruction cache, and code that a CU runs once per layer is otherwise fetched anew each time.
+// nxt: the CU's next task in this launch, or null. staged: on entry, whether this wave's stage already
+// holds this task's units (staged by the previous task); on return, whether it holds the next task's.
 __device__ __forceinline__ void gemv_task(const KernelParams& p, const TaskDesc& t, float* lds, Ctl* ctl, WPipe& wp,
-                                          uint16_t* const* pools) {
+                                          uint16_t* const* pools, const TaskDesc* nxt, bool& staged) {
   const int type = t.type, l = t.layer, s = 0, tid = threadIdx.x;
   const uint32_t ep = p.epoch, what = (uint32_t)t.wait_ev;
   const GemvGeom gm = ctl->geoms[t.geom];
@@ -1069,9 +1076,20 @@ __device__ __forceinline__ void gemv_task(const KernelParams& p, const TaskDesc&
   // which are needed only after the GEMV.
   // Input words: thread t polls words i0 + 64k (see poll_vector), landing at xs_index(i0) + 32k.
   // The LDS stage's DMA goes out first, ahead of every other load of the task (see stage_units).
+  // An O-projection task runs while HBM is nearly idle (its weights arrived during attention) and is
+  // followed on its CU by a gate/up task: it fills the stage with that task's units, at once when
+  // its own units fit the registers, else as soon as it has read its own staged units.
   WaveRun wrun = wave_run(p, t, gm);
   if (wrun.nunits <= 0) wrun = dummy_run(p);
-  stage_units(wrun);
+  if (!staged) stage_units(wrun);
+  const bool restage_next = type == T_OPROJ && nxt != nullptr && is_gemv(nxt->type);
+  WaveRun wnext = wrun;
+  if (restage_next) {
+    wnext = wave_run(p, *nxt, ctl->geoms[nxt->geom]);
+    if (wnext.nunits <= 0) wnext = dummy_run(p);
+    if (wrun.nunits <= NSLOT) stage_units(wnext);
+  }
+  staged = restage_next;
   const __amdgpu_buffer_rsrc_t rin = tag_rsrc(src);
   const int i0 = poll_index(n, 0);
   uint32_t pending = in_embed ? 0u : first_words(min(poll_chunk(n) / 64, (n - i0 + 63) / 64));
@@ -1173,7 +1191,7 @@ __device__ __forceinline__ void gemv_task(const KernelParams& p, const TaskDesc&
   }
   if (p.trace && tid == 0) ctl->t_ready = __builtin_amdgcn_s_memrealtime();
 
-  gemv_tile(p, t, gm, xs, ys, wp);
+  gemv_tile(p, t, gm, xs, ys, wp, restage_next && wrun.nunits > NSLOT, wnext);
   bar();
   if (p.trace && tid == 0) ctl->t_streamed = __builtin_amdgcn_s_memrealtime();
 
@@ -1654,6 +1672,7 @@ __global__ __launch_bounds__(NT, 1) void mk_megakernel(KernelParams p) {
   }
   bar();
   WPipe wp;
+  bool staged = false;  // this wave's LDS stage holds the next GEMV task's units
   for (int qi = q0; qi < q1; ++qi) {
     const TaskDesc t = tq[qi - q0];
     // Only the LM head's partial maxima travel under flags (the argmax task waits for them); every
@@ -1671,14 +1690,16 @@ __global__ __launch_bounds__(NT, 1) void mk_megakernel(KernelParams p) {
       // position groups in flight per wave: more for batches (long streams), fewer for one sequence
       // and for many heads per KV head (register budget)
       task_attn<DH, GMAX, (GMAX > 4 || !BATCHED) ? 4 : 8>(p, t, lds, ctl, pools, alo);
+      staged = false;
     } else if (t.type == T_ARGMAX) {
+      staged = false;
       if (t.wait_ev >= 0) wait_event(p, t, ctl);
       if (p.trace && threadIdx.x == 0) ctl->t_ready = __builtin_amdgcn_s_memrealtime();
       if (t.wait_ev < 0 || !ctl->aborted) task_argmax(p, t, ctl);
     } else if constexpr (BATCHED) {
       gemv_task_b(p, t, lds, ctl, pools);
     } else {
-      gemv_task(p, t, lds, ctl, wp, pools);
+      gemv_task(p, t, lds, ctl, wp, pools, qi + 1 < q1 ? &tq[qi + 1 - q0] : nullptr, staged);
     }
     // The LM head's stores must be complete before its flags go out; other tasks' consumers check
     // the tags themselves.
