@@ -13,6 +13,7 @@
 // every CU streams an equal share of each weight matrix.
 #include <algorithm>
 #include <climits>
+#include <cstdio>
 #include <cstdlib>
 #include <cstring>
 #include <numeric>
@@ -65,6 +66,26 @@ std::vector<Range> distribute(int N, int A, int n) {
     const int64_t u0 = units * c / n, u1 = units * (c + 1) / n;
     out[c].r0 = (int)std::min<int64_t>(N, u0 * A);
     out[c].r1 = (int)std::min<int64_t>(N, u1 * A);
+  }
+  return out;
+}
+
+// Rows [0, N) in units of A rows over n CUs in proportion to weights w (all positive): CU c gets the
+// units between the rounded cumulative shares of CUs < c and <= c.
+std::vector<Range> distribute_weighted(int N, int A, const std::vector<double>& w) {
+  const int n = (int)w.size();
+  std::vector<Range> out(n);
+  const int64_t units = (N + A - 1) / A;
+  double tot = 0.0;
+  for (double x : w) tot += x;
+  double acc = 0.0;
+  int64_t u0 = 0;
+  for (int c = 0; c < n; ++c) {
+    acc += w[c];
+    const int64_t u1 = c == n - 1 ? units : std::min<int64_t>(units, (int64_t)std::llround(units * acc / tot));
+    out[c].r0 = (int)std::min<int64_t>(N, u0 * A);
+    out[c].r1 = (int)std::min<int64_t>(N, std::max(u0, u1) * A);
+    u0 = std::max(u0, u1);
   }
   return out;
 }
@@ -148,11 +169,13 @@ struct Builder {
   }
   // A GEMV stage: one task per CU with a non-empty row range, over the CUs not marked in `skip`.
   std::vector<int> gemv_stage(int type, int layer, int geom, int N, int A, int wait_ev,
-                              const std::vector<char>* skip = nullptr) {
+                              const std::vector<char>* skip = nullptr, const std::vector<double>* weight = nullptr) {
     std::vector<int> ids, cus;
     for (int cu = 0; cu < g.n_cus; ++cu)
       if (!skip || !(*skip)[cu]) cus.push_back(cu);
-    auto rs = distribute(N, A, (int)cus.size());
+    std::vector<double> w;
+    for (int cu : cus) w.push_back(weight ? (*weight)[cu] : 1.0);
+    auto rs = weight ? distribute_weighted(N, A, w) : distribute(N, A, (int)cus.size());
     for (size_t k = 0; k < cus.size(); ++k) {
       const int cu = cus[k];
       if (rs[k].r1 <= rs[k].r0) continue;
@@ -300,10 +323,10 @@ std::string build_graph(const mk_model_config& c, int n_cus, HostGraph& g) {
   // groups, each split by columns over kS CUs; each split then sums the kS partials of its share of
   // the tile's rows (a quarter-row-group granularity) and applies the epilogue to it.
   auto stage = [&](int type, int l, int geom, int N, int K, int align, int wait_ev,
-                   const std::vector<char>* skip) -> std::vector<StageTask> {
+                   const std::vector<char>* skip, const std::vector<double>* weight = nullptr) -> std::vector<StageTask> {
     std::vector<StageTask> out;
     if (S == 1) {
-      for (int id : b.gemv_stage(type, l, geom, N, align, wait_ev, skip)) {
+      for (int id : b.gemv_stage(type, l, geom, N, align, wait_ev, skip, weight)) {
         in_acc(id, type, l, 0, K);
         out.push_back({id, g.tasks[id].row0, g.tasks[id].row1, false});
       }
@@ -426,7 +449,13 @@ std::string build_graph(const mk_model_config& c, int n_cus, HostGraph& g) {
       out_acc(op[i].id, T_OPROJ, l, op[i].r0, op[i].r1, op[i].comb);
     }
     // ---- RMSNorm + gate/up + SwiGLU
-    auto gu = stage(T_GATEUP, l, G_GU, 2 * f, d, lcm_i(2, g.geoms[G_GU].rg), ev_o, nullptr);
+    // One sequence: the CUs that ran attention (and no O projection) start gate/up early, and CUs on
+    // odd XCDs (workgroup i runs on XCD i % 8) stream it measurably slower; their row shares are
+    // weighted so that the stage ends together (weights measured on the 8B decode).
+    std::vector<double> gu_w(n_cus, 1.0);
+    if (S == 1 && few_attn)
+      for (int cu = 0; cu < n_cus; ++cu) gu_w[cu] = 1.0 + (attn_cu[cu] ? 0.05 : 0.0) - ((cu & 1) ? 0.02 : 0.0);
+    auto gu = stage(T_GATEUP, l, G_GU, 2 * f, d, lcm_i(2, g.geoms[G_GU].rg), ev_o, nullptr, S == 1 && few_attn ? &gu_w : nullptr);
     if (!err.empty()) return err;
     const int ev_gu = b.new_event((int)gu.size());
     for (size_t i = 0; i < gu.size(); ++i) {
@@ -445,7 +474,10 @@ std::string build_graph(const mk_model_config& c, int n_cus, HostGraph& g) {
     }
   }
   // ---- final RMSNorm + LM head + partial argmax (one part per task)
-  auto lm = stage(T_LMHEAD, L, G_LM, V, d, g.geoms[G_LM].rg, ev_x, nullptr);
+  // the LM head streams about 7% slower on odd XCDs: their CUs take proportionally fewer rows
+  std::vector<double> lm_w(n_cus, 1.0);
+  for (int cu = 0; cu < n_cus; ++cu) lm_w[cu] = (cu & 1) ? 0.965 : 1.035;
+  auto lm = stage(T_LMHEAD, L, G_LM, V, d, g.geoms[G_LM].rg, ev_x, nullptr, S == 1 ? &lm_w : nullptr);
   if (!err.empty()) return err;
   g.n_lm_parts = (int)lm.size();
   g.sym_size[S_AMAX] = (int64_t)S * g.n_lm_parts;
