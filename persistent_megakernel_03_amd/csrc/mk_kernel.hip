@@ -198,6 +198,23 @@ __device__ __forceinline__ uint64_t ld_tag(__amdgpu_buffer_rsrc_t r, int voff, i
 }
 __device__ __forceinline__ uint32_t first_words(int n) { return n >= 32 ? ~0u : n <= 0 ? 0u : (1u << n) - 1u; }
 
+// Every 8th pass of a poll: whether the kernel is aborting, or the wait has outlived the watchdog
+// (then the timeout is raised, naming `what`, and the kernel aborts). The abort flag is a load of its
+// own that would double the time of every pass if read on each; an abort only drains the grid after
+// an error, so the few extra passes it takes to notice cost nothing that matters.
+__device__ __forceinline__ bool poll_give_up(const KernelParams& p, uint32_t pass, uint64_t t0, uint32_t what) {
+  if ((pass & 7u) != 0u) return false;
+  if (ldc(&p.err[E_ABORT])) return true;
+  if (__builtin_amdgcn_s_memrealtime() - t0 > p.watchdog_ticks) {
+    if ((threadIdx.x & 63) == 0) {
+      raise_error(p, ERR_TIMEOUT, what, p.epoch);
+      stc(&p.err[E_ABORT], 1u);
+    }
+    return true;
+  }
+  return false;
+}
+
 // Polls this thread's tagged words k (bit k of `pending`, k < K); word k sits at byte base + voff(k)
 // + soff(k), soff uniform across the wave. sink(k, bits) receives a word's low half once the word
 // carries the epoch. Each pass issues the loads of all words still stale before checking any. A wave
@@ -208,7 +225,7 @@ __device__ __forceinline__ void poll_tagged(const KernelParams& p, const uint64_
                                             uint32_t pending, uint32_t what, Sink sink) {
   const __amdgpu_buffer_rsrc_t r = tag_rsrc(base);
   const uint64_t t0 = __builtin_amdgcn_s_memrealtime();
-  while (true) {
+  for (uint32_t pass = 1;; ++pass) {
     uint64_t w[K];
 #pragma unroll
     for (int k = 0; k < K; ++k)
@@ -221,14 +238,7 @@ __device__ __forceinline__ void poll_tagged(const KernelParams& p, const uint64_
       }
     }
     if (!__any(pending != 0u)) break;
-    if (ldc(&p.err[E_ABORT])) break;
-    if (__builtin_amdgcn_s_memrealtime() - t0 > p.watchdog_ticks) {
-      if ((threadIdx.x & 63) == 0) {
-        raise_error(p, ERR_TIMEOUT, what, p.epoch);
-        stc(&p.err[E_ABORT], 1u);
-      }
-      break;
-    }
+    if (poll_give_up(p, pass, t0, what)) break;
     __builtin_amdgcn_s_sleep(1);
   }
 }
@@ -240,7 +250,7 @@ template <int K, typename Reload, typename Sink>
 __device__ __forceinline__ void poll_finish(const KernelParams& p, uint64_t (&w)[K], uint32_t pending, uint32_t what,
                                             Reload reload, Sink sink) {
   const uint64_t t0 = __builtin_amdgcn_s_memrealtime();
-  while (true) {
+  for (uint32_t pass = 1;; ++pass) {
 #pragma unroll
     for (int k = 0; k < K; ++k) {
       if (((pending >> k) & 1u) && (uint32_t)(w[k] >> 32) == p.epoch) {
@@ -249,14 +259,7 @@ __device__ __forceinline__ void poll_finish(const KernelParams& p, uint64_t (&w)
       }
     }
     if (!__any(pending != 0u)) break;
-    if (ldc(&p.err[E_ABORT])) break;
-    if (__builtin_amdgcn_s_memrealtime() - t0 > p.watchdog_ticks) {
-      if ((threadIdx.x & 63) == 0) {
-        raise_error(p, ERR_TIMEOUT, what, p.epoch);
-        stc(&p.err[E_ABORT], 1u);
-      }
-      break;
-    }
+    if (poll_give_up(p, pass, t0, what)) break;
     __builtin_amdgcn_s_sleep(1);
 #pragma unroll
     for (int k = 0; k < K; ++k)
