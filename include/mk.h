@@ -136,8 +136,11 @@ mk_status mk_load_weights(mk_ctx* ctx, const mk_tensor* ts, int n, void* stream)
  *   - It attends to positions 0..d_ctx_lens[s].
  *   - It writes its logits and greedy token (argmax, lowest index on ties).
  *   - d_ctx_lens[s] is incremented.
- * Asynchronous: one cooperative kernel launch on `stream`, with no host
- * synchronisation. n_seqs must be at most max_seqs. */
+ * Asynchronous: one kernel launch on `stream` (one workgroup per compute
+ * unit, all resident at once on a device running nothing else; with the
+ * environment variable MK_COOPERATIVE_LAUNCH set, a cooperative launch that
+ * the runtime guarantees co-resident), with no host synchronisation. n_seqs
+ * must be at most max_seqs. */
 mk_status mk_decode_step(mk_ctx* ctx, const int32_t* d_tokens_in, int n_seqs, int32_t* d_tokens_out, void* stream);
 
 /* The same decode step as mk_decode_step, launched as one kernel dispatch per dependency stage

@@ -1,8 +1,8 @@
 // Host runtime behind the C ABI declared in include/mk.h.
 //
 // It owns only host structures: the config and the task graph. All device memory
-// belongs to the caller and is bound once. A decode step is one cooperative
-// launch of the megakernel; the host does no synchronisation and no per-token
+// belongs to the caller and is bound once. A decode step is one launch of the
+// megakernel; the host does no synchronisation and no per-token
 // bookkeeping beyond incrementing the step epoch.
 #include <hip/hip_runtime.h>
 

@@ -20,6 +20,7 @@
 // Weights and the KV rows of earlier steps are immutable within a step. They are read with
 // plain nontemporal loads.
 #include <hip/hip_runtime.h>
+#include <cstdlib>
 #include <stdint.h>
 
 #include "mk_graph.h"
@@ -1794,8 +1795,17 @@ static const void* megakernel_for(int dh, int hq, int hk, bool batched) {
 hipError_t launch_megakernel(const KernelParams& p, int grid, size_t lds_bytes, hipStream_t stream) {
   KernelParams copy = p;
   void* args[] = {(void*)&copy};
-  return hipLaunchCooperativeKernel(megakernel_for(p.dh, p.hq, p.hk, p.max_seqs > 1), dim3(grid), dim3(NT), args,
-                                    (unsigned)lds_bytes, stream);
+  // The grid is one workgroup per CU and the LDS allows one per CU, so on a device running nothing
+  // else every workgroup is resident at once, which the task queues need. A plain launch is used:
+  // the cooperative launch path added about 18 us per dispatch on MI355X. Where other work may hold
+  // CUs, MK_COOPERATIVE_LAUNCH=1 makes the runtime guarantee co-residency. (Without it, waits that
+  // cannot be met end at the watchdog with an error, not in a hang.)
+  static const bool coop = std::getenv("MK_COOPERATIVE_LAUNCH") != nullptr;
+  if (coop)
+    return hipLaunchCooperativeKernel(megakernel_for(p.dh, p.hq, p.hk, p.max_seqs > 1), dim3(grid), dim3(NT), args,
+                                      (unsigned)lds_bytes, stream);
+  return hipLaunchKernel(megakernel_for(p.dh, p.hq, p.hk, p.max_seqs > 1), dim3(grid), dim3(NT), args,
+                         (unsigned)lds_bytes, stream);
 }
 
 hipError_t megakernel_occupancy(int* blocks_per_cu, size_t lds_bytes, int dh, int hq, int hk, bool batched) {
