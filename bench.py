@@ -26,6 +26,29 @@ def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
+def cpu_model():
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def timed_steps(torch, stream, step, K):
+    """Runs step() K times between events recorded on `stream` before the first and after every step;
+    returns (ms over all K steps, per-step ms)."""
+    evs = [torch.cuda.Event(enable_timing=True) for _ in range(K + 1)]
+    torch.cuda.synchronize()
+    evs[0].record(stream)
+    for i in range(K):
+        step()
+        evs[i + 1].record(stream)
+    torch.cuda.synchronize()
+    return evs[0].elapsed_time(evs[K]), [evs[i].elapsed_time(evs[i + 1]) for i in range(K)]
+
+
 def cpu_baseline(shape, weights, prompt, seconds):
     """The oracle as it stands, on this host's cores: decode steps of the same model from
     position 0 (teacher-forced on the prompt tokens) until `seconds` have passed."""
@@ -45,6 +68,7 @@ def cpu_baseline(shape, weights, prompt, seconds):
     om.close()
     ms = 1e3 * sum(times) / len(times)
     return {"value": ms, "unit": "ms/token", "tokens_per_s": 1e3 / ms, "cores": orc.threads(), "kind": "oracle",
+            "cpu": cpu_model(),
             "sample": "%d decode steps of the full model at positions 0..%d (fp64 oracle, all weights streamed "
                       "from host memory each step)" % (len(times), len(times) - 1)}
 
@@ -72,6 +96,7 @@ def cpu_baseline_batched(wl, weights, seconds):
     om.close()
     ms = 1e3 * sum(times) / len(times)
     return {"value": ms, "unit": "ms/token", "tokens_per_s": 1e3 / ms, "cores": orc.threads(), "kind": "oracle",
+            "cpu": cpu_model(),
             "sample": "%d decode steps of sequence 0 alone (context %d, fp64 oracle, weights streamed from host "
                       "memory each step)" % (len(times), ctx0)}
 
@@ -82,9 +107,10 @@ def si_mod():
 
 
 def bench_batched(args, wl):
-    """Batched decode: all sequences of the workload in every step, each from its own KV cache
-    pre-filled to its context length (seeded N(0, 1) bf16 values, keys taken as rotated), pages
-    permuted. A step's algorithmic bytes are the weights once plus every sequence's KV rows."""
+    """Decode from pre-filled caches: all sequences of the workload in every step (one for the long-
+    context workload, several for the batched ones), each from its own KV cache pre-filled to its
+    context length, pages permuted. A step's algorithmic bytes are the weights once plus every
+    sequence's KV rows."""
     import numpy as np
     import torch
     import persistent_megakernel_03_amd as mk
@@ -117,14 +143,8 @@ def bench_batched(args, wl):
     dec.set_ctx_lens(ctx)
     dec.tokens[:n].copy_(first)
     stream = torch.cuda.current_stream(dec.dev)
-    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize(dec.dev)
-    ev0.record(stream)
-    for _ in range(K):
-        dec.step(dec.tokens, n)
-    ev1.record(stream)
-    torch.cuda.synchronize(dec.dev)
-    ms = ev0.elapsed_time(ev1) / K
+    ms_total, per_step = timed_steps(torch, stream, lambda: dec.step(dec.tokens, n), K)
+    ms = ms_total / K
     dec.sync_check()
     assert (dec.ctx_lens.cpu().numpy()[:n] == ctx + K).all()
     bytes_avg = sum(rf.step_bytes(m, list(ctx + i + 1)) for i in range(K)) / K
@@ -140,14 +160,23 @@ def bench_batched(args, wl):
     traffic = None
     if wl.name == "llama8b_b16":
         traffic = rf.profiled_traffic(os.path.join(ROOT, "profiles", "mk_megakernel_llama8b_b16_decode.md"))
+    if n == 1:
+        metric = "decode ms/token (batch 1, %s-shape bf16, %d-position context); achieved HBM GB/s vs peak" % (
+            m.name, int(ctx[0]))
+        workload = "%s: one sequence, cache pre-filled to %d positions, %d steps" % (wl.name, int(ctx[0]), K)
+    else:
+        metric = "decode ms/step (%d sequences, %s-shape bf16); achieved HBM GB/s vs peak" % (n, m.name)
+        workload = "%s: %d sequences, contexts %d..%d (seeded uniform in [%d, %d]), %d steps" % (
+            wl.name, n, int(ctx.min()), int(ctx.max()), wl.ctx_range[0], wl.ctx_range[1], K)
     out = {
-        "metric": "decode ms/step (%d sequences, %s-shape bf16); achieved HBM GB/s vs peak" % (n, m.name),
+        "metric": metric,
         "value": round(ms, 5),
-        "unit": "ms/step",
+        "unit": "ms/token" if n == 1 else "ms/step",
         "n_gpus": 1,
         "steps": K,
         "warmup": W,
         "ms_per_step": round(ms, 5),
+        "ms_per_step_median": round(float(np.median(per_step)), 5),
         "tokens_per_s": round(n * 1e3 / ms, 1),
         "achieved_hbm_gbs": round(achieved, 1),
         "higher_is_better": False,
@@ -156,14 +185,14 @@ def bench_batched(args, wl):
         "dtype": "f32",
         "weights_dtype": "bf16",
         "data": "synthetic",
-        "config": {"workload": "%s: %d sequences, contexts %d..%d (seeded uniform in [%d, %d]), %d steps"
-                               % (wl.name, n, int(ctx.min()), int(ctx.max()), wl.ctx_range[0], wl.ctx_range[1], K),
+        "config": {"workload": workload,
                    "batch": n, "decode_steps": K, "weight_bytes_per_step": rf.weight_bytes_per_token(m),
                    "kv": "bf16, paged in 16-token blocks, permuted page tables"},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": rf.MI355X_HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(achieved / rf.MI355X_HBM_PEAK_GBS, 4), "traffic": traffic,
                      "traffic_unit": "HBM bytes/launch (FETCH_SIZE + WRITE_SIZE, copy-calibrated)",
-                     "bytes_per_launch": int(bytes_avg), "kernel": "mk_megakernel, batched (one launch per step)"},
+                     "bytes_per_launch": int(bytes_avg),
+                     "kernel": "mk_megakernel%s (one launch per step)" % (", batched" if n > 1 else "")},
         "cpu_baseline": cpu,
     }
     print(json.dumps(out), flush=True)
@@ -204,12 +233,8 @@ def main():
 
     wl = si.WORKLOADS[args.workload]
     m = wl.model
-    if wl.n_seqs > 1:
+    if wl.n_seqs > 1 or wl.prompt_len == 0:  # pre-filled caches: the batched and long-context workloads
         return bench_batched(args, wl)
-    if wl.prompt_len == 0:
-        print("bench.py times the prompt workloads (tiny, qwen0.5b, llama8b) and the batched ones "
-              "(llama8b_b16, mid_b16, tiny_b4)", file=sys.stderr)
-        sys.exit(2)
     K, W = args.steps, args.warmup
     P = wl.prompt_len
     n_pos = P + max(K, W)
@@ -236,13 +261,7 @@ def main():
     tokens.copy_(g0)
     stream = torch.cuda.current_stream(dec.dev)
     ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize(dec.dev)
-    ev0.record(stream)
-    for _ in range(K):
-        dec.step(tokens)
-    ev1.record(stream)
-    torch.cuda.synchronize(dec.dev)
-    ms_total = ev0.elapsed_time(ev1)
+    ms_total, per_step = timed_steps(torch, stream, lambda: dec.step(tokens), K)
     dec.sync_check()
     assert int(dec.ctx_lens.item()) == P + K
     ms = ms_total / K
@@ -299,13 +318,14 @@ def main():
         log("cpu baseline: %.1f ms/token on %d cores (%.1fs)" % (cpu["value"], cpu["cores"], time.time() - t0))
 
     out = {
-        "metric": METRIC,
+        "metric": METRIC if m.name == "llama8b" else METRIC.replace("8B-shape", "%s-shape" % m.name),
         "value": round(ms, 5),
         "unit": "ms/token",
         "n_gpus": 1,
         "steps": K,
         "warmup": W,
         "ms_per_step": round(ms, 5),
+        "ms_per_step_median": round(float(np.median(per_step)), 5),
         "tokens_per_s": round(1e3 / ms, 2),
         "achieved_hbm_gbs": round(achieved, 1),
         "higher_is_better": False,

@@ -225,10 +225,12 @@ std::string build_graph(const mk_model_config& c, int n_cus, HostGraph& g) {
   if (c.attn_splits > 0) {
     g.splits = c.attn_splits;
   } else if (S == 1) {
-    // one sequence: attention is a latency hop between two stages, and eight tasks per KV head (the
-    // step's blocks cut evenly over them) measured fastest on the 8B decode across contexts from 60
-    // to 400 positions; more tasks take too many CUs away from the O projection
-    g.splits = std::max(1, std::min(8, c.max_blocks_per_seq));
+    // one sequence: with a short cache attention is a latency hop between two stages, and eight tasks
+    // per KV head (the step's blocks cut evenly over them) measured fastest on the 8B decode across
+    // contexts from 60 to 400 positions; more tasks take CUs away from the O projection. A long cache
+    // makes attention the largest stream of the layer, so the tasks grow with it, to 32 per KV head
+    // from 2,048 blocks (32K positions) on.
+    g.splits = std::max(1, std::min(c.max_blocks_per_seq, std::clamp(c.max_blocks_per_seq / 64, 8, 32)));
   } else {
     // about one staged chunk of positions per split (8 waves x 64/(dh/8) positions x 4 slots)
     const int chunk_blocks = 8 * (64 / (dh / 8)) * 4 / 16;
