@@ -90,6 +90,15 @@ def test_tiny_permuted_pages_bit_identical(tiny):
     a.close(); b.close()
 
 
+def test_tiny_min_blocks_per_attention_task(tiny):
+    # at least 4 cache blocks per attention task: the tiny contexts run on fewer tasks than the graph has
+    w, prompt, wl = tiny
+    log("case: tiny attn_splits 3, attn_min_blocks 4")
+    res = teacher_forced(si.TINY, w, prompt, 8, attn_splits=3, paging="permuted", attn_min_blocks=4)
+    check(res, "tiny min blocks 4")
+    res["dec"].close()
+
+
 @pytest.mark.parametrize("splits", [1, 2, 3])
 def test_tiny_split_counts(tiny, splits):
     # one cache block per task at least: the tiny contexts then split each KV head's blocks over

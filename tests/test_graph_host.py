@@ -64,6 +64,21 @@ def test_graph_validates(L, shape, blocks):
         mk.mk_destroy(ctx)
 
 
+@pytest.mark.parametrize("blocks,attn_tasks", [(35, 64), (512, 64), (2052, 256)])
+def test_one_sequence_attention_split_rule(L, blocks, attn_tasks):
+    # one sequence at the 8B shape: 8 attention tasks per KV head for a short cache, growing with a long
+    # one (blocks / 64 per KV head, at most 32): 256 tasks, one per CU, at 32K positions
+    ctx = mk.mk_create_host(cfg_for(si.LLAMA8B, blocks, blocks), 256)
+    try:
+        info = mk.mk_graph_stats(ctx)
+        m = si.LLAMA8B
+        other = m.n_layers * 256 * 3 + 256 + 1  # QKV, gate/up and down on every CU, the LM head, the argmax
+        o_tasks = 256 - attn_tasks if attn_tasks * 4 <= 256 else 256  # O skips the attention CUs when they are few
+        assert info.n_tasks == other + m.n_layers * (attn_tasks + o_tasks)
+    finally:
+        mk.mk_destroy(ctx)
+
+
 def test_8b_tiles_have_no_padding(L):
     ctx = mk.mk_create_host(cfg_for(si.LLAMA8B, 35, 35), 256)
     try:
