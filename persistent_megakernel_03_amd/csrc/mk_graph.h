@@ -34,6 +34,11 @@ constexpr int kStageUnits = 10;
 // blocks. With 1, every attention task gets blocks once there are as many blocks as tasks: on
 // MI355X the extra merges cost less than fewer, longer tasks.
 constexpr int kAttnMinBlocks = 1;
+// Several sequences: the blocks are cut by cost instead, each block costing 1 and each segment start
+// (a new (sequence, KV head) piece for a task to begin) kAttnPieceBlocks more. On MI355X a piece costs
+// a query poll that waits behind its first row loads, the wave merges and a partial write: with 16
+// sequences of mixed lengths, about 24 blocks' streaming.
+constexpr int kAttnPieceBlocks = 24;
 constexpr int kStageBytes = 8 * kStageUnits * 1024;
 
 // Geometry of one GEMV operand in the packed (streaming) layout. A row of K bf16 values is

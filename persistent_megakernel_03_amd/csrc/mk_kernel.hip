@@ -609,13 +609,42 @@ struct AttnShape {
   static constexpr int EPT = (GMAX * DH + NT - 1) / NT;  // output elements (head, dim) per thread
 };
 
-// First block of attention task i's range: T tasks cut W blocks evenly.
-// (W * i / T for i = 0..T is tabulated in LDS once per launch: alo[i]; tasks past the T used this
-// step start at W.)
+// First block of attention task i's range: T tasks cut W blocks evenly. (The first blocks are
+// tabulated in LDS once per launch, alo[i] for i = 0..T; tasks past the T used this step start at W.)
 __device__ __forceinline__ int attn_lo_of(int W, int T, int i) { return (int)((uint32_t)W * (uint32_t)i / (uint32_t)T); }
-// The task whose range holds block x: the last i with alo[i] <= x.
+// With a cost per segment start PB > 0: T tasks cut the layer's cost evenly, where each block costs 1
+// and each segment start after the first PB more (a cut that lands inside a start's cost falls on the
+// segment's first block). Segment j (s, g) covers blocks aoff[s] + g nb .. + nb, nb = anb[s], and costs
+// [S_j + PB j, S_j+1 + PB j) plus the PB before the next start.
+__device__ int attn_lo_cost(const Ctl* ctl, int hk, int W, int T, int i, int PB) {
+  if (PB == 0 || W == 0) return attn_lo_of(W, T, i);
+  int nseg = 0;
+  for (int s = 0; s < 16; ++s) nseg += ctl->anb[s] > 0 ? hk : 0;
+  const int64_t t = ((int64_t)W + (int64_t)PB * (nseg - 1)) * i / T;
+  int j = 0;
+  for (int s = 0; s < 16; ++s) {
+    const int nb = ctl->anb[s];
+    if (nb == 0) continue;
+    for (int g = 0; g < hk; ++g, ++j) {
+      const int64_t s0 = ctl->aoff[s] + (int64_t)g * nb, s1 = s0 + nb;
+      if (t < s1 + (int64_t)PB * (j + 1)) return (int)min(s1, max(s0, t - (int64_t)PB * j));
+    }
+  }
+  return W;
+}
+// The task whose range holds block x: the last i < T with alo[i] <= x. With an even cut of W blocks
+// this has a closed form; with a cut by cost, a search of alo (in LDS, non-decreasing).
 __device__ __forceinline__ int attn_task_of(int W, int T, int x) {
   return min(T - 1, (int)(((uint32_t)(x + 1) * (uint32_t)T - 1u) / (uint32_t)W));
+}
+__device__ __forceinline__ int attn_task_of(const int32_t* alo, int T, int x) {
+  int lo = 0, hi = T - 1;
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) >> 1;
+    if (alo[mid] <= x) lo = mid;
+    else hi = mid - 1;
+  }
+  return lo;
 }
 
 // Scores of one position for every head: s_h = q_h . k, this lane's 8 dimensions summed over the
@@ -871,7 +900,7 @@ __device__ __forceinline__ void attn_part(const KernelParams& p, const TaskDesc&
   }
 }
 
-template <int DH, int GMAX, int ANS>
+template <int DH, int GMAX, int ANS, bool COST>
 __device__ __forceinline__ void task_attn(const KernelParams& p, const TaskDesc& t, float* lds, Ctl* ctl,
                                           uint16_t* const* pools, const int32_t* alo) {
   using AS = AttnShape<DH, GMAX>;
@@ -889,14 +918,26 @@ __device__ __forceinline__ void task_attn(const KernelParams& p, const TaskDesc&
     while (s < 15 && ctl->aoff[s + 1] <= x) ++s;
     return __builtin_amdgcn_readfirstlane(ctl->aoff[s] + (x - ctl->aoff[s]) / ctl->anb[s] * ctl->anb[s]);
   };
+  auto seg_end = [&](int x) {  // one past the last block of the segment holding block x
+    int s = 0;
+    while (s < 15 && ctl->aoff[s + 1] <= x) ++s;
+    return seg_start(x) + __builtin_amdgcn_readfirstlane(ctl->anb[s]);
+  };
   // When the task's last segment goes on past it, that partial is computed and written first: partials
   // never wait on merges, so a merge waits at most for its writers' streaming, never for a chain of
-  // other merges.
+  // other merges. The rest of the range follows in block order, or, with a cut by cost (where a task
+  // may hold several whole segments), the segments that lie whole in the range first and last the
+  // piece that ends a segment begun by earlier tasks: its merge polls their partials, which by then
+  // have had the longest to land.
   const int b_last = hi > lo ? max(lo, seg_start(hi - 1)) : hi;
   int s_last = 0;
   while (hi > lo && s_last < 15 && ctl->aoff[s_last + 1] <= hi - 1) ++s_last;
   const bool last_partial = hi > lo && seg_start(hi - 1) + __builtin_amdgcn_readfirstlane(ctl->anb[s_last]) > hi;
-  for (int k = 0, x = last_partial ? b_last : lo; x < hi; ++k) {
+  const int p_end = last_partial ? b_last : hi;  // the partial is [b_last, hi)
+  const int lead_end = hi > lo && seg_start(lo) < lo ? min(hi, seg_end(lo)) : lo;  // the merge piece: [lo, lead_end)
+  const bool lead = lead_end > lo && p_end > lo;  // (with b_last == lo the whole range is the partial)
+  int phase = last_partial ? 0 : lead_end < p_end ? 1 : 2;
+  for (int k = 0, x = COST ? (phase == 0 ? b_last : phase == 1 ? lead_end : lo) : (last_partial ? b_last : lo); x < hi; ++k) {
     // the segment holding block x (values read from LDS are made explicitly wave-uniform, so that the
     // page-table reads that depend on them are scalar loads)
     int s = 0;
@@ -930,7 +971,8 @@ __device__ __forceinline__ void task_attn(const KernelParams& p, const TaskDesc&
     } else {
       // This task holds the segment's last block: merge the earlier tasks' partials in task order,
       // then its own, R tasks per poll round (3 words per task and element: m, l, o[dim]).
-      const int first = attn_task_of(W, __builtin_amdgcn_readfirstlane(ctl->ate), B);
+      const int first = COST ? __builtin_amdgcn_readfirstlane(attn_task_of(alo, __builtin_amdgcn_readfirstlane(ctl->ate), B))
+                             : attn_task_of(W, __builtin_amdgcn_readfirstlane(ctl->ate), B);
       float Mm[EPT], Lm[EPT], Am[EPT];
 #pragma unroll
       for (int e = 0; e < EPT; ++e) {
@@ -1006,13 +1048,27 @@ __device__ __forceinline__ void task_attn(const KernelParams& p, const TaskDesc&
       }
     }
     bar();  // the next part reuses the LDS staging
-    // after the leading partial, go back to the start of the range; stop before the partial's blocks
-    if (last_partial && k == 0) {
-      if (b_last == lo) break;
-      x = lo;
+    if constexpr (COST) {
+      if (phase == 1 && xe < p_end) {
+        x = xe;  // the next whole segment
+      } else if (phase == 0 && lead_end < p_end) {
+        phase = 1;
+        x = lead_end;
+      } else if (phase <= 1 && lead) {
+        phase = 2;
+        x = lo;
+      } else {
+        break;
+      }
     } else {
-      x = xe;
-      if (last_partial && x >= b_last) break;
+      // after the leading partial, go back to the start of the range; stop before the partial's blocks
+      if (last_partial && k == 0) {
+        if (b_last == lo) break;
+        x = lo;
+      } else {
+        x = xe;
+        if (last_partial && x >= b_last) break;
+      }
     }
   }
 }
@@ -1671,7 +1727,11 @@ __global__ __launch_bounds__(NT, 1) void mk_megakernel(KernelParams p) {
   bar();
   {
     const int W = ctl->aoff[16], te = min(p.attn_tasks, max(1, (W + p.attn_min_blocks - 1) / p.attn_min_blocks));
-    for (int i = threadIdx.x; i <= p.attn_tasks; i += NT) alo[i] = attn_lo_of(W, te, min(i, te));
+    if constexpr (BATCHED) {  // several sequences: a cut by cost, each segment start counting kAttnPieceBlocks blocks
+      for (int i = threadIdx.x; i <= p.attn_tasks; i += NT) alo[i] = attn_lo_cost(ctl, p.hk, W, te, min(i, te), kAttnPieceBlocks);
+    } else {
+      for (int i = threadIdx.x; i <= p.attn_tasks; i += NT) alo[i] = attn_lo_of(W, te, min(i, te));
+    }
     if (threadIdx.x == 0) ctl->ate = te;
   }
   bar();
@@ -1693,7 +1753,7 @@ __global__ __launch_bounds__(NT, 1) void mk_megakernel(KernelParams p) {
     if (t.type == T_ATTN) {
       // position groups in flight per wave: more for batches (long streams), fewer for one sequence
       // and for many heads per KV head (register budget)
-      task_attn<DH, GMAX, (GMAX > 4 || !BATCHED) ? 4 : 8>(p, t, lds, ctl, pools, alo);
+      task_attn<DH, GMAX, (GMAX > 4 || !BATCHED) ? 4 : 8, BATCHED>(p, t, lds, ctl, pools, alo);
       staged = false;
     } else if (t.type == T_ARGMAX) {
       staged = false;
