@@ -65,7 +65,10 @@ typedef struct mk_ctx mk_ctx; /* opaque, owned by the library */
  *     max_seqs * n_kv_heads * attn_splits (and at most one per compute unit).
  *   - attn_min_blocks: each step cuts its cache blocks over at most
  *     ceil(blocks / attn_min_blocks) of those tasks (fewer tasks, fewer
- *     merges); 0 = 1, every task gets blocks once there are enough. */
+ *     merges); 0 = 1, every task gets blocks once there are enough.
+ *     With max_seqs > 1 the cut is by cost: each (sequence, KV head)
+ *     segment start counts as 24 blocks more, so a task that begins
+ *     several segments gets fewer blocks (possibly none). */
 typedef struct {
   int32_t n_layers, d_model, n_q_heads, n_kv_heads, head_dim, d_ffn, vocab;
   float rms_eps, rope_theta;
