@@ -84,6 +84,8 @@ WORKLOADS = {
     # small batched workloads with the same structure (per-sequence contexts, permuted pages)
     "tiny_b4": Workload("tiny_b4", TINY, 4, steps=8, ctx_range=(5, 60), paging="permuted"),
     "mid_b16": Workload("mid_b16", MID, 16, steps=4, ctx_range=(16, 300), paging="permuted"),
+    # longer mixed contexts: with one split per KV head an attention task holds up to three pieces
+    "mid_b16_long": Workload("mid_b16_long", MID, 16, steps=2, ctx_range=(256, 2048), paging="permuted"),
 }
 
 

@@ -24,11 +24,11 @@ def log(*a):
     sys.stdout.flush()
 
 
-def run_batched(wl, n_decode, n_active=None):
+def run_batched(wl, n_decode, n_active=None, attn_splits=0):
     import torch
     n = wl.n_seqs
     na = n if n_active is None else n_active
-    dec, om, ctx, table, w = prefilled_case(wl, n_decode)
+    dec, om, ctx, table, w = prefilled_case(wl, n_decode, attn_splits=attn_splits)
     toks = si.first_tokens(wl).astype(np.int64).copy()
     rels, agree, gaps_bad = [], [], []
     out = torch.zeros(n, dtype=torch.int32, device=dec.dev)
@@ -83,6 +83,13 @@ def test_mid_sixteen_sequences_row_tiles(monkeypatch):
     monkeypatch.setenv("MK_BATCHED_MAX_KSPLIT", "1")
     log("case: mid_b16, 16 sequences, 2 steps, row tiles only")
     run_batched(si.WORKLOADS["mid_b16"], 2)
+
+
+def test_mid_long_contexts_several_pieces_per_task():
+    # one split per KV head (64 attention tasks) over contexts 300..1847: the cut by cost gives tasks
+    # two whole segments, or the end of a segment (merged last) plus whole segments plus a partial
+    log("case: mid_b16_long, 16 sequences, 2 steps, 64 attention tasks")
+    run_batched(si.WORKLOADS["mid_b16_long"], 2, attn_splits=1)
 
 
 @pytest.mark.timeout(900)
