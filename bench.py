@@ -26,14 +26,26 @@ def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
-def cpu_model():
+def cpu_info():
+    """The host CPU as /proc/cpuinfo names it (model string, family/model/stepping) and the cores this
+    process may use."""
+    info = {"model": "unknown", "family": None, "model_id": None, "stepping": None}
     try:
         for line in open("/proc/cpuinfo"):
-            if line.startswith("model name"):
-                return line.split(":", 1)[1].strip()
+            k, _, v = line.partition(":")
+            k, v = k.strip(), v.strip()
+            if k == "model name" and info["model"] == "unknown":
+                info["model"] = v
+            elif k == "cpu family" and info["family"] is None:
+                info["family"] = v
+            elif k == "model" and info["model_id"] is None:
+                info["model_id"] = v
+            elif k == "stepping" and info["stepping"] is None:
+                info["stepping"] = v
     except OSError:
         pass
-    return "unknown"
+    info["cores"] = len(os.sched_getaffinity(0))
+    return info
 
 
 def timed_steps(torch, stream, step, K):
@@ -49,61 +61,113 @@ def timed_steps(torch, stream, step, K):
     return evs[0].elapsed_time(evs[K]), [evs[i].elapsed_time(evs[i + 1]) for i in range(K)]
 
 
-def cpu_baseline(shape, weights, prompt, seconds):
-    """The oracle as it stands, on this host's cores: decode steps of the same model from
-    position 0 (teacher-forced on the prompt tokens) until `seconds` have passed."""
-    import oracle as orc
-    cores = len(os.sched_getaffinity(0))
-    orc.set_threads(cores)
-    n_max = max(2, len(prompt))
-    om = orc.OracleModel(shape, weights, 1, n_max)
-    times = []
-    t_all = time.perf_counter()
-    for i in range(n_max):
-        t0 = time.perf_counter()
-        om.step(0, int(prompt[i]), i)
-        times.append(time.perf_counter() - t0)
-        if time.perf_counter() - t_all > seconds and len(times) >= 2:
-            break
-    om.close()
-    ms = 1e3 * sum(times) / len(times)
-    return {"value": ms, "unit": "ms/token", "tokens_per_s": 1e3 / ms, "cores": orc.threads(), "kind": "oracle",
-            "cpu": cpu_model(),
-            "sample": "%d decode steps of the full model at positions 0..%d (fp64 oracle, all weights streamed "
-                      "from host memory each step)" % (len(times), len(times) - 1)}
+def timed_once(torch, stream, fn):
+    """ms of one call of fn() between two events on `stream`."""
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record(stream)
+    fn()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1)
 
 
-def cpu_baseline_batched(wl, weights, seconds):
-    """The oracle on this host's cores over a bounded sample of a batched workload: sequence 0 alone,
-    its KV cache pre-filled as in the workload, decode steps at its context length."""
+def oracle_sample(wl, weights, positions, precision, seconds):
+    """The oracle as it stands, on this host's cores: single-sequence decode steps of the workload's model
+    at the given positions, with a cache holding the workload's seeded N(0, 1) K/V below each position
+    (the values do not change the work). Stops after `seconds` (at least 2 steps).
+    Returns (ms per step, steps run, threads)."""
     import oracle as orc
+    si = si_mod()
+    orc.set_threads(len(os.sched_getaffinity(0)))
     m = wl.model
-    cores = len(os.sched_getaffinity(0))
-    orc.set_threads(cores)
-    ctx0 = int(si_mod().context_lengths(wl)[0])
-    om = orc.OracleModel(m, weights, 1, ctx0 + 4)
+    max_pos = max(positions) + 1
+    om = orc.OracleModel(m, weights, 1, max_pos, precision=precision)
     for l in range(m.n_layers):
-        om.set_kv(l, 0, 0, si_mod().kv_fill(wl, l, 0, ctx0, "k"), si_mod().kv_fill(wl, l, 0, ctx0, "v"))
-    tok = int(si_mod().first_tokens(wl)[0])
+        om.set_kv(l, 0, 0, si.kv_fill(wl, l, 0, max_pos, "k"), si.kv_fill(wl, l, 0, max_pos, "v"))
     times = []
     t_all = time.perf_counter()
-    for i in range(4):
+    for i, pos in enumerate(positions):
         t0 = time.perf_counter()
-        tok, _ = om.step(0, tok, ctx0 + i)
+        om.step(0, (1 + 7919 * i) % m.vocab, pos)
         times.append(time.perf_counter() - t0)
         if time.perf_counter() - t_all > seconds and len(times) >= 2:
             break
+    th = orc.threads()
     om.close()
-    ms = 1e3 * sum(times) / len(times)
-    return {"value": ms, "unit": "ms/token", "tokens_per_s": 1e3 / ms, "cores": orc.threads(), "kind": "oracle",
-            "cpu": cpu_model(),
-            "sample": "%d decode steps of sequence 0 alone (context %d, fp64 oracle, weights streamed from host "
-                      "memory each step)" % (len(times), ctx0)}
+    return 1e3 * sum(times) / len(times), len(times), th
+
+
+def cpu_baseline(wl, weights, positions, seconds, what):
+    """The plain fp32 oracle (the reported baseline) and its fp64 build beside it, each on a bounded
+    sample of the timed workload's decode steps."""
+    cpu = cpu_info()
+    ms32, n32, th32 = oracle_sample(wl, weights, positions, "f32", seconds * 0.5)
+    ms64, n64, _ = oracle_sample(wl, weights, positions, "f64", seconds * 0.5)
+    return {"value": ms32, "unit": "ms/token", "tokens_per_s": 1e3 / ms32, "cores": th32, "kind": "oracle",
+            "precision": "fp32 (plain C, OpenMP over rows and heads)",
+            "cpu": cpu["model"], "cpu_family_model_stepping": [cpu["family"], cpu["model_id"], cpu["stepping"]],
+            "sample": "%d single-sequence decode steps of the full model (%s) at positions %s; weights read "
+                      "from host memory each step" % (n32, what, ", ".join(str(p) for p in positions[:n32])),
+            "fp64": {"value": ms64, "unit": "ms/token", "steps": n64,
+                     "what": "the fp64 build of the same oracle (the parity reference), same positions"},
+            "note": "a reported baseline, not the optimisation target"}
+
+
+def spread(lo, hi, n):
+    """n integer points spread evenly over [lo, hi]."""
+    if n <= 1 or hi <= lo:
+        return [lo]
+    return [lo + (hi - lo) * i // (n - 1) for i in range(n)]
+
+
+def graph_info(mk, dec):
+    """The task graph the timed decoder runs (what the parity tests pin by hash)."""
+    info = mk.mk_graph_stats(dec.ctx)
+    c = dec.cfg
+    return {"n_cus": int(info.n_cus), "max_blocks_per_seq": int(c.max_blocks_per_seq), "num_blocks": int(c.num_blocks),
+            "n_tasks": int(info.n_tasks), "attn_tasks_per_layer": int(info.attn_tasks),
+            "n_stages": int(info.n_stages), "max_queue_len": int(info.max_queue_len),
+            "hash": "0x%016x" % int(info.hash)}
 
 
 def si_mod():
     import seeded_inputs as si
     return si
+
+
+def decode_legs(torch, dec, n, K, first, reset, stream):
+    """The timed decode of K greedy steps of n sequences from one starting state, two ways:
+      - resident: mk_decode_n, all K steps in one launch (each step's argmax feeds the next on the device);
+      - per launch: K calls of mk_decode_step, one launch each, events around every step.
+    reset() restores the starting context lengths. Returns (resident ms, per-launch ms, per-step ms list,
+    whether both produced the same tokens)."""
+    toks = torch.zeros((K + 1, n), dtype=torch.int32, device=dec.dev)
+    toks[0].copy_(first)
+    reset()
+    rows = iter(range(K))
+
+    def one_step():  # step i reads row i and writes row i + 1
+        i = next(rows)
+        dec.step(toks[i], n, toks[i + 1])
+
+    ms_launch, per_step = timed_steps(torch, stream, one_step, K)
+    dec.sync_check()
+    reset()
+    out = torch.zeros((K, n), dtype=torch.int32, device=dec.dev)
+    ms_res = timed_once(torch, stream, lambda: dec.decode_n(first, K, n, out))
+    dec.sync_check()
+    same = bool(torch.equal(out, toks[1:]))
+    return ms_res, ms_launch, per_step, same
+
+
+def finish(dec):
+    """Release the decoder and its device buffers, with the device idle, before the process exits."""
+    import torch
+    torch.cuda.synchronize()
+    dec.close()
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
 
 
 def bench_batched(args, wl):
@@ -118,9 +182,10 @@ def bench_batched(args, wl):
     si = si_mod()
     m = wl.model
     n = wl.n_seqs
-    K, W = min(args.steps, wl.steps), args.warmup
+    K, W = args.steps if args.steps else wl.steps, args.warmup
     ctx = si.context_lengths(wl).astype(np.int64)
-    cap = ctx + max(K, W)
+    # the cache (and so the task graph) holds the workload's full decode, whatever K is
+    cap = ctx + max(wl.steps, K, W)
     table, nblocks = si.block_tables(wl, cap)
     t0 = time.time()
     weights = si.gen_weights(m)
@@ -129,6 +194,7 @@ def bench_batched(args, wl):
     dec = mk.Decoder(cfg, 0)
     dec.load_weights(weights)
     dec.set_page_table(table)
+    graph = graph_info(mk, dec)
     # cache contents do not change the work; fill them on the device from a seeded generator
     g = torch.Generator(device=dec.dev)
     g.manual_seed(1234)
@@ -140,22 +206,22 @@ def bench_batched(args, wl):
     for _ in range(W):
         dec.step(dec.tokens, n)
     dec.sync_check()
-    dec.set_ctx_lens(ctx)
-    dec.tokens[:n].copy_(first)
     stream = torch.cuda.current_stream(dec.dev)
-    ms_total, per_step = timed_steps(torch, stream, lambda: dec.step(dec.tokens, n), K)
-    ms = ms_total / K
-    dec.sync_check()
+    ms_res, ms_launch, per_step, same = decode_legs(torch, dec, n, K, first, lambda: dec.set_ctx_lens(ctx), stream)
     assert (dec.ctx_lens.cpu().numpy()[:n] == ctx + K).all()
+    ms, ms1 = ms_res / K, ms_launch / K
     bytes_avg = sum(rf.step_bytes(m, list(ctx + i + 1)) for i in range(K)) / K
     achieved = bytes_avg / (ms * 1e-3) / 1e9
-    log("batched decode (%d sequences): %.4f ms/step, %.1f tok/s, %.1f GB/s (%.1f%% of %.0f GB/s)" %
-        (n, ms, n * 1e3 / ms, achieved, 100 * achieved / rf.MI355X_HBM_PEAK_GBS, rf.MI355X_HBM_PEAK_GBS))
-    dec.close()
+    log("decode (%d sequences): resident %.4f ms/step, one launch per step %.4f ms/step; %.1f GB/s "
+        "(%.1f%% of %.0f GB/s); tokens equal: %s" % (n, ms, ms1, achieved, 100 * achieved / rf.MI355X_HBM_PEAK_GBS,
+                                                    rf.MI355X_HBM_PEAK_GBS, same))
+    finish(dec)
     cpu = None
     if not args.no_cpu_baseline:
         t0 = time.time()
-        cpu = cpu_baseline_batched(wl, weights, args.cpu_seconds)
+        c0 = int(ctx[0])
+        cpu = cpu_baseline(wl, weights, spread(c0, c0 + K - 1, 8), args.cpu_seconds,
+                           "%s, sequence 0 alone, cache pre-filled to its context" % wl.name)
         log("cpu baseline: %.1f ms/token on %d cores (%.1fs)" % (cpu["value"], cpu["cores"], time.time() - t0))
     traffic = None
     if wl.name == "llama8b_b16":
@@ -176,7 +242,6 @@ def bench_batched(args, wl):
         "steps": K,
         "warmup": W,
         "ms_per_step": round(ms, 5),
-        "ms_per_step_median": round(float(np.median(per_step)), 5),
         "tokens_per_s": round(n * 1e3 / ms, 1),
         "achieved_hbm_gbs": round(achieved, 1),
         "higher_is_better": False,
@@ -185,14 +250,18 @@ def bench_batched(args, wl):
         "dtype": "f32",
         "weights_dtype": "bf16",
         "data": "synthetic",
-        "config": {"workload": workload,
-                   "batch": n, "decode_steps": K, "weight_bytes_per_step": rf.weight_bytes_per_token(m),
-                   "kv": "bf16, paged in 16-token blocks, permuted page tables"},
+        "config": {"workload": workload, "batch": n, "decode_steps": K,
+                   "weight_bytes_per_step": rf.weight_bytes_per_token(m),
+                   "kv": "bf16, paged in 16-token blocks, permuted page tables", "graph": graph,
+                   "timed": "mk_decode_n: all %d steps in one launch" % K},
+        "one_launch_per_step": {"ms_per_step": round(ms1, 5),
+                                "ms_per_step_median": round(float(np.median(per_step)), 5),
+                                "tokens_equal_to_resident": same},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": rf.MI355X_HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(achieved / rf.MI355X_HBM_PEAK_GBS, 4), "traffic": traffic,
-                     "traffic_unit": "HBM bytes/launch (FETCH_SIZE + WRITE_SIZE, copy-calibrated)",
-                     "bytes_per_launch": int(bytes_avg),
-                     "kernel": "mk_megakernel%s (one launch per step)" % (", batched" if n > 1 else "")},
+                     "traffic_unit": "HBM bytes per step (FETCH_SIZE + WRITE_SIZE, copy-calibrated)",
+                     "bytes_per_step": int(bytes_avg),
+                     "kernel": "mk_megakernel%s" % (", batched" if n > 1 else "")},
         "cpu_baseline": cpu,
     }
     print(json.dumps(out), flush=True)
@@ -201,10 +270,10 @@ def bench_batched(args, wl):
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=512)
+    ap.add_argument("--steps", type=int, default=0, help="timed decode steps (0: the workload's own count)")
     ap.add_argument("--warmup", type=int, default=8)
     ap.add_argument("--workload", default="llama8b")
-    ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--cpu-seconds", type=float, default=20.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--staged-steps", type=int, default=64, help="steps of the stage-sliced comparison run (0: skip it)")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -221,8 +290,8 @@ def main():
         print(json.dumps({"copy_calibration_bytes_per_dispatch": 1 << 30, "dispatches": 5}))
         return
     if args.gpus != 1:
-        print("bench.py measures one GPU: this build has no multi-GPU path (--gpus %d requested)" % args.gpus,
-              file=sys.stderr)
+        print("bench.py measures one GPU: this decode path runs on one GPU and has no multi-GPU mode "
+              "(--gpus %d requested)" % args.gpus, file=sys.stderr)
         sys.exit(2)
 
     import numpy as np
@@ -235,9 +304,11 @@ def main():
     m = wl.model
     if wl.n_seqs > 1 or wl.prompt_len == 0:  # pre-filled caches: the batched and long-context workloads
         return bench_batched(args, wl)
-    K, W = args.steps, args.warmup
+    K, W = args.steps if args.steps else wl.steps, args.warmup
     P = wl.prompt_len
-    n_pos = P + max(K, W)
+    # The cache, and so the task graph, is sized for the workload's whole decode (prompt + its steps),
+    # whatever K is: the timed graph is the one the parity tests run.
+    n_pos = P + max(wl.steps, K, W)
     t0 = time.time()
     weights = si.gen_weights(m)
     prompt = si.prompt_tokens(wl)
@@ -248,6 +319,7 @@ def main():
     t0 = time.time()
     dec.load_weights(weights)
     log("weights loaded in %.1fs" % (time.time() - t0))
+    graph = graph_info(mk, dec)
     dec.set_page_table(np.arange(nb, dtype=np.int32).reshape(1, nb))
     dec.set_ctx_lens([0])
     g0 = torch.zeros(1, dtype=torch.int32, device=dec.dev)
@@ -255,57 +327,46 @@ def main():
     tokens = g0.clone()
     for _ in range(W):
         dec.step(tokens)
+    dec.decode_n(g0, W, 1)
     dec.sync_check()
-    # timed region: K greedy steps at positions P .. P+K-1 starting from the first generated token
-    dec.set_ctx_lens([P])
-    tokens.copy_(g0)
     stream = torch.cuda.current_stream(dec.dev)
-    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    ms_total, per_step = timed_steps(torch, stream, lambda: dec.step(tokens), K)
-    dec.sync_check()
+    # timed: K greedy steps at positions P .. P+K-1 starting from the first generated token
+    ms_res, ms_launch, per_step, same = decode_legs(torch, dec, 1, K, g0, lambda: dec.set_ctx_lens([P]), stream)
     assert int(dec.ctx_lens.item()) == P + K
-    ms = ms_total / K
+    ms, ms1 = ms_res / K, ms_launch / K
     bytes_avg = sum(rf.step_bytes(m, [P + i + 1]) for i in range(K)) / K
     achieved = bytes_avg / (ms * 1e-3) / 1e9
-    log("decode: %.4f ms/token, %.1f tok/s, %.1f GB/s (%.1f%% of %.0f GB/s)" %
-        (ms, 1e3 / ms, achieved, 100 * achieved / rf.MI355X_HBM_PEAK_GBS, rf.MI355X_HBM_PEAK_GBS))
+    log("decode: resident %.4f ms/token (%.1f tok/s), one launch per token %.4f ms/token; %.1f GB/s "
+        "(%.1f%% of %.0f GB/s); tokens equal: %s" % (ms, 1e3 / ms, ms1, achieved,
+                                                    100 * achieved / rf.MI355X_HBM_PEAK_GBS,
+                                                    rf.MI355X_HBM_PEAK_GBS, same))
     # The same steps as one dispatch per dependency stage (same kernel and graph): the stop-and-go
     # execution the single launch replaces. Its extra time per token is the pass-to-pass cost removed.
-    n_stages = int(mk.mk_graph_stats(dec.ctx).n_stages)
+    n_stages = graph["n_stages"]
     Ks = min(K, args.staged_steps)
     pass_to_pass = None
     if Ks > 0:
         dec.set_ctx_lens([P])
         tokens.copy_(g0)
-        torch.cuda.synchronize(dec.dev)
-        ev0.record(stream)
-        for _ in range(Ks):
-            dec.step_staged(tokens)
-        ev1.record(stream)
-        torch.cuda.synchronize(dec.dev)
-        ms_staged = ev0.elapsed_time(ev1) / Ks
+        ms_staged = timed_once(torch, stream, lambda: [dec.step_staged(tokens) for _ in range(Ks)]) / Ks
         dec.sync_check()
-        if Ks < K:  # the one-launch time over the same positions
-            dec.set_ctx_lens([P])
-            tokens.copy_(g0)
-            torch.cuda.synchronize(dec.dev)
-            ev0.record(stream)
-            for _ in range(Ks):
-                dec.step(tokens)
-            ev1.record(stream)
-            torch.cuda.synchronize(dec.dev)
-            ms_fused_same = ev0.elapsed_time(ev1) / Ks
-        else:
-            ms_fused_same = ms
-        log("staged: %.4f ms/token in %d dispatches (one launch: %.4f ms/token over the same %d steps)" %
-            (ms_staged, n_stages, ms_fused_same, Ks))
+        dec.set_ctx_lens([P])
+        tokens.copy_(g0)
+        ms_fused_same = timed_once(torch, stream, lambda: [dec.step(tokens) for _ in range(Ks)]) / Ks
+        dec.set_ctx_lens([P])
+        ms_res_same = timed_once(torch, stream, lambda: dec.decode_n(g0, Ks, 1)) / Ks
+        dec.sync_check()
+        log("staged: %.4f ms/token in %d dispatches; one launch per token %.4f, resident %.4f ms/token over the "
+            "same %d steps" % (ms_staged, n_stages, ms_fused_same, ms_res_same, Ks))
         pass_to_pass = {"stage_sliced_ms_per_token": round(ms_staged, 5), "dispatches_per_token": n_stages,
-                        "one_launch_ms_per_token": round(ms_fused_same, 5), "steps": Ks,
-                        "removed_ms_per_token": round(ms_staged - ms_fused_same, 5),
+                        "one_launch_per_token_ms": round(ms_fused_same, 5),
+                        "resident_ms_per_token": round(ms_res_same, 5), "steps": Ks,
+                        "removed_by_one_launch_ms_per_token": round(ms_staged - ms_fused_same, 5),
                         "removed_us_per_boundary": round(1e3 * (ms_staged - ms_fused_same) / max(1, n_stages - 1), 3),
-                        "what": "the same kernel and task graph launched once per dependency stage (stop-and-go) "
-                                "vs once per step"}
-    dec.close()
+                        "removed_by_resident_ms_per_token": round(ms_fused_same - ms_res_same, 5),
+                        "what": "the same kernel and task graph launched once per dependency stage (stop-and-go), "
+                                "once per token, and once for all the steps"}
+    finish(dec)
 
     traffic = None
     if wl.name == "llama8b":
@@ -314,7 +375,8 @@ def main():
     cpu = None
     if not args.no_cpu_baseline:
         t0 = time.time()
-        cpu = cpu_baseline(m, weights, prompt, args.cpu_seconds)
+        cpu = cpu_baseline(wl, weights, spread(P, P + K - 1, 8), args.cpu_seconds,
+                           "%s, batch 1, the timed positions" % wl.name)
         log("cpu baseline: %.1f ms/token on %d cores (%.1fs)" % (cpu["value"], cpu["cores"], time.time() - t0))
 
     out = {
@@ -325,7 +387,6 @@ def main():
         "steps": K,
         "warmup": W,
         "ms_per_step": round(ms, 5),
-        "ms_per_step_median": round(float(np.median(per_step)), 5),
         "tokens_per_s": round(1e3 / ms, 2),
         "achieved_hbm_gbs": round(achieved, 1),
         "higher_is_better": False,
@@ -338,11 +399,15 @@ def main():
                                % (wl.name, P, P, P + K - 1),
                    "batch": 1, "prompt_len": P, "decode_steps": K,
                    "weight_bytes_per_token": rf.weight_bytes_per_token(m),
-                   "kv": "bf16, paged in 16-token blocks"},
+                   "kv": "bf16, paged in 16-token blocks", "graph": graph,
+                   "timed": "mk_decode_n: all %d steps in one launch" % K},
+        "one_launch_per_step": {"ms_per_step": round(ms1, 5),
+                                "ms_per_step_median": round(float(np.median(per_step)), 5),
+                                "tokens_equal_to_resident": same},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": rf.MI355X_HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(achieved / rf.MI355X_HBM_PEAK_GBS, 4), "traffic": traffic,
-                     "traffic_unit": "HBM bytes/launch (FETCH_SIZE + WRITE_SIZE, copy-calibrated)",
-                     "bytes_per_launch": int(bytes_avg), "kernel": "mk_megakernel (one launch per decode step)"},
+                     "traffic_unit": "HBM bytes per step (FETCH_SIZE + WRITE_SIZE, copy-calibrated)",
+                     "bytes_per_step": int(bytes_avg), "kernel": "mk_megakernel"},
         "cpu_baseline": cpu,
         "pass_to_pass": pass_to_pass,
     }

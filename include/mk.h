@@ -47,7 +47,7 @@ typedef int32_t mk_status;
 #define MK_ERR_STATE (-3)           /* call out of order (e.g. decode before weights are loaded) */
 #define MK_ERR_HIP (-4)             /* a HIP runtime call failed; mk_last_error() names it */
 #define MK_ERR_DEVICE_TIMEOUT (-5)  /* a device-side wait exceeded the watchdog; results are invalid */
-#define MK_ERR_DEVICE_FAULT (-6)    /* the device saw a token id, page index or context length out of range */
+#define MK_ERR_DEVICE_FAULT (-6)    /* the device saw a token id, page index or context length out of range, or a NaN logit */
 #define MK_ERR_UNSUPPORTED (-7)     /* a valid request this build does not implement */
 
 typedef struct mk_ctx mk_ctx; /* opaque, owned by the library */
@@ -92,7 +92,11 @@ typedef struct {
 /* Validate `cfg` and build the task graph (host only, deterministic).
  * `device` is the HIP device ordinal. The graph is sized for that device's
  * compute-unit count. *out receives the new context.
- * Errors: MK_ERR_INVALID_ARG, MK_ERR_SHAPE, MK_ERR_HIP. */
+ * The builder refines every operator into per-CU tasks joined by events ("LLMs
+ * in einen MegaKernel kompilieren", "Part 1. Compiler"; "MPK: A Compiler and
+ * Runtime for Mega-Kernelizing Tensor Programs", analogy 2).
+ * Errors: MK_ERR_INVALID_ARG, MK_ERR_SHAPE, MK_ERR_HIP, MK_ERR_UNSUPPORTED
+ * (the device lacks cooperative launch, or one workgroup per CU does not fit). */
 mk_status mk_create(const mk_model_config* cfg, int device, mk_ctx** out);
 
 /* Like mk_create, but builds the graph for `n_cus` compute units without
@@ -100,7 +104,9 @@ mk_status mk_create(const mk_model_config* cfg, int device, mk_ctx** out);
  * inspection calls below. Any call that needs a device returns MK_ERR_STATE. */
 mk_status mk_create_host(const mk_model_config* cfg, int n_cus, mk_ctx** out);
 
-/* Bytes the caller must allocate before mk_bind_memory.
+/* Bytes the caller must allocate before mk_bind_memory. The KV pools are the
+ * block-managed cache of "LLM高速化勉強会資料", slide 17 (PagedAttention); a
+ * pool's size follows the deck's KV-cache size formula (slide 10).
  *   - weights_bytes: one device buffer for the re-laid-out weights.
  *   - kv_pool_bytes: bytes of EACH per-layer K pool and EACH per-layer V
  *     pool, laid out [num_blocks, n_kv_heads, block_size, head_dim] bf16.
@@ -109,7 +115,10 @@ mk_status mk_create_host(const mk_model_config* cfg, int n_cus, mk_ctx** out);
  * Alignment: every buffer must be 256-byte aligned. */
 mk_status mk_workspace_size(const mk_ctx* ctx, size_t* weights_bytes, size_t* kv_pool_bytes, size_t* scratch_bytes);
 
-/* Bind caller-owned device memory. All pointers are device pointers.
+/* Bind caller-owned device memory. All pointers are device pointers. The KV
+ * cache keeps every earlier position's keys and values for reuse ("Crear desde
+ * cero un motor de inferencia para LLM usando C++ y CUDA", section 1.1), in
+ * 16-position blocks named by a page table ("LLM高速化勉強会資料", slide 17).
  *   - d_k_pools, d_v_pools: HOST arrays of n_layers device pointers.
  *   - d_page_table: [max_seqs, max_blocks_per_seq] int32. Logical position
  *     p of sequence s is stored in block d_page_table[s][p / 16] at offset
@@ -125,15 +134,20 @@ mk_status mk_bind_memory(mk_ctx* ctx, void* d_weights, void* const* d_k_pools, v
                          void* d_scratch, int32_t* d_page_table, int32_t* d_ctx_lens, float* d_logits);
 
 /* Copy the model weights into the bound weights buffer, re-laid out into
- * the per-tile streaming order. Runs kernels on `stream`. The source
+ * the per-tile streaming order (loading a model means filling its blocks with
+ * stored weights: "Crear desde cero un motor de inferencia para LLM usando C++
+ * y CUDA", section 1). Runs kernels on `stream`. The source
  * tensors may be freed once the stream has passed this call. Every tensor
  * the config needs must be present.
  * Errors: MK_ERR_INVALID_ARG (unknown or duplicate name), MK_ERR_SHAPE
  * (wrong numel), MK_ERR_STATE (memory not bound). */
 mk_status mk_load_weights(mk_ctx* ctx, const mk_tensor* ts, int n, void* stream);
 
-/* One decode step for sequences 0..n_seqs-1. d_tokens_in and d_tokens_out
- * are [n_seqs] int32 device arrays (they may be the same array).
+/* One decode step for sequences 0..n_seqs-1: one new token per sequence
+ * against its KV cache ("Crear desde cero un motor de inferencia para LLM
+ * usando C++ y CUDA", section 1.1, the decode phase).
+ * d_tokens_in and d_tokens_out are [n_seqs] int32 device arrays (they may be
+ * the same array).
  *   - Sequence s takes token d_tokens_in[s] at position d_ctx_lens[s].
  *   - Its key and value are appended at that position.
  *   - It attends to positions 0..d_ctx_lens[s].
@@ -146,18 +160,41 @@ mk_status mk_load_weights(mk_ctx* ctx, const mk_tensor* ts, int n, void* stream)
  * must be at most max_seqs. */
 mk_status mk_decode_step(mk_ctx* ctx, const int32_t* d_tokens_in, int n_seqs, int32_t* d_tokens_out, void* stream);
 
+/* n_steps greedy decode steps in ONE kernel launch: the megakernel stays
+ * resident and each step's argmax feeds the next step's embedding lookup on
+ * the device, so no launch separates the tokens ("LLMs in einen MegaKernel
+ * kompilieren", "Überblick und Vorteile des MegaKernel-Ansatzes": no repeated
+ * kernel launches; "MPK: A Compiler and Runtime for Mega-Kernelizing Tensor
+ * Programs", analogy 1).
+ *   - d_tokens_in: [n_seqs] int32, the first step's tokens (device memory).
+ *   - d_tokens_out: [n_steps, n_seqs] int32 device array; row i receives
+ *     step i's greedy tokens. It must not overlap d_tokens_in.
+ *   - Step i of sequence s runs at position d_ctx_lens[s] + i; afterwards
+ *     d_ctx_lens[s] has grown by n_steps.
+ *   - d_logits holds the LAST step's logits.
+ * The results are those of n_steps calls of mk_decode_step, each fed the
+ * previous call's tokens (same graph, same arithmetic, bit for bit).
+ * The launch is cooperative, so the runtime guarantees that every workgroup is
+ * resident. Asynchronous. Errors: MK_ERR_INVALID_ARG (n_steps < 1 or above
+ * 65536, n_seqs out of range, NULL arrays), MK_ERR_STATE. A position past the
+ * cache is reported by the next synchronising call, like mk_decode_step's. */
+mk_status mk_decode_n(mk_ctx* ctx, const int32_t* d_tokens_in, int n_seqs, int n_steps, int32_t* d_tokens_out,
+                      void* stream);
+
 /* The same decode step as mk_decode_step, launched as one kernel dispatch per dependency stage
  * (QKV, attention, O projection, gate/up and down of each layer, then the LM head and the argmax):
  * the same kernel, task graph and arithmetic, so the results are identical. Each dispatch runs only
  * its stage's tasks, so a stage starts only after the previous one has fully drained. This is the
  * operator-by-operator execution the persistent kernel replaces ("LLMs in einen MegaKernel
- * kompilieren", the stop-and-go execution of kernel-per-operator frameworks); it exists to measure
+ * kompilieren", "Part 1. Compiler": one kernel per operator in conventional designs); it exists to measure
  * the pass-to-pass gaps that the single launch removes. Asynchronous, same arguments and errors as
  * mk_decode_step; mk_graph_info.n_stages dispatches per step. */
 mk_status mk_decode_step_staged(mk_ctx* ctx, const int32_t* d_tokens_in, int n_seqs, int32_t* d_tokens_out,
                                 void* stream);
 
-/* Prefill by repeated decode steps: the n_tokens host tokens h_tokens run
+/* Prefill by repeated decode steps (the prefill phase fills the KV cache from
+ * the prompt: "Crear desde cero un motor de inferencia para LLM usando C++ y
+ * CUDA", section 1.1; a batched prefill is not built): the n_tokens host tokens h_tokens run
  * through the step one position at a time, for sequence `seq` only. When
  * d_token_out is not NULL, it receives the greedy token after the last
  * prompt token. Asynchronous like mk_decode_step. Needs max_seqs == 1 and
@@ -166,26 +203,38 @@ mk_status mk_prefill(mk_ctx* ctx, int seq, const int32_t* h_tokens, int n_tokens
                      void* stream);
 
 /* Copy the last step's logits of sequence `seq` (n <= vocab floats) to host
- * memory. Synchronises `stream`. Returns the device error word if one is
- * set. */
+ * memory. (No passage: the boundary's own, for parity checks.) Synchronises
+ * `stream`. Returns the device error word if one is set. */
 mk_status mk_read_logits(mk_ctx* ctx, int seq, float* h_dst, size_t n, void* stream);
 
-/* Synchronise `stream` and report the device error word (MK_OK if clear). */
+/* Synchronise `stream` and report the device error word (MK_OK if clear). The
+ * pages give no error model; this is the boundary's own. */
 mk_status mk_sync_check(mk_ctx* ctx, void* stream);
 
-/* Task tracing. With a device buffer of at least n_tasks * 40 bytes (n_tasks from
- * mk_graph_stats), every later step writes one record per task, indexed by the task's
- * position in the global order. A record is {uint64 t_queue, t_ready, t_streamed, t_done;
- * uint16 cu; uint8 type; uint8 layer; uint32 epoch}: the times (100 MHz device real-time
- * counter) when the CU reached the task, when its inputs were all present, when its own
- * streaming ended (a GEMV's weights, before the epilogue; attention's cache rows and its
- * in-task merge, before partials are written or merged) and when it published its outputs; the CU; the task type (1 QKV, 2 attention, 3 O projection, 4 gate/up, 5 down,
- * 6 LM head, 7 argmax); its layer (n_layers for the LM head and argmax, mod 256). Each step overwrites
- * the records. d_buf == NULL turns tracing off. The buffer stays the caller's.
+/* Task tracing: the per-task timing behind the pages' 1-2 us between tasks
+ * ("LLMs in einen MegaKernel kompilieren", "Ereignisbasierte Ausführung").
+ * With a device buffer of at least n_tasks * 48 bytes (n_tasks from
+ * mk_graph_stats), every later step writes one record per task, indexed by the
+ * task's position in the global order. A record is {uint64 t_queue, t_ready,
+ * t_streamed, t_done; uint16 cu; uint8 type; uint8 layer; uint32 epoch;
+ * uint32 xcc; uint32 step}:
+ *   - the times (100 MHz device real-time counter) when the CU reached the
+ *     task, when its inputs were all present, when its own streaming ended (a
+ *     GEMV's weights, before the epilogue; attention's cache rows and its
+ *     in-task merge, before partials are written or merged) and when it
+ *     published its outputs;
+ *   - the workgroup (queue) index; the task type (1 QKV, 2 attention, 3 O
+ *     projection, 4 gate/up, 5 down, 6 LM head, 7 argmax); its layer (n_layers
+ *     for the LM head and argmax, mod 256); the step's epoch; the XCD the
+ *     workgroup ran on (read from the hardware); the step's index in its launch.
+ * Each step overwrites the records. d_buf == NULL turns tracing off. The
+ * buffer stays the caller's.
  * Errors: MK_ERR_INVALID_ARG (too small or not 8-byte aligned). */
 mk_status mk_set_trace(mk_ctx* ctx, void* d_buf, size_t bytes);
 
-/* Graph inspection (host only, no GPU needed).
+/* Graph inspection (host only, no GPU needed). The pages' compiler emits the
+ * task graph ahead of time ("MPK: A Compiler and Runtime for Mega-Kernelizing
+ * Tensor Programs", analogy 3); these calls check what the builder emitted.
  *   - mk_graph_stats: counts of tasks, events, flag slots and per-CU queue
  *     length (max), and the graph's 64-bit FNV-1a hash over its serialised
  *     form.
@@ -202,12 +251,26 @@ typedef struct {
   int64_t weight_bytes, lds_bytes;
   uint64_t hash;
   int64_t n_stages; /* dependency stages: the dispatches of mk_decode_step_staged */
+  int64_t attn_tasks; /* attention tasks per layer */
+  int64_t n_cus;      /* compute units (queues) the graph was built for */
 } mk_graph_info;
 mk_status mk_graph_stats(const mk_ctx* ctx, mk_graph_info* out);
 mk_status mk_graph_validate(const mk_ctx* ctx);
 mk_status mk_graph_simulate(const mk_ctx* ctx, uint64_t seed, int n_steps);
 
-/* Release host structures. Device memory stays with the caller. */
+/* Test hook, host-only contexts (mk_create_host) only: breaks the built graph in
+ * one way, so that tests can show mk_graph_validate and mk_graph_simulate reject
+ * it. kind: 1 two tasks of a queue swapped (queue out of the global order);
+ * 2 a task waits on a later producer (a cycle); 3 a flag slot with two writers;
+ * 4 a producer that never publishes (a slot with no writer); 5 two tiles of a
+ * stage overlapping (rows written twice); 6 a consumer with its wait removed;
+ * 7 a stage's last tile ending early (rows never written).
+ * Errors: MK_ERR_STATE (a device context), MK_ERR_INVALID_ARG (unknown kind, or
+ * the graph has no task of the kind's type). */
+mk_status mk_graph_corrupt(mk_ctx* ctx, int kind);
+
+/* Release host structures. Device memory stays with the caller. (No passage:
+ * the boundary's own.) */
 void mk_destroy(mk_ctx* ctx);
 
 const char* mk_status_str(mk_status s);

@@ -17,6 +17,17 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 _LIB_PATHS = {"f64": os.path.join(_HERE, "liboracle.so"), "f32": os.path.join(_HERE, "liboracle_f32.so")}
 _LIB_PATH = _LIB_PATHS["f64"]
 _libs = {}
+_default_precision = "f64"
+
+
+def set_default_precision(precision: str) -> str:
+    """Select the build the piece functions below call ("f64", the parity reference, or "f32"); returns
+    the previous choice. Used by the pins that check the fp32 build on its own."""
+    global _default_precision
+    if precision not in _LIB_PATHS:
+        raise ValueError(precision)
+    old, _default_precision = _default_precision, precision
+    return old
 
 _dp = ctypes.POINTER(ctypes.c_double)
 _u16p = ctypes.c_void_p
@@ -43,7 +54,8 @@ def build_lib(force: bool = False) -> str:
     return _LIB_PATH
 
 
-def lib(precision: str = "f64"):
+def lib(precision: str | None = None):
+    precision = precision or _default_precision
     if precision not in _libs:
         path = _LIB_PATHS[precision]
         if not os.path.exists(path):

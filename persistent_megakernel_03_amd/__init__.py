@@ -46,12 +46,13 @@ class mk_tensor(ctypes.Structure):
 class mk_graph_info(ctypes.Structure):
     _fields_ = [("n_tasks", ctypes.c_int64), ("n_events", ctypes.c_int64), ("n_flag_slots", ctypes.c_int64),
                 ("n_attn_groups", ctypes.c_int64), ("max_queue_len", ctypes.c_int64), ("weight_bytes", ctypes.c_int64),
-                ("lds_bytes", ctypes.c_int64), ("hash", ctypes.c_uint64), ("n_stages", ctypes.c_int64)]
+                ("lds_bytes", ctypes.c_int64), ("hash", ctypes.c_uint64), ("n_stages", ctypes.c_int64),
+                ("attn_tasks", ctypes.c_int64), ("n_cus", ctypes.c_int64)]
 
 
 EXPORTS = ["mk_create", "mk_create_host", "mk_workspace_size", "mk_bind_memory", "mk_load_weights", "mk_decode_step",
-           "mk_decode_step_staged", "mk_prefill", "mk_read_logits", "mk_sync_check", "mk_graph_stats", "mk_graph_validate",
-           "mk_graph_simulate", "mk_set_trace", "mk_destroy", "mk_status_str", "mk_last_error"]
+           "mk_decode_n", "mk_decode_step_staged", "mk_prefill", "mk_read_logits", "mk_sync_check", "mk_graph_stats", "mk_graph_validate",
+           "mk_graph_simulate", "mk_graph_corrupt", "mk_set_trace", "mk_destroy", "mk_status_str", "mk_last_error"]
 
 
 def build(force: bool = True) -> str:
@@ -83,6 +84,7 @@ def lib():
             "mk_bind_memory": [vp, vp, ctypes.POINTER(vp), ctypes.POINTER(vp), vp, vp, vp, vp],
             "mk_load_weights": [vp, ctypes.POINTER(mk_tensor), ctypes.c_int, vp],
             "mk_decode_step": [vp, vp, ctypes.c_int, vp, vp],
+            "mk_decode_n": [vp, vp, ctypes.c_int, ctypes.c_int, vp, vp],
             "mk_decode_step_staged": [vp, vp, ctypes.c_int, vp, vp],
             "mk_prefill": [vp, ctypes.c_int, ctypes.POINTER(i32), ctypes.c_int, vp, vp],
             "mk_read_logits": [vp, ctypes.c_int, ctypes.POINTER(ctypes.c_float), sz, vp],
@@ -90,6 +92,7 @@ def lib():
             "mk_graph_stats": [vp, ctypes.POINTER(mk_graph_info)],
             "mk_graph_validate": [vp],
             "mk_graph_simulate": [vp, ctypes.c_uint64, ctypes.c_int],
+            "mk_graph_corrupt": [vp, ctypes.c_int],
             "mk_set_trace": [vp, vp, sz],
         }
         for name, args in sig.items():
@@ -104,6 +107,16 @@ def lib():
         L.mk_last_error.restype = ctypes.c_char_p
         _lib = L
     return _lib
+
+
+TRACE_REC_BYTES = 48
+
+
+def trace_dtype():
+    """numpy dtype of one task record written by mk_set_trace's buffer (48 bytes)."""
+    import numpy as np
+    return np.dtype([("t_queue", "<u8"), ("t_ready", "<u8"), ("t_streamed", "<u8"), ("t_done", "<u8"), ("cu", "<u2"),
+                     ("type", "u1"), ("layer", "u1"), ("epoch", "<u4"), ("xcc", "<u4"), ("step", "<u4")])
 
 
 def _check(status):
@@ -162,6 +175,10 @@ def mk_decode_step(ctx, tokens_in, n_seqs, tokens_out, stream=None):
     _check(lib().mk_decode_step(ctx, _vp(tokens_in), n_seqs, _vp(tokens_out), _vp(stream)))
 
 
+def mk_decode_n(ctx, tokens_in, n_seqs, n_steps, tokens_out, stream=None):
+    _check(lib().mk_decode_n(ctx, _vp(tokens_in), n_seqs, n_steps, _vp(tokens_out), _vp(stream)))
+
+
 def mk_decode_step_staged(ctx, tokens_in, n_seqs, tokens_out, stream=None):
     _check(lib().mk_decode_step_staged(ctx, _vp(tokens_in), n_seqs, _vp(tokens_out), _vp(stream)))
 
@@ -195,6 +212,10 @@ def mk_graph_validate(ctx):
 
 def mk_graph_simulate(ctx, seed: int, n_steps: int):
     _check(lib().mk_graph_simulate(ctx, seed, n_steps))
+
+
+def mk_graph_corrupt(ctx, kind: int):
+    _check(lib().mk_graph_corrupt(ctx, kind))
 
 
 def mk_set_trace(ctx, buf, nbytes):
@@ -274,6 +295,13 @@ class Decoder:
         mk_decode_step(self.ctx, tokens_in, n_seqs, tokens_out if tokens_out is not None else tokens_in,
                        self.stream_ptr())
 
+    def decode_n(self, tokens_in, n_steps, n_seqs=1, tokens_out=None):
+        """n_steps greedy steps in one launch; returns the [n_steps, n_seqs] int32 device tensor of tokens."""
+        if tokens_out is None:
+            tokens_out = self.torch.empty((n_steps, n_seqs), dtype=self.torch.int32, device=self.dev)
+        mk_decode_n(self.ctx, tokens_in, n_seqs, n_steps, tokens_out, self.stream_ptr())
+        return tokens_out
+
     def step_staged(self, tokens_in, n_seqs=1, tokens_out=None):
         """The same step as one kernel dispatch per dependency stage (to measure pass-to-pass gaps)."""
         mk_decode_step_staged(self.ctx, tokens_in, n_seqs, tokens_out if tokens_out is not None else tokens_in,
@@ -287,17 +315,14 @@ class Decoder:
 
     def enable_trace(self):
         n = mk_graph_stats(self.ctx).n_tasks
-        self.trace_buf = self.torch.zeros(n * 40, dtype=self.torch.uint8, device=self.dev)
-        mk_set_trace(self.ctx, self.trace_buf, n * 40)
+        self.trace_buf = self.torch.zeros(n * TRACE_REC_BYTES, dtype=self.torch.uint8, device=self.dev)
+        mk_set_trace(self.ctx, self.trace_buf, n * TRACE_REC_BYTES)
 
     def read_trace(self):
         """Per-task records of the last step: structured numpy array (t_queue, t_ready, t_streamed, t_done,
-        cu, type, layer, epoch), indexed by the task's position in the global order."""
-        import numpy as np
+        cu, type, layer, epoch, xcc, step), indexed by the task's position in the global order."""
         self.torch.cuda.synchronize(self.dev)
-        dt = np.dtype([("t_queue", "<u8"), ("t_ready", "<u8"), ("t_streamed", "<u8"), ("t_done", "<u8"), ("cu", "<u2"), ("type", "u1"),
-                       ("layer", "u1"), ("epoch", "<u4")])
-        return self.trace_buf.cpu().numpy().view(dt)
+        return self.trace_buf.cpu().numpy().view(trace_dtype())
 
     def close(self):
         if self.ctx:

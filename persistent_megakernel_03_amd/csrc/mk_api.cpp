@@ -17,7 +17,7 @@
 #include "mk_host.h"
 
 namespace mk {
-hipError_t launch_megakernel(const KernelParams& p, int grid, size_t lds_bytes, hipStream_t stream);
+hipError_t launch_megakernel(const KernelParams& p, int grid, size_t lds_bytes, hipStream_t stream, bool coop);
 hipError_t megakernel_occupancy(int* blocks_per_cu, size_t lds_bytes, int dh, int hq, int hk, bool batched);
 hipError_t launch_repack(const RepackArgs& a, int64_t units, hipStream_t stream);
 hipError_t launch_repack_bias(const uint16_t* bq, const uint16_t* bk, const uint16_t* bv, int G, int dh, int nrows,
@@ -109,8 +109,10 @@ mk_status read_error_word(mk_ctx* c, hipStream_t st) {
   if (e[E_CODE] == ERR_TOKEN) what = "token id out of range (seq " + std::to_string(e[1]) + ", token " + std::to_string((int32_t)e[2]) + ")";
   else if (e[E_CODE] == ERR_PAGE) what = "page table entry out of range (seq " + std::to_string(e[1]) + ", block " + std::to_string((int32_t)e[2]) + ")";
   else if (e[E_CODE] == ERR_CTX) what = "context length outside the cache (seq " + std::to_string(e[1]) + ", length " + std::to_string((int32_t)e[2]) + ")";
+  else if (e[E_CODE] == ERR_NAN) what = "NaN among the logits (seq " + std::to_string(e[1]) + ", first at index " + std::to_string((int32_t)e[2]) + ")";
   else {
-    what = "device wait exceeded the watchdog (event " + std::to_string(e[1]) + ", epoch " + std::to_string(e[2]) + ")";
+    const std::string ev = e[1] == 0xFFFFFFFEu ? std::string("the next step's token") : "event " + std::to_string(e[1]);
+    what = "device wait exceeded the watchdog (" + ev + ", epoch " + std::to_string(e[2]) + ")";
     s = MK_ERR_DEVICE_TIMEOUT;
   }
   if (e[E_ABORT] || s == MK_ERR_DEVICE_TIMEOUT) {
@@ -152,6 +154,7 @@ KernelParams make_params(mk_ctx* c) {
   p.ht = (uint64_t*)(S + g.sl.ht);
   p.pt = (uint64_t*)(S + g.sl.pt);
   p.bpt = (uint64_t*)(S + g.sl.bpt);
+  p.tokt = (uint64_t*)(S + g.sl.tokt);
   p.logits = c->d_logits;
   p.amax = (uint64_t*)(S + g.sl.amax);
   p.n_layers = m.n_layers;
@@ -177,18 +180,39 @@ KernelParams make_params(mk_ctx* c) {
   return p;
 }
 
-// One decode step: one launch over the whole task graph, or (staged) one launch per dependency
-// stage, in order, each running only that stage's tasks with the same kernel and step epoch.
-mk_status launch_step(mk_ctx* c, const int32_t* tin, int n_active, int32_t* tout, hipStream_t st, bool staged = false) {
+// Epochs grow by one per step. Long before the 32-bit tags could wrap (a tag of epoch 0 or 1 would pass
+// the checks of a restarted count), the flags and tagged buffers are cleared and epochs restart at 1.
+constexpr uint32_t kEpochLimit = 0x40000000u;
+// Steps one mk_decode_n launch may run (each step's tokens go to its own row of the output array).
+constexpr int kMaxStepsPerLaunch = 1 << 16;
+
+mk_status reserve_epochs(mk_ctx* c, int n_steps, hipStream_t st) {
+  if (c->epoch + (uint32_t)n_steps + 1u < kEpochLimit) return MK_OK;
+  HIPCHK(hipStreamSynchronize(st));
+  HIPCHK(hipMemset(c->d_scratch + c->g.sl.flags, 0, (size_t)c->g.n_flag_slots * 4));
+  HIPCHK(hipMemset(c->d_scratch + c->g.sl.tagged_begin, 0, (size_t)(c->g.sl.tagged_end - c->g.sl.tagged_begin)));
+  HIPCHK(hipDeviceSynchronize());
+  c->epoch = 0;
+  return MK_OK;
+}
+
+// Decode steps: one launch over the whole task graph for n_steps steps (each feeding its tokens to the
+// next; cooperative when n_steps > 1), or (staged, one step) one launch per dependency stage, in order,
+// each running only that stage's tasks with the same kernel and step epoch.
+mk_status launch_step(mk_ctx* c, const int32_t* tin, int n_active, int32_t* tout, hipStream_t st, bool staged = false,
+                      int n_steps = 1) {
+  if (mk_status s = reserve_epochs(c, n_steps, st)) return s;
   KernelParams p = make_params(c);
   p.tokens_in = tin;
   p.tokens_out = tout;
   p.n_active = n_active;
-  p.epoch = ++c->epoch;
+  p.n_steps = n_steps;
+  p.epoch = c->epoch + 1;
+  c->epoch += (uint32_t)n_steps;
   if (!staged) {
     p.task_lo = 0;
     p.task_hi = (int32_t)c->g.tasks.size();
-    HIPCHK(launch_megakernel(p, c->g.n_cus, (size_t)c->g.lds_bytes, st));
+    HIPCHK(launch_megakernel(p, c->g.n_cus, (size_t)c->g.lds_bytes, st, n_steps > 1));
     return MK_OK;
   }
   const auto& t = c->g.tasks;
@@ -197,7 +221,7 @@ mk_status launch_step(mk_ctx* c, const int32_t* tin, int n_active, int32_t* tout
     while (b < t.size() && t[b].type == t[a].type && t[b].layer == t[a].layer) ++b;
     p.task_lo = (int32_t)a;
     p.task_hi = (int32_t)b;
-    HIPCHK(launch_megakernel(p, c->g.n_cus, (size_t)c->g.lds_bytes, st));
+    HIPCHK(launch_megakernel(p, c->g.n_cus, (size_t)c->g.lds_bytes, st, false));
     a = b;
   }
   return MK_OK;
@@ -388,6 +412,16 @@ mk_status mk_decode_step(mk_ctx* c, const int32_t* d_tokens_in, int n_seqs, int3
   return launch_step(c, d_tokens_in, n_seqs, d_tokens_out, (hipStream_t)stream);
 }
 
+mk_status mk_decode_n(mk_ctx* c, const int32_t* d_tokens_in, int n_seqs, int n_steps, int32_t* d_tokens_out,
+                      void* stream) {
+  if (!c || !d_tokens_in || !d_tokens_out) return fail(MK_ERR_INVALID_ARG, "null argument");
+  if (!c->bound || !c->loaded) return fail(MK_ERR_STATE, "bind memory and load weights before decoding");
+  if (n_seqs < 1 || n_seqs > c->g.cfg.max_seqs) return fail(MK_ERR_INVALID_ARG, "n_seqs out of range");
+  if (n_steps < 1 || n_steps > kMaxStepsPerLaunch) return fail(MK_ERR_INVALID_ARG, "n_steps out of range");
+  DeviceGuard dg(c->device);
+  return launch_step(c, d_tokens_in, n_seqs, d_tokens_out, (hipStream_t)stream, false, n_steps);
+}
+
 mk_status mk_decode_step_staged(mk_ctx* c, const int32_t* d_tokens_in, int n_seqs, int32_t* d_tokens_out, void* stream) {
   if (!c || !d_tokens_in || !d_tokens_out) return fail(MK_ERR_INVALID_ARG, "null argument");
   if (!c->bound || !c->loaded) return fail(MK_ERR_STATE, "bind memory and load weights before decoding");
@@ -464,6 +498,8 @@ mk_status mk_graph_stats(const mk_ctx* c, mk_graph_info* out) {
   for (size_t a = 0; a < g.tasks.size(); ++a)
     if (a == 0 || g.tasks[a].type != g.tasks[a - 1].type || g.tasks[a].layer != g.tasks[a - 1].layer) ++stages;
   out->n_stages = stages;
+  out->attn_tasks = g.attn_tasks;
+  out->n_cus = g.n_cus;
   return MK_OK;
 }
 
@@ -477,6 +513,13 @@ mk_status mk_graph_simulate(const mk_ctx* c, uint64_t seed, int n_steps) {
   if (!c || n_steps < 0) return fail(MK_ERR_INVALID_ARG, "bad argument");
   const std::string why = simulate_graph(c->g, seed, n_steps);
   return why.empty() ? MK_OK : fail(MK_ERR_SHAPE, why);
+}
+
+mk_status mk_graph_corrupt(mk_ctx* c, int kind) {
+  if (!c) return fail(MK_ERR_INVALID_ARG, "null context");
+  if (c->device >= 0) return fail(MK_ERR_STATE, "only host-only contexts may be corrupted");
+  const std::string why = corrupt_graph(c->g, kind);
+  return why.empty() ? MK_OK : fail(MK_ERR_INVALID_ARG, why);
 }
 
 void mk_destroy(mk_ctx* c) { delete c; }

@@ -13,6 +13,7 @@
 // every CU streams an equal share of each weight matrix.
 #include <algorithm>
 #include <climits>
+#include <cmath>
 #include <cstdio>
 #include <cstdlib>
 #include <cstring>
@@ -212,6 +213,9 @@ std::string build_graph(const mk_model_config& c, int n_cus, HostGraph& g) {
   if (c.d_model > 8192 || c.n_q_heads * c.head_dim > 8192 || c.d_ffn > 16384) return "model too wide for the activation polls";
   if (c.block_size != 16) return "block_size must be 16";
   if (c.max_seqs < 1 || c.max_seqs > 16) return "max_seqs must be 1..16 (one 16-row MFMA tile of sequences)";
+  // batched tiles stage the normalised inputs 32 columns at a time; every staged column of a normalised
+  // input must be a real one
+  if (c.max_seqs > 1 && c.d_model % 32) return "batched decode needs d_model to be a multiple of 32";
   if (c.max_blocks_per_seq < 1 || c.num_blocks < 1) return "empty KV cache";
   if (!(c.rms_eps >= 0.f) || !(c.rope_theta > 0.f)) return "bad rms_eps or rope_theta";
   if (c.attn_splits < 0 || c.attn_splits > 64) return "attn_splits out of range";
@@ -547,7 +551,9 @@ std::string build_graph(const mk_model_config& c, int n_cus, HostGraph& g) {
   g.wl.embed = g.wl.packed_bytes;
   g.wl.norms = align_up(g.wl.embed + (int64_t)V * d * 2, 256);
   g.wl.bias = align_up(g.wl.norms + (int64_t)(2 * L + 1) * d * 2, 256);
-  g.wl.total = align_up(g.wl.bias + (c.qkv_bias ? (int64_t)L * Nqkv * 2 : 0), 256);
+  // a tail pad: batched tasks load gains and embedding columns a block at a time and may read up to one
+  // 1024-column block (2 KB) past a row's end (the values are not used)
+  g.wl.total = align_up(g.wl.bias + (c.qkv_bias ? (int64_t)L * Nqkv * 2 : 0), 256) + 2048;
 
   // ---- scratch layout
   int64_t o = 0;
@@ -569,6 +575,7 @@ std::string build_graph(const mk_model_config& c, int n_cus, HostGraph& g) {
   g.sl.ht = take((int64_t)L * S * f * 8);
   g.sl.pt = take((int64_t)L * g.attn_tasks * 2 * G * (dh + 2) * 8);
   g.sl.bpt = take(bpt_words * 8);
+  g.sl.tokt = take((int64_t)S * 8);
   g.sl.tagged_end = o;
   g.sl.amax = take((int64_t)S * g.n_lm_parts * 8);
   g.sl.tokbuf = take((int64_t)std::max(g.max_pos, 64) * 4);
@@ -646,7 +653,35 @@ std::string validate_graph(const HostGraph& g) {
     for (int s = ev.slot0; s < ev.slot0 + ev.nslots; ++s)
       if (last_writer_task[s] >= t) return "task " + std::to_string(t) + " waits on a later producer";
   }
-  // GEMV tiles: rows covered exactly once per stage, tiles disjoint and in range
+  // every output row of a GEMV stage is written exactly once (once per column split when the stage's
+  // tiles are split by columns): the row ranges of the tasks with one split index tile [0, N)
+  for (int t0 = 0; t0 < nt;) {
+    int t1 = t0 + 1;
+    while (t1 < nt && g.tasks[t1].type == g.tasks[t0].type && g.tasks[t1].layer == g.tasks[t0].layer) ++t1;
+    const TaskDesc& a = g.tasks[t0];
+    if (a.type != T_ATTN && a.type != T_ARGMAX) {
+      const mk_model_config& c = g.cfg;
+      const int N = a.type == T_QKV ? qkv_rows(c) : a.type == T_GATEUP ? 2 * c.d_ffn : a.type == T_LMHEAD ? c.vocab : c.d_model;
+      const int kS = g.geoms[a.geom].mfma ? std::max(1, a.a3 >> 8) : 1;
+      for (int j = 0; j < kS; ++j) {
+        std::vector<std::pair<int, int>> rs;
+        for (int t = t0; t < t1; ++t)
+          if (!g.geoms[a.geom].mfma || (g.tasks[t].a3 & 0xFF) == j) rs.push_back({g.tasks[t].row0, g.tasks[t].row1});
+        std::sort(rs.begin(), rs.end());
+        int at = 0;
+        for (auto& r : rs) {
+          if (r.first != at)
+            return "stage of type " + std::to_string(a.type) + " (layer " + std::to_string(a.layer) + ") " +
+                   (r.first < at ? "writes rows " + std::to_string(r.first) + ".." + std::to_string(at) + " twice"
+                                 : "leaves rows " + std::to_string(at) + ".." + std::to_string(r.first) + " unwritten");
+          at = r.second;
+        }
+        if (at != N) return "stage of type " + std::to_string(a.type) + " (layer " + std::to_string(a.layer) + ") does not end at row " + std::to_string(N);
+      }
+    }
+    t0 = t1;
+  }
+  // GEMV tiles: contiguous in stage order and in range
   int64_t end = 0;
   for (int t = 0; t < nt; ++t) {
     const TaskDesc& td = g.tasks[t];
@@ -829,6 +864,76 @@ std::string simulate_graph(const HostGraph& g, uint64_t seed, int n_steps) {
     }
   }
   return "";
+}
+
+// ----------------------------------------------------------------------------- test hook
+// Breaks a built graph in one named way, so that tests can show the validator and the simulator
+// reject it. Host graphs only; never used on a graph a kernel runs.
+std::string corrupt_graph(HostGraph& g, int kind) {
+  const int nt = (int)g.tasks.size();
+  auto first_of = [&](int type, int layer) {
+    for (int t = 0; t < nt; ++t)
+      if (g.tasks[t].type == type && g.tasks[t].layer == layer) return t;
+    return -1;
+  };
+  switch (kind) {
+    case 1: {  // two tasks of one CU's queue swapped: the queue leaves the global order
+      for (int cu = 0; cu < g.n_cus; ++cu)
+        if (g.queue_off[cu + 1] - g.queue_off[cu] >= 2) {
+          std::swap(g.queue_idx[g.queue_off[cu]], g.queue_idx[g.queue_off[cu] + 1]);
+          return "";
+        }
+      return "no queue holds two tasks";
+    }
+    case 2: {  // a task waits on an event whose producers come after it (a dependency cycle)
+      const int t = first_of(T_QKV, 0), p = first_of(T_DOWN, 0);
+      if (t < 0 || p < 0 || g.tasks[p].sig_n < 1) return "no QKV or down task";
+      const int slot = g.sig_slots[g.tasks[p].sig_off];
+      for (size_t e = 0; e < g.events.size(); ++e)
+        if (g.events[e].slot0 <= slot && slot < g.events[e].slot0 + g.events[e].nslots) {
+          g.tasks[t].wait_ev = (int32_t)e;
+          g.tasks[t].wait_slot0 = g.events[e].slot0;
+          g.tasks[t].wait_nslots = g.events[e].nslots;
+          return "";
+        }
+      return "no event";
+    }
+    case 3: {  // a flag slot with two writers: a second GEMV task publishes into the first one's slot
+      const int t = first_of(T_OPROJ, 0);
+      if (t < 0 || t + 1 >= nt || g.tasks[t + 1].type != T_OPROJ) return "no two O tasks";
+      g.sig_slots[g.tasks[t + 1].sig_off] = g.sig_slots[g.tasks[t].sig_off];
+      return "";
+    }
+    case 4: {  // a producer that never publishes: its slot has no writer
+      const int t = first_of(T_GATEUP, 0);
+      if (t < 0) return "no gate/up task";
+      g.tasks[t].sig_n = 0;
+      return "";
+    }
+    case 5: {  // two tiles of one stage overlap: rows written twice
+      const int t = first_of(T_DOWN, 0);
+      if (t < 0 || t + 1 >= nt || g.tasks[t + 1].type != T_DOWN) return "no two down tasks";
+      g.tasks[t].row1 += 1;
+      return "";
+    }
+    case 6: {  // a consumer that does not wait: an attention task's input wait removed
+      const int t = first_of(T_ATTN, 0);
+      if (t < 0) return "no attention task";
+      g.tasks[t].wait_ev = -1;
+      g.tasks[t].wait_slot0 = 0;
+      g.tasks[t].wait_nslots = 0;
+      return "";
+    }
+    case 7: {  // rows left unwritten: a stage's last tile ends early
+      int t = first_of(T_LMHEAD, g.cfg.n_layers);
+      if (t < 0) return "no LM-head task";
+      while (t + 1 < nt && g.tasks[t + 1].type == T_LMHEAD) ++t;
+      g.tasks[t].row1 -= 1;
+      return "";
+    }
+    default:
+      return "unknown corruption kind";
+  }
 }
 
 uint64_t graph_hash(const HostGraph& g) {

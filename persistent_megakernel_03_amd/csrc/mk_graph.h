@@ -86,6 +86,7 @@ struct ScratchLayout {
   int64_t flags, err;
   // tagged activations (64-bit words: value bits | step epoch << 32), one buffer per layer
   int64_t xt, qt, kvt, ot, ht, pt;
+  int64_t tokt;                      // [max_seqs]: the token each sequence feeds into the next step
   int64_t bpt;                       // batched GEMV: per-tile partial sums of each column split
   int64_t tagged_begin, tagged_end;  // byte range holding all tagged buffers
   int64_t amax, tokbuf, tokout, pools;
@@ -103,7 +104,7 @@ struct WeightLayout {
 
 // Device error word layout (uint32 slots in scratch).
 enum ErrSlot : int32_t { E_CODE = 0, E_INFO0 = 1, E_INFO1 = 2, E_ABORT = 3, E_COUNT = 16 };
-enum ErrCode : uint32_t { ERR_NONE = 0, ERR_TOKEN = 1, ERR_PAGE = 2, ERR_TIMEOUT = 3, ERR_CTX = 4 };
+enum ErrCode : uint32_t { ERR_NONE = 0, ERR_TOKEN = 1, ERR_PAGE = 2, ERR_TIMEOUT = 3, ERR_CTX = 4, ERR_NAN = 5 };
 
 // One task's timestamps (s_memrealtime, 100 MHz), written when tracing is on.
 struct TraceRec {
@@ -111,12 +112,14 @@ struct TraceRec {
   uint64_t t_ready;   // its inputs were all present
   uint64_t t_streamed;  // its own streaming ended: GEMV before the epilogue, attention before the partials
   uint64_t t_done;    // its outputs were published
-  uint16_t cu;
+  uint16_t cu;        // the workgroup (queue) index
   uint8_t type;       // TaskType
   uint8_t layer;      // layer index (n_layers for the LM head and argmax), mod 256
   uint32_t epoch;
+  uint32_t xcc;       // the XCD the workgroup ran on (hardware register)
+  uint32_t step;      // the step's index within its launch
 };
-static_assert(sizeof(TraceRec) == 40, "TraceRec is 40 bytes");
+static_assert(sizeof(TraceRec) == 48, "TraceRec is 48 bytes");
 
 // Everything the megakernel reads, passed by value.
 struct KernelParams {
@@ -149,18 +152,19 @@ struct KernelParams {
                               // (sums of squares per sequence), one block per tile (see TaskDesc)
   float* logits;              // [max_seqs][V]
   uint64_t* amax;             // [max_seqs][n_lm_parts] packed argmax keys
-  const int32_t* tokens_in;   // [max_seqs]
-  int32_t* tokens_out;        // [max_seqs]
+  const int32_t* tokens_in;   // [max_seqs]: the first step's tokens
+  int32_t* tokens_out;        // [n_steps][n_active]: each step's greedy tokens
+  uint64_t* tokt;             // [max_seqs] tagged: the token each sequence feeds into the next step
   int32_t n_layers, d, hq, hk, dh, f, vocab;
   float eps;
   int32_t max_seqs, n_active, max_blocks, num_blocks, block_size, splits, n_lm_parts, max_pos;
-  uint32_t epoch;
+  uint32_t epoch;             // the first step's epoch; step i runs with epoch + i
+  int32_t n_steps;            // steps this launch runs, each feeding its tokens to the next
   uint32_t watchdog_ticks;    // s_memrealtime ticks (100 MHz) a wait may spin before the kernel aborts
   int32_t max_queue;          // longest per-CU queue (its descriptors are staged in LDS)
   int32_t attn_tasks;         // attention tasks per layer (they cut the layer's KV blocks evenly)
   int32_t task_lo, task_hi;   // this launch runs the tasks [task_lo, task_hi) of the global order
   int32_t attn_min_blocks;    // cache blocks per attention task at least (fewer tasks get blocks)
-  int32_t pad_;
   TraceRec* trace;            // per-task timestamps of the last step, or nullptr
 };
 

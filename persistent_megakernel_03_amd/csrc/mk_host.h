@@ -60,6 +60,8 @@ std::string build_graph(const mk_model_config& cfg, int n_cus, HostGraph& g);
 std::string validate_graph(const HostGraph& g);
 std::string simulate_graph(const HostGraph& g, uint64_t seed, int n_steps);
 uint64_t graph_hash(const HostGraph& g);
+// Test hook: breaks the graph in one of the ways mk_graph_corrupt names; "" on success.
+std::string corrupt_graph(HostGraph& g, int kind);
 GemvGeom choose_geom(int K);
 GemvGeom choose_geom_batched(int K);
 

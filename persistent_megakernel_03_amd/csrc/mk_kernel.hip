@@ -1,7 +1,10 @@
 // The persistent decode megakernel for gfx950 (CDNA4), and the weight re-layout kernel.
 //
-// One workgroup of 512 threads (8 wave64s) runs on each CU, launched cooperatively, so all
-// are co-resident. Each workgroup walks its own task queue. For each task it:
+// One workgroup of 512 threads (8 wave64s) runs on each CU, and all of them must be resident at once
+// (the LDS allows one per CU, the grid is the CU count; multi-step launches are cooperative, so the
+// runtime guarantees it; a single step uses a plain launch on a device running nothing else, and a
+// wait that can never be met ends at the watchdog). Each workgroup walks its own task queue, once per
+// step of the launch. For each task it:
 //   - waits for its input event,
 //   - runs the tile,
 //   - publishes its epoch number into its flag slots.
@@ -33,6 +36,9 @@ typedef float v4f __attribute__((ext_vector_type(4)));
 constexpr int NT = 512;     // threads per workgroup
 constexpr int NW = NT / 64; // waves per workgroup
 constexpr int NSLOT = 16;   // 1 KB weight units in flight per wave (16 KB), one register slot each
+// s_getreg operand for the hardware register holding the wave's XCD id (register 20 on gfx940-family
+// parts, bits 3..0): id | offset << 6 | (size - 1) << 11
+constexpr int kHwRegXccId = 20 | (0 << 6) | ((4 - 1) << 11);
 
 // ----------------------------------------------------------------------------- helpers
 __device__ __forceinline__ float ldc(const float* p) { return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT); }
@@ -203,12 +209,12 @@ __device__ __forceinline__ uint32_t first_words(int n) { return n >= 32 ? ~0u : 
 // (then the timeout is raised, naming `what`, and the kernel aborts). The abort flag is a load of its
 // own that would double the time of every pass if read on each; an abort only drains the grid after
 // an error, so the few extra passes it takes to notice cost nothing that matters.
-__device__ __forceinline__ bool poll_give_up(const KernelParams& p, uint32_t pass, uint64_t t0, uint32_t what) {
+__device__ __forceinline__ bool poll_give_up(const KernelParams& p, uint32_t ep, uint32_t pass, uint64_t t0, uint32_t what) {
   if ((pass & 7u) != 0u) return false;
   if (ldc(&p.err[E_ABORT])) return true;
   if (__builtin_amdgcn_s_memrealtime() - t0 > p.watchdog_ticks) {
     if ((threadIdx.x & 63) == 0) {
-      raise_error(p, ERR_TIMEOUT, what, p.epoch);
+      raise_error(p, ERR_TIMEOUT, what, ep);
       stc(&p.err[E_ABORT], 1u);
     }
     return true;
@@ -218,11 +224,11 @@ __device__ __forceinline__ bool poll_give_up(const KernelParams& p, uint32_t pas
 
 // Polls this thread's tagged words k (bit k of `pending`, k < K); word k sits at byte base + voff(k)
 // + soff(k), soff uniform across the wave. sink(k, bits) receives a word's low half once the word
-// carries the epoch. Each pass issues the loads of all words still stale before checking any. A wave
+// carries the step's epoch `ep`. Each pass issues the loads of all words still stale before checking any. A wave
 // stops when all its lanes are done, when the kernel is aborting, or when the watchdog expires (which
 // raises the timeout, naming `what`, and aborts the kernel).
 template <int K, typename Voff, typename Soff, typename Sink>
-__device__ __forceinline__ void poll_tagged(const KernelParams& p, const uint64_t* base, Voff voff, Soff soff,
+__device__ __forceinline__ void poll_tagged(const KernelParams& p, uint32_t ep, const uint64_t* base, Voff voff, Soff soff,
                                             uint32_t pending, uint32_t what, Sink sink) {
   const __amdgpu_buffer_rsrc_t r = tag_rsrc(base);
   const uint64_t t0 = __builtin_amdgcn_s_memrealtime();
@@ -233,13 +239,13 @@ __device__ __forceinline__ void poll_tagged(const KernelParams& p, const uint64_
       if ((pending >> k) & 1u) w[k] = ld_tag(r, voff(k), soff(k));
 #pragma unroll
     for (int k = 0; k < K; ++k) {
-      if (((pending >> k) & 1u) && (uint32_t)(w[k] >> 32) == p.epoch) {
+      if (((pending >> k) & 1u) && (uint32_t)(w[k] >> 32) == ep) {
         sink(k, (uint32_t)w[k]);
         pending &= ~(1u << k);
       }
     }
     if (!__any(pending != 0u)) break;
-    if (poll_give_up(p, pass, t0, what)) break;
+    if (poll_give_up(p, ep, pass, t0, what)) break;
     __builtin_amdgcn_s_sleep(1);
   }
 }
@@ -248,25 +254,28 @@ __device__ __forceinline__ void poll_tagged(const KernelParams& p, const uint64_
 // seen current): checks the words, and re-issues reload(k) for those still stale, reusing w, with the
 // same abort and watchdog rules as poll_tagged.
 template <int K, typename Reload, typename Sink>
-__device__ __forceinline__ void poll_finish(const KernelParams& p, uint64_t (&w)[K], uint32_t pending, uint32_t what,
-                                            Reload reload, Sink sink) {
+__device__ __forceinline__ void poll_finish(const KernelParams& p, uint32_t ep, uint64_t (&w)[K], uint32_t pending,
+                                            uint32_t what, Reload reload, Sink sink) {
   const uint64_t t0 = __builtin_amdgcn_s_memrealtime();
   for (uint32_t pass = 1;; ++pass) {
 #pragma unroll
     for (int k = 0; k < K; ++k) {
-      if (((pending >> k) & 1u) && (uint32_t)(w[k] >> 32) == p.epoch) {
+      if (((pending >> k) & 1u) && (uint32_t)(w[k] >> 32) == ep) {
         sink(k, (uint32_t)w[k]);
         pending &= ~(1u << k);
       }
     }
     if (!__any(pending != 0u)) break;
-    if (poll_give_up(p, pass, t0, what)) break;
+    if (poll_give_up(p, ep, pass, t0, what)) break;
     __builtin_amdgcn_s_sleep(1);
 #pragma unroll
     for (int k = 0; k < K; ++k)
       if ((pending >> k) & 1u) w[k] = reload(k);
   }
 }
+
+// The watchdog's name for a wait on the next step's token (event indices name the other waits).
+constexpr uint32_t kWhatToken = 0xFFFFFFFEu;
 
 // A whole vector src[0, n): wave w polls the contiguous words [w * chunk, (w + 1) * chunk), chunk =
 // n / 8 rounded up to 64, lane l taking words l, l + 64, ..., so each load is one coalesced 512-byte
@@ -276,30 +285,31 @@ __device__ __forceinline__ int poll_index(int n, int k) {
   return (int)(threadIdx.x >> 6) * poll_chunk(n) + (int)(threadIdx.x & 63) + 64 * k;
 }
 template <int K, typename Sink>
-__device__ __forceinline__ void poll_vector(const KernelParams& p, const uint64_t* src, int n, uint32_t what, Sink sink) {
+__device__ __forceinline__ void poll_vector(const KernelParams& p, uint32_t ep, const uint64_t* src, int n, uint32_t what,
+                                            Sink sink) {
   const int i0 = poll_index(n, 0);
   const int cnt = min(poll_chunk(n) / 64, (n - i0 + 63) / 64);
-  poll_tagged<K>(p, src, [&](int k) { return i0 * 8 + (k & 7) * 512; }, [](int k) { return (k >> 3) * 4096; },
+  poll_tagged<K>(p, ep, src, [&](int k) { return i0 * 8 + (k & 7) * 512; }, [](int k) { return (k >> 3) * 4096; },
                  first_words(cnt), what, sink);
 }
 
 // ----------------------------------------------------------------------------- events
-// Wave 0 polls every producer flag of the event until all hold >= epoch. A watchdog on the
+// Wave 0 polls every producer flag of the event until all hold >= the step's epoch. A watchdog on the
 // 100 MHz real-time counter turns a wait that never ends into an error and a kernel-wide abort.
-__device__ __forceinline__ void wait_event(const KernelParams& p, const TaskDesc& t, Ctl* ctl) {
+__device__ __forceinline__ void wait_event(const KernelParams& p, uint32_t ep, const TaskDesc& t, Ctl* ctl) {
   if (threadIdx.x < 64) {
     const uint64_t t0 = __builtin_amdgcn_s_memrealtime();
     const int lane = threadIdx.x;
     uint32_t ab = 0;
     while (true) {
       bool ok = true;
-      for (int i = lane; i < t.wait_nslots; i += 64) ok = ok && (ldc(&p.flags[t.wait_slot0 + i]) >= p.epoch);
+      for (int i = lane; i < t.wait_nslots; i += 64) ok = ok && (ldc(&p.flags[t.wait_slot0 + i]) >= ep);
       if (__all(ok)) break;
       ab = ldc(&p.err[E_ABORT]);
       if (ab) break;
       if (__builtin_amdgcn_s_memrealtime() - t0 > p.watchdog_ticks) {
         if (lane == 0) {
-          raise_error(p, ERR_TIMEOUT, (uint32_t)t.wait_ev, p.epoch);
+          raise_error(p, ERR_TIMEOUT, (uint32_t)t.wait_ev, ep);
           stc(&p.err[E_ABORT], 1u);
         }
         ab = 1;
@@ -316,8 +326,8 @@ __device__ __forceinline__ void wait_event(const KernelParams& p, const TaskDesc
 // barrier, and then one lane per slot stores the epoch. `my_sig` is this thread's slot (loaded
 // when the task started, so no load sits on the publish path), or -1. Only wave 0 holds slots
 // (a task has at most 64).
-__device__ __forceinline__ void publish(const KernelParams& p, int my_sig) {
-  if (my_sig >= 0) stc(&p.flags[my_sig], p.epoch);
+__device__ __forceinline__ void publish(const KernelParams& p, uint32_t ep, int my_sig) {
+  if (my_sig >= 0) stc(&p.flags[my_sig], ep);
 }
 
 // ----------------------------------------------------------------------------- GEMV tile
@@ -736,7 +746,7 @@ __device__ __forceinline__ void attn_lane_merge(int G, float (&mr)[GMAX], float 
 }
 
 template <int DH, int GMAX, int ANS>
-__device__ __forceinline__ void attn_part(const KernelParams& p, const TaskDesc& t, float* lds, Ctl* ctl,
+__device__ __forceinline__ void attn_part(const KernelParams& p, uint32_t ep, const TaskDesc& t, float* lds, Ctl* ctl,
                                           uint16_t* const* pools, int s, int grp, int pos, int c0, int c1,
                                           float (&Mo)[AttnShape<DH, GMAX>::EPT], float (&Lo)[AttnShape<DH, GMAX>::EPT],
                                           float (&Ao)[AttnShape<DH, GMAX>::EPT]) {
@@ -809,7 +819,7 @@ __device__ __forceinline__ void attn_part(const KernelParams& p, const TaskDesc&
     uint32_t pend = first_words(min(poll_chunk(nq) / 64, (nq - iq + 63) / 64));
     if (cur && tid < DH / 2) pend |= 3u << KQ;
     poll_tagged<KQ + 2>(
-        p, qsrc, [&](int k) { return k < KQ ? iq * 8 + k * 512 : tid * 8; },
+        p, ep, qsrc, [&](int k) { return k < KQ ? iq * 8 + k * 512 : tid * 8; },
         [&](int k) { return k < KQ ? 0 : k == KQ ? dk : dv; }, pend, what, [&](int k, uint32_t b) {
           if (k < KQ) q_slot(iq + 64 * k) = __uint_as_float(b) * qscale;
           else kvc[(k - KQ) * (DH / 2) + tid] = b;
@@ -901,7 +911,7 @@ __device__ __forceinline__ void attn_part(const KernelParams& p, const TaskDesc&
 }
 
 template <int DH, int GMAX, int ANS, bool COST>
-__device__ __forceinline__ void task_attn(const KernelParams& p, const TaskDesc& t, float* lds, Ctl* ctl,
+__device__ __forceinline__ void task_attn(const KernelParams& p, uint32_t ep, const TaskDesc& t, float* lds, Ctl* ctl,
                                           uint16_t* const* pools, const int32_t* alo) {
   using AS = AttnShape<DH, GMAX>;
   constexpr int EPT = AS::EPT;
@@ -909,7 +919,7 @@ __device__ __forceinline__ void task_attn(const KernelParams& p, const TaskDesc&
   asm volatile("" : "+v"(tid));
   const int T = p.attn_tasks, ti = t.a2, W = __builtin_amdgcn_readfirstlane(ctl->aoff[16]);
   const int G = p.hq / p.hk, l = t.layer;
-  const uint32_t ep = p.epoch, what = (uint32_t)t.wait_ev;
+  const uint32_t what = (uint32_t)t.wait_ev;
   const int lo = __builtin_amdgcn_readfirstlane(alo[ti]), hi = __builtin_amdgcn_readfirstlane(alo[ti + 1]);
   // this task's partial slots: [2][G][DH + 2] words (m, l, unnormalised o)
   auto part_base = [&](int task, int slot) { return p.pt + (((size_t)l * T + task) * 2 + slot) * G * (DH + 2); };
@@ -952,7 +962,7 @@ __device__ __forceinline__ void task_attn(const KernelParams& p, const TaskDesc&
     const int c0 = ok ? 16 * (x - B) : 0, c1 = ok ? min(16 * (xe - B), pos + 1) : 0;
     if (!ok) pos = -1;
     float M[EPT], L[EPT], A[EPT];
-    attn_part<DH, GMAX, ANS>(p, t, lds, ctl, pools, s, grp, pos, c0, c1, M, L, A);
+    attn_part<DH, GMAX, ANS>(p, ep, t, lds, ctl, pools, s, grp, pos, c0, c1, M, L, A);
     if (p.trace && tid == 0) ctl->t_streamed = __builtin_amdgcn_s_memrealtime();
     if (xe < E) {  // the segment goes on in later tasks: this task's partial
       uint64_t* pb = part_base(ti, x == lo ? 0 : 1);
@@ -1007,7 +1017,7 @@ __device__ __forceinline__ void task_attn(const KernelParams& p, const TaskDesc&
             if (((live >> r) & 1u) && tid + e * NT < G * DH) pend |= 7u << ((e * R + r) * 3);
         float mv[EPT][R], lv[EPT][R], ov[EPT][R];
         poll_tagged<3 * R * EPT>(
-            p, part_base(0, 0),
+            p, ep, part_base(0, 0),
             [&](int k) {
               const int e = k / (3 * R), c3 = k % 3;
               return c3 == 2 ? ob[e] : hb[e] + c3 * 8;
@@ -1074,10 +1084,13 @@ __device__ __forceinline__ void task_attn(const KernelParams& p, const TaskDesc&
 }
 
 // ----------------------------------------------------------------------------- argmax keys
-// Order-preserving key: larger float -> larger key; on equal values the lower index wins.
+// Order-preserving key: larger float -> larger key; on equal values the lower index wins. A NaN of
+// either sign takes the top key (above +inf), so the argmax task sees it and reports it.
+constexpr uint32_t kNanKey = 0xFFFFFFFFu;
 __device__ __forceinline__ uint64_t argmax_key(float v, int idx) {
   uint32_t u = __float_as_uint(v);
   u = (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+  if (v != v) u = kNanKey;
   return ((uint64_t)u << 32) | (uint64_t)(0xFFFFFFFFu - (uint32_t)idx);
 }
 
@@ -1107,12 +1120,14 @@ __device__ __forceinline__ uint64_t block_max_u64(uint64_t k, Ctl* ctl) {
 //   LM head  final x -> RMSNorm -> logits and the tile's argmax key
 // One shared path keeps the instruction footprint small. The kernel's code is larger than the
 // instruction cache, and code that a CU runs once per layer is otherwise fetched anew each time.
-// nxt: the CU's next task in this launch, or null. staged: on entry, whether this wave's stage already
-// holds this task's units (staged by the previous task); on return, whether it holds the next task's.
-__device__ __forceinline__ void gemv_task(const KernelParams& p, const TaskDesc& t, float* lds, Ctl* ctl, WPipe& wp,
-                                          uint16_t* const* pools, const TaskDesc* nxt, bool& staged) {
+// ep: the step's epoch; step: the step's index within this launch. nxt: the CU's next task in this
+// launch, or null. staged: on entry, whether this wave's stage already holds this task's units (staged
+// by the previous task); on return, whether it holds the next task's.
+__device__ __forceinline__ void gemv_task(const KernelParams& p, uint32_t ep, int step, const TaskDesc& t, float* lds,
+                                          Ctl* ctl, WPipe& wp, uint16_t* const* pools, const TaskDesc* nxt,
+                                          bool& staged) {
   const int type = t.type, l = t.layer, s = 0, tid = threadIdx.x;
-  const uint32_t ep = p.epoch, what = (uint32_t)t.wait_ev;
+  const uint32_t what = (uint32_t)t.wait_ev;
   const GemvGeom gm = ctl->geoms[t.geom];
   const int padded = gm.S * gm.lpr * 8, np = padded >> 3;
   float* xs = lds;
@@ -1127,7 +1142,9 @@ __device__ __forceinline__ void gemv_task(const KernelParams& p, const TaskDesc&
                                            : ht_at(p, l, s);
   const bool in_embed = type == T_QKV && l == 0;     // the first QKV reads the embedding row
   const bool res_embed = type == T_OPROJ && l == 0;  // the first O-proj adds to it
-  const uint16_t* erow = (in_embed || res_embed) ? p.embed + (size_t)token_of(p, s) * p.d : nullptr;
+  // After a launch's first step the token is the tagged word the previous step's argmax published; its
+  // first load goes out with the input poll, ahead of the weights.
+  const bool tok_tagged = (in_embed || res_embed) && step > 0;
 
   // Everything the task loads before its GEMV is issued ahead of the weight stream: the wait counter
   // of vector memory completes in order, so a load issued after the stream's first NSLOT units per
@@ -1157,6 +1174,8 @@ __device__ __forceinline__ void gemv_task(const KernelParams& p, const TaskDesc&
 #pragma unroll
   for (int k = 0; k < 32; ++k)
     if ((pending >> k) & 1u) w1[k] = ld_tag(rin, i0 * 8 + (k & 7) * 512, (k >> 3) * 4096);
+  uint64_t tw[1] = {0};
+  if (tok_tagged) tw[0] = ld_tag(tag_rsrc(p.tokt), s * 8, 0);
   // Gains: thread t scales elements [8t, 8t + 8) and [4096 + 8t, 4096 + 8t + 8) (n <= 8192).
   const uint16_t* gain = type == T_QKV      ? layer_norm_gain(p, l, 0)
                          : type == T_GATEUP ? layer_norm_gain(p, l, 1)
@@ -1190,6 +1209,19 @@ __device__ __forceinline__ void gemv_task(const KernelParams& p, const TaskDesc&
     pos = checked_pos(p, ctl, s);
     if (tid < nsets) pre = qkv_set_consts(p, l, t.row0 + 4 * tid, pos < 0 ? 0 : pos, s);
   }
+  const uint16_t* erow = nullptr;
+  if (in_embed || res_embed) {
+    int tok;
+    if (tok_tagged) {
+      uint32_t b = 0;
+      poll_finish<1>(p, ep, tw, 1u, kWhatToken, [&](int) { return ld_tag(tag_rsrc(p.tokt), s * 8, 0); },
+                     [&](int, uint32_t v) { b = v; });
+      tok = (int)min(b, (uint32_t)(p.vocab - 1));
+    } else {
+      tok = token_of(p, s);
+    }
+    erow = p.embed + (size_t)tok * p.d;
+  }
 
   // the input vector, two-plane layout in LDS, zero past n
   float* xd = xs + xs_index(i0, np);
@@ -1204,7 +1236,7 @@ __device__ __forceinline__ void gemv_task(const KernelParams& p, const TaskDesc&
       }
     }
     if (__any(pending != 0u))
-      poll_tagged<32>(p, src, [&](int k) { return i0 * 8 + (k & 7) * 512; }, [](int k) { return (k >> 3) * 4096; },
+      poll_tagged<32>(p, ep, src, [&](int k) { return i0 * 8 + (k & 7) * 512; }, [](int k) { return (k >> 3) * 4096; },
                       pending, what, [&](int k, uint32_t b) { xd[32 * k] = __uint_as_float(b); });
   }
   for (int i = n + tid; i < padded; i += NT) xs[xs_index(i, np)] = 0.f;
@@ -1246,7 +1278,7 @@ __device__ __forceinline__ void gemv_task(const KernelParams& p, const TaskDesc&
       }
     }
     if (__any(stale != 0u))
-      poll_tagged<4>(p, rsrc + t.row0, [&](int k) { return (tid + k * NT) * 8; }, [](int) { return 0; }, stale, what,
+      poll_tagged<4>(p, ep, rsrc + t.row0, [&](int k) { return (tid + k * NT) * 8; }, [](int) { return 0; }, stale, what,
                      [&](int k, uint32_t b) { res[k] = __uint_as_float(b); });
   }
   if (p.trace && tid == 0) ctl->t_ready = __builtin_amdgcn_s_memrealtime();
@@ -1311,8 +1343,15 @@ __device__ __forceinline__ v4f mfma_bf16(const v4u a, const v4u b, const v4f c) 
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a), __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
 }
 
-// Token and position of sequence s; any thread may report a bad one (the first report is kept).
-__device__ __forceinline__ int token_any(const KernelParams& p, int s) {
+// Token and position of sequence s; any thread may report a bad one (the first report is kept). After a
+// launch's first step the token is the tagged word the previous step's argmax published.
+__device__ __forceinline__ int token_any(const KernelParams& p, uint32_t ep, int step, int s) {
+  if (step > 0) {
+    uint32_t b = 0;
+    poll_tagged<1>(p, ep, p.tokt, [&](int) { return s * 8; }, [](int) { return 0; }, 1u, kWhatToken,
+                   [&](int, uint32_t v) { b = v; });
+    return (int)min(b, (uint32_t)(p.vocab - 1));
+  }
   int tok = p.tokens_in[s];
   if (tok < 0 || tok >= p.vocab) {
     raise_error(p, ERR_TOKEN, (uint32_t)s, (uint32_t)tok);
@@ -1329,8 +1368,8 @@ __device__ __forceinline__ int pos_any(const KernelParams& p, const Ctl* ctl, in
   return pos;
 }
 
-__device__ __forceinline__ void gemv_task_b(const KernelParams& p, const TaskDesc& t, float* lds, Ctl* ctl,
-                                            uint16_t* const* pools) {
+__device__ __forceinline__ void gemv_task_b(const KernelParams& p, uint32_t ep, int step, const TaskDesc& t, float* lds,
+                                            Ctl* ctl, uint16_t* const* pools) {
   WPipe wp;  // task-local: no weight loads are carried into the next task
   // The thread index made opaque per task: per-lane offsets are computed here rather than hoisted out of
   // the task loop and held in registers through every other task.
@@ -1338,7 +1377,7 @@ __device__ __forceinline__ void gemv_task_b(const KernelParams& p, const TaskDes
   asm volatile("" : "+v"(tid));
   const int type = t.type, l = t.layer, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const uint32_t ep = p.epoch, what = (uint32_t)t.wait_ev;
+  const uint32_t what = (uint32_t)t.wait_ev;
   const int nact = min(p.n_active, p.max_seqs);
   const int rows = t.row1 - t.row0, R = (rows + 15) >> 4, Q = (rows + 3) >> 2;
   const int kb0 = t.a2 & 0xFFFF, nu = t.a2 >> 16, js = t.a3 & 0xFF, kS = t.a3 >> 8;
@@ -1368,8 +1407,13 @@ __device__ __forceinline__ void gemv_task_b(const KernelParams& p, const TaskDes
 
   // Input staging. Thread (wave w, lane) holds sequences 2w and 2w + 1, columns 64 c + lane of the
   // block (c < 16): each load is a coalesced 512-byte row of one sequence's tagged words. The loads are
-  // unconditional and bounded by their buffer's size (out-of-range loads return zero), so all of them
-  // issue together; only the words of active sequences inside K are polled.
+  // unconditional, so all of them issue together; only the words of active sequences inside K are
+  // polled. The buffer range check covers the lane offset, not the uniform one, so a sequence past the
+  // configured ones reads the last configured sequence's row instead, and columns past the task's
+  // (or past K) read at most one 1024-column block past a row: for tagged words inside the scratch
+  // buffer, for gains and embedding rows inside the weights buffer (whose layout ends with a pad of
+  // that size). Such values are never used: with K a multiple of 32, every column a task stages lies
+  // inside K.
   const int ln = lane;
   const int s0 = 2 * wave;
   float ss[2] = {0.f, 0.f};
@@ -1379,8 +1423,8 @@ __device__ __forceinline__ void gemv_task_b(const KernelParams& p, const TaskDes
   const __amdgpu_buffer_rsrc_t rx = __builtin_amdgcn_make_buffer_rsrc((void*)src, (short)0, p.max_seqs * K * 8, 0x00020000);
   const __amdgpu_buffer_rsrc_t rgain = __builtin_amdgcn_make_buffer_rsrc((void*)gain, (short)0, K * 2, 0x00020000);
   auto x_word = [&](int b, int kw) {
-    const int c0 = 32 * (kb0 + b * ub), c = kw & 15;
-    return ld_tag(rx, ln * 8 + (c & 7) * 512, ((s0 + (kw >> 4)) * K + c0) * 8 + (c >> 3) * 4096);
+    const int c0 = 32 * (kb0 + b * ub), c = kw & 15, sq = min(s0 + (kw >> 4), p.max_seqs - 1);
+    return ld_tag(rx, ln * 8 + (c & 7) * 512, (sq * K + c0) * 8 + (c >> 3) * 4096);
   };
   auto x_issue = [&](int b) {
     const int c0 = 32 * (kb0 + b * ub), ncol = 32 * min(ub, nu - b * ub);
@@ -1393,7 +1437,7 @@ __device__ __forceinline__ void gemv_task_b(const KernelParams& p, const TaskDes
     if (in_embed) {  // the first layer's input: the tokens' embedding rows, as current words
       xpend = 0;
       for (int h = 0; h < 2; ++h) {
-        const int tk = s0 + h < nact ? token_any(p, s0 + h) : 0;
+        const int tk = s0 + h < nact ? token_any(p, ep, step, s0 + h) : 0;
         const __amdgpu_buffer_rsrc_t re =
             __builtin_amdgcn_make_buffer_rsrc((void*)(p.embed + (size_t)tk * p.d), (short)0, p.d * 2, 0x00020000);
 #pragma unroll
@@ -1412,7 +1456,7 @@ __device__ __forceinline__ void gemv_task_b(const KernelParams& p, const TaskDes
   };
   auto x_finish = [&](int b) {
     const int ncol = 32 * min(ub, nu - b * ub);
-    poll_finish<32>(p, xw, xpend, what, [&](int kw) { return x_word(b, kw); }, [](int, uint32_t) {});
+    poll_finish<32>(p, ep, xw, xpend, what, [&](int kw) { return x_word(b, kw); }, [](int, uint32_t) {});
     // Fragments: sequence s, column col -> unit col / 32, lane s + 16 ((col % 32) / 8), element col % 8.
     // Lane pairs swap halves so each lane stores one dword: the even lane two high parts, the odd lane
     // two remainders. With col = 64 c + lane, word kw lands at dword 1024 c + 8 h past the lane's base.
@@ -1565,7 +1609,7 @@ __device__ __forceinline__ void gemv_task_b(const KernelParams& p, const TaskDes
         }
         float v[30];
         poll_tagged<30>(
-            p, bp,
+            p, ep, bp,
             [&](int k) {
               const int i = k / 5, c = k % 5;
               return ((jb + i * tpp) * SW + (c < 4 ? eo + c : R * 256 + s)) * 8;
@@ -1628,11 +1672,11 @@ __device__ __forceinline__ void gemv_task_b(const KernelParams& p, const TaskDes
     } else if (resid) {
       float xo[4] = {0.f, 0.f, 0.f, 0.f};
       if (type == T_OPROJ && l == 0) {
-        const uint16_t* er = p.embed + (size_t)token_any(p, s) * p.d;
+        const uint16_t* er = p.embed + (size_t)token_any(p, ep, step, s) * p.d;
         for (int r = 0; r < nr; ++r) xo[r] = bf2f(er[r0 + r]);
       } else {
         const uint64_t* rb = type == T_OPROJ ? xt_at(p, l - 1, 1, 0) : xt_at(p, l, 0, 0);
-        poll_tagged<4>(p, rb, [&](int k) { return (s * p.d + r0 + k) * 8; }, [](int) { return 0; }, first_words(nr), what,
+        poll_tagged<4>(p, ep, rb, [&](int k) { return (s * p.d + r0 + k) * 8; }, [](int) { return 0; }, first_words(nr), what,
                        [&](int k, uint32_t bits) { xo[k] = __uint_as_float(bits); });
       }
       uint64_t* dst = xt_at(p, l, type == T_OPROJ ? 0 : 1, s) + r0;
@@ -1661,7 +1705,10 @@ __device__ __forceinline__ void gemv_task_b(const KernelParams& p, const TaskDes
   }
 }
 
-__device__ __forceinline__ void task_argmax(const KernelParams& p, const TaskDesc& t, Ctl* ctl) {
+// The step's token of sequence s: the largest of the LM tiles' keys. It goes to the caller's output
+// row of this step and, tagged with the next step's epoch, to the next step's embedding lookups; the
+// sequence's context length becomes this step's position + 1.
+__device__ __forceinline__ void task_argmax(const KernelParams& p, uint32_t ep, int step, const TaskDesc& t, Ctl* ctl) {
   const int s = t.a0;
   uint64_t best = 0;
   for (int i = threadIdx.x; i < p.n_lm_parts; i += NT) {
@@ -1670,8 +1717,11 @@ __device__ __forceinline__ void task_argmax(const KernelParams& p, const TaskDes
   }
   best = block_max_u64(best, ctl);
   if (threadIdx.x == 0 && s < p.n_active) {
-    p.tokens_out[s] = (int32_t)(0xFFFFFFFFu - (uint32_t)(best & 0xFFFFFFFFu));
-    p.ctx_lens[s] = p.ctx_lens[s] + 1;
+    const int32_t tok = (int32_t)(0xFFFFFFFFu - (uint32_t)(best & 0xFFFFFFFFu));
+    if ((uint32_t)(best >> 32) == kNanKey) raise_error(p, ERR_NAN, (uint32_t)s, (uint32_t)tok);
+    p.tokens_out[(size_t)step * p.n_active + s] = tok;
+    p.ctx_lens[s] = ctl->ctx[s] + 1;
+    st_tag(&p.tokt[s], (uint32_t)tok, ep + 1);
   }
 }
 
@@ -1703,41 +1753,50 @@ __global__ __launch_bounds__(NT, 1) void mk_megakernel(KernelParams p) {
     pools[i] = p.kpool[i];
     pools[p.n_layers + i] = p.vpool[i];
   }
-  // context lengths change only at the end of the step (the argmax task), after every reader
-  if (threadIdx.x < 16) {
-    const int s = threadIdx.x;
-    const int pos = s < p.max_seqs ? p.ctx_lens[s] : 0;
-    ctl->ctx[s] = pos;
-    // an active sequence attends to blocks 0 .. pos / 16 (one block when its position is out of range:
-    // the task holding it reports the error and writes zeros)
-    ctl->anb[s] = s < min(p.n_active, p.max_seqs) ? ((pos >= 0 && pos < p.max_pos) ? (pos >> 4) + 1 : 1) : 0;
-  }
   // Stage the queue's descriptors in LDS: a task switch then costs an LDS read instead of two
   // dependent scalar loads from memory on the path between one task's publish and the next wait.
   for (int i = threadIdx.x; i < (q1 - q0) * 16; i += NT) {
     const int k = i >> 4, w = i & 15;
     ((int32_t*)&tq[k])[w] = ((const int32_t*)&p.tasks[p.queue_idx[q0 + k]])[w];
   }
-  bar();
-  if (threadIdx.x < 17) {  // first block of sequence s's segments: hk segments per earlier sequence
-    int o = 0;
-    for (int s = 0; s < (int)threadIdx.x; ++s) o += ctl->anb[s];
-    ctl->aoff[threadIdx.x] = o * p.hk;
-  }
-  bar();
-  {
-    const int W = ctl->aoff[16], te = min(p.attn_tasks, max(1, (W + p.attn_min_blocks - 1) / p.attn_min_blocks));
-    if constexpr (BATCHED) {  // several sequences: a cut by cost, each segment start counting kAttnPieceBlocks blocks
-      for (int i = threadIdx.x; i <= p.attn_tasks; i += NT) alo[i] = attn_lo_cost(ctl, p.hk, W, te, min(i, te), kAttnPieceBlocks);
-    } else {
-      for (int i = threadIdx.x; i <= p.attn_tasks; i += NT) alo[i] = attn_lo_of(W, te, min(i, te));
-    }
-    if (threadIdx.x == 0) ctl->ate = te;
-  }
-  bar();
   WPipe wp;
   bool staged = false;  // this wave's LDS stage holds the next GEMV task's units
-  for (int qi = q0; qi < q1; ++qi) {
+  // Steps run one after another, each with its own epoch. Every task of a step is an ancestor of the
+  // step's argmax, which every task of the next step follows, so a buffer rewritten in the next step has
+  // no reader left in this one. One loop walks (step, task): a nested step loop keeps more values live
+  // across the whole launch and costs registers.
+  for (int step = 0, qi = q0; qi < q1;) {
+    const uint32_t ep = p.epoch + (uint32_t)step;
+    if (qi == q0) {
+      // Context lengths: read at launch, then one more per step for the running sequences (the argmax
+      // task stores the same values). They change only between steps, after every reader.
+      if (threadIdx.x < 16) {
+        const int s = threadIdx.x;
+        const bool act = s < min(p.n_active, p.max_seqs);
+        const int pos = step == 0 ? (s < p.max_seqs ? p.ctx_lens[s] : 0) : ctl->ctx[s] + (act ? 1 : 0);
+        ctl->ctx[s] = pos;
+        // an active sequence attends to blocks 0 .. pos / 16 (one block when its position is out of
+        // range: the task holding it reports the error and writes zeros)
+        ctl->anb[s] = act ? ((pos >= 0 && pos < p.max_pos) ? (pos >> 4) + 1 : 1) : 0;
+      }
+      bar();
+      if (threadIdx.x < 17) {  // first block of sequence s's segments: hk segments per earlier sequence
+        int o = 0;
+        for (int s = 0; s < (int)threadIdx.x; ++s) o += ctl->anb[s];
+        ctl->aoff[threadIdx.x] = o * p.hk;
+      }
+      bar();
+      {
+        const int W = ctl->aoff[16], te = min(p.attn_tasks, max(1, (W + p.attn_min_blocks - 1) / p.attn_min_blocks));
+        if constexpr (BATCHED) {  // several sequences: a cut by cost, each segment start counting kAttnPieceBlocks blocks
+          for (int i = threadIdx.x; i <= p.attn_tasks; i += NT) alo[i] = attn_lo_cost(ctl, p.hk, W, te, min(i, te), kAttnPieceBlocks);
+        } else {
+          for (int i = threadIdx.x; i <= p.attn_tasks; i += NT) alo[i] = attn_lo_of(W, te, min(i, te));
+        }
+        if (threadIdx.x == 0) ctl->ate = te;
+      }
+      bar();
+    }
     const TaskDesc t = tq[qi - q0];
     // Only the LM head's partial maxima travel under flags (the argmax task waits for them); every
     // other input is a tagged activation that its consumer polls for inside the task.
@@ -1753,23 +1812,23 @@ __global__ __launch_bounds__(NT, 1) void mk_megakernel(KernelParams p) {
     if (t.type == T_ATTN) {
       // position groups in flight per wave: more for batches (long streams), fewer for one sequence
       // and for many heads per KV head (register budget)
-      task_attn<DH, GMAX, (GMAX > 4 || !BATCHED) ? 4 : 8, BATCHED>(p, t, lds, ctl, pools, alo);
+      task_attn<DH, GMAX, (GMAX > 4 || !BATCHED) ? 4 : 8, BATCHED>(p, ep, t, lds, ctl, pools, alo);
       staged = false;
     } else if (t.type == T_ARGMAX) {
       staged = false;
-      if (t.wait_ev >= 0) wait_event(p, t, ctl);
+      if (t.wait_ev >= 0) wait_event(p, ep, t, ctl);
       if (p.trace && threadIdx.x == 0) ctl->t_ready = __builtin_amdgcn_s_memrealtime();
-      if (t.wait_ev < 0 || !ctl->aborted) task_argmax(p, t, ctl);
+      if (t.wait_ev < 0 || !ctl->aborted) task_argmax(p, ep, step, t, ctl);
     } else if constexpr (BATCHED) {
-      gemv_task_b(p, t, lds, ctl, pools);
+      gemv_task_b(p, ep, step, t, lds, ctl, pools);
     } else {
-      gemv_task(p, t, lds, ctl, wp, pools, qi + 1 < q1 ? &tq[qi + 1 - q0] : nullptr, staged);
+      gemv_task(p, ep, step, t, lds, ctl, wp, pools, qi + 1 < q1 ? &tq[qi + 1 - q0] : nullptr, staged);
     }
     // The LM head's stores must be complete before its flags go out; other tasks' consumers check
     // the tags themselves.
     if (t.type == T_LMHEAD) wait_stores();
     bar();
-    publish(p, my_sig);
+    publish(p, ep, my_sig);
     if (p.trace && threadIdx.x == 0) {
       TraceRec r;
       r.t_queue = t_queue;
@@ -1779,9 +1838,12 @@ __global__ __launch_bounds__(NT, 1) void mk_megakernel(KernelParams p) {
       r.cu = (uint16_t)cu;
       r.type = (uint8_t)t.type;
       r.layer = (uint8_t)t.layer;
-      r.epoch = p.epoch;
+      r.epoch = ep;
+      r.xcc = __builtin_amdgcn_s_getreg(kHwRegXccId) & 0xFu;  // the XCD this CU sits on
+      r.step = (uint32_t)step;
       p.trace[p.queue_idx[qi]] = r;
     }
+    if (++qi == q1 && ++step < p.n_steps) qi = q0;  // the next step walks the queue again
   }
 }
 
@@ -1852,16 +1914,17 @@ static const void* megakernel_for(int dh, int hq, int hk, bool batched) {
   return batched ? megakernel_for_t<true>(dh, hq / hk) : megakernel_for_t<false>(dh, hq / hk);
 }
 
-hipError_t launch_megakernel(const KernelParams& p, int grid, size_t lds_bytes, hipStream_t stream) {
+hipError_t launch_megakernel(const KernelParams& p, int grid, size_t lds_bytes, hipStream_t stream, bool coop) {
   KernelParams copy = p;
   void* args[] = {(void*)&copy};
   // The grid is one workgroup per CU and the LDS allows one per CU, so on a device running nothing
-  // else every workgroup is resident at once, which the task queues need. A plain launch is used:
-  // the cooperative launch path added about 18 us per dispatch on MI355X. Where other work may hold
-  // CUs, MK_COOPERATIVE_LAUNCH=1 makes the runtime guarantee co-residency. (Without it, waits that
-  // cannot be met end at the watchdog with an error, not in a hang.)
-  static const bool coop = std::getenv("MK_COOPERATIVE_LAUNCH") != nullptr;
-  if (coop)
+  // else every workgroup is resident at once, which the task queues need. A launch of several steps is
+  // cooperative: the runtime then guarantees co-residency, for about 18 us per dispatch on MI355X,
+  // which the steps share. A single step uses a plain launch by default; where other work may hold
+  // CUs, MK_COOPERATIVE_LAUNCH=1 makes it cooperative too. (Without it, waits that cannot be met end at
+  // the watchdog with an error, not in a hang.)
+  static const bool coop_env = std::getenv("MK_COOPERATIVE_LAUNCH") != nullptr;
+  if (coop || coop_env)
     return hipLaunchCooperativeKernel(megakernel_for(p.dh, p.hq, p.hk, p.max_seqs > 1), dim3(grid), dim3(NT), args,
                                       (unsigned)lds_bytes, stream);
   return hipLaunchKernel(megakernel_for(p.dh, p.hq, p.hk, p.max_seqs > 1), dim3(grid), dim3(NT), args,

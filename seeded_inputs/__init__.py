@@ -80,6 +80,9 @@ WORKLOADS = {
     "qwen0.5b": Workload("qwen0.5b", QWEN05B, 1, prompt_len=39, steps=512),
     "llama8b": Workload("llama8b", LLAMA8B, 1, prompt_len=39, steps=512),
     "llama8b_long": Workload("llama8b_long", LLAMA8B, 1, steps=64, prefill_ctx=32768, paging="permuted"),
+    # the 8B decode's last steps: a cache already holding 530 positions (near the end of the 39 + 512
+    # workload), for parity on the same 35-block cache and graph
+    "llama8b_pf530": Workload("llama8b_pf530", LLAMA8B, 1, steps=16, prefill_ctx=530),
     "llama8b_b16": Workload("llama8b_b16", LLAMA8B, 16, steps=128, ctx_range=(512, 8192), paging="permuted"),
     # small batched workloads with the same structure (per-sequence contexts, permuted pages)
     "tiny_b4": Workload("tiny_b4", TINY, 4, steps=8, ctx_range=(5, 60), paging="permuted"),

@@ -18,6 +18,35 @@ REL_L2_BAR = 5e-3     # teacher-forced per-step logits, relative L2 (the stated 
 BUG_FLOOR = 1e-5
 
 
+_WEIGHTS = {}
+
+
+def cached_weights(shape):
+    """The seeded weights of a model shape, generated once per test session (the 8B set is 16 GB)."""
+    if shape.name not in _WEIGHTS:
+        _WEIGHTS[shape.name] = si.gen_weights(shape)
+    return _WEIGHTS[shape.name]
+
+
+def graph_hash(dec) -> int:
+    import persistent_megakernel_03_amd as mk
+    return int(mk.mk_graph_stats(dec.ctx).hash)
+
+
+def golden_graph_hash(name: str, n_cus: int):
+    """The stored hash of a workload's task graph for n_cus compute units (tests/golden/graph_hashes.json),
+    or None when none is stored for that CU count."""
+    import json
+    import os
+    path = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden", "graph_hashes.json")
+    with open(path) as f:
+        g = json.load(f)
+    e = g["graphs"].get(name)
+    if e is None or e["n_cus"] != n_cus:
+        return None
+    return int(e["hash"], 16)
+
+
 def rel_l2(a, b) -> float:
     a = np.asarray(a, dtype=np.float64)
     b = np.asarray(b, dtype=np.float64)
@@ -93,18 +122,19 @@ def bug_bar(res) -> float:
     return max(BUG_FLOOR, 2.0 * max(res["rel_f32"])) if res["rel_f32"] else REL_L2_BAR
 
 
-def prefilled_case(wl, n_decode, attn_splits=0, device=0, precision_check=False):
+def prefilled_case(wl, n_decode, attn_splits=0, device=0, weights=None, capacity=None):
     """A decode workload whose sequences start from a pre-filled KV cache (N(0, 1) bf16 K/V at
-    positions < ctx, keys taken as already rotated), on both sides. Returns (decoder, oracle,
-    ctx lengths, block table)."""
+    positions < ctx, keys taken as already rotated), on both sides. The cache holds `capacity`
+    positions per sequence (default ctx + n_decode). Returns (decoder, oracle, ctx lengths, block
+    table, weights)."""
     import torch
     import oracle as orc
     import persistent_megakernel_03_amd as mk
     m = wl.model
     ctx = si.context_lengths(wl)
-    cap = ctx + n_decode
+    cap = ctx + n_decode if capacity is None else np.maximum(ctx + n_decode, capacity)
     table, nblocks = si.block_tables(wl, cap)
-    weights = si.gen_weights(m)
+    weights = si.gen_weights(m) if weights is None else weights
     cfg = mk.make_config(m, max_seqs=wl.n_seqs, max_blocks_per_seq=table.shape[1], num_blocks=nblocks,
                          attn_splits=attn_splits)
     dec = mk.Decoder(cfg, device)

@@ -14,7 +14,7 @@ import numpy as np
 import pytest
 
 import seeded_inputs as si
-from parity_util import REL_L2_BAR, prefilled_case, rel_l2
+from parity_util import REL_L2_BAR, cached_weights, prefilled_case, rel_l2
 
 pytestmark = pytest.mark.gpu
 
@@ -24,11 +24,11 @@ def log(*a):
     sys.stdout.flush()
 
 
-def run_batched(wl, n_decode, n_active=None, attn_splits=0):
+def run_batched(wl, n_decode, n_active=None, attn_splits=0, weights=None, capacity=None):
     import torch
     n = wl.n_seqs
     na = n if n_active is None else n_active
-    dec, om, ctx, table, w = prefilled_case(wl, n_decode, attn_splits=attn_splits)
+    dec, om, ctx, table, w = prefilled_case(wl, n_decode, attn_splits=attn_splits, weights=weights, capacity=capacity)
     toks = si.first_tokens(wl).astype(np.int64).copy()
     rels, agree, gaps_bad = [], [], []
     out = torch.zeros(n, dtype=torch.int32, device=dec.dev)
@@ -94,10 +94,12 @@ def test_mid_long_contexts_several_pieces_per_task():
 
 @pytest.mark.timeout(900)
 def test_llama8b_sixteen_sequences():
-    # the 8B shape at full size, 16 sequences with contexts in [512, 8192], in the launch
-    # configuration the benchmark times
-    log("case: llama8b_b16 full size, 16 sequences, 1 step")
-    run_batched(si.WORKLOADS["llama8b_b16"], 1)
+    # the 8B shape at full size, 16 sequences with contexts in [512, 8192], on the cache and graph the
+    # benchmark times (each cache sized for the workload's 128 steps)
+    wl = si.WORKLOADS["llama8b_b16"]
+    n = 4
+    log("case: llama8b_b16 full size, 16 sequences, %d steps" % n)
+    run_batched(wl, n, weights=cached_weights(wl.model), capacity=si.context_lengths(wl) + wl.steps)
 
 
 def test_mid_staged_launch_matches_fused():

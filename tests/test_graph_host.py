@@ -230,3 +230,103 @@ def test_batched_weights_cover_every_column_once(L, ksplit_cap):
         w = mk.mk_graph_stats(ctx).weight_bytes
         assert gemv <= w <= gemv * 1.1, (cap, w, gemv)
         mk.mk_destroy(ctx)
+
+
+# --------------------------------------------------------------------------- the checks reject broken graphs
+# Each case breaks a freshly built graph in one way (mk_graph_corrupt, host-only) and names the message
+# the validator must give. A validator that accepted everything would fail every case.
+@pytest.mark.parametrize("kind,message", [
+    (1, "queue not in global order"),
+    (2, "waits on a later producer"),
+    (3, "has two writers"),
+    (4, "has no writer"),
+    (5, "twice"),
+    (7, "does not end at row"),
+])
+@pytest.mark.parametrize("shape,n_seqs,n_cus", [(si.TINY, 1, 256), (si.TINY, 1, 7), (si.MID, 16, 256)])
+def test_validator_rejects_broken_graphs(L, ksplit_cap, kind, message, shape, n_seqs, n_cus):
+    ksplit_cap(None)
+    cfg = batched_cfg(shape, n_seqs, 4) if n_seqs > 1 else cfg_for(shape, 3, 3)
+    ctx = mk.mk_create_host(cfg, n_cus)
+    try:
+        mk.mk_graph_validate(ctx)
+        mk.mk_graph_corrupt(ctx, kind)
+        with pytest.raises(mk.MKError) as e:
+            mk.mk_graph_validate(ctx)
+        assert e.value.status == -2 and message in str(e.value), str(e.value)
+    finally:
+        mk.mk_destroy(ctx)
+
+
+@pytest.mark.parametrize("n_cus", [256, 16])
+def test_simulator_catches_a_consumer_that_does_not_wait(L, n_cus):
+    # an attention task whose wait on the QKV stage is removed: the graph still validates (nothing in
+    # it is out of order), but some interleaving runs the task before its queries exist
+    ctx = mk.mk_create_host(cfg_for(si.TINY, 3, 3, 2), n_cus)
+    try:
+        mk.mk_graph_corrupt(ctx, 6)
+        mk.mk_graph_validate(ctx)
+        failures = []
+        for seed in range(16):
+            try:
+                mk.mk_graph_simulate(ctx, seed, 1)
+            except mk.MKError as e:
+                failures.append(str(e))
+        assert failures and all("before its producer finished" in f for f in failures), failures[:2]
+    finally:
+        mk.mk_destroy(ctx)
+
+
+def test_simulator_catches_rows_written_twice(L):
+    # overlapping down tiles: the validator names it; the simulator's data checks stay consistent
+    # (the extra row's second writer is the later task)
+    ctx = mk.mk_create_host(cfg_for(si.TINY, 3, 3), 256)
+    try:
+        mk.mk_graph_corrupt(ctx, 5)
+        with pytest.raises(mk.MKError):
+            mk.mk_graph_validate(ctx)
+    finally:
+        mk.mk_destroy(ctx)
+
+
+def test_corruption_needs_a_host_context_and_a_known_kind(L):
+    ctx = mk.mk_create_host(cfg_for(si.TINY, 3, 3), 256)
+    try:
+        with pytest.raises(mk.MKError) as e:
+            mk.mk_graph_corrupt(ctx, 99)
+        assert e.value.status == -1
+    finally:
+        mk.mk_destroy(ctx)
+
+
+# --------------------------------------------------------------------------- determinism
+def test_golden_graph_hashes(L, ksplit_cap):
+    # every workload's graph, built as the benchmark and the parity tests build it, hashes to the
+    # stored value (tests/golden/graph_hashes.json, written by tests/golden/make_graph_hashes.py)
+    import importlib.util
+    import json
+    ksplit_cap(None)
+    spec = importlib.util.spec_from_file_location("make_graph_hashes", os.path.join(ROOT, "tests", "golden", "make_graph_hashes.py"))
+    mod = importlib.util.module_from_spec(spec)
+    spec.loader.exec_module(mod)
+    stored = json.load(open(os.path.join(ROOT, "tests", "golden", "graph_hashes.json")))["graphs"]
+    assert set(stored) == set(mod.NAMES)
+    for name in mod.NAMES:
+        got = mod.graph_entry(name, stored[name]["n_cus"])
+        assert got == stored[name], (name, got, stored[name])
+
+
+def test_graph_hash_is_the_same_in_a_fresh_process(L):
+    # the builder keeps no state between contexts and depends on no address: a new interpreter (other
+    # heap addresses) builds the same graph
+    import subprocess
+    import sys
+    code = ("import sys; sys.path.insert(0, %r); import persistent_megakernel_03_amd as mk, seeded_inputs as si;"
+            "c = mk.make_config(si.LLAMA8B, max_seqs=1, max_blocks_per_seq=35, num_blocks=35);"
+            "x = mk.mk_create_host(c, 256); print(mk.mk_graph_stats(x).hash)" % ROOT)
+    out = subprocess.run([sys.executable, "-c", code], capture_output=True, text=True, check=True).stdout
+    ctx = mk.mk_create_host(cfg_for(si.LLAMA8B, 35, 35), 256)
+    try:
+        assert int(out.strip()) == mk.mk_graph_stats(ctx).hash
+    finally:
+        mk.mk_destroy(ctx)
