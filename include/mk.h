@@ -181,6 +181,27 @@ mk_status mk_decode_step(mk_ctx* ctx, const int32_t* d_tokens_in, int n_seqs, in
 mk_status mk_decode_n(mk_ctx* ctx, const int32_t* d_tokens_in, int n_seqs, int n_steps, int32_t* d_tokens_out,
                       void* stream);
 
+/* mk_decode_step for callers that cannot allocate device memory (code under HIP
+ * graph capture, tight serving loops, harnesses that forbid allocation): the
+ * same step, but the working memory it writes (event flags, tagged
+ * activations, attention and column-split partials, argmax keys) lives in the
+ * library's static device array of 64 MiB per GPU instead of the bound scratch
+ * buffer. It allocates nothing and copies nothing from the host: it clears
+ * that array's flags and tagged buffers with a fill kernel on `stream`, then
+ * launches the step. The read-only task graph, rotary table and pool pointers
+ * come from the bound scratch buffer (uploaded by mk_bind_memory), and device
+ * errors are latched in the context's own error word, reported by the next
+ * synchronising call as for mk_decode_step.
+ *   - Arguments, results and context-length update: as mk_decode_step.
+ *   - Every call on one GPU shares that GPU's array; calls whose launches
+ *     overlap on one GPU (two streams, two threads) race and must not be made.
+ *   - The array keeps the last call's contents; each call clears what must
+ *     start at zero, so calls from different contexts may alternate.
+ * Errors: as mk_decode_step, plus MK_ERR_SHAPE when the graph's scratch
+ * layout (mk_workspace_size's scratch_bytes) exceeds 64 MiB. */
+mk_status mk_decode_step_static(mk_ctx* ctx, const int32_t* d_tokens_in, int n_seqs, int32_t* d_tokens_out,
+                                void* stream);
+
 /* The same decode step as mk_decode_step, launched as one kernel dispatch per dependency stage
  * (QKV, attention, O projection, gate/up and down of each layer, then the LM head and the argmax):
  * the same kernel, task graph and arithmetic, so the results are identical. Each dispatch runs only

@@ -51,7 +51,7 @@ class mk_graph_info(ctypes.Structure):
 
 
 EXPORTS = ["mk_create", "mk_create_host", "mk_workspace_size", "mk_bind_memory", "mk_load_weights", "mk_decode_step",
-           "mk_decode_n", "mk_decode_step_staged", "mk_prefill", "mk_read_logits", "mk_sync_check", "mk_graph_stats", "mk_graph_validate",
+           "mk_decode_n", "mk_decode_step_static", "mk_decode_step_staged", "mk_prefill", "mk_read_logits", "mk_sync_check", "mk_graph_stats", "mk_graph_validate",
            "mk_graph_simulate", "mk_graph_corrupt", "mk_set_trace", "mk_destroy", "mk_status_str", "mk_last_error"]
 
 
@@ -85,6 +85,7 @@ def lib():
             "mk_load_weights": [vp, ctypes.POINTER(mk_tensor), ctypes.c_int, vp],
             "mk_decode_step": [vp, vp, ctypes.c_int, vp, vp],
             "mk_decode_n": [vp, vp, ctypes.c_int, ctypes.c_int, vp, vp],
+            "mk_decode_step_static": [vp, vp, ctypes.c_int, vp, vp],
             "mk_decode_step_staged": [vp, vp, ctypes.c_int, vp, vp],
             "mk_prefill": [vp, ctypes.c_int, ctypes.POINTER(i32), ctypes.c_int, vp, vp],
             "mk_read_logits": [vp, ctypes.c_int, ctypes.POINTER(ctypes.c_float), sz, vp],
@@ -177,6 +178,10 @@ def mk_decode_step(ctx, tokens_in, n_seqs, tokens_out, stream=None):
 
 def mk_decode_n(ctx, tokens_in, n_seqs, n_steps, tokens_out, stream=None):
     _check(lib().mk_decode_n(ctx, _vp(tokens_in), n_seqs, n_steps, _vp(tokens_out), _vp(stream)))
+
+
+def mk_decode_step_static(ctx, tokens_in, n_seqs, tokens_out, stream=None):
+    _check(lib().mk_decode_step_static(ctx, _vp(tokens_in), n_seqs, _vp(tokens_out), _vp(stream)))
 
 
 def mk_decode_step_staged(ctx, tokens_in, n_seqs, tokens_out, stream=None):

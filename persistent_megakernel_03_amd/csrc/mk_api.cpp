@@ -22,6 +22,8 @@ hipError_t megakernel_occupancy(int* blocks_per_cu, size_t lds_bytes, int dh, in
 hipError_t launch_repack(const RepackArgs& a, int64_t units, hipStream_t stream);
 hipError_t launch_repack_bias(const uint16_t* bq, const uint16_t* bk, const uint16_t* bv, int G, int dh, int nrows,
                               uint16_t* out, hipStream_t stream);
+hipError_t static_scratch_address(int device, void** out);
+hipError_t launch_fill_zero(void* p, size_t bytes, hipStream_t stream);
 }  // namespace mk
 
 using namespace mk;
@@ -39,6 +41,9 @@ struct mk_ctx {
   uint32_t epoch = 0;
   uint32_t watchdog_ticks = 200000000u;  // 2 s at 100 MHz
   TraceRec* d_trace = nullptr;
+  uint8_t* d_static = nullptr;     // this device's static scratch array (mk_decode_step_static)
+  std::vector<float> rope_host;    // the rotary table and the per-layer pool pointers, as uploaded at bind
+  std::vector<void*> pool_table;
 };
 
 namespace {
@@ -125,26 +130,30 @@ mk_status read_error_word(mk_ctx* c, hipStream_t st) {
   return fail(s, what);
 }
 
-KernelParams make_params(mk_ctx* c) {
+// Kernel arguments. The read-only tables (task graph, rotary table, pool pointers) and the error word
+// come from the bound scratch buffer; the working memory a step writes (flags, tagged activations,
+// partials, argmax keys) from the scratch region at W: the bound buffer, or the static array.
+KernelParams make_params(mk_ctx* c, uint8_t* W) {
   const HostGraph& g = c->g;
   const mk_model_config& m = g.cfg;
-  uint8_t* S = c->d_scratch;
+  uint8_t* R = c->d_scratch;
   KernelParams p{};
-  p.tasks = (const TaskDesc*)(S + g.sl.tasks);
-  p.queue_off = (const int32_t*)(S + g.sl.queue_off);
-  p.queue_idx = (const int32_t*)(S + g.sl.queue_idx);
-  p.events = (const EventDesc*)(S + g.sl.events);
-  p.sig_slots = (const int32_t*)(S + g.sl.sig_slots);
-  p.geoms = (const GemvGeom*)(S + g.sl.geoms);
-  p.rope = (const float*)(S + g.sl.rope);
+  p.tasks = (const TaskDesc*)(R + g.sl.tasks);
+  p.queue_off = (const int32_t*)(R + g.sl.queue_off);
+  p.queue_idx = (const int32_t*)(R + g.sl.queue_idx);
+  p.events = (const EventDesc*)(R + g.sl.events);
+  p.sig_slots = (const int32_t*)(R + g.sl.sig_slots);
+  p.geoms = (const GemvGeom*)(R + g.sl.geoms);
+  p.rope = (const float*)(R + g.sl.rope);
+  p.err = (uint32_t*)(R + g.sl.err);
+  uint8_t* S = W;
   p.flags = (uint32_t*)(S + g.sl.flags);
-  p.err = (uint32_t*)(S + g.sl.err);
   p.wpacked = c->d_weights;
   p.embed = (const uint16_t*)(c->d_weights + g.wl.embed);
   p.norms = (const uint16_t*)(c->d_weights + g.wl.norms);
   p.bias = m.qkv_bias ? (const uint16_t*)(c->d_weights + g.wl.bias) : nullptr;
-  p.kpool = (uint16_t* const*)(S + g.sl.pools);
-  p.vpool = (uint16_t* const*)(S + g.sl.pools + (size_t)m.n_layers * 8);
+  p.kpool = (uint16_t* const*)(R + g.sl.pools);
+  p.vpool = (uint16_t* const*)(R + g.sl.pools + (size_t)m.n_layers * 8);
   p.page_table = c->d_page_table;
   p.ctx_lens = c->d_ctx_lens;
   p.xt = (uint64_t*)(S + g.sl.xt);
@@ -202,7 +211,7 @@ mk_status reserve_epochs(mk_ctx* c, int n_steps, hipStream_t st) {
 mk_status launch_step(mk_ctx* c, const int32_t* tin, int n_active, int32_t* tout, hipStream_t st, bool staged = false,
                       int n_steps = 1) {
   if (mk_status s = reserve_epochs(c, n_steps, st)) return s;
-  KernelParams p = make_params(c);
+  KernelParams p = make_params(c, c->d_scratch);
   p.tokens_in = tin;
   p.tokens_out = tout;
   p.n_active = n_active;
@@ -253,6 +262,15 @@ mk_status mk_create(const mk_model_config* cfg, int device, mk_ctx** out) {
     *out = nullptr;
     return fail(MK_ERR_UNSUPPORTED, "one workgroup per CU does not fit (LDS or registers)");
   }
+  // this device's copy of the static scratch array, resolved once per device at set-up
+  void* st = nullptr;
+  const hipError_t e = static_scratch_address(device, &st);
+  if (e != hipSuccess) {
+    mk_destroy(*out);
+    *out = nullptr;
+    return fail(MK_ERR_HIP, std::string("hipGetSymbolAddress(scratch): ") + hipGetErrorString(e));
+  }
+  (*out)->d_static = (uint8_t*)st;
   return MK_OK;
 }
 
@@ -296,12 +314,11 @@ mk_status mk_bind_memory(mk_ctx* c, void* d_weights, void* const* d_k_pools, voi
   HIPCHK(up(g.sl.events, g.events.data(), g.events.size() * sizeof(EventDesc)));
   if (!g.sig_slots.empty()) HIPCHK(up(g.sl.sig_slots, g.sig_slots.data(), g.sig_slots.size() * 4));
   HIPCHK(up(g.sl.geoms, g.geoms, sizeof(g.geoms)));
-  std::vector<float> rope;
-  rope_table(g.cfg, g.max_pos, rope);
-  HIPCHK(up(g.sl.rope, rope.data(), rope.size() * 4));
-  std::vector<void*> pools(c->kpools);
-  pools.insert(pools.end(), c->vpools.begin(), c->vpools.end());
-  HIPCHK(up(g.sl.pools, pools.data(), pools.size() * 8));
+  rope_table(g.cfg, g.max_pos, c->rope_host);
+  HIPCHK(up(g.sl.rope, c->rope_host.data(), c->rope_host.size() * 4));
+  c->pool_table = c->kpools;
+  c->pool_table.insert(c->pool_table.end(), c->vpools.begin(), c->vpools.end());
+  HIPCHK(up(g.sl.pools, c->pool_table.data(), c->pool_table.size() * 8));
   HIPCHK(hipMemset(S + g.sl.flags, 0, (size_t)g.n_flag_slots * 4));
   HIPCHK(hipMemset(S + g.sl.err, 0, E_COUNT * 4));
   HIPCHK(hipMemset(S + g.sl.tagged_begin, 0, (size_t)(g.sl.tagged_end - g.sl.tagged_begin)));
@@ -420,6 +437,35 @@ mk_status mk_decode_n(mk_ctx* c, const int32_t* d_tokens_in, int n_seqs, int n_s
   if (n_steps < 1 || n_steps > kMaxStepsPerLaunch) return fail(MK_ERR_INVALID_ARG, "n_steps out of range");
   DeviceGuard dg(c->device);
   return launch_step(c, d_tokens_in, n_seqs, d_tokens_out, (hipStream_t)stream, false, n_steps);
+}
+
+mk_status mk_decode_step_static(mk_ctx* c, const int32_t* d_tokens_in, int n_seqs, int32_t* d_tokens_out, void* stream) {
+  if (!c || !d_tokens_in || !d_tokens_out) return fail(MK_ERR_INVALID_ARG, "null argument");
+  if (!c->bound || !c->loaded) return fail(MK_ERR_STATE, "bind memory and load weights before decoding");
+  if (n_seqs < 1 || n_seqs > c->g.cfg.max_seqs) return fail(MK_ERR_INVALID_ARG, "n_seqs out of range");
+  const HostGraph& g = c->g;
+  if ((size_t)g.sl.total > kStaticScratchBytes)
+    return fail(MK_ERR_SHAPE, "this graph's working memory (" + std::to_string(g.sl.total) +
+                                  " bytes) exceeds the static scratch array (" + std::to_string(kStaticScratchBytes) + " bytes)");
+  if (!c->d_static) return fail(MK_ERR_STATE, "no static scratch on this device");
+  DeviceGuard dg(c->device);
+  hipStream_t st = (hipStream_t)stream;
+  uint8_t* S = c->d_static;
+  // The array keeps whatever the last call on this device left in it: the flags and the tagged buffers
+  // are cleared (a fill kernel on the stream), so the step starts from epoch 1. The argmax keys and the
+  // partial results are written before they are read within the step.
+  HIPCHK(launch_fill_zero(S + g.sl.flags, ((size_t)g.n_flag_slots * 4 + 255) & ~(size_t)255, st));
+  HIPCHK(launch_fill_zero(S + g.sl.tagged_begin, (size_t)(g.sl.tagged_end - g.sl.tagged_begin), st));
+  KernelParams p = make_params(c, S);
+  p.tokens_in = d_tokens_in;
+  p.tokens_out = d_tokens_out;
+  p.n_active = n_seqs;
+  p.n_steps = 1;
+  p.epoch = 1;
+  p.task_lo = 0;
+  p.task_hi = (int32_t)g.tasks.size();
+  HIPCHK(launch_megakernel(p, g.n_cus, (size_t)g.lds_bytes, st, false));
+  return MK_OK;
 }
 
 mk_status mk_decode_step_staged(mk_ctx* c, const int32_t* d_tokens_in, int n_seqs, int32_t* d_tokens_out, void* stream) {

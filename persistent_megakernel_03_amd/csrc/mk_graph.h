@@ -40,6 +40,9 @@ constexpr int kAttnMinBlocks = 1;
 // sequences of mixed lengths, about 24 blocks' streaming.
 constexpr int kAttnPieceBlocks = 24;
 constexpr int kStageBytes = 8 * kStageUnits * 1024;
+// Size of the static device array that holds a step's working memory for the entry point that
+// allocates nothing (mk_decode_step_static); larger graphs are refused there.
+constexpr size_t kStaticScratchBytes = (size_t)64 << 20;
 
 // Geometry of one GEMV operand in the packed (streaming) layout. A row of K bf16 values is
 // P = K/8 pieces of 16 bytes. A "unit" is 1 KB: 64 lanes x 16 B.

@@ -24,6 +24,7 @@
 // plain nontemporal loads.
 #include <hip/hip_runtime.h>
 #include <cstdlib>
+#include <mutex>
 #include <stdint.h>
 
 #include "mk_graph.h"
@@ -1933,6 +1934,50 @@ hipError_t launch_megakernel(const KernelParams& p, int grid, size_t lds_bytes, 
 
 hipError_t megakernel_occupancy(int* blocks_per_cu, size_t lds_bytes, int dh, int hq, int hk, bool batched) {
   return hipOccupancyMaxActiveBlocksPerMultiprocessor(blocks_per_cu, megakernel_for(dh, hq, hk, batched), NT, lds_bytes);
+}
+
+// ----------------------------------------------------------------------------- static scratch
+// The working memory of the entry point that allocates nothing (mk_decode_step_static): the step's copy
+// of the task graph and rotary table, the event flags, the tagged activations, the partial results and
+// the argmax keys live in this array instead of the caller's scratch buffer. Every GPU the library runs
+// on holds its own copy until the process ends. In host code the name is a stand-in, not a device
+// address: host code uses only the address hipGetSymbolAddress returns for the current device.
+static __device__ __align__(256) uint8_t scratch[kStaticScratchBytes];
+
+// The device address of `scratch` on `device`, resolved once per device with that device current.
+hipError_t static_scratch_address(int device, void** out) {
+  static std::mutex mu;
+  static void* addr[64] = {};
+  if (device < 0 || device >= 64) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(mu);
+  if (!addr[device]) {
+    int cur = -1;
+    hipError_t e = hipGetDevice(&cur);
+    if (e != hipSuccess) return e;
+    if (cur != device) return hipErrorInvalidDevice;  // the caller makes `device` current first
+    void* ptr = nullptr;
+    e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    if (!ptr) return hipErrorInvalidSymbol;
+    addr[device] = ptr;
+  }
+  *out = addr[device];
+  return hipSuccess;
+}
+
+// Zeroes [p, p + bytes) (16-byte aligned, a multiple of 16) with plain stores: a fill kernel rather than
+// hipMemsetAsync, so that the clearing can sit in a captured graph.
+extern "C" __global__ __launch_bounds__(256) void mk_fill_zero(v4u* p, int64_t n16) {
+  for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n16; i += (int64_t)gridDim.x * 256) p[i] = v4u{0u, 0u, 0u, 0u};
+}
+
+hipError_t launch_fill_zero(void* p, size_t bytes, hipStream_t stream) {
+  if (bytes == 0) return hipSuccess;
+  if (((uintptr_t)p & 15) || (bytes & 15)) return hipErrorInvalidValue;
+  const int64_t n16 = (int64_t)(bytes / 16);
+  const int64_t blocks = (n16 + 255) / 256;
+  hipLaunchKernelGGL(mk_fill_zero, dim3((unsigned)(blocks < 1024 ? blocks : 1024)), dim3(256), 0, stream, (v4u*)p, n16);
+  return hipGetLastError();
 }
 
 hipError_t launch_repack(const RepackArgs& a, int64_t units, hipStream_t stream) {
