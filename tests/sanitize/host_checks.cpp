@@ -18,6 +18,8 @@ hipError_t launch_repack(const RepackArgs&, int64_t, hipStream_t) { return hipEr
 hipError_t launch_repack_bias(const uint16_t*, const uint16_t*, const uint16_t*, int, int, int, uint16_t*, hipStream_t) {
   return hipErrorNotSupported;
 }
+hipError_t static_scratch_address(int, void**) { return hipErrorNotSupported; }
+hipError_t launch_fill_zero(void*, size_t, hipStream_t) { return hipErrorNotSupported; }
 }  // namespace mk
 
 static int failures = 0;
