@@ -1197,9 +1197,9 @@ __device__ __forceinline__ void gemv_task(const KernelParams& p, uint32_t ep, in
 #pragma unroll
     for (int k = 0; k < 4; ++k) rw[k] = ld_tag(rr, min(tid + k * NT, nrows - 1) * 8, 0);
   }
-  // the wave's first NSLOT weight units
+  // the wave's first NSLOT / 2 weight units (the rest go out after the input's second poll pass)
 #pragma unroll
-  for (int j = 0; j < NSLOT; ++j) wp.R[j] = load_unit(wrun, j);
+  for (int j = 0; j < NSLOT / 2; ++j) wp.R[j] = load_unit(wrun, j);
   // QKV: the rotary, bias and page-table constants of the thread's 4-row set. An out-of-range
   // position is reported and the row is not appended, but q, k and v are still written (at
   // position 0's rotation) so that no consumer waits for them.
@@ -1227,6 +1227,8 @@ __device__ __forceinline__ void gemv_task(const KernelParams& p, uint32_t ep, in
   // the input vector, two-plane layout in LDS, zero past n
   float* xd = xs + xs_index(i0, np);
   if (in_embed) {
+#pragma unroll
+    for (int j = NSLOT / 2; j < NSLOT; ++j) wp.R[j] = load_unit(wrun, j);
     for (int i = tid; i < n; i += NT) xs[xs_index(i, np)] = bf2f(erow[i]);
   } else {
 #pragma unroll
@@ -1236,9 +1238,19 @@ __device__ __forceinline__ void gemv_task(const KernelParams& p, uint32_t ep, in
         pending &= ~(1u << k);
       }
     }
-    if (__any(pending != 0u))
-      poll_tagged<32>(p, ep, src, [&](int k) { return i0 * 8 + (k & 7) * 512; }, [](int k) { return (k >> 3) * 4096; },
-                      pending, what, [&](int k, uint32_t b) { xd[32 * k] = __uint_as_float(b); });
+    if (__any(pending != 0u)) {
+      // the second pass goes out ahead of the second half of the prefetch, so it waits only behind the first
+#pragma unroll
+      for (int k = 0; k < 32; ++k)
+        if ((pending >> k) & 1u) w1[k] = ld_tag(rin, i0 * 8 + (k & 7) * 512, (k >> 3) * 4096);
+#pragma unroll
+      for (int j = NSLOT / 2; j < NSLOT; ++j) wp.R[j] = load_unit(wrun, j);
+      poll_finish<32>(p, ep, w1, pending, what, [&](int k) { return ld_tag(rin, i0 * 8 + (k & 7) * 512, (k >> 3) * 4096); },
+                      [&](int k, uint32_t b) { xd[32 * k] = __uint_as_float(b); });
+    } else {
+#pragma unroll
+      for (int j = NSLOT / 2; j < NSLOT; ++j) wp.R[j] = load_unit(wrun, j);
+    }
   }
   for (int i = n + tid; i < padded; i += NT) xs[xs_index(i, np)] = 0.f;
   bar();
