@@ -161,6 +161,69 @@ def decode_legs(torch, dec, n, K, first, reset, stream):
     return ms_res, ms_launch, per_step, same
 
 
+def trace_leg(dec, first, positions):
+    """After the timed legs: one traced step at each of the given positions (a two-step resident launch
+    whose second step is the one the trace keeps), summarised per stage. Returns {position: summary}."""
+    from persistent_megakernel_03_amd import trace as tz
+    dec.enable_trace()
+    res = {}
+    for pos in positions:
+        dec.set_ctx_lens([pos - 1])
+        dec.decode_n(first, 2, 1)
+        dec.sync_check()
+        summ, total = tz.stage_summary(dec.read_trace())
+        log(tz.format_summary(summ, total, "traced step at position %d" % pos))
+        res[str(pos)] = {"step_span_us": round(total, 2),
+                         "stages": [{k: (round(v, 2) if isinstance(v, float) else v) for k, v in x.items()} for x in summ]}
+    dec.disable_trace()
+    return res
+
+
+def prefill_leg(mk, torch, np, m, weights, prompt, nb, dec, g0, rf):
+    """Time to the first token for the workload's prompt, two ways: one decode step per prompt token
+    (the context `dec`, one-sequence graph) and chunked through the 16-row batched graph (a second
+    context with prefill_rows = 16). Each is timed on the host around one mk_prefill call after one
+    untimed call, from an empty cache; both must give the same next token unless the logits tie."""
+    P = len(prompt)
+    g1 = torch.zeros(1, dtype=torch.int32, device=dec.dev)
+    dec.set_ctx_lens([0])
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    dec.prefill(list(prompt), g1)
+    torch.cuda.synchronize()
+    ms_seq = 1e3 * (time.perf_counter() - t0)
+    dec.sync_check()
+    seq_logits = dec.read_logits(0)
+    cfg = mk.make_config(m, max_seqs=1, max_blocks_per_seq=nb, num_blocks=nb, prefill_rows=16)
+    d2 = mk.Decoder(cfg, 0)
+    d2.load_weights(weights)
+    d2.set_page_table(np.arange(nb, dtype=np.int32).reshape(1, nb))
+    g2 = torch.zeros(1, dtype=torch.int32, device=d2.dev)
+    times = []
+    for _ in range(3):
+        d2.set_ctx_lens([0])
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        d2.prefill(list(prompt), g2)   # synchronises and checks the device error word itself
+        times.append(1e3 * (time.perf_counter() - t0))
+    ms_chunk = float(np.median(times[1:]))
+    chunk_logits = d2.read_logits(0)
+    rel = float(np.linalg.norm(chunk_logits - seq_logits) / np.linalg.norm(seq_logits))
+    n_chunks = (P + 15) // 16
+    chunk_bytes = n_chunks * rf.weight_bytes_per_token(m) + sum(rf.kv_read_bytes_per_token(m, i + 1) for i in range(P))
+    finish(d2)
+    same = int(g1.item()) == int(g2.item())
+    log("prefill of %d tokens: one step per token %.2f ms, chunks of 16 %.2f ms (%d launches); next token "
+        "equal: %s; logits rel L2 between the two %.2e" % (P, ms_seq, ms_chunk, n_chunks, same, rel))
+    return {"prompt_tokens": P, "one_step_per_token_ms": round(ms_seq, 3), "chunked_16_rows_ms": round(ms_chunk, 3),
+            "chunk_launches": n_chunks, "speedup": round(ms_seq / ms_chunk, 2),
+            "chunked_hbm_gbs": round(chunk_bytes / (ms_chunk * 1e-3) / 1e9, 1),
+            "next_token_equal": same, "logits_rel_l2_between": float("%.3e" % rel),
+            "what": "host wall time of one mk_prefill call from an empty cache (the chunked call synchronises "
+                    "itself); algorithmic bytes of the chunked run: the weights once per chunk plus each "
+                    "position's KV rows"}
+
+
 def finish(dec):
     """Release the decoder and its device buffers, with the device idle, before the process exits."""
     import torch
@@ -276,6 +339,9 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=20.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--staged-steps", type=int, default=64, help="steps of the stage-sliced comparison run (0: skip it)")
+    ap.add_argument("--no-prefill", action="store_true", help="skip the time-to-first-token comparison")
+    ap.add_argument("--trace-summary", action="store_true",
+                    help="after the timed legs, trace one step at three positions and report per-stage times")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 1 GiB device-to-device copy 5 times (to scale HBM byte counters)")
     args = ap.parse_args()
@@ -366,6 +432,8 @@ def main():
                         "removed_by_resident_ms_per_token": round(ms_fused_same - ms_res_same, 5),
                         "what": "the same kernel and task graph launched once per dependency stage (stop-and-go), "
                                 "once per token, and once for all the steps"}
+    task_trace = trace_leg(dec, g0, spread(P + 1, P + K - 1, 3)) if args.trace_summary else None
+    prefill = None if args.no_prefill else prefill_leg(mk, torch, np, m, weights, prompt, nb, dec, g0, rf)
     finish(dec)
 
     traffic = None
@@ -411,6 +479,10 @@ def main():
         "cpu_baseline": cpu,
         "pass_to_pass": pass_to_pass,
     }
+    if prefill is not None:
+        out["prefill"] = prefill
+    if task_trace is not None:
+        out["task_trace"] = task_trace
     print(json.dumps(out), flush=True)
 
 

@@ -68,7 +68,13 @@ typedef struct mk_ctx mk_ctx; /* opaque, owned by the library */
  *     merges); 0 = 1, every task gets blocks once there are enough.
  *     With max_seqs > 1 the cut is by cost: each (sequence, KV head)
  *     segment start counts as 24 blocks more, so a task that begins
- *     several segments gets fewer blocks (possibly none). */
+ *     several segments gets fewer blocks (possibly none).
+ *   - prefill_rows: one-sequence contexts only (0 when max_seqs > 1). 0 or 1:
+ *     mk_prefill runs the prompt one decode step per token. 2..16: the
+ *     context also holds the batched (matrix-core) task graph for that many
+ *     rows, and mk_prefill runs the prompt through it that many positions per
+ *     step; its weights and working memory are counted by mk_workspace_size
+ *     (about twice the weight bytes). Needs d_model to be a multiple of 32. */
 typedef struct {
   int32_t n_layers, d_model, n_q_heads, n_kv_heads, head_dim, d_ffn, vocab;
   float rms_eps, rope_theta;
@@ -76,6 +82,7 @@ typedef struct {
   int32_t max_seqs, block_size, max_blocks_per_seq, num_blocks;
   int32_t attn_splits;
   int32_t attn_min_blocks;
+  int32_t prefill_rows;
 } mk_model_config;
 
 /* One weight tensor for mk_load_weights.
@@ -213,13 +220,28 @@ mk_status mk_decode_step_static(mk_ctx* ctx, const int32_t* d_tokens_in, int n_s
 mk_status mk_decode_step_staged(mk_ctx* ctx, const int32_t* d_tokens_in, int n_seqs, int32_t* d_tokens_out,
                                 void* stream);
 
-/* Prefill by repeated decode steps (the prefill phase fills the KV cache from
- * the prompt: "Crear desde cero un motor de inferencia para LLM usando C++ y
- * CUDA", section 1.1; a batched prefill is not built): the n_tokens host tokens h_tokens run
- * through the step one position at a time, for sequence `seq` only. When
- * d_token_out is not NULL, it receives the greedy token after the last
- * prompt token. Asynchronous like mk_decode_step. Needs max_seqs == 1 and
- * seq == 0 (MK_ERR_UNSUPPORTED otherwise). */
+/* Prefill: build sequence `seq`'s KV cache from the prompt (the prefill phase
+ * of "LLM高速化勉強会資料", slide 9; "Crear desde cero un motor de inferencia
+ * para LLM usando C++ y CUDA", section 1.1), appending the n_tokens host tokens
+ * h_tokens at the sequence's current length (d_ctx_lens[seq]).
+ *   - Batched contexts (max_seqs > 1), and one-sequence contexts with
+ *     prefill_rows > 1: chunked prefill (slide 43 of the deck, "Chunked
+ *     Prefill"; several prompt tokens at once for a shorter time to the first
+ *     token, "Crear desde cero ...", section 4). Each step of the batched
+ *     graph carries R = max_seqs (or prefill_rows) consecutive positions as
+ *     its rows: the GEMVs become R-row matrix-core tiles that read the weights
+ *     once for all R positions, and row i attends only to the positions up to
+ *     its own (causal masking; the masked part is never visited, "Hạt nhân là
+ *     gì"). The other sequences' caches, lengths and logits are untouched.
+ *     The call synchronises the stream and reports any device error.
+ *   - One-sequence contexts with prefill_rows 0 or 1: one decode step per
+ *     prompt token, asynchronous like mk_decode_step.
+ * Afterwards d_ctx_lens[seq] has grown by n_tokens, the logits row of `seq`
+ * holds the last prompt token's logits and, when d_token_out is not NULL, it
+ * receives the greedy token after the prompt.
+ * Errors: MK_ERR_INVALID_ARG (seq out of range, a token outside [0, vocab),
+ * the prompt running past the sequence's cache); device errors as for
+ * mk_sync_check. */
 mk_status mk_prefill(mk_ctx* ctx, int seq, const int32_t* h_tokens, int n_tokens, int32_t* d_token_out,
                      void* stream);
 

@@ -36,7 +36,8 @@ class mk_model_config(ctypes.Structure):
                 ("vocab", ctypes.c_int32), ("rms_eps", ctypes.c_float), ("rope_theta", ctypes.c_float),
                 ("tied_embeddings", ctypes.c_int32), ("qkv_bias", ctypes.c_int32), ("max_seqs", ctypes.c_int32),
                 ("block_size", ctypes.c_int32), ("max_blocks_per_seq", ctypes.c_int32), ("num_blocks", ctypes.c_int32),
-                ("attn_splits", ctypes.c_int32), ("attn_min_blocks", ctypes.c_int32)]
+                ("attn_splits", ctypes.c_int32), ("attn_min_blocks", ctypes.c_int32),
+                ("prefill_rows", ctypes.c_int32)]
 
 
 class mk_tensor(ctypes.Structure):
@@ -241,12 +242,12 @@ def mk_last_error() -> str:
 
 # ------------------------------------------------------------------- convenience
 def make_config(shape, max_seqs=1, max_blocks_per_seq=64, num_blocks=64, attn_splits=0, block_size=16,
-                attn_min_blocks=0):
+                attn_min_blocks=0, prefill_rows=0):
     """mk_model_config from any object with the model-shape attributes."""
     return mk_model_config(shape.n_layers, shape.d_model, shape.n_q_heads, shape.n_kv_heads, shape.head_dim,
                            shape.d_ffn, shape.vocab, float(shape.rms_eps), float(shape.rope_theta),
                            int(bool(shape.tied_embeddings)), int(bool(shape.qkv_bias)), max_seqs, block_size,
-                           max_blocks_per_seq, num_blocks, attn_splits, attn_min_blocks)
+                           max_blocks_per_seq, num_blocks, attn_splits, attn_min_blocks, prefill_rows)
 
 
 class Decoder:
@@ -293,8 +294,8 @@ class Decoder:
     def stream_ptr(self):
         return self.torch.cuda.current_stream(self.dev).cuda_stream
 
-    def prefill(self, tokens, token_out=None):
-        mk_prefill(self.ctx, 0, tokens, token_out, self.stream_ptr())
+    def prefill(self, tokens, token_out=None, seq=0):
+        mk_prefill(self.ctx, seq, tokens, token_out, self.stream_ptr())
 
     def step(self, tokens_in, n_seqs=1, tokens_out=None):
         mk_decode_step(self.ctx, tokens_in, n_seqs, tokens_out if tokens_out is not None else tokens_in,
@@ -322,6 +323,10 @@ class Decoder:
         n = mk_graph_stats(self.ctx).n_tasks
         self.trace_buf = self.torch.zeros(n * TRACE_REC_BYTES, dtype=self.torch.uint8, device=self.dev)
         mk_set_trace(self.ctx, self.trace_buf, n * TRACE_REC_BYTES)
+
+    def disable_trace(self):
+        mk_set_trace(self.ctx, None, 0)
+        self.trace_buf = None
 
     def read_trace(self):
         """Per-task records of the last step: structured numpy array (t_queue, t_ready, t_streamed, t_done,

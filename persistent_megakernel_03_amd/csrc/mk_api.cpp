@@ -10,6 +10,7 @@
 #include <cstdlib>
 #include <cstring>
 #include <map>
+#include <memory>
 #include <string>
 #include <vector>
 
@@ -44,6 +45,11 @@ struct mk_ctx {
   uint8_t* d_static = nullptr;     // this device's static scratch array (mk_decode_step_static)
   std::vector<float> rope_host;    // the rotary table and the per-layer pool pointers, as uploaded at bind
   std::vector<void*> pool_table;
+  // One-sequence contexts with prefill_rows > 1: the batched graph the prompt runs through, with its
+  // re-laid-out weights and its working memory at these offsets in the bound weights and scratch buffers.
+  std::unique_ptr<HostGraph> pg;
+  int64_t pg_w = 0, pg_s = 0;
+  uint32_t pg_epoch = 0;
 };
 
 namespace {
@@ -74,6 +80,8 @@ struct DeviceGuard {
   }
 };
 
+int64_t align256(int64_t x) { return (x + 255) & ~(int64_t)255; }
+
 mk_status build(const mk_model_config* cfg, int n_cus, mk_ctx** out) {
   if (!cfg || !out) return fail(MK_ERR_INVALID_ARG, "null argument");
   *out = nullptr;
@@ -82,6 +90,19 @@ mk_status build(const mk_model_config* cfg, int n_cus, mk_ctx** out) {
   if (!why.empty()) {
     delete c;
     return fail(MK_ERR_SHAPE, why);
+  }
+  if (cfg->max_seqs == 1 && cfg->prefill_rows > 1) {
+    mk_model_config pc = *cfg;
+    pc.max_seqs = cfg->prefill_rows;
+    pc.prefill_rows = 0;
+    c->pg.reset(new HostGraph());
+    const std::string pwhy = build_graph(pc, n_cus, *c->pg);
+    if (!pwhy.empty()) {
+      delete c;
+      return fail(MK_ERR_SHAPE, "prefill graph: " + pwhy);
+    }
+    c->pg_w = align256(c->g.wl.total);
+    c->pg_s = align256(c->g.sl.total);
   }
   if (const char* w = std::getenv("MK_WATCHDOG_US")) {  // wait budget in microseconds (100 ticks each)
     const long us = std::atol(w);
@@ -100,6 +121,13 @@ void rope_table(const mk_model_config& c, int max_pos, std::vector<float>& out) 
       out[((size_t)p * half + i) * 2 + 0] = (float)std::cos(a);
       out[((size_t)p * half + i) * 2 + 1] = (float)std::sin(a);
     }
+}
+
+// Clears a graph's event flags and tagged buffers (synchronous memsets, outside any step).
+hipError_t clear_working(const HostGraph& g, uint8_t* S) {
+  hipError_t e = hipMemset(S + g.sl.flags, 0, (size_t)g.n_flag_slots * 4);
+  if (e != hipSuccess) return e;
+  return hipMemset(S + g.sl.tagged_begin, 0, (size_t)(g.sl.tagged_end - g.sl.tagged_begin));
 }
 
 mk_status read_error_word(mk_ctx* c, hipStream_t st) {
@@ -121,22 +149,23 @@ mk_status read_error_word(mk_ctx* c, hipStream_t st) {
     s = MK_ERR_DEVICE_TIMEOUT;
   }
   if (e[E_ABORT] || s == MK_ERR_DEVICE_TIMEOUT) {
-    HIPCHK(hipMemset(c->d_scratch + c->g.sl.flags, 0, (size_t)c->g.n_flag_slots * 4));
-    // epochs restart at 1, so tags of the aborted steps must not survive
-    HIPCHK(hipMemset(c->d_scratch + c->g.sl.tagged_begin, 0, (size_t)(c->g.sl.tagged_end - c->g.sl.tagged_begin)));
-    HIPCHK(hipDeviceSynchronize());
+    HIPCHK(clear_working(c->g, c->d_scratch));  // epochs restart at 1: no tag of the aborted steps survives
     c->epoch = 0;
+    if (c->pg) {
+      HIPCHK(clear_working(*c->pg, c->d_scratch + c->pg_s));
+      c->pg_epoch = 0;
+    }
+    HIPCHK(hipDeviceSynchronize());
   }
   return fail(s, what);
 }
 
-// Kernel arguments. The read-only tables (task graph, rotary table, pool pointers) and the error word
-// come from the bound scratch buffer; the working memory a step writes (flags, tagged activations,
-// partials, argmax keys) from the scratch region at W: the bound buffer, or the static array.
-KernelParams make_params(mk_ctx* c, uint8_t* W) {
-  const HostGraph& g = c->g;
+// Kernel arguments of graph g. Its read-only tables (task graph, rotary table, pool pointers) come from
+// its region R of the bound scratch buffer, the working memory a step writes (flags, tagged activations,
+// partials, argmax keys) from the region at W (R itself, or the static array), its re-laid-out weights
+// from Wt. Errors always go to the context's own error word.
+KernelParams make_params(mk_ctx* c, const HostGraph& g, uint8_t* R, uint8_t* W, uint8_t* Wt) {
   const mk_model_config& m = g.cfg;
-  uint8_t* R = c->d_scratch;
   KernelParams p{};
   p.tasks = (const TaskDesc*)(R + g.sl.tasks);
   p.queue_off = (const int32_t*)(R + g.sl.queue_off);
@@ -145,13 +174,13 @@ KernelParams make_params(mk_ctx* c, uint8_t* W) {
   p.sig_slots = (const int32_t*)(R + g.sl.sig_slots);
   p.geoms = (const GemvGeom*)(R + g.sl.geoms);
   p.rope = (const float*)(R + g.sl.rope);
-  p.err = (uint32_t*)(R + g.sl.err);
+  p.err = (uint32_t*)(c->d_scratch + c->g.sl.err);
   uint8_t* S = W;
   p.flags = (uint32_t*)(S + g.sl.flags);
-  p.wpacked = c->d_weights;
-  p.embed = (const uint16_t*)(c->d_weights + g.wl.embed);
-  p.norms = (const uint16_t*)(c->d_weights + g.wl.norms);
-  p.bias = m.qkv_bias ? (const uint16_t*)(c->d_weights + g.wl.bias) : nullptr;
+  p.wpacked = Wt;
+  p.embed = (const uint16_t*)(Wt + g.wl.embed);
+  p.norms = (const uint16_t*)(Wt + g.wl.norms);
+  p.bias = m.qkv_bias ? (const uint16_t*)(Wt + g.wl.bias) : nullptr;
   p.kpool = (uint16_t* const*)(R + g.sl.pools);
   p.vpool = (uint16_t* const*)(R + g.sl.pools + (size_t)m.n_layers * 8);
   p.page_table = c->d_page_table;
@@ -185,9 +214,11 @@ KernelParams make_params(mk_ctx* c, uint8_t* W) {
   p.max_queue = g.max_queue;
   p.attn_tasks = g.attn_tasks;
   p.attn_min_blocks = g.cfg.attn_min_blocks > 0 ? g.cfg.attn_min_blocks : kAttnMinBlocks;
-  p.trace = c->d_trace;
+  p.trace = &g == &c->g ? c->d_trace : nullptr;
   return p;
 }
+
+KernelParams make_params(mk_ctx* c, uint8_t* W) { return make_params(c, c->g, c->d_scratch, W, c->d_weights); }
 
 // Epochs grow by one per step. Long before the 32-bit tags could wrap (a tag of epoch 0 or 1 would pass
 // the checks of a restarted count), the flags and tagged buffers are cleared and epochs restart at 1.
@@ -195,13 +226,12 @@ constexpr uint32_t kEpochLimit = 0x40000000u;
 // Steps one mk_decode_n launch may run (each step's tokens go to its own row of the output array).
 constexpr int kMaxStepsPerLaunch = 1 << 16;
 
-mk_status reserve_epochs(mk_ctx* c, int n_steps, hipStream_t st) {
-  if (c->epoch + (uint32_t)n_steps + 1u < kEpochLimit) return MK_OK;
+mk_status reserve_epochs(const HostGraph& g, uint8_t* S, uint32_t& epoch, int n_steps, hipStream_t st) {
+  if (epoch + (uint32_t)n_steps + 1u < kEpochLimit) return MK_OK;
   HIPCHK(hipStreamSynchronize(st));
-  HIPCHK(hipMemset(c->d_scratch + c->g.sl.flags, 0, (size_t)c->g.n_flag_slots * 4));
-  HIPCHK(hipMemset(c->d_scratch + c->g.sl.tagged_begin, 0, (size_t)(c->g.sl.tagged_end - c->g.sl.tagged_begin)));
+  HIPCHK(clear_working(g, S));
   HIPCHK(hipDeviceSynchronize());
-  c->epoch = 0;
+  epoch = 0;
   return MK_OK;
 }
 
@@ -210,7 +240,7 @@ mk_status reserve_epochs(mk_ctx* c, int n_steps, hipStream_t st) {
 // each running only that stage's tasks with the same kernel and step epoch.
 mk_status launch_step(mk_ctx* c, const int32_t* tin, int n_active, int32_t* tout, hipStream_t st, bool staged = false,
                       int n_steps = 1) {
-  if (mk_status s = reserve_epochs(c, n_steps, st)) return s;
+  if (mk_status s = reserve_epochs(c->g, c->d_scratch, c->epoch, n_steps, st)) return s;
   KernelParams p = make_params(c, c->d_scratch);
   p.tokens_in = tin;
   p.tokens_out = tout;
@@ -233,6 +263,58 @@ mk_status launch_step(mk_ctx* c, const int32_t* tin, int n_active, int32_t* tout
     HIPCHK(launch_megakernel(p, c->g.n_cus, (size_t)c->g.lds_bytes, st, false));
     a = b;
   }
+  return MK_OK;
+}
+// Re-lays out the weights for graph g (its task table at R on the device) into the weights region Wt:
+// every GEMV stage's tiles in the graph's order, then the embedding, norm gains and bias copies.
+mk_status load_graph_weights(const HostGraph& g, uint8_t* R, uint8_t* Wt,
+                             const std::map<std::string, const uint16_t*>& have, hipStream_t st) {
+  const mk_model_config& m = g.cfg;
+  const int L = m.n_layers, d = m.d_model, hq = m.n_q_heads, hk = m.n_kv_heads, V = m.vocab, dh = m.head_dim;
+  const TaskDesc* dtasks = (const TaskDesc*)(R + g.sl.tasks);
+  // re-lay out each GEMV stage (its tasks are contiguous in the task array)
+  const int nt = (int)g.tasks.size();
+  for (int t0 = 0; t0 < nt;) {
+    const TaskDesc& a = g.tasks[t0];
+    int t1 = t0 + 1;
+    while (t1 < nt && g.tasks[t1].type == a.type && g.tasks[t1].layer == a.layer) ++t1;
+    if (a.type == T_ATTN || a.type == T_ARGMAX) {
+      t0 = t1;
+      continue;
+    }
+    RepackArgs r{};
+    r.tasks = dtasks;
+    r.task0 = t0;
+    r.ntasks = t1 - t0;
+    r.gm = g.geoms[a.geom];
+    r.G = hq / hk;
+    r.dh = dh;
+    r.out = Wt;
+    const std::string p = "layers." + std::to_string(a.layer) + ".";
+    switch (a.type) {
+      case T_QKV: r.kind = RK_QKV; r.w0 = have.at(p + "wq"); r.w1 = have.at(p + "wk"); r.w2 = have.at(p + "wv"); break;
+      case T_OPROJ: r.kind = RK_PLAIN; r.w0 = have.at(p + "wo"); break;
+      case T_GATEUP: r.kind = RK_GU; r.w0 = have.at(p + "wg"); r.w1 = have.at(p + "wu"); break;
+      case T_DOWN: r.kind = RK_PLAIN; r.w0 = have.at(p + "wd"); break;
+      case T_LMHEAD: r.kind = RK_PLAIN; r.w0 = m.tied_embeddings ? have.at("embed") : have.at("lm_head"); break;
+      default: break;
+    }
+    const TaskDesc& last = g.tasks[t1 - 1];
+    const int64_t bytes = last.wofs + task_tile_bytes(r.gm, last) - a.wofs;
+    HIPCHK(launch_repack(r, bytes / 1024, st));
+    t0 = t1;
+  }
+  HIPCHK(hipMemcpyAsync(Wt + g.wl.embed, have.at("embed"), (size_t)V * d * 2, hipMemcpyDeviceToDevice, st));
+  uint8_t* norms = Wt + g.wl.norms;
+  for (int l = 0; l < L; ++l) {
+    const std::string p = "layers." + std::to_string(l) + ".";
+    HIPCHK(hipMemcpyAsync(norms + (size_t)(2 * l) * d * 2, have.at(p + "attn_norm"), (size_t)d * 2, hipMemcpyDeviceToDevice, st));
+    HIPCHK(hipMemcpyAsync(norms + (size_t)(2 * l + 1) * d * 2, have.at(p + "ffn_norm"), (size_t)d * 2, hipMemcpyDeviceToDevice, st));
+    if (m.qkv_bias)
+      HIPCHK(launch_repack_bias(have.at(p + "bq"), have.at(p + "bk"), have.at(p + "bv"), hq / hk, dh, qkv_rows(m),
+                                (uint16_t*)(Wt + g.wl.bias) + (size_t)l * qkv_rows(m), st));
+  }
+  HIPCHK(hipMemcpyAsync(norms + (size_t)(2 * L) * d * 2, have.at("final_norm"), (size_t)d * 2, hipMemcpyDeviceToDevice, st));
   return MK_OK;
 }
 }  // namespace
@@ -262,6 +344,13 @@ mk_status mk_create(const mk_model_config* cfg, int device, mk_ctx** out) {
     *out = nullptr;
     return fail(MK_ERR_UNSUPPORTED, "one workgroup per CU does not fit (LDS or registers)");
   }
+  if ((*out)->pg && (megakernel_occupancy(&blocks, (size_t)(*out)->pg->lds_bytes, cfg->head_dim, cfg->n_q_heads,
+                                          cfg->n_kv_heads, true) != hipSuccess ||
+                     blocks < 1)) {
+    mk_destroy(*out);
+    *out = nullptr;
+    return fail(MK_ERR_UNSUPPORTED, "prefill graph: one workgroup per CU does not fit (LDS or registers)");
+  }
   // this device's copy of the static scratch array, resolved once per device at set-up
   void* st = nullptr;
   const hipError_t e = static_scratch_address(device, &st);
@@ -279,9 +368,9 @@ mk_status mk_create_host(const mk_model_config* cfg, int n_cus, mk_ctx** out) { 
 mk_status mk_workspace_size(const mk_ctx* c, size_t* wb, size_t* kvb, size_t* sb) {
   if (!c) return fail(MK_ERR_INVALID_ARG, "null context");
   const mk_model_config& m = c->g.cfg;
-  if (wb) *wb = (size_t)c->g.wl.total;
+  if (wb) *wb = (size_t)(c->pg ? c->pg_w + c->pg->wl.total : c->g.wl.total);
   if (kvb) *kvb = (size_t)m.num_blocks * m.n_kv_heads * m.block_size * m.head_dim * 2;
-  if (sb) *sb = (size_t)c->g.sl.total;
+  if (sb) *sb = (size_t)(c->pg ? c->pg_s + c->pg->sl.total : c->g.sl.total);
   return MK_OK;
 }
 
@@ -306,24 +395,31 @@ mk_status mk_bind_memory(mk_ctx* c, void* d_weights, void* const* d_k_pools, voi
   c->d_page_table = d_page_table;
   c->d_ctx_lens = d_ctx_lens;
   c->d_logits = d_logits;
-  uint8_t* S = c->d_scratch;
-  auto up = [&](int64_t off, const void* src, size_t n) { return hipMemcpy(S + off, src, n, hipMemcpyHostToDevice); };
-  HIPCHK(up(g.sl.tasks, g.tasks.data(), g.tasks.size() * sizeof(TaskDesc)));
-  HIPCHK(up(g.sl.queue_off, g.queue_off.data(), g.queue_off.size() * 4));
-  HIPCHK(up(g.sl.queue_idx, g.queue_idx.data(), g.queue_idx.size() * 4));
-  HIPCHK(up(g.sl.events, g.events.data(), g.events.size() * sizeof(EventDesc)));
-  if (!g.sig_slots.empty()) HIPCHK(up(g.sl.sig_slots, g.sig_slots.data(), g.sig_slots.size() * 4));
-  HIPCHK(up(g.sl.geoms, g.geoms, sizeof(g.geoms)));
   rope_table(g.cfg, g.max_pos, c->rope_host);
-  HIPCHK(up(g.sl.rope, c->rope_host.data(), c->rope_host.size() * 4));
   c->pool_table = c->kpools;
   c->pool_table.insert(c->pool_table.end(), c->vpools.begin(), c->vpools.end());
-  HIPCHK(up(g.sl.pools, c->pool_table.data(), c->pool_table.size() * 8));
-  HIPCHK(hipMemset(S + g.sl.flags, 0, (size_t)g.n_flag_slots * 4));
-  HIPCHK(hipMemset(S + g.sl.err, 0, E_COUNT * 4));
-  HIPCHK(hipMemset(S + g.sl.tagged_begin, 0, (size_t)(g.sl.tagged_end - g.sl.tagged_begin)));
+  // each graph's read-only tables into its region of the scratch buffer (the prefill graph has the same
+  // positions and pools, so the same rotary table and pool pointers)
+  auto upload = [&](const HostGraph& h, uint8_t* S) -> hipError_t {
+    auto up = [&](int64_t off, const void* src, size_t n) { return hipMemcpy(S + off, src, n, hipMemcpyHostToDevice); };
+    hipError_t e;
+    if ((e = up(h.sl.tasks, h.tasks.data(), h.tasks.size() * sizeof(TaskDesc))) != hipSuccess) return e;
+    if ((e = up(h.sl.queue_off, h.queue_off.data(), h.queue_off.size() * 4)) != hipSuccess) return e;
+    if ((e = up(h.sl.queue_idx, h.queue_idx.data(), h.queue_idx.size() * 4)) != hipSuccess) return e;
+    if ((e = up(h.sl.events, h.events.data(), h.events.size() * sizeof(EventDesc))) != hipSuccess) return e;
+    if (!h.sig_slots.empty() && (e = up(h.sl.sig_slots, h.sig_slots.data(), h.sig_slots.size() * 4)) != hipSuccess)
+      return e;
+    if ((e = up(h.sl.geoms, h.geoms, sizeof(h.geoms))) != hipSuccess) return e;
+    if ((e = up(h.sl.rope, c->rope_host.data(), c->rope_host.size() * 4)) != hipSuccess) return e;
+    if ((e = up(h.sl.pools, c->pool_table.data(), c->pool_table.size() * 8)) != hipSuccess) return e;
+    if ((e = hipMemset(S + h.sl.err, 0, E_COUNT * 4)) != hipSuccess) return e;
+    return clear_working(h, S);
+  };
+  HIPCHK(upload(g, c->d_scratch));
+  if (c->pg) HIPCHK(upload(*c->pg, c->d_scratch + c->pg_s));
   HIPCHK(hipDeviceSynchronize());
   c->epoch = 0;
+  c->pg_epoch = 0;
   c->bound = true;
   c->loaded = false;
   return MK_OK;
@@ -373,50 +469,9 @@ mk_status mk_load_weights(mk_ctx* c, const mk_tensor* ts, int n, void* stream) {
     if (!have.count(w.first)) return fail(MK_ERR_INVALID_ARG, "missing tensor " + w.first);
   DeviceGuard dg(c->device);
   hipStream_t st = (hipStream_t)stream;
-  const TaskDesc* dtasks = (const TaskDesc*)(c->d_scratch + g.sl.tasks);
-  // re-lay out each GEMV stage (its tasks are contiguous in the task array)
-  const int nt = (int)g.tasks.size();
-  for (int t0 = 0; t0 < nt;) {
-    const TaskDesc& a = g.tasks[t0];
-    int t1 = t0 + 1;
-    while (t1 < nt && g.tasks[t1].type == a.type && g.tasks[t1].layer == a.layer) ++t1;
-    if (a.type == T_ATTN || a.type == T_ARGMAX) {
-      t0 = t1;
-      continue;
-    }
-    RepackArgs r{};
-    r.tasks = dtasks;
-    r.task0 = t0;
-    r.ntasks = t1 - t0;
-    r.gm = g.geoms[a.geom];
-    r.G = hq / hk;
-    r.dh = dh;
-    r.out = c->d_weights;
-    const std::string p = "layers." + std::to_string(a.layer) + ".";
-    switch (a.type) {
-      case T_QKV: r.kind = RK_QKV; r.w0 = have[p + "wq"]; r.w1 = have[p + "wk"]; r.w2 = have[p + "wv"]; break;
-      case T_OPROJ: r.kind = RK_PLAIN; r.w0 = have[p + "wo"]; break;
-      case T_GATEUP: r.kind = RK_GU; r.w0 = have[p + "wg"]; r.w1 = have[p + "wu"]; break;
-      case T_DOWN: r.kind = RK_PLAIN; r.w0 = have[p + "wd"]; break;
-      case T_LMHEAD: r.kind = RK_PLAIN; r.w0 = m.tied_embeddings ? have["embed"] : have["lm_head"]; break;
-      default: break;
-    }
-    const TaskDesc& last = g.tasks[t1 - 1];
-    const int64_t bytes = last.wofs + task_tile_bytes(r.gm, last) - a.wofs;
-    HIPCHK(launch_repack(r, bytes / 1024, st));
-    t0 = t1;
-  }
-  HIPCHK(hipMemcpyAsync(c->d_weights + g.wl.embed, have["embed"], (size_t)V * d * 2, hipMemcpyDeviceToDevice, st));
-  uint8_t* norms = c->d_weights + g.wl.norms;
-  for (int l = 0; l < L; ++l) {
-    const std::string p = "layers." + std::to_string(l) + ".";
-    HIPCHK(hipMemcpyAsync(norms + (size_t)(2 * l) * d * 2, have[p + "attn_norm"], (size_t)d * 2, hipMemcpyDeviceToDevice, st));
-    HIPCHK(hipMemcpyAsync(norms + (size_t)(2 * l + 1) * d * 2, have[p + "ffn_norm"], (size_t)d * 2, hipMemcpyDeviceToDevice, st));
-    if (m.qkv_bias)
-      HIPCHK(launch_repack_bias(have[p + "bq"], have[p + "bk"], have[p + "bv"], hq / hk, dh, qkv_rows(m),
-                                (uint16_t*)(c->d_weights + g.wl.bias) + (size_t)l * qkv_rows(m), st));
-  }
-  HIPCHK(hipMemcpyAsync(norms + (size_t)(2 * L) * d * 2, have["final_norm"], (size_t)d * 2, hipMemcpyDeviceToDevice, st));
+  if (mk_status e = load_graph_weights(g, c->d_scratch, c->d_weights, have, st)) return e;
+  if (c->pg)
+    if (mk_status e = load_graph_weights(*c->pg, c->d_scratch + c->pg_s, c->d_weights + c->pg_w, have, st)) return e;
   c->loaded = true;
   return MK_OK;
 }
@@ -479,22 +534,79 @@ mk_status mk_decode_step_staged(mk_ctx* c, const int32_t* d_tokens_in, int n_seq
 mk_status mk_prefill(mk_ctx* c, int seq, const int32_t* h_tokens, int n_tokens, int32_t* d_token_out, void* stream) {
   if (!c || (!h_tokens && n_tokens > 0) || n_tokens < 0) return fail(MK_ERR_INVALID_ARG, "null argument");
   if (!c->bound || !c->loaded) return fail(MK_ERR_STATE, "bind memory and load weights before prefill");
-  if (c->g.cfg.max_seqs != 1 || seq != 0) return fail(MK_ERR_UNSUPPORTED, "prefill runs batch-1 contexts, sequence 0");
+  const mk_model_config& m = c->g.cfg;
+  if (seq < 0 || seq >= m.max_seqs) return fail(MK_ERR_INVALID_ARG, "seq out of range");
   if (n_tokens == 0) return MK_OK;
   if (n_tokens > c->g.max_pos) return fail(MK_ERR_INVALID_ARG, "prompt longer than the cache");
   for (int i = 0; i < n_tokens; ++i)
-    if (h_tokens[i] < 0 || h_tokens[i] >= c->g.cfg.vocab) return fail(MK_ERR_INVALID_ARG, "prompt token out of range");
+    if (h_tokens[i] < 0 || h_tokens[i] >= m.vocab) return fail(MK_ERR_INVALID_ARG, "prompt token out of range");
   DeviceGuard dg(c->device);
   hipStream_t st = (hipStream_t)stream;
-  int32_t* tokbuf = (int32_t*)(c->d_scratch + c->g.sl.tokbuf);
-  int32_t* tokout = (int32_t*)(c->d_scratch + c->g.sl.tokout);
-  HIPCHK(hipMemcpyAsync(tokbuf, h_tokens, (size_t)n_tokens * 4, hipMemcpyHostToDevice, st));
-  HIPCHK(hipStreamSynchronize(st));  // the host array may be released when this call returns
-  for (int i = 0; i < n_tokens; ++i) {
-    int32_t* out = (i == n_tokens - 1 && d_token_out) ? d_token_out : tokout;
-    mk_status s = launch_step(c, tokbuf + i, 1, out, st);
-    if (s != MK_OK) return s;
+  if (m.max_seqs == 1 && !c->pg) {  // one decode step per prompt token
+    int32_t* tokbuf = (int32_t*)(c->d_scratch + c->g.sl.tokbuf);
+    int32_t* tokout = (int32_t*)(c->d_scratch + c->g.sl.tokout);
+    HIPCHK(hipMemcpyAsync(tokbuf, h_tokens, (size_t)n_tokens * 4, hipMemcpyHostToDevice, st));
+    HIPCHK(hipStreamSynchronize(st));  // the host array may be released when this call returns
+    for (int i = 0; i < n_tokens; ++i) {
+      int32_t* out = (i == n_tokens - 1 && d_token_out) ? d_token_out : tokout;
+      mk_status s = launch_step(c, tokbuf + i, 1, out, st);
+      if (s != MK_OK) return s;
+    }
+    return MK_OK;
   }
+  // Chunked: steps of the batched graph whose R rows are R consecutive positions of sequence seq. Every
+  // row reads seq's page table row (copied R times) and its own context length, so row i appends its
+  // key and value at position p0 + i and attends to positions 0 .. p0 + i; the QKV stage (every row's
+  // append) completes before any attention task starts, so the earlier rows' entries are in the cache.
+  const bool own = !c->pg;
+  const HostGraph& g = own ? c->g : *c->pg;
+  uint8_t* S = own ? c->d_scratch : c->d_scratch + c->pg_s;
+  uint8_t* Wt = own ? c->d_weights : c->d_weights + c->pg_w;
+  uint32_t& epoch = own ? c->epoch : c->pg_epoch;
+  const int R = g.cfg.max_seqs, MB = m.max_blocks_per_seq, V = m.vocab;
+  int32_t p0 = 0;
+  HIPCHK(hipStreamSynchronize(st));
+  HIPCHK(hipMemcpy(&p0, c->d_ctx_lens + seq, 4, hipMemcpyDeviceToHost));
+  if (p0 < 0 || (int64_t)p0 + n_tokens > g.max_pos)
+    return fail(MK_ERR_INVALID_ARG, "the prompt runs past the sequence's cache (length " + std::to_string(p0) + ")");
+  const int n_chunks = (n_tokens + R - 1) / R;
+  if ((int64_t)n_chunks * 16 * 4 > (int64_t)(g.max_pos / R + 2) * 16 * 4) return fail(MK_ERR_SHAPE, "prefill chunk table too small");
+  std::vector<int32_t> lens((size_t)n_chunks * 16, 0);
+  for (int k = 0; k < n_chunks; ++k)
+    for (int i = 0; i < R && k * R + i < n_tokens; ++i) lens[(size_t)k * 16 + i] = p0 + k * R + i;
+  int32_t* tokbuf = (int32_t*)(S + g.sl.tokbuf);
+  int32_t* ptab = (int32_t*)(S + g.sl.pf_ptab);
+  int32_t* ctxs = (int32_t*)(S + g.sl.pf_ctx);
+  float* logits = (float*)(S + g.sl.pf_logits);
+  int32_t* toks = (int32_t*)(S + g.sl.pf_tok);
+  HIPCHK(hipMemcpyAsync(tokbuf, h_tokens, (size_t)n_tokens * 4, hipMemcpyHostToDevice, st));
+  HIPCHK(hipMemcpyAsync(ctxs, lens.data(), lens.size() * 4, hipMemcpyHostToDevice, st));
+  for (int r = 0; r < R; ++r)
+    HIPCHK(hipMemcpyAsync(ptab + (size_t)r * MB, c->d_page_table + (size_t)seq * MB, (size_t)MB * 4,
+                          hipMemcpyDeviceToDevice, st));
+  HIPCHK(hipStreamSynchronize(st));  // the host arrays may be released when this call returns
+  if (mk_status s = reserve_epochs(g, S, epoch, n_chunks, st)) return s;
+  for (int k = 0; k < n_chunks; ++k) {
+    KernelParams p = make_params(c, g, S, S, Wt);
+    p.page_table = ptab;
+    p.ctx_lens = ctxs + (size_t)k * 16;
+    p.logits = logits;
+    p.tokens_in = tokbuf + (size_t)k * R;
+    p.tokens_out = toks;
+    p.n_active = std::min(R, n_tokens - k * R);
+    p.prefill = 1;
+    p.n_steps = 1;
+    p.epoch = ++epoch;
+    p.task_lo = 0;
+    p.task_hi = (int32_t)g.tasks.size();
+    HIPCHK(launch_megakernel(p, g.n_cus, (size_t)g.lds_bytes, st, false));
+  }
+  const int last = (n_tokens - 1) % R;
+  HIPCHK(hipMemcpyAsync(c->d_logits + (size_t)seq * V, logits + (size_t)last * V, (size_t)V * 4, hipMemcpyDeviceToDevice, st));
+  if (d_token_out) HIPCHK(hipMemcpyAsync(d_token_out, toks + last, 4, hipMemcpyDeviceToDevice, st));
+  if (mk_status s = read_error_word(c, st)) return s;  // synchronises the stream
+  const int32_t len = p0 + n_tokens;
+  HIPCHK(hipMemcpy(c->d_ctx_lens + seq, &len, 4, hipMemcpyHostToDevice));
   return MK_OK;
 }
 

@@ -220,6 +220,10 @@ std::string build_graph(const mk_model_config& c, int n_cus, HostGraph& g) {
   if (!(c.rms_eps >= 0.f) || !(c.rope_theta > 0.f)) return "bad rms_eps or rope_theta";
   if (c.attn_splits < 0 || c.attn_splits > 64) return "attn_splits out of range";
   if (c.attn_min_blocks < 0 || c.attn_min_blocks > (1 << 20)) return "attn_min_blocks out of range";
+  if (c.prefill_rows < 0 || c.prefill_rows > 16) return "prefill_rows must be 0..16";
+  if (c.max_seqs > 1 && c.prefill_rows != 0)
+    return "prefill_rows applies to one-sequence contexts (a batched context prefills through its own rows)";
+  if (c.prefill_rows > 1 && c.d_model % 32) return "chunked prefill needs d_model to be a multiple of 32";
   g.cfg = c;
   g.n_cus = n_cus;
   g.max_pos = c.max_blocks_per_seq * c.block_size;
@@ -581,6 +585,12 @@ std::string build_graph(const mk_model_config& c, int n_cus, HostGraph& g) {
   g.sl.tokbuf = take((int64_t)std::max(g.max_pos, 64) * 4);
   g.sl.tokout = take(64 * 4);
   g.sl.pools = take((int64_t)2 * L * 8);
+  if (S > 1) {  // chunked prefill: the rows of a step are consecutive positions of one sequence
+    g.sl.pf_ptab = take((int64_t)S * c.max_blocks_per_seq * 4);
+    g.sl.pf_ctx = take((int64_t)(g.max_pos / S + 2) * 16 * 4);
+    g.sl.pf_logits = take((int64_t)S * V * 4);
+    g.sl.pf_tok = take(64 * 4);
+  }
   g.sl.total = o;
 
   // ---- LDS: padded GEMV input vector + per-row results, or the attention working set
@@ -593,7 +603,9 @@ std::string build_graph(const mk_model_config& c, int n_cus, HostGraph& g) {
   // attention: the staged queries (G rounded up to 2, 4 or 8 heads), the current key and value rows,
   // each wave's merged (m, l, o) per head
   const int gmax = G <= 2 ? 2 : G <= 4 ? 4 : 8;
-  const int64_t attn_lds = (int64_t)gmax * dh * 4 + (int64_t)dh * 4 + (int64_t)8 * G * (dh + 2) * 4;
+  // (batched graphs: each wave's buffer sized for gmax heads, then a chunked prefill's 16 key/value rows)
+  const int64_t attn_lds = (int64_t)gmax * dh * 4 + (int64_t)dh * 4 +
+                           (S > 1 ? (int64_t)8 * gmax * (dh + 2) * 4 + (int64_t)16 * dh * 4 : (int64_t)8 * G * (dh + 2) * 4);
   int max_q = 0;
   for (int cu = 0; cu < n_cus; ++cu) max_q = std::max(max_q, g.queue_off[cu + 1] - g.queue_off[cu]);
   g.max_queue = max_q;

@@ -93,6 +93,9 @@ struct ScratchLayout {
   int64_t bpt;                       // batched GEMV: per-tile partial sums of each column split
   int64_t tagged_begin, tagged_end;  // byte range holding all tagged buffers
   int64_t amax, tokbuf, tokout, pools;
+  // batched graphs, chunked prefill: the rows' page table (copies of one sequence's row), their context
+  // lengths (16 per chunk), the rows' logits and tokens
+  int64_t pf_ptab = -1, pf_ctx = -1, pf_logits = -1, pf_tok = -1;
   int64_t total;
 };
 
@@ -168,6 +171,7 @@ struct KernelParams {
   int32_t attn_tasks;         // attention tasks per layer (they cut the layer's KV blocks evenly)
   int32_t task_lo, task_hi;   // this launch runs the tasks [task_lo, task_hi) of the global order
   int32_t attn_min_blocks;    // cache blocks per attention task at least (fewer tasks get blocks)
+  int32_t prefill;            // batched graphs: 1 = the rows are consecutive positions of one sequence
   TraceRec* trace;            // per-task timestamps of the last step, or nullptr
 };
 

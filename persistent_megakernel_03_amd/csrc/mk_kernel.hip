@@ -746,7 +746,7 @@ __device__ __forceinline__ void attn_lane_merge(int G, float (&mr)[GMAX], float 
   attn_merge_level<32, GMAX>(G, mr, lr, orr);
 }
 
-template <int DH, int GMAX, int ANS>
+template <int DH, int GMAX, int ANS, bool PF>
 __device__ __forceinline__ void attn_part(const KernelParams& p, uint32_t ep, const TaskDesc& t, float* lds, Ctl* ctl,
                                           uint16_t* const* pools, int s, int grp, int pos, int c0, int c1,
                                           float (&Mo)[AttnShape<DH, GMAX>::EPT], float (&Lo)[AttnShape<DH, GMAX>::EPT],
@@ -765,7 +765,19 @@ __device__ __forceinline__ void attn_part(const KernelParams& p, uint32_t ep, co
   float* wbuf = (float*)(kvc + DH);          // [NW][G][DH + 2]: each wave's merged (m, l, o)
   const uint32_t what = (uint32_t)t.wait_ev;
   const bool cur = pos >= 0 && c1 == pos + 1;  // the part ends with the current position
-  const int ce = cur ? pos : c1;             // cached positions [c0, ce)
+  // Chunked prefill (PF, p.prefill): row r of the step is position cs + r of one sequence, so the
+  // positions cs .. pos were all written in this step. They come from those rows' tagged key and value
+  // words (xn of them, from x0), not from the cache, whose entries this step's rows may still be
+  // writing; the cache supplies [c0, ce) below cs.
+  int x0 = c1, xn = 0;
+  if constexpr (PF) {
+    if (p.prefill && pos >= 0) {
+      const int cs = __builtin_amdgcn_readfirstlane(ctl->ctx[0]);
+      x0 = max(c0, cs);
+      xn = max(0, c1 - x0);
+    }
+  }
+  const int ce = min(cur ? pos : c1, x0);    // cached positions [c0, ce)
   const int ngr = ce > c0 ? (ce - c0 + PPW - 1) / PPW : 0;
   const int nw = ngr > wave ? (ngr - wave + NW - 1) / NW : 0;  // this wave's groups: wave + NW k
   // Cache rows: this lane's 8 dims of group k's position (clamped to the last cached position), with
@@ -818,13 +830,34 @@ __device__ __forceinline__ void attn_part(const KernelParams& p, uint32_t ep, co
     const int dk = (int)((const char*)kvt_at(p, l, s, 0, grp) - (const char*)qsrc);  // bytes, > 0
     const int dv = dk + p.hk * (DH / 2) * 8;
     uint32_t pend = first_words(min(poll_chunk(nq) / 64, (nq - iq + 63) / 64));
-    if (cur && tid < DH / 2) pend |= 3u << KQ;
+    if (cur && xn == 0 && tid < DH / 2) pend |= 3u << KQ;
     poll_tagged<KQ + 2>(
         p, ep, qsrc, [&](int k) { return k < KQ ? iq * 8 + k * 512 : tid * 8; },
         [&](int k) { return k < KQ ? 0 : k == KQ ? dk : dv; }, pend, what, [&](int k, uint32_t b) {
           if (k < KQ) q_slot(iq + 64 * k) = __uint_as_float(b) * qscale;
           else kvc[(k - KQ) * (DH / 2) + tid] = b;
         });
+    if constexpr (PF) {
+      if (xn > 0) {
+        // the rows' key and value words, [xn][DH] after the merge buffers: word i of the block is row
+        // i / DH, its key (first DH / 2) or value (last DH / 2) pair i % DH
+        constexpr int KX = (16 * DH + NT - 1) / NT;
+        uint32_t* kvx = (uint32_t*)(wbuf + NW * GMAX * (DH + 2));
+        const int rx0 = x0 - __builtin_amdgcn_readfirstlane(ctl->ctx[0]);
+        uint32_t px = 0;
+#pragma unroll
+        for (int j = 0; j < KX; ++j)
+          if (tid + NT * j < xn * DH) px |= 1u << j;
+        poll_tagged<KX>(
+            p, ep, qsrc,
+            [&](int j) {
+              const int i = tid + NT * j, r = min(i / DH, xn - 1), w = i % DH;
+              return (int)((const char*)(kvt_at(p, l, rx0 + r, w < DH / 2 ? 0 : 1, grp) + (w % (DH / 2))) -
+                           (const char*)qsrc);
+            },
+            [](int) { return 0; }, px, what, [&](int j, uint32_t b) { kvx[tid + NT * j] = b; });
+      }
+    }
   }
   bar();
   if (p.trace && tid == 0) ctl->t_ready = __builtin_amdgcn_s_memrealtime();
@@ -870,7 +903,21 @@ __device__ __forceinline__ void attn_part(const KernelParams& p, uint32_t ep, co
       __builtin_amdgcn_sched_barrier(0);
     }
   }
-  if (cur && wave == 0) {  // the current position: lane c's 8 dims are words 4c..4c+3 of each row
+  if constexpr (PF) {
+    // the positions written in this step: the chunk's rows x0 .. x0 + xn - 1 (chunked prefill), or the
+    // current position; one per round on wave 0, lane c's 8 dims are words 4c..4c+3 of each row
+    const uint32_t* xb = xn > 0 ? (const uint32_t*)(wbuf + NW * GMAX * (DH + 2)) : kvc;
+    const int xr = xn > 0 ? xn : (cur ? 1 : 0);
+    if (wave == 0) {
+      for (int b = 0; b < xr; ++b) {
+        const v4u kq = *(const v4u*)(xb + b * DH + 4 * c), vq = *(const v4u*)(xb + b * DH + DH / 2 + 4 * c);
+        float sq[GMAX];
+        attn_scores<DH, GMAX>(kq, pg == 0, G, qr, sq);
+        attn_rescale<GMAX>(G, sq, mr, lr, orr);
+        attn_accum<GMAX>(vq, G, sq, mr, lr, orr);
+      }
+    }
+  } else if (cur && wave == 0) {  // the current position: lane c's 8 dims are words 4c..4c+3 of each row
     const v4u kq = *(const v4u*)(kvc + 4 * c), vq = *(const v4u*)(kvc + DH / 2 + 4 * c);
     float sq[GMAX];
     attn_scores<DH, GMAX>(kq, pg == 0, G, qr, sq);
@@ -963,7 +1010,7 @@ __device__ __forceinline__ void task_attn(const KernelParams& p, uint32_t ep, co
     const int c0 = ok ? 16 * (x - B) : 0, c1 = ok ? min(16 * (xe - B), pos + 1) : 0;
     if (!ok) pos = -1;
     float M[EPT], L[EPT], A[EPT];
-    attn_part<DH, GMAX, ANS>(p, ep, t, lds, ctl, pools, s, grp, pos, c0, c1, M, L, A);
+    attn_part<DH, GMAX, ANS, COST>(p, ep, t, lds, ctl, pools, s, grp, pos, c0, c1, M, L, A);
     if (p.trace && tid == 0) ctl->t_streamed = __builtin_amdgcn_s_memrealtime();
     if (xe < E) {  // the segment goes on in later tasks: this task's partial
       uint64_t* pb = part_base(ti, x == lo ? 0 : 1);

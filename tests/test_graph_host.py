@@ -147,6 +147,37 @@ def test_rejects_bad_configs(L):
     assert e.value.status == -2
 
 
+def test_prefill_rows_config(L):
+    # prefill_rows > 1 adds the batched graph's re-laid-out weights (every GEMV matrix once more) and its
+    # working memory to the buffers mk_workspace_size asks for; 0 and 1 add nothing
+    base = mk.mk_create_host(cfg_for(si.TINY, 3, 3), 64)
+    w0, kv0, s0 = mk.mk_workspace_size(base)
+    mk.mk_destroy(base)
+    for rows in (0, 1):
+        c = cfg_for(si.TINY, 3, 3)
+        c.prefill_rows = rows
+        ctx = mk.mk_create_host(c, 64)
+        assert mk.mk_workspace_size(ctx) == (w0, kv0, s0)
+        mk.mk_destroy(ctx)
+    m = si.TINY
+    gemv = 2 * (m.n_layers * ((m.n_q_heads + 2 * m.n_kv_heads) * m.head_dim * m.d_model
+                              + m.d_model * m.n_q_heads * m.head_dim + 3 * m.d_ffn * m.d_model) + m.vocab * m.d_model)
+    for rows in (2, 16):
+        c = cfg_for(si.TINY, 3, 3)
+        c.prefill_rows = rows
+        ctx = mk.mk_create_host(c, 64)
+        w, kv, s = mk.mk_workspace_size(ctx)
+        assert kv == kv0 and s > s0 and w >= w0 + gemv
+        mk.mk_graph_validate(ctx)
+        mk.mk_destroy(ctx)
+    for rows, n_seqs in ((17, 1), (-1, 1), (4, 4)):     # out of range; a batched context prefills through its own rows
+        c = mk.make_config(si.TINY, max_seqs=n_seqs, max_blocks_per_seq=3, num_blocks=3 * n_seqs)
+        c.prefill_rows = rows
+        with pytest.raises(mk.MKError) as e:
+            mk.mk_create_host(c, 64)
+        assert e.value.status == -2
+
+
 def test_host_context_refuses_device_calls(L):
     ctx = mk.mk_create_host(cfg_for(si.TINY, 3, 3), 16)
     try:
