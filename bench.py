@@ -224,6 +224,55 @@ def prefill_leg(mk, torch, np, m, weights, prompt, nb, dec, g0, rf):
                     "position's KV rows"}
 
 
+def roofline_obj(rf, achieved, traffic_per_step, bytes_avg, K, ms_launch, kernel):
+    """The roofline object of the timed kernel. One launch runs all K steps: `achieved` is the launch's
+    algorithmic bytes (K x bytes_per_step) over its event-timed duration; `traffic` is the launch's HBM
+    bytes from the rocprofv3 counters (FETCH_SIZE + WRITE_SIZE, copy-calibrated) recorded for these
+    kernel sources, else null."""
+    return {"bound": "hbm", "achieved": round(achieved, 1), "peak": rf.MI355X_HBM_PEAK_GBS, "unit": "GB/s",
+            "frac": round(achieved / rf.MI355X_HBM_PEAK_GBS, 4),
+            "traffic": None if traffic_per_step is None else int(traffic_per_step * K),
+            "traffic_unit": "HBM bytes per launch of %d steps" % K,
+            "traffic_per_step": traffic_per_step, "bytes_per_step": int(bytes_avg),
+            "bytes_per_launch": int(bytes_avg * K), "launch_ms": round(ms_launch, 3), "steps_per_launch": K,
+            "kernel": kernel}
+
+
+def fp8_leg(mk, torch, np, m, weights, prompt, nb, K, W, rf, ms_bf16):
+    """The same decode with FP8 weights (weight_format = 1: E4M3 codes, one power-of-two scale per row,
+    quantised on the device at load): the prompt, W warm-up steps, then K greedy steps at positions
+    P .. P+K-1 in one resident launch, timed with events. Its bytes per step count one byte per GEMV
+    weight plus the row scales."""
+    P = len(prompt)
+    cfg = mk.make_config(m, max_seqs=1, max_blocks_per_seq=nb, num_blocks=nb, weight_format=1)
+    d8 = mk.Decoder(cfg, 0)
+    d8.load_weights(weights)
+    d8.set_page_table(np.arange(nb, dtype=np.int32).reshape(1, nb))
+    d8.set_ctx_lens([0])
+    g0 = torch.zeros(1, dtype=torch.int32, device=d8.dev)
+    d8.prefill(list(prompt), g0)
+    d8.decode_n(g0, W, 1)
+    d8.set_ctx_lens([P])
+    d8.sync_check()
+    stream = torch.cuda.current_stream(d8.dev)
+    out = torch.zeros((K, 1), dtype=torch.int32, device=d8.dev)
+    ms_launch = timed_once(torch, stream, lambda: d8.decode_n(g0, K, 1, out))
+    d8.sync_check()
+    ms = ms_launch / K
+    bytes_avg = sum(rf.step_bytes(m, [P + i + 1], fp8=True) for i in range(K)) / K
+    achieved = bytes_avg / (ms * 1e-3) / 1e9
+    info = mk.mk_graph_stats(d8.ctx)
+    finish(d8)
+    log("fp8 weights: resident %.4f ms/token (%.1f tok/s), %.1f GB/s (%.1f%% of %.0f GB/s); %.2fx the bf16 decode"
+        % (ms, 1e3 / ms, achieved, 100 * achieved / rf.MI355X_HBM_PEAK_GBS, rf.MI355X_HBM_PEAK_GBS, ms_bf16 / ms))
+    return {"ms_per_token": round(ms, 5), "tokens_per_s": round(1e3 / ms, 2), "steps": K,
+            "weight_bytes_per_token": rf.weight_bytes_per_token_fp8(m), "graph_hash": "0x%016x" % info.hash,
+            "roofline": roofline_obj(rf, achieved, None, bytes_avg, K, ms_launch, "mk_megakernel, FP8 weights"),
+            "speedup_vs_bf16": round(ms_bf16 / ms, 3),
+            "what": "E4M3 weight codes with one power-of-two scale per output row, decoded in the GEMV tile "
+                    "(fp32 accumulation); the same prompt and positions as the bf16 decode"}
+
+
 def finish(dec):
     """Release the decoder and its device buffers, with the device idle, before the process exits."""
     import torch
@@ -320,11 +369,8 @@ def bench_batched(args, wl):
         "one_launch_per_step": {"ms_per_step": round(ms1, 5),
                                 "ms_per_step_median": round(float(np.median(per_step)), 5),
                                 "tokens_equal_to_resident": same},
-        "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": rf.MI355X_HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": round(achieved / rf.MI355X_HBM_PEAK_GBS, 4), "traffic": traffic,
-                     "traffic_unit": "HBM bytes per step (FETCH_SIZE + WRITE_SIZE, copy-calibrated)",
-                     "bytes_per_step": int(bytes_avg),
-                     "kernel": "mk_megakernel%s" % (", batched" if n > 1 else "")},
+        "roofline": roofline_obj(rf, achieved, traffic, bytes_avg, K, ms_res,
+                                 "mk_megakernel%s" % (", batched" if n > 1 else "")),
         "cpu_baseline": cpu,
     }
     print(json.dumps(out), flush=True)
@@ -340,6 +386,7 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--staged-steps", type=int, default=64, help="steps of the stage-sliced comparison run (0: skip it)")
     ap.add_argument("--no-prefill", action="store_true", help="skip the time-to-first-token comparison")
+    ap.add_argument("--no-fp8", action="store_true", help="skip the FP8-weights decode")
     ap.add_argument("--trace-summary", action="store_true",
                     help="after the timed legs, trace one step at three positions and report per-stage times")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -435,6 +482,7 @@ def main():
     task_trace = trace_leg(dec, g0, spread(P + 1, P + K - 1, 3)) if args.trace_summary else None
     prefill = None if args.no_prefill else prefill_leg(mk, torch, np, m, weights, prompt, nb, dec, g0, rf)
     finish(dec)
+    fp8 = None if args.no_fp8 else fp8_leg(mk, torch, np, m, weights, prompt, nb, K, W, rf, ms)
 
     traffic = None
     if wl.name == "llama8b":
@@ -472,15 +520,14 @@ def main():
         "one_launch_per_step": {"ms_per_step": round(ms1, 5),
                                 "ms_per_step_median": round(float(np.median(per_step)), 5),
                                 "tokens_equal_to_resident": same},
-        "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": rf.MI355X_HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": round(achieved / rf.MI355X_HBM_PEAK_GBS, 4), "traffic": traffic,
-                     "traffic_unit": "HBM bytes per step (FETCH_SIZE + WRITE_SIZE, copy-calibrated)",
-                     "bytes_per_step": int(bytes_avg), "kernel": "mk_megakernel"},
+        "roofline": roofline_obj(rf, achieved, traffic, bytes_avg, K, ms_res, "mk_megakernel"),
         "cpu_baseline": cpu,
         "pass_to_pass": pass_to_pass,
     }
     if prefill is not None:
         out["prefill"] = prefill
+    if fp8 is not None:
+        out["fp8_weights"] = fp8
     if task_trace is not None:
         out["task_trace"] = task_trace
     print(json.dumps(out), flush=True)

@@ -74,7 +74,18 @@ typedef struct mk_ctx mk_ctx; /* opaque, owned by the library */
  *     context also holds the batched (matrix-core) task graph for that many
  *     rows, and mk_prefill runs the prompt through it that many positions per
  *     step; its weights and working memory are counted by mk_workspace_size
- *     (about twice the weight bytes). Needs d_model to be a multiple of 32. */
+ *     (about twice the weight bytes). Needs d_model to be a multiple of 32.
+ *   - weight_format: MK_WEIGHTS_BF16 (0), or MK_WEIGHTS_FP8_E4M3 (1): weight-
+ *     only quantisation of every GEMV matrix ("LLM高速化勉強会資料", slide 33:
+ *     fewer bits per weight, fewer bytes per step; slide 34: products
+ *     accumulate in a wider format). mk_load_weights quantises the bf16
+ *     tensors on the device: each output row is one block with a power-of-two
+ *     scale 2^e, e the smallest integer with max |w| <= 448 * 2^e (clamped to
+ *     [-100, 100], 0 for a zero row), and each weight becomes the OCP E4M3
+ *     code nearest to w * 2^-e (ties to an even mantissa). The step then
+ *     computes with decode(code) * 2^e, exactly, accumulating in fp32. The
+ *     embedding table, norm gains and biases stay bf16. One-sequence contexts
+ *     without prefill_rows only. */
 typedef struct {
   int32_t n_layers, d_model, n_q_heads, n_kv_heads, head_dim, d_ffn, vocab;
   float rms_eps, rope_theta;
@@ -83,7 +94,10 @@ typedef struct {
   int32_t attn_splits;
   int32_t attn_min_blocks;
   int32_t prefill_rows;
+  int32_t weight_format;
 } mk_model_config;
+#define MK_WEIGHTS_BF16 0
+#define MK_WEIGHTS_FP8_E4M3 1
 
 /* One weight tensor for mk_load_weights.
  *   - name: "embed", "final_norm", "lm_head", or "layers.<l>.<t>" with t in
@@ -244,6 +258,17 @@ mk_status mk_decode_step_staged(mk_ctx* ctx, const int32_t* d_tokens_in, int n_s
  * mk_sync_check. */
 mk_status mk_prefill(mk_ctx* ctx, int seq, const int32_t* h_tokens, int n_tokens, int32_t* d_token_out,
                      void* stream);
+
+/* The FP8 codes a context with weight_format MK_WEIGHTS_FP8_E4M3 streams for
+ * one matrix, read back from its tiles into natural layout (inspection, for
+ * checking the quantiser; the format is described at weight_format).
+ *   - name: "layers.<l>.wq" (wk, wv, wo, wg, wu, wd), or "lm_head" ("embed"
+ *     for a tied head).
+ *   - h_codes: host, [out_rows, in] uint8 E4M3 codes; h_exps: host,
+ *     [out_rows] int32, each row's scale exponent e (scale 2^e).
+ * Synchronises `stream`. Errors: MK_ERR_INVALID_ARG (unknown name),
+ * MK_ERR_STATE (weights not loaded, or not FP8). */
+mk_status mk_read_fp8_weights(mk_ctx* ctx, const char* name, uint8_t* h_codes, int32_t* h_exps, void* stream);
 
 /* Copy the last step's logits of sequence `seq` (n <= vocab floats) to host
  * memory. (No passage: the boundary's own, for parity checks.) Synchronises

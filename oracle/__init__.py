@@ -97,6 +97,18 @@ def lib(precision: str | None = None):
         L.orc_threads.argtypes = []
         L.orc_set_threads.restype = None
         L.orc_set_threads.argtypes = [ctypes.c_int]
+        _u8p = ctypes.POINTER(ctypes.c_uint8)
+        _i32p = ctypes.POINTER(ctypes.c_int32)
+        L.orc_fp8_decode.restype = ctypes.c_double
+        L.orc_fp8_decode.argtypes = [ctypes.c_uint8]
+        L.orc_fp8_encode.restype = ctypes.c_uint8
+        L.orc_fp8_encode.argtypes = [ctypes.c_double]
+        L.orc_fp8_row_exp.restype = ctypes.c_int
+        L.orc_fp8_row_exp.argtypes = [_u16p, ctypes.c_int]
+        L.orc_fp8_quantize.restype = None
+        L.orc_fp8_quantize.argtypes = [_u16p, ctypes.c_int, ctypes.c_int, _u8p, _i32p]
+        L.orc_fp8_dequantize.restype = None
+        L.orc_fp8_dequantize.argtypes = [_u8p, _i32p, ctypes.c_int, ctypes.c_int, _u16p]
         _libs[precision] = L
     return _libs[precision]
 
@@ -184,6 +196,66 @@ def threads():
 
 def set_threads(n):
     lib().orc_set_threads(int(n))
+
+
+# ----------------------------------------------------------------- FP8 weights
+def fp8_decode(code: int) -> float:
+    """The value of one OCP E4M3 code."""
+    return lib().orc_fp8_decode(int(code))
+
+
+def fp8_encode(x: float) -> int:
+    """The nearest finite E4M3 code to x (|x| <= 448), ties to an even mantissa."""
+    return int(lib().orc_fp8_encode(float(x)))
+
+
+def fp8_row_exp(row) -> int:
+    r = _u16(row)
+    return int(lib().orc_fp8_row_exp(r.ctypes.data, r.size))
+
+
+def fp8_quantize(w):
+    """[n, k] bf16 bits -> (codes [n, k] uint8, exps [n] int32): each row scaled by its own 2^-e."""
+    w = _u16(w)
+    n, k = w.shape
+    codes = np.empty((n, k), dtype=np.uint8)
+    exps = np.empty(n, dtype=np.int32)
+    lib().orc_fp8_quantize(w.ctypes.data, n, k,
+                           codes.ctypes.data_as(ctypes.POINTER(ctypes.c_uint8)),
+                           exps.ctypes.data_as(ctypes.POINTER(ctypes.c_int32)))
+    return codes, exps
+
+
+def fp8_dequantize(codes, exps):
+    """bf16 bits of decode(codes) * 2^exps per row (exact)."""
+    codes = np.ascontiguousarray(codes, dtype=np.uint8)
+    exps = np.ascontiguousarray(exps, dtype=np.int32)
+    n, k = codes.shape
+    out = np.empty((n, k), dtype=np.uint16)
+    lib().orc_fp8_dequantize(codes.ctypes.data_as(ctypes.POINTER(ctypes.c_uint8)),
+                             exps.ctypes.data_as(ctypes.POINTER(ctypes.c_int32)), n, k, out.ctypes.data)
+    return out
+
+
+FP8_MATRICES = ("wq", "wk", "wv", "wo", "wg", "wu", "wd")
+
+
+def fp8_model(shape, weights: dict):
+    """The model whose GEMV matrices are FP8-quantised: every projection and the LM head replaced by
+    its exact dequantised values; embeddings, norm gains and biases unchanged. A tied LM head becomes
+    an untied one (the embedding lookup keeps the bf16 table). Returns (shape, weights)."""
+    import dataclasses
+    d = shape.d_model
+    out = dict(weights)
+    for l in range(shape.n_layers):
+        for t in FP8_MATRICES:
+            name = "layers.%d.%s" % (l, t)
+            w = _u16(weights[name])
+            rows = w.size // (shape.d_ffn if t == "wd" else shape.n_q_heads * shape.head_dim if t == "wo" else d)
+            out[name] = fp8_dequantize(*fp8_quantize(w.reshape(rows, -1))).reshape(w.shape)
+    head = weights["embed"] if shape.tied_embeddings else weights["lm_head"]
+    out["lm_head"] = fp8_dequantize(*fp8_quantize(_u16(head).reshape(shape.vocab, d))).reshape(np.shape(head))
+    return dataclasses.replace(shape, name=shape.name + "-fp8", tied_embeddings=False), out
 
 
 # ----------------------------------------------------------------- model

@@ -210,6 +210,74 @@ int orc_argmax(const double* v, int n) {
   return best;
 }
 
+/* ------------------------------------------------------------------ FP8 weights
+ * Weight-only quantisation ("LLM高速化勉強会資料", slides 33 and 34: fewer bits per parameter cut the
+ * bytes a step moves; block-wise scaling keeps the precision, and products accumulate in a wider
+ * format). Format: OCP 8-bit floating point E4M3 ("E4M3FN"): a sign bit, 4 exponent bits with bias 7
+ * and 3 mantissa bits; exponent field 0 holds the subnormals m * 2^-9; S.1111.111 is NaN; there is no
+ * infinity, and the largest finite value is 448 (0x7E). Each output row of a weight matrix is one block
+ * with a power-of-two scale 2^e, so the dequantised weight decode(code) * 2^e is exact. */
+
+/* The value of an E4M3 code, from the format's definition. */
+double orc_fp8_decode(uint8_t c) {
+  const int sign = c >> 7, ef = (c >> 3) & 15, mf = c & 7;
+  double v;
+  if (ef == 15 && mf == 7) return NAN;
+  if (ef == 0) v = ldexp((double)mf, -9);
+  else v = ldexp(1.0 + mf / 8.0, ef - 7);
+  return sign ? -v : v;
+}
+
+/* The finite E4M3 code nearest to x (|x| <= 448), ties to the code with an even mantissa. The
+ * non-negative finite codes 0x00..0x7E decode to increasing values, so the candidates are the largest
+ * code not above |x| and the next one. */
+uint8_t orc_fp8_encode(double x) {
+  const double a = fabs(x);
+  int lo = 0, hi = 0x7E;  /* invariant: decode(lo) <= a; find the largest such code */
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) / 2;
+    if (orc_fp8_decode((uint8_t)mid) <= a) lo = mid;
+    else hi = mid - 1;
+  }
+  int c = lo;
+  if (lo < 0x7E) {
+    const double dl = a - orc_fp8_decode((uint8_t)lo), du = orc_fp8_decode((uint8_t)(lo + 1)) - a;
+    if (du < dl || (du == dl && ((lo + 1) & 1) == 0)) c = lo + 1;
+  }
+  return (uint8_t)(c | (signbit(x) ? 0x80 : 0));
+}
+
+/* The row's scale exponent: the smallest integer e with max_k |w_k| <= 448 * 2^e, clamped to
+ * [-100, 100]; 0 for an all-zero row. */
+int orc_fp8_row_exp(const uint16_t* w, int k) {
+  double m = 0.0;
+  for (int j = 0; j < k; ++j) m = fmax(m, fabs(orc_from_bf16(w[j])));
+  if (m == 0.0) return 0;
+  int e = -100;
+  while (e < 100 && m > ldexp(448.0, e)) ++e;
+  return e;
+}
+
+/* codes[i][j] = encode(w[i][j] * 2^-e_i), exps[i] = e_i, for n rows of k bf16 weights. */
+void orc_fp8_quantize(const uint16_t* w, int n, int k, uint8_t* codes, int32_t* exps) {
+#pragma omp parallel for schedule(static)
+  for (int i = 0; i < n; ++i) {
+    const uint16_t* row = w + (size_t)i * k;
+    const int e = orc_fp8_row_exp(row, k);
+    exps[i] = e;
+    for (int j = 0; j < k; ++j) codes[(size_t)i * k + j] = orc_fp8_encode(ldexp(orc_from_bf16(row[j]), -e));
+  }
+}
+
+/* The bf16 bits of decode(codes[i][j]) * 2^exps[i]: exact, since an E4M3 value has at most 4
+ * significant bits and the scaled value stays inside bf16's range. */
+void orc_fp8_dequantize(const uint8_t* codes, const int32_t* exps, int n, int k, uint16_t* w_out) {
+#pragma omp parallel for schedule(static)
+  for (int i = 0; i < n; ++i)
+    for (int j = 0; j < k; ++j)
+      w_out[(size_t)i * k + j] = orc_bf16(ldexp(orc_fp8_decode(codes[(size_t)i * k + j]), exps[i]));
+}
+
 /* ------------------------------------------------------------------ model */
 #define T_EMBED(m) ((m)->t[ORC_T_EMBED])
 #define T_FNORM(m) ((m)->t[ORC_T_FINAL_NORM])

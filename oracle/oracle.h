@@ -81,6 +81,13 @@ double orc_from_bf16(uint16_t b);
 int orc_threads(void);
 void orc_set_threads(int n);
 
+/* FP8 weights: OCP E4M3 codes with one power-of-two scale per output row (see oracle.c). */
+double orc_fp8_decode(uint8_t c);
+uint8_t orc_fp8_encode(double x);
+int orc_fp8_row_exp(const uint16_t* w, int k);
+void orc_fp8_quantize(const uint16_t* w, int n, int k, uint8_t* codes, int32_t* exps);
+void orc_fp8_dequantize(const uint8_t* codes, const int32_t* exps, int n, int k, uint16_t* w_out);
+
 #ifdef __cplusplus
 }
 #endif

@@ -37,7 +37,7 @@ class mk_model_config(ctypes.Structure):
                 ("tied_embeddings", ctypes.c_int32), ("qkv_bias", ctypes.c_int32), ("max_seqs", ctypes.c_int32),
                 ("block_size", ctypes.c_int32), ("max_blocks_per_seq", ctypes.c_int32), ("num_blocks", ctypes.c_int32),
                 ("attn_splits", ctypes.c_int32), ("attn_min_blocks", ctypes.c_int32),
-                ("prefill_rows", ctypes.c_int32)]
+                ("prefill_rows", ctypes.c_int32), ("weight_format", ctypes.c_int32)]
 
 
 class mk_tensor(ctypes.Structure):
@@ -52,7 +52,8 @@ class mk_graph_info(ctypes.Structure):
 
 
 EXPORTS = ["mk_create", "mk_create_host", "mk_workspace_size", "mk_bind_memory", "mk_load_weights", "mk_decode_step",
-           "mk_decode_n", "mk_decode_step_static", "mk_decode_step_staged", "mk_prefill", "mk_read_logits", "mk_sync_check", "mk_graph_stats", "mk_graph_validate",
+           "mk_decode_n", "mk_decode_step_static", "mk_decode_step_staged", "mk_prefill", "mk_read_fp8_weights", "mk_read_logits",
+           "mk_sync_check", "mk_graph_stats", "mk_graph_validate",
            "mk_graph_simulate", "mk_graph_corrupt", "mk_set_trace", "mk_destroy", "mk_status_str", "mk_last_error"]
 
 
@@ -89,6 +90,7 @@ def lib():
             "mk_decode_step_static": [vp, vp, ctypes.c_int, vp, vp],
             "mk_decode_step_staged": [vp, vp, ctypes.c_int, vp, vp],
             "mk_prefill": [vp, ctypes.c_int, ctypes.POINTER(i32), ctypes.c_int, vp, vp],
+            "mk_read_fp8_weights": [vp, ctypes.c_char_p, vp, vp, vp],
             "mk_read_logits": [vp, ctypes.c_int, ctypes.POINTER(ctypes.c_float), sz, vp],
             "mk_sync_check": [vp, vp],
             "mk_graph_stats": [vp, ctypes.POINTER(mk_graph_info)],
@@ -189,6 +191,15 @@ def mk_decode_step_staged(ctx, tokens_in, n_seqs, tokens_out, stream=None):
     _check(lib().mk_decode_step_staged(ctx, _vp(tokens_in), n_seqs, _vp(tokens_out), _vp(stream)))
 
 
+def mk_read_fp8_weights(ctx, name, rows, cols, stream=None):
+    """(codes [rows, cols] uint8, exps [rows] int32) of one FP8 matrix, read back in natural layout."""
+    import numpy as np
+    codes = np.zeros((rows, cols), dtype=np.uint8)
+    exps = np.zeros(rows, dtype=np.int32)
+    _check(lib().mk_read_fp8_weights(ctx, name.encode(), codes.ctypes.data, exps.ctypes.data, _vp(stream)))
+    return codes, exps
+
+
 def mk_prefill(ctx, seq, tokens, token_out=None, stream=None):
     n = len(tokens)
     arr = (ctypes.c_int32 * max(n, 1))(*[int(t) for t in tokens])
@@ -242,12 +253,13 @@ def mk_last_error() -> str:
 
 # ------------------------------------------------------------------- convenience
 def make_config(shape, max_seqs=1, max_blocks_per_seq=64, num_blocks=64, attn_splits=0, block_size=16,
-                attn_min_blocks=0, prefill_rows=0):
+                attn_min_blocks=0, prefill_rows=0, weight_format=0):
     """mk_model_config from any object with the model-shape attributes."""
     return mk_model_config(shape.n_layers, shape.d_model, shape.n_q_heads, shape.n_kv_heads, shape.head_dim,
                            shape.d_ffn, shape.vocab, float(shape.rms_eps), float(shape.rope_theta),
                            int(bool(shape.tied_embeddings)), int(bool(shape.qkv_bias)), max_seqs, block_size,
-                           max_blocks_per_seq, num_blocks, attn_splits, attn_min_blocks, prefill_rows)
+                           max_blocks_per_seq, num_blocks, attn_splits, attn_min_blocks, prefill_rows,
+                           weight_format)
 
 
 class Decoder:

@@ -19,8 +19,10 @@
 
 namespace mk {
 hipError_t launch_megakernel(const KernelParams& p, int grid, size_t lds_bytes, hipStream_t stream, bool coop);
-hipError_t megakernel_occupancy(int* blocks_per_cu, size_t lds_bytes, int dh, int hq, int hk, bool batched);
+hipError_t megakernel_occupancy(int* blocks_per_cu, size_t lds_bytes, int dh, int hq, int hk, bool batched, bool fp8);
 hipError_t launch_repack(const RepackArgs& a, int64_t units, hipStream_t stream);
+hipError_t launch_row_scales(const RepackArgs& a, int nrows, hipStream_t stream);
+hipError_t launch_repack_fp8(const RepackArgs& a, int64_t units, hipStream_t stream);
 hipError_t launch_repack_bias(const uint16_t* bq, const uint16_t* bk, const uint16_t* bv, int G, int dh, int nrows,
                               uint16_t* out, hipStream_t stream);
 hipError_t static_scratch_address(int device, void** out);
@@ -215,6 +217,8 @@ KernelParams make_params(mk_ctx* c, const HostGraph& g, uint8_t* R, uint8_t* W, 
   p.attn_tasks = g.attn_tasks;
   p.attn_min_blocks = g.cfg.attn_min_blocks > 0 ? g.cfg.attn_min_blocks : kAttnMinBlocks;
   p.trace = &g == &c->g ? c->d_trace : nullptr;
+  p.fp8_weights = m.weight_format == MK_WEIGHTS_FP8_E4M3 ? 1 : 0;
+  p.wscale = p.fp8_weights ? (const float*)(Wt + g.wl.scales) : nullptr;
   return p;
 }
 
@@ -301,7 +305,14 @@ mk_status load_graph_weights(const HostGraph& g, uint8_t* R, uint8_t* Wt,
     }
     const TaskDesc& last = g.tasks[t1 - 1];
     const int64_t bytes = last.wofs + task_tile_bytes(r.gm, last) - a.wofs;
-    HIPCHK(launch_repack(r, bytes / 1024, st));
+    if (r.gm.fp8) {  // the rows' scales first, then the codes (the stage's first task starts at row 0)
+      r.scales = (float*)(Wt + g.wl.scales);
+      r.scale0 = a.a1;
+      HIPCHK(launch_row_scales(r, last.row1, st));
+      HIPCHK(launch_repack_fp8(r, bytes / 1024, st));
+    } else {
+      HIPCHK(launch_repack(r, bytes / 1024, st));
+    }
     t0 = t1;
   }
   HIPCHK(hipMemcpyAsync(Wt + g.wl.embed, have.at("embed"), (size_t)V * d * 2, hipMemcpyDeviceToDevice, st));
@@ -337,7 +348,7 @@ mk_status mk_create(const mk_model_config* cfg, int device, mk_ctx** out) {
   DeviceGuard dg(device);
   int blocks = 0;
   if (megakernel_occupancy(&blocks, (size_t)(*out)->g.lds_bytes, cfg->head_dim, cfg->n_q_heads, cfg->n_kv_heads,
-                           cfg->max_seqs > 1) !=
+                           cfg->max_seqs > 1, cfg->weight_format == MK_WEIGHTS_FP8_E4M3) !=
           hipSuccess ||
       blocks < 1) {
     mk_destroy(*out);
@@ -345,7 +356,7 @@ mk_status mk_create(const mk_model_config* cfg, int device, mk_ctx** out) {
     return fail(MK_ERR_UNSUPPORTED, "one workgroup per CU does not fit (LDS or registers)");
   }
   if ((*out)->pg && (megakernel_occupancy(&blocks, (size_t)(*out)->pg->lds_bytes, cfg->head_dim, cfg->n_q_heads,
-                                          cfg->n_kv_heads, true) != hipSuccess ||
+                                          cfg->n_kv_heads, true, false) != hipSuccess ||
                      blocks < 1)) {
     mk_destroy(*out);
     *out = nullptr;
@@ -607,6 +618,89 @@ mk_status mk_prefill(mk_ctx* c, int seq, const int32_t* h_tokens, int n_tokens, 
   if (mk_status s = read_error_word(c, st)) return s;  // synchronises the stream
   const int32_t len = p0 + n_tokens;
   HIPCHK(hipMemcpy(c->d_ctx_lens + seq, &len, 4, hipMemcpyHostToDevice));
+  return MK_OK;
+}
+
+mk_status mk_read_fp8_weights(mk_ctx* c, const char* name, uint8_t* h_codes, int32_t* h_exps, void* stream) {
+  if (!c || !name || !h_codes || !h_exps) return fail(MK_ERR_INVALID_ARG, "null argument");
+  if (!c->bound || !c->loaded) return fail(MK_ERR_STATE, "bind memory and load weights first");
+  const HostGraph& g = c->g;
+  const mk_model_config& m = g.cfg;
+  if (m.weight_format != MK_WEIGHTS_FP8_E4M3) return fail(MK_ERR_STATE, "the context's weights are not FP8");
+  // which stage holds the matrix, and which of its packed rows are the matrix's
+  const std::string nm = name;
+  int type = -1, layer = m.n_layers, which = 0;
+  if (nm == "lm_head" || (nm == "embed" && m.tied_embeddings)) {
+    type = T_LMHEAD;
+  } else if (nm.rfind("layers.", 0) == 0) {
+    const size_t dot = nm.find('.', 7);
+    if (dot == std::string::npos) return fail(MK_ERR_INVALID_ARG, "unknown tensor " + nm);
+    layer = std::atoi(nm.substr(7, dot - 7).c_str());
+    const std::string t = nm.substr(dot + 1);
+    if (t == "wq") { type = T_QKV; which = 0; }
+    else if (t == "wk") { type = T_QKV; which = 1; }
+    else if (t == "wv") { type = T_QKV; which = 2; }
+    else if (t == "wo") type = T_OPROJ;
+    else if (t == "wg") { type = T_GATEUP; which = 0; }
+    else if (t == "wu") { type = T_GATEUP; which = 1; }
+    else if (t == "wd") type = T_DOWN;
+    if (layer < 0 || layer >= m.n_layers) type = -1;
+  }
+  if (type < 0) return fail(MK_ERR_INVALID_ARG, "not an FP8 matrix: " + nm);
+  size_t t0 = 0;
+  while (t0 < g.tasks.size() && !(g.tasks[t0].type == type && g.tasks[t0].layer == layer)) ++t0;
+  size_t t1 = t0;
+  while (t1 < g.tasks.size() && g.tasks[t1].type == type && g.tasks[t1].layer == layer) ++t1;
+  if (t0 == t1) return fail(MK_ERR_STATE, "no such stage");
+  const GemvGeom& q = g.geoms[g.tasks[t0].geom];
+  const int64_t b0 = g.tasks[t0].wofs, b1 = g.tasks[t1 - 1].wofs + task_tile_bytes(q, g.tasks[t1 - 1]);
+  const int nrows = g.tasks[t1 - 1].row1;
+  std::vector<uint8_t> tiles((size_t)(b1 - b0));
+  std::vector<float> sc((size_t)nrows);
+  DeviceGuard dg(c->device);
+  hipStream_t st = (hipStream_t)stream;
+  HIPCHK(hipMemcpyAsync(tiles.data(), c->d_weights + b0, tiles.size(), hipMemcpyDeviceToHost, st));
+  HIPCHK(hipMemcpyAsync(sc.data(), c->d_weights + g.wl.scales + (size_t)g.tasks[t0].a1 * 4, sc.size() * 4,
+                        hipMemcpyDeviceToHost, st));
+  HIPCHK(hipStreamSynchronize(st));
+  const int G = m.n_q_heads / m.n_kv_heads, dh = m.head_dim, K = q.K, su = q.S / 2;
+  // packed row -> (sub-matrix, its row), the mapping the re-layout applies
+  auto source = [&](int pr, int* sub) {
+    if (type == T_QKV) {
+      const int Rg = (G + 2) * dh, grp = pr / Rg, within = pr % Rg, slot = within / dh, jh = within % dh;
+      const int dim = (jh & 1) ? (jh >> 1) + dh / 2 : (jh >> 1);
+      if (slot < G) { *sub = 0; return (grp * G + slot) * dh + dim; }
+      *sub = slot == G ? 1 : 2;
+      return grp * dh + dim;
+    }
+    if (type == T_GATEUP) { *sub = pr & 1; return pr >> 1; }
+    *sub = 0;
+    return pr;
+  };
+  for (size_t ti = t0; ti < t1; ++ti) {
+    const TaskDesc& t = g.tasks[ti];
+    const int64_t units = task_tile_bytes(q, t) / 1024;
+    for (int64_t u = 0; u < units; ++u) {
+      const int gi = (int)(u / su), ui = (int)(u % su);
+      for (int lane = 0; lane < 64; ++lane) {
+        const int rl = gi * q.rg + lane / q.lpr;
+        if (rl >= t.row1 - t.row0) continue;
+        const int pr = t.row0 + rl;
+        int sub = 0;
+        const int row = source(pr, &sub);
+        if (sub != which) continue;
+        int ex = 0;
+        (void)std::frexp(sc[(size_t)pr], &ex);  // the scale is 2^(ex - 1)
+        h_exps[row] = ex - 1;
+        for (int h = 0; h < 2; ++h) {
+          const int piece = (2 * ui + h) * q.lpr + (lane & (q.lpr - 1));
+          if (piece >= q.P) continue;
+          const uint8_t* src = tiles.data() + (t.wofs - b0) + u * 1024 + lane * 16 + h * 8;
+          std::memcpy(h_codes + (size_t)row * K + (size_t)piece * 8, src, 8);
+        }
+      }
+    }
+  }
   return MK_OK;
 }
 

@@ -166,8 +166,9 @@ struct Builder {
   }
   int64_t tile_bytes(int geom, int rows) const {
     const GemvGeom& q = g.geoms[geom];
-    return (int64_t)((rows + q.rg - 1) / q.rg) * q.S * 1024;
+    return (int64_t)((rows + q.rg - 1) / q.rg) * (q.fp8 ? q.S / 2 : q.S) * 1024;
   }
+  int64_t scale_rows = 0;  // FP8 weights: packed GEMV rows so far, the row-scale array's length
   // A GEMV stage: one task per CU with a non-empty row range, over the CUs not marked in `skip`.
   std::vector<int> gemv_stage(int type, int layer, int geom, int N, int A, int wait_ev,
                               const std::vector<char>* skip = nullptr, const std::vector<double>* weight = nullptr) {
@@ -188,9 +189,11 @@ struct Builder {
       t.row1 = rs[k].r1;
       t.geom = geom;
       t.wofs = packed;
+      if (g.geoms[geom].fp8) t.a1 = (int32_t)(scale_rows + t.row0);
       packed += tile_bytes(geom, t.row1 - t.row0);
       ids.push_back(add_task(t, cu));
     }
+    if (g.geoms[geom].fp8) scale_rows += N;
     return ids;
   }
 };
@@ -224,6 +227,9 @@ std::string build_graph(const mk_model_config& c, int n_cus, HostGraph& g) {
   if (c.max_seqs > 1 && c.prefill_rows != 0)
     return "prefill_rows applies to one-sequence contexts (a batched context prefills through its own rows)";
   if (c.prefill_rows > 1 && c.d_model % 32) return "chunked prefill needs d_model to be a multiple of 32";
+  if (c.weight_format != MK_WEIGHTS_BF16 && c.weight_format != MK_WEIGHTS_FP8_E4M3) return "unknown weight_format";
+  if (c.weight_format == MK_WEIGHTS_FP8_E4M3 && (c.max_seqs != 1 || c.prefill_rows > 1))
+    return "FP8 weights run one-sequence contexts without prefill_rows";
   g.cfg = c;
   g.n_cus = n_cus;
   g.max_pos = c.max_blocks_per_seq * c.block_size;
@@ -254,6 +260,19 @@ std::string build_graph(const mk_model_config& c, int n_cus, HostGraph& g) {
   g.geoms[G_GU] = geom(d);
   g.geoms[G_D] = geom(f);
   g.geoms[G_LM] = geom(d);
+  if (c.weight_format == MK_WEIGHTS_FP8_E4M3)
+    for (int i = 0; i < G_COUNT; ++i) {
+      // An FP8 unit carries two bf16-layout units of a row group, so a group needs an even count: an
+      // odd one is doubled by halving the lanes per row (twice the rows per group), then padded.
+      GemvGeom& q = g.geoms[i];
+      q.fp8 = 1;
+      if ((q.S & 1) && q.lpr > 1) {
+        q.lpr /= 2;
+        q.rg = 64 / q.lpr;
+        q.S = (q.P + q.lpr - 1) / q.lpr;
+      }
+      q.S += q.S & 1;
+    }
 
   g.sym_size[S_X] = (int64_t)S * d;
   g.sym_size[S_Q] = (int64_t)S * qd;
@@ -557,7 +576,9 @@ std::string build_graph(const mk_model_config& c, int n_cus, HostGraph& g) {
   g.wl.bias = align_up(g.wl.norms + (int64_t)(2 * L + 1) * d * 2, 256);
   // a tail pad: batched tasks load gains and embedding columns a block at a time and may read up to one
   // 1024-column block (2 KB) past a row's end (the values are not used)
-  g.wl.total = align_up(g.wl.bias + (c.qkv_bias ? (int64_t)L * Nqkv * 2 : 0), 256) + 2048;
+  g.wl.scales = align_up(g.wl.bias + (c.qkv_bias ? (int64_t)L * Nqkv * 2 : 0), 256);
+  g.wl.n_scale_rows = b.scale_rows;
+  g.wl.total = align_up(g.wl.scales + b.scale_rows * 4, 256) + 2048;
 
   // ---- scratch layout
   int64_t o = 0;
@@ -597,6 +618,11 @@ std::string build_graph(const mk_model_config& c, int n_cus, HostGraph& g) {
   int64_t xs = 0;
   for (int i = 0; i < G_COUNT; ++i) xs = std::max<int64_t>(xs, (int64_t)g.geoms[i].S * g.geoms[i].lpr * 8);
   int64_t gemv_lds = xs * 4 + (int64_t)align_up(max_task_rows, 64) * 4 * S + 1024;
+  if (c.weight_format == MK_WEIGHTS_FP8_E4M3) {
+    // a task's row scales are loaded two rows per thread
+    if (max_task_rows > 2 * 512) return "FP8 weights: a GEMV task of more than 1024 rows";
+    gemv_lds += (int64_t)align_up(max_task_rows, 64) * 4;  // the row scales beside the results
+  }
   if (S > 1)  // batched: the input columns as MFMA fragments (32 units x 64 lanes x 32 B), the tile's
               // partial sums (1 KB per 16-row group), two edge tiles per wave, per-sequence scalars
     gemv_lds = 32 * 64 * 32 + (int64_t)g.max_tile_groups * 1024 + 8 * 2 * 1024 + 256;

@@ -56,7 +56,10 @@ constexpr size_t kStaticScratchBytes = (size_t)64 << 20;
 struct GemvGeom {
   int32_t K, P, lpr, rg, S;
   int32_t mfma;
-  int32_t pad[2];
+  // FP8 weights: a 1 KB unit holds 16 codes per lane, the lane's pieces of two consecutive bf16-layout
+  // units (S is then even: a row group streams S / 2 units)
+  int32_t fp8;
+  int32_t pad;
 };
 enum GeomIndex : int32_t { G_QKV = 0, G_O = 1, G_GU = 2, G_D = 3, G_LM = 4, G_COUNT = 5 };
 
@@ -74,6 +77,7 @@ struct TaskDesc {       // 64 bytes; read with scalar loads
   //   a1 = word offset of the tile's partial sums in KernelParams::bpt (kS > 1),
   //   a2 = first column unit | units << 16 (units of 32 columns),
   //   a3 = split index | kS << 8.
+  // One-sequence GEMV with FP8 weights: a1 = index of the task's first row in the row-scale array.
   int32_t a0, a1, a2, a3;
   int32_t wait_slot0, wait_nslots;  // the wait event's flag slots (copied from events[wait_ev])
 };
@@ -105,6 +109,8 @@ struct WeightLayout {
   int64_t embed;         // natural [V, d] copy for the embedding gather
   int64_t norms;         // [L][2][d] (attn, ffn) then final [d]
   int64_t bias;          // packed-QKV-order bias [L][Nqkv] (when qkv_bias)
+  int64_t scales;        // FP8 weights: fp32 scale 2^e of every packed GEMV row, stage after stage
+  int64_t n_scale_rows;
   int64_t total;
 };
 
@@ -172,6 +178,8 @@ struct KernelParams {
   int32_t task_lo, task_hi;   // this launch runs the tasks [task_lo, task_hi) of the global order
   int32_t attn_min_blocks;    // cache blocks per attention task at least (fewer tasks get blocks)
   int32_t prefill;            // batched graphs: 1 = the rows are consecutive positions of one sequence
+  int32_t fp8_weights;        // 1: GEMV tiles hold E4M3 codes, row r's products scale by wscale[r]
+  const float* wscale;        // FP8 weights: 2^e of every packed GEMV row (TaskDesc::a1 indexes it)
   TraceRec* trace;            // per-task timestamps of the last step, or nullptr
 };
 
@@ -188,6 +196,8 @@ struct RepackArgs {
   const uint16_t* w2;     // QKV: wv
   int32_t G, dh;
   uint8_t* out;           // packed weights base
+  float* scales;          // FP8 weights: the row-scale array, and the index of the stage's first row in it
+  int32_t scale0;
 };
 
 }  // namespace mk

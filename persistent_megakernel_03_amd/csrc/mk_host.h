@@ -68,7 +68,7 @@ GemvGeom choose_geom_batched(int K);
 // Bytes of a GEMV task's packed tile.
 inline int64_t task_tile_bytes(const GemvGeom& q, const TaskDesc& t) {
   if (q.mfma) return (int64_t)((t.row1 - t.row0 + 15) / 16) * (t.a2 >> 16) * 1024;
-  return (int64_t)((t.row1 - t.row0 + q.rg - 1) / q.rg) * q.S * 1024;
+  return (int64_t)((t.row1 - t.row0 + q.rg - 1) / q.rg) * (q.fp8 ? q.S / 2 : q.S) * 1024;
 }
 
 // Packed-row bookkeeping shared with the weight re-layout.

@@ -357,6 +357,38 @@ __device__ __forceinline__ void unit_fma(const v4u w, const float* xa, const flo
   acc1 = fmaf(bf_hi(w.w), b.w, acc1);
 }
 
+// FP8 weights: the lane's 16 bytes are the E4M3 codes of two pieces, the piece of bf16-layout unit
+// 2u (bytes 0..7, elements 0..7) and of unit 2u + 1 (bytes 8..15); the conversion to fp32 is exact.
+typedef float v2f __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ void unit_fma8(const v4u w, const float* xa0, const float* xb0, const float* xa1,
+                                          const float* xb1, float& acc0, float& acc1) {
+  const v4f a0 = *(const v4f*)xa0, b0 = *(const v4f*)xb0, a1 = *(const v4f*)xa1, b1 = *(const v4f*)xb1;
+  v2f c = __builtin_amdgcn_cvt_pk_f32_fp8((int)w.x, false);
+  acc0 = fmaf(c.x, a0.x, acc0);
+  acc1 = fmaf(c.y, a0.y, acc1);
+  c = __builtin_amdgcn_cvt_pk_f32_fp8((int)w.x, true);
+  acc0 = fmaf(c.x, a0.z, acc0);
+  acc1 = fmaf(c.y, a0.w, acc1);
+  c = __builtin_amdgcn_cvt_pk_f32_fp8((int)w.y, false);
+  acc0 = fmaf(c.x, b0.x, acc0);
+  acc1 = fmaf(c.y, b0.y, acc1);
+  c = __builtin_amdgcn_cvt_pk_f32_fp8((int)w.y, true);
+  acc0 = fmaf(c.x, b0.z, acc0);
+  acc1 = fmaf(c.y, b0.w, acc1);
+  c = __builtin_amdgcn_cvt_pk_f32_fp8((int)w.z, false);
+  acc0 = fmaf(c.x, a1.x, acc0);
+  acc1 = fmaf(c.y, a1.y, acc1);
+  c = __builtin_amdgcn_cvt_pk_f32_fp8((int)w.z, true);
+  acc0 = fmaf(c.x, a1.z, acc0);
+  acc1 = fmaf(c.y, a1.w, acc1);
+  c = __builtin_amdgcn_cvt_pk_f32_fp8((int)w.w, false);
+  acc0 = fmaf(c.x, b1.x, acc0);
+  acc1 = fmaf(c.y, b1.y, acc1);
+  c = __builtin_amdgcn_cvt_pk_f32_fp8((int)w.w, true);
+  acc0 = fmaf(c.x, b1.z, acc0);
+  acc1 = fmaf(c.y, b1.w, acc1);
+}
+
 // Register pipeline of one wave's weight stream: NSLOT slots of one unit each. A task's first
 // NSLOT units are loaded before the task polls for its inputs: weights do not depend on
 // activations, so the HBM stream keeps running across the dependency wait. The registers flow
@@ -371,6 +403,7 @@ struct WaveRun {
   int nunits, g0;  // units in the run; first row group
 };
 
+template <bool FP8>
 __device__ __forceinline__ WaveRun wave_run(const KernelParams& p, const TaskDesc& t, const GemvGeom& gm) {
   // The wave index is made explicitly wave-uniform so that unit counts and loop bounds live in
   // scalar registers and loads need no per-lane branches.
@@ -380,8 +413,9 @@ __device__ __forceinline__ WaveRun wave_run(const KernelParams& p, const TaskDes
   const int gA = ngroups * wave / NW, gB = ngroups * (wave + 1) / NW;
   WaveRun r;
   r.g0 = gA;
-  r.nunits = (gB - gA) * gm.S;
-  r.src = (const v4u*)(p.wpacked + t.wofs) + (size_t)gA * gm.S * 64 + (threadIdx.x & 63);
+  const int su = FP8 ? gm.S >> 1 : gm.S;  // units per row group
+  r.nunits = (gB - gA) * su;
+  r.src = (const v4u*)(p.wpacked + t.wofs) + (size_t)gA * su * 64 + (threadIdx.x & 63);
   return r;
 }
 
@@ -429,9 +463,12 @@ __device__ __forceinline__ void stage_units(const WaveRun& w) {
 }
 
 // restage: once this task has read its own staged units, the stage receives those of run `next`.
+// FP8: each unit covers two bf16-layout units of the row group, and a finished row is scaled by its
+// row's 2^e (ysc, in LDS).
+template <bool FP8>
 __device__ __forceinline__ void gemv_tile(const KernelParams& p, const TaskDesc& t, const GemvGeom gm, const float* xs, float* ys,
-                          WPipe& wp, bool restage, const WaveRun next) {
-  const WaveRun w = wave_run(p, t, gm);
+                          WPipe& wp, bool restage, const WaveRun next, const float* ysc) {
+  const WaveRun w = wave_run<FP8>(p, t, gm);
   const int nunits = w.nunits;
   if (nunits <= 0) return;
   const int lane = threadIdx.x & 63;
@@ -445,11 +482,17 @@ __device__ __forceinline__ void gemv_tile(const KernelParams& p, const TaskDesc&
   float acc0 = 0.f, acc1 = 0.f;
 
   auto unit = [&](const v4u& wv) {
-    unit_fma(wv, xa + ug * lpr * 4, xb + ug * lpr * 4, acc0, acc1);
-    if (++ug == S) {
+    if constexpr (FP8) {
+      unit_fma8(wv, xa + ug * lpr * 4, xb + ug * lpr * 4, xa + (ug + 1) * lpr * 4, xb + (ug + 1) * lpr * 4, acc0, acc1);
+      ug += 2;
+    } else {
+      unit_fma(wv, xa + ug * lpr * 4, xb + ug * lpr * 4, acc0, acc1);
+      ++ug;
+    }
+    if (ug == S) {
       const float acc = lanes_sum(acc0 + acc1, lpr);
       const int r = g * gm.rg + rin;
-      if (sub == 0 && r < rows) ys[r] = acc;
+      if (sub == 0 && r < rows) ys[r] = FP8 ? acc * ysc[r] : acc;
       acc0 = 0.f;
       acc1 = 0.f;
       ug = 0;
@@ -1171,6 +1214,7 @@ __device__ __forceinline__ uint64_t block_max_u64(uint64_t k, Ctl* ctl) {
 // ep: the step's epoch; step: the step's index within this launch. nxt: the CU's next task in this
 // launch, or null. staged: on entry, whether this wave's stage already holds this task's units (staged
 // by the previous task); on return, whether it holds the next task's.
+template <bool FP8>
 __device__ __forceinline__ void gemv_task(const KernelParams& p, uint32_t ep, int step, const TaskDesc& t, float* lds,
                                           Ctl* ctl, WPipe& wp, uint16_t* const* pools, const TaskDesc* nxt,
                                           bool& staged) {
@@ -1204,13 +1248,13 @@ __device__ __forceinline__ void gemv_task(const KernelParams& p, uint32_t ep, in
   // An O-projection task runs while HBM is nearly idle (its weights arrived during attention) and is
   // followed on its CU by a gate/up task: it fills the stage with that task's units, at once when
   // its own units fit the registers, else as soon as it has read its own staged units.
-  WaveRun wrun = wave_run(p, t, gm);
+  WaveRun wrun = wave_run<FP8>(p, t, gm);
   if (wrun.nunits <= 0) wrun = dummy_run(p);
   if (!staged) stage_units(wrun);
   const bool restage_next = type == T_OPROJ && nxt != nullptr && is_gemv(nxt->type);
   WaveRun wnext = wrun;
   if (restage_next) {
-    wnext = wave_run(p, *nxt, ctl->geoms[nxt->geom]);
+    wnext = wave_run<FP8>(p, *nxt, ctl->geoms[nxt->geom]);
     if (wnext.nunits <= 0) wnext = dummy_run(p);
     if (wrun.nunits <= NSLOT) stage_units(wnext);
   }
@@ -1243,6 +1287,13 @@ __device__ __forceinline__ void gemv_task(const KernelParams& p, uint32_t ep, in
     const __amdgpu_buffer_rsrc_t rr = tag_rsrc(rsrc + t.row0);
 #pragma unroll
     for (int k = 0; k < 4; ++k) rw[k] = ld_tag(rr, min(tid + k * NT, nrows - 1) * 8, 0);
+  }
+  // FP8 weights: the scales 2^e of the task's rows (thread t: rows t and t + 512)
+  float scv[2] = {1.f, 1.f};
+  if constexpr (FP8) {
+#pragma unroll
+    for (int k = 0; k < 2; ++k)
+      if (tid + k * NT < nrows) scv[k] = p.wscale[t.a1 + tid + k * NT];
   }
   // the wave's first NSLOT / 2 weight units (the rest go out after the input's second poll pass)
 #pragma unroll
@@ -1300,6 +1351,12 @@ __device__ __forceinline__ void gemv_task(const KernelParams& p, uint32_t ep, in
     }
   }
   for (int i = n + tid; i < padded; i += NT) xs[xs_index(i, np)] = 0.f;
+  float* ysc = ys + ((nrows + 63) & ~63);
+  if constexpr (FP8) {
+#pragma unroll
+    for (int k = 0; k < 2; ++k)
+      if (tid + k * NT < nrows) ysc[tid + k * NT] = scv[k];
+  }
   bar();
   if (norm) {  // the sum of squares runs over the staged values in a fixed order
     float ss = 0.f;
@@ -1343,7 +1400,7 @@ __device__ __forceinline__ void gemv_task(const KernelParams& p, uint32_t ep, in
   }
   if (p.trace && tid == 0) ctl->t_ready = __builtin_amdgcn_s_memrealtime();
 
-  gemv_tile(p, t, gm, xs, ys, wp, restage_next && wrun.nunits > NSLOT, wnext);
+  gemv_tile<FP8>(p, t, gm, xs, ys, wp, restage_next && wrun.nunits > NSLOT, wnext, ysc);
   bar();
   if (p.trace && tid == 0) ctl->t_streamed = __builtin_amdgcn_s_memrealtime();
 
@@ -1789,7 +1846,7 @@ __device__ __forceinline__ void task_argmax(const KernelParams& p, uint32_t ep, 
 // One instantiation per (head dim, query heads per KV head rounded up to 2, 4 or 8): the
 // attention tile keeps GMAX x 8 query values and accumulators per lane in registers, and a
 // kernel's register budget is set by its largest path.
-template <int DH, int GMAX, bool BATCHED>
+template <int DH, int GMAX, bool BATCHED, bool FP8>
 __global__ __launch_bounds__(NT, 1) void mk_megakernel(KernelParams p) {
   extern __shared__ __attribute__((aligned(16))) unsigned char lds_raw[];
   static_assert(sizeof(Ctl) <= 1024, "control block fits its 1 KB");
@@ -1882,7 +1939,7 @@ __global__ __launch_bounds__(NT, 1) void mk_megakernel(KernelParams p) {
     } else if constexpr (BATCHED) {
       gemv_task_b(p, ep, step, t, lds, ctl, pools);
     } else {
-      gemv_task(p, ep, step, t, lds, ctl, wp, pools, qi + 1 < q1 ? &tq[qi + 1 - q0] : nullptr, staged);
+      gemv_task<FP8>(p, ep, step, t, lds, ctl, wp, pools, qi + 1 < q1 ? &tq[qi + 1 - q0] : nullptr, staged);
     }
     // The LM head's stores must be complete before its flags go out; other tasks' consumers check
     // the tags themselves.
@@ -1911,6 +1968,20 @@ __global__ __launch_bounds__(NT, 1) void mk_megakernel(KernelParams p) {
 // One 64-thread block per 1 KB unit of a stage's tiles. Tasks [task0, task0 + ntasks) of the
 // stage are contiguous in the task array with contiguous tiles.
 // RepackArgs and RepackKind are declared in mk_graph.h.
+// The natural-layout source row of packed row pr of a stage: QKV rows grouped per KV head and
+// pair-interleaved within a head, gate/up rows alternating, other stages in order.
+__device__ __forceinline__ const uint16_t* repack_src_row(const RepackArgs& a, int pr) {
+  if (a.kind == RK_QKV) {
+    const int Rg = (a.G + 2) * a.dh, grp = pr / Rg, within = pr % Rg, slot = within / a.dh, jh = within % a.dh;
+    const int dim = (jh & 1) ? (jh >> 1) + a.dh / 2 : (jh >> 1);
+    if (slot < a.G) return a.w0 + ((size_t)(grp * a.G + slot) * a.dh + dim) * a.gm.K;
+    if (slot == a.G) return a.w1 + ((size_t)grp * a.dh + dim) * a.gm.K;
+    return a.w2 + ((size_t)grp * a.dh + dim) * a.gm.K;
+  }
+  if (a.kind == RK_GU) return ((pr & 1) ? a.w1 : a.w0) + (size_t)(pr >> 1) * a.gm.K;
+  return a.w0 + (size_t)pr * a.gm.K;
+}
+
 extern "C" __global__ __launch_bounds__(64) void mk_repack(RepackArgs a) {
   const int64_t unit = blockIdx.x;
   const int64_t byte = a.tasks[a.task0].wofs + unit * 1024;
@@ -1948,6 +2019,75 @@ extern "C" __global__ __launch_bounds__(64) void mk_repack(RepackArgs a) {
 }
 
 // QKV bias in packed row order: one thread per packed row.
+// ---- FP8 weights (OCP E4M3 codes, one power-of-two scale per packed row)
+// The row's scale 2^e: e is the smallest integer with max |w| <= 448 * 2^e (448 = 0.875 * 2^9, the
+// largest E4M3 value), clamped to [-100, 100]; 0 for a zero row. One wave per packed row.
+extern "C" __global__ __launch_bounds__(64) void mk_row_scales(RepackArgs a, int nrows) {
+  const int pr = blockIdx.x;
+  if (pr >= nrows) return;
+  const uint16_t* src = repack_src_row(a, pr);
+  float m = 0.f;
+  for (int k = threadIdx.x; k < a.gm.K; k += 64) m = fmaxf(m, fabsf(bf2f(src[k])));
+  for (int o = 32; o > 0; o >>= 1) m = fmaxf(m, __shfl_xor(m, o));
+  if (threadIdx.x == 0) {
+    int e = 0;
+    if (m > 0.f) {
+      int ex;
+      const float fr = frexpf(m, &ex);  // m = fr 2^ex, fr in [0.5, 1)
+      e = min(100, max(-100, ex - 9 + (fr > 0.875f ? 1 : 0)));
+    }
+    a.scales[a.scale0 + pr] = ldexpf(1.0f, e);
+  }
+}
+
+// The E4M3 code nearest to v (|v| <= 448), ties to an even mantissa. In the normal range (exponents
+// -6..8) the fp32 mantissa is rounded to 3 bits, to nearest even; below 2^-6 to the nearest multiple
+// of 2^-9 (the subnormal step), where 8 steps carry into the smallest normal code.
+__device__ __forceinline__ uint32_t e4m3_rne(float v) {
+  const uint32_t u = __float_as_uint(v), sign = (u >> 31) << 7, a = u & 0x7FFFFFFFu;
+  const int E = (int)(a >> 23) - 127;
+  uint32_t code;
+  if (E < -6) {
+    code = (uint32_t)rintf(__uint_as_float(a) * 512.0f);
+  } else {
+    const uint32_t r = a + 0x7FFFFu + ((a >> 20) & 1u);
+    code = (((r >> 23) - 120u) << 3) | ((r >> 20) & 7u);
+  }
+  return sign | code;
+}
+
+// One 1 KB unit per block: lane (row rl, sub) packs the 16 codes of its row's pieces of bf16-layout
+// units 2u and 2u + 1, each weight scaled by its row's 2^-e first (exact).
+extern "C" __global__ __launch_bounds__(64) void mk_repack_fp8(RepackArgs a) {
+  const int64_t unit = blockIdx.x;
+  const int64_t byte = a.tasks[a.task0].wofs + unit * 1024;
+  int lo = a.task0, hi = a.task0 + a.ntasks - 1;
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) >> 1;
+    if (a.tasks[mid].wofs <= byte) lo = mid; else hi = mid - 1;
+  }
+  const TaskDesc t = a.tasks[lo];
+  const int64_t u = (byte - t.wofs) / 1024;
+  const int su = a.gm.S / 2;
+  const int gi = (int)(u / su), ui = (int)(u % su);
+  const int lane = threadIdx.x;
+  const int rl = gi * a.gm.rg + lane / a.gm.lpr, sub = lane & (a.gm.lpr - 1);
+  uint32_t wd[4] = {0u, 0u, 0u, 0u};
+  if (rl < t.row1 - t.row0) {
+    const int pr = t.row0 + rl;
+    const uint16_t* src = repack_src_row(a, pr);
+    const float inv = 1.0f / a.scales[a.scale0 + pr];  // 2^-e, exact
+    for (int h = 0; h < 2; ++h) {
+      const int piece = (2 * ui + h) * a.gm.lpr + sub;
+      if (piece >= a.gm.P) continue;
+      for (int e = 0; e < 8; ++e) wd[2 * h + e / 4] |= e4m3_rne(bf2f(src[(size_t)piece * 8 + e]) * inv) << (8 * (e % 4));
+    }
+  }
+  v4u v;
+  v.x = wd[0]; v.y = wd[1]; v.z = wd[2]; v.w = wd[3];
+  *((v4u*)(a.out + byte) + lane) = v;
+}
+
 extern "C" __global__ __launch_bounds__(256) void mk_repack_bias(const uint16_t* bq, const uint16_t* bk,
                                                                   const uint16_t* bv, int G, int dh, int nrows,
                                                                   uint16_t* out) {
@@ -1963,15 +2103,17 @@ extern "C" __global__ __launch_bounds__(256) void mk_repack_bias(const uint16_t*
 }
 
 // ----------------------------------------------------------------------------- host-side launchers
-template <bool B>
+template <bool B, bool F>
 static const void* megakernel_for_t(int dh, int g) {
   if (dh == 128)
-    return g <= 2 ? (const void*)mk_megakernel<128, 2, B> : g <= 4 ? (const void*)mk_megakernel<128, 4, B> : (const void*)mk_megakernel<128, 8, B>;
-  return g <= 2 ? (const void*)mk_megakernel<64, 2, B> : g <= 4 ? (const void*)mk_megakernel<64, 4, B> : (const void*)mk_megakernel<64, 8, B>;
+    return g <= 2 ? (const void*)mk_megakernel<128, 2, B, F> : g <= 4 ? (const void*)mk_megakernel<128, 4, B, F> : (const void*)mk_megakernel<128, 8, B, F>;
+  return g <= 2 ? (const void*)mk_megakernel<64, 2, B, F> : g <= 4 ? (const void*)mk_megakernel<64, 4, B, F> : (const void*)mk_megakernel<64, 8, B, F>;
 }
-// One sequence: GEMV tiles on the vector units. Several: the batched instantiation (MFMA tiles).
-static const void* megakernel_for(int dh, int hq, int hk, bool batched) {
-  return batched ? megakernel_for_t<true>(dh, hq / hk) : megakernel_for_t<false>(dh, hq / hk);
+// One sequence: GEMV tiles on the vector units, over bf16 or FP8 weights. Several: the batched
+// instantiation (MFMA tiles, bf16 weights).
+static const void* megakernel_for(int dh, int hq, int hk, bool batched, bool fp8) {
+  if (batched) return megakernel_for_t<true, false>(dh, hq / hk);
+  return fp8 ? megakernel_for_t<false, true>(dh, hq / hk) : megakernel_for_t<false, false>(dh, hq / hk);
 }
 
 hipError_t launch_megakernel(const KernelParams& p, int grid, size_t lds_bytes, hipStream_t stream, bool coop) {
@@ -1985,14 +2127,14 @@ hipError_t launch_megakernel(const KernelParams& p, int grid, size_t lds_bytes, 
   // the watchdog with an error, not in a hang.)
   static const bool coop_env = std::getenv("MK_COOPERATIVE_LAUNCH") != nullptr;
   if (coop || coop_env)
-    return hipLaunchCooperativeKernel(megakernel_for(p.dh, p.hq, p.hk, p.max_seqs > 1), dim3(grid), dim3(NT), args,
+    return hipLaunchCooperativeKernel(megakernel_for(p.dh, p.hq, p.hk, p.max_seqs > 1, p.fp8_weights != 0), dim3(grid), dim3(NT), args,
                                       (unsigned)lds_bytes, stream);
-  return hipLaunchKernel(megakernel_for(p.dh, p.hq, p.hk, p.max_seqs > 1), dim3(grid), dim3(NT), args,
+  return hipLaunchKernel(megakernel_for(p.dh, p.hq, p.hk, p.max_seqs > 1, p.fp8_weights != 0), dim3(grid), dim3(NT), args,
                          (unsigned)lds_bytes, stream);
 }
 
-hipError_t megakernel_occupancy(int* blocks_per_cu, size_t lds_bytes, int dh, int hq, int hk, bool batched) {
-  return hipOccupancyMaxActiveBlocksPerMultiprocessor(blocks_per_cu, megakernel_for(dh, hq, hk, batched), NT, lds_bytes);
+hipError_t megakernel_occupancy(int* blocks_per_cu, size_t lds_bytes, int dh, int hq, int hk, bool batched, bool fp8) {
+  return hipOccupancyMaxActiveBlocksPerMultiprocessor(blocks_per_cu, megakernel_for(dh, hq, hk, batched, fp8), NT, lds_bytes);
 }
 
 // ----------------------------------------------------------------------------- static scratch
@@ -2042,6 +2184,16 @@ hipError_t launch_fill_zero(void* p, size_t bytes, hipStream_t stream) {
 hipError_t launch_repack(const RepackArgs& a, int64_t units, hipStream_t stream) {
   if (units <= 0) return hipSuccess;
   hipLaunchKernelGGL(mk_repack, dim3((unsigned)units), dim3(64), 0, stream, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_row_scales(const RepackArgs& a, int nrows, hipStream_t stream) {
+  hipLaunchKernelGGL(mk_row_scales, dim3((unsigned)nrows), dim3(64), 0, stream, a, nrows);
+  return hipGetLastError();
+}
+
+hipError_t launch_repack_fp8(const RepackArgs& a, int64_t units, hipStream_t stream) {
+  hipLaunchKernelGGL(mk_repack_fp8, dim3((unsigned)units), dim3(64), 0, stream, a);
   return hipGetLastError();
 }
 

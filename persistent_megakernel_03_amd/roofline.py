@@ -28,6 +28,20 @@ def weight_bytes_per_token(m) -> int:
     return b
 
 
+def gemv_rows(m) -> int:
+    """Output rows of every GEMV matrix a step streams (each FP8 row carries one fp32 scale)."""
+    return m.n_layers * ((m.n_q_heads + 2 * m.n_kv_heads) * m.head_dim + m.d_model + 2 * m.d_ffn + m.d_model) + m.vocab
+
+
+def weight_bytes_per_token_fp8(m) -> int:
+    """Weights read per token with FP8 GEMV matrices: one byte per matrix weight plus a 4-byte scale per
+    row; the embedding row, the gains and the bias stay bf16."""
+    b = gemv_weight_bytes(m) // 2 + 4 * gemv_rows(m) + 2 * m.d_model + 2 * (2 * m.n_layers + 1) * m.d_model
+    if m.qkv_bias:
+        b += 2 * m.n_layers * (m.n_q_heads + 2 * m.n_kv_heads) * m.head_dim
+    return b
+
+
 def kv_bytes(batch: int, layers: int, seq: int, head_dim: int, heads: int, elem_bytes: int = 2) -> int:
     """Size of a K+V cache: 2 (K and V) * batch * layers * seq * head_dim * heads * bytes."""
     return 2 * batch * layers * seq * head_dim * heads * elem_bytes
@@ -38,10 +52,11 @@ def kv_read_bytes_per_token(m, ctx: int) -> int:
     return kv_bytes(1, m.n_layers, ctx, m.head_dim, m.n_kv_heads, 2)
 
 
-def step_bytes(m, ctxs) -> int:
+def step_bytes(m, ctxs, fp8: bool = False) -> int:
     """Algorithmic bytes of one decode step over sequences with the given attended lengths:
     the weights once plus each sequence's KV rows."""
-    return weight_bytes_per_token(m) + sum(kv_read_bytes_per_token(m, c) for c in ctxs)
+    w = weight_bytes_per_token_fp8(m) if fp8 else weight_bytes_per_token(m)
+    return w + sum(kv_read_bytes_per_token(m, c) for c in ctxs)
 
 
 def roofline_ms(bytes_: float, peak_gbs: float = MI355X_HBM_PEAK_GBS) -> float:
@@ -66,15 +81,15 @@ def kernel_source_hash() -> str:
 
 
 def profiled_traffic(summary_path: str):
-    """HBM bytes per launch measured with FETCH_SIZE/WRITE_SIZE (scaled by a copy-kernel
-    calibration) as recorded in a profile summary, or None when the summary is missing or the
-    kernel sources have changed since it was taken."""
+    """HBM bytes per decode step measured with FETCH_SIZE/WRITE_SIZE (scaled by a copy-kernel
+    calibration) over a resident launch, as recorded in a profile summary, or None when the summary is
+    missing or the kernel sources have changed since it was taken."""
     import os
     import re
     if not os.path.exists(summary_path):
         return None
     txt = open(summary_path).read()
-    mb = re.search(r"traffic_bytes_per_dispatch = (\d+)", txt)
+    mb = re.search(r"traffic_bytes_per_step = (\d+)", txt)
     mh = re.search(r"source_sha256_16 = ([0-9a-f]{16})", txt)
     if not mb or not mh or mh.group(1) != kernel_source_hash():
         return None

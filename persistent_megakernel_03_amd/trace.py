@@ -38,8 +38,10 @@ def stage_rows(tr):
             if not m.any():
                 continue
             end = float(d[m].max())
+            # a task with no stream of its own (the argmax) records t_streamed at its start: stream 0
+            st = np.maximum(s[m], r[m])
             rows.append(dict(type=t, layer=l, n=int(m.sum()), span=end - prev_end,
-                             handoff=r[m] - np.maximum(q[m], prev_end), stream=s[m] - r[m], epilogue=d[m] - s[m]))
+                             handoff=r[m] - np.maximum(q[m], prev_end), stream=st - r[m], epilogue=d[m] - st))
             prev_end = end
     return rows
 

@@ -161,3 +161,47 @@ def prefilled_case(wl, n_decode, attn_splits=0, device=0, weights=None, capacity
         dec.v_pools[l].copy_(vpool.reshape(-1))
     torch.cuda.synchronize()
     return dec, om, ctx, table, weights
+
+
+def cached_kv(dec, table_row, m, l, p0, p1):
+    kp = dec.k_pools[l].cpu().numpy().view(np.uint16).reshape(-1, m.n_kv_heads, 16, m.head_dim)
+    vp = dec.v_pools[l].cpu().numpy().view(np.uint16).reshape(-1, m.n_kv_heads, 16, m.head_dim)
+    kg = np.stack([kp[table_row[p // 16], :, p % 16] for p in range(p0, p1)])
+    vg = np.stack([vp[table_row[p // 16], :, p % 16] for p in range(p0, p1)])
+    return kg, vg
+
+
+def check_kv(dec, table_row, om, seq, m, p0, p1, layers=None, o32=None):
+    """The cached keys and values of positions [p0, p1). Layer 0 (inputs exact in both: the embedding
+    rows) and every layer of a shallow model: each element within one bf16 ulp of the oracle's (plus
+    1e-5 of the head row's scale), > 99% equal. Deeper layers of a deep model, where fp32 rounding
+    grows through the layers: relative L2 within twice the oracle's fp32 build's (given as o32, floor
+    1e-3), else within the stated 5e-3."""
+    strict_all = m.n_layers <= 4
+    for l in (range(m.n_layers) if layers is None else layers):
+        k_ref, v_ref = om.get_kv(l, seq, p0, p1 - p0)
+        kg, vg = cached_kv(dec, table_row, m, l, p0, p1)
+        if l == 0 or strict_all:
+            for g, r in ((kg, k_ref), (vg, v_ref)):
+                gf, rf = _orc().bf16_to_f64(g), _orc().bf16_to_f64(r)
+                err = np.abs(gf - rf)
+                scale = np.abs(rf).max(axis=-1, keepdims=True)
+                ulp = np.maximum(np.abs(rf), np.abs(gf)) * 2.0 ** -7 + 1e-5 * scale
+                assert (err <= ulp + 1e-30).all(), "layer %d: a cached entry is off by more than one bf16 ulp" % l
+                assert (g == r).mean() > 0.99, "layer %d: only %.4f of the cached entries equal" % (l, (g == r).mean())
+            continue
+        if o32 is not None:
+            k32, v32 = o32.get_kv(l, seq, p0, p1 - p0)
+            bar = max(1e-3, 2.0 * max(rel_l2(_orc().bf16_to_f64(k32), _orc().bf16_to_f64(k_ref)),
+                                      rel_l2(_orc().bf16_to_f64(v32), _orc().bf16_to_f64(v_ref))))
+        else:
+            bar = REL_L2_BAR
+        for g, r, what in ((kg, k_ref, "keys"), (vg, v_ref, "values")):
+            rel = rel_l2(_orc().bf16_to_f64(g), _orc().bf16_to_f64(r))
+            print("  layer %d %s: rel L2 %.3e (bar %.3e)" % (l, what, rel, bar), flush=True)
+            assert rel <= bar, "layer %d: cached %s off by %.3e" % (l, what, rel)
+
+
+def _orc():
+    import oracle
+    return oracle

@@ -13,7 +13,9 @@
 
 namespace mk {  // the device-side entry points live in the kernel source, which this build leaves out
 hipError_t launch_megakernel(const KernelParams&, int, size_t, hipStream_t, bool) { return hipErrorNotSupported; }
-hipError_t megakernel_occupancy(int*, size_t, int, int, int, bool) { return hipErrorNotSupported; }
+hipError_t megakernel_occupancy(int*, size_t, int, int, int, bool, bool) { return hipErrorNotSupported; }
+hipError_t launch_row_scales(const RepackArgs&, int, hipStream_t) { return hipErrorNotSupported; }
+hipError_t launch_repack_fp8(const RepackArgs&, int64_t, hipStream_t) { return hipErrorNotSupported; }
 hipError_t launch_repack(const RepackArgs&, int64_t, hipStream_t) { return hipErrorNotSupported; }
 hipError_t launch_repack_bias(const uint16_t*, const uint16_t*, const uint16_t*, int, int, int, uint16_t*, hipStream_t) {
   return hipErrorNotSupported;

@@ -178,6 +178,40 @@ def test_prefill_rows_config(L):
         assert e.value.status == -2
 
 
+@pytest.mark.parametrize("shape,blocks", [(si.TINY, 3), (si.QWEN05B, 35), (si.LLAMA8B, 35)])
+def test_fp8_weights_graph(L, shape, blocks):
+    # FP8 weights: half-size tiles (16 codes per lane per unit, units per row group
+    # padded to even), one fp32 scale per packed GEMV row; the graph validates and simulates
+    c = cfg_for(shape, blocks, blocks)
+    c.weight_format = 1
+    ctx = mk.mk_create_host(c, 256)
+    base = mk.mk_create_host(cfg_for(shape, blocks, blocks), 256)
+    try:
+        mk.mk_graph_validate(ctx)
+        mk.mk_graph_simulate(ctx, 3, 1)
+        i8, i16 = mk.mk_graph_stats(ctx), mk.mk_graph_stats(base)
+        assert i8.hash != i16.hash
+        m = shape
+        rows = m.n_layers * ((m.n_q_heads + 2 * m.n_kv_heads) * m.head_dim + m.d_model + 2 * m.d_ffn + m.d_model) + m.vocab
+        assert i8.weight_bytes * 2 == i16.weight_bytes    # these shapes need no extra padding
+        w8, _, _ = mk.mk_workspace_size(ctx)
+        w16, _, _ = mk.mk_workspace_size(base)
+        assert w8 - i8.weight_bytes >= (w16 - i16.weight_bytes) + 4 * rows   # the row scales
+    finally:
+        mk.mk_destroy(ctx)
+        mk.mk_destroy(base)
+    for n_seqs, rows_pf in ((4, 0), (1, 16)):     # batched contexts and chunked prefill keep bf16
+        c = mk.make_config(si.TINY, max_seqs=n_seqs, max_blocks_per_seq=3, num_blocks=3 * n_seqs,
+                           prefill_rows=rows_pf, weight_format=1)
+        with pytest.raises(mk.MKError) as e:
+            mk.mk_create_host(c, 64)
+        assert e.value.status == -2
+    c = cfg_for(si.TINY, 3, 3)
+    c.weight_format = 2
+    with pytest.raises(mk.MKError):
+        mk.mk_create_host(c, 64)
+
+
 def test_host_context_refuses_device_calls(L):
     ctx = mk.mk_create_host(cfg_for(si.TINY, 3, 3), 16)
     try:
