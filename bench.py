@@ -263,11 +263,14 @@ def fp8_leg(mk, torch, np, m, weights, prompt, nb, K, W, rf, ms_bf16):
     achieved = bytes_avg / (ms * 1e-3) / 1e9
     info = mk.mk_graph_stats(d8.ctx)
     finish(d8)
+    traffic = None
+    if m.name == "llama8b":
+        traffic = rf.profiled_traffic(os.path.join(ROOT, "profiles", "mk_megakernel_llama8b_b1_fp8_decode.md"))
     log("fp8 weights: resident %.4f ms/token (%.1f tok/s), %.1f GB/s (%.1f%% of %.0f GB/s); %.2fx the bf16 decode"
         % (ms, 1e3 / ms, achieved, 100 * achieved / rf.MI355X_HBM_PEAK_GBS, rf.MI355X_HBM_PEAK_GBS, ms_bf16 / ms))
     return {"ms_per_token": round(ms, 5), "tokens_per_s": round(1e3 / ms, 2), "steps": K,
             "weight_bytes_per_token": rf.weight_bytes_per_token_fp8(m), "graph_hash": "0x%016x" % info.hash,
-            "roofline": roofline_obj(rf, achieved, None, bytes_avg, K, ms_launch, "mk_megakernel, FP8 weights"),
+            "roofline": roofline_obj(rf, achieved, traffic, bytes_avg, K, ms_launch, "mk_megakernel, FP8 weights"),
             "speedup_vs_bf16": round(ms_bf16 / ms, 3),
             "what": "E4M3 weight codes with one power-of-two scale per output row, decoded in the GEMV tile "
                     "(fp32 accumulation); the same prompt and positions as the bf16 decode"}
