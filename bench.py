@@ -320,6 +320,9 @@ def bench_batched(args, wl):
     dec.tokens[:n].copy_(first)
     for _ in range(W):
         dec.step(dec.tokens, n)
+    # and one resident launch: the process's first cooperative launch of a kernel pays a one-time setup
+    # (about 5 ms for the batched kernel), which is not a step's cost
+    dec.decode_n(first, max(W, 1), n)
     dec.sync_check()
     stream = torch.cuda.current_stream(dec.dev)
     ms_res, ms_launch, per_step, same = decode_legs(torch, dec, n, K, first, lambda: dec.set_ctx_lens(ctx), stream)
