@@ -179,6 +179,34 @@ def trace_leg(dec, first, positions):
     return res
 
 
+def dynamic_leg(torch, np, dec, g0, P, n, stream):
+    """The same n steps from position P, one launch per step, with the tasks scheduled ahead of time
+    (mk_decode_step) and at run time from the device's ready queue (mk_decode_step_dynamic); both must
+    give the same tokens. Returns {ms per token each way, tokens equal}."""
+    res = {}
+    toks = {}
+    for name, fn in (("static", dec.step), ("dynamic", dec.step_dynamic)):
+        dec.set_ctx_lens([P])
+        t = torch.zeros((n + 1, 1), dtype=torch.int32, device=dec.dev)
+        t[0].copy_(g0)
+        rows = iter(range(n))
+
+        def one(fn=fn, t=t, rows=rows):
+            i = next(rows)
+            fn(t[i], 1, t[i + 1])
+
+        res[name] = timed_once(torch, stream, lambda: [one() for _ in range(n)]) / n
+        dec.sync_check()
+        toks[name] = t
+    same = bool(torch.equal(toks["static"], toks["dynamic"]))
+    log("scheduling: ahead of time %.4f ms/token, at run time (ready queue) %.4f ms/token over %d steps; tokens "
+        "equal: %s" % (res["static"], res["dynamic"], n, same))
+    return {"static_ms_per_token": round(res["static"], 5), "dynamic_ms_per_token": round(res["dynamic"], 5),
+            "steps": n, "tokens_equal": same,
+            "what": "one launch per step both ways: per-CU queues built ahead of time, or a device-side ready "
+                    "queue fed by event completion (mk_decode_step_dynamic)"}
+
+
 def prefill_leg(mk, torch, np, m, weights, prompt, nb, dec, g0, rf):
     """Time to the first token for the workload's prompt, two ways: one decode step per prompt token
     (the context `dec`, one-sequence graph) and chunked through the 16-row batched graph (a second
@@ -393,6 +421,8 @@ def main():
     ap.add_argument("--staged-steps", type=int, default=64, help="steps of the stage-sliced comparison run (0: skip it)")
     ap.add_argument("--no-prefill", action="store_true", help="skip the time-to-first-token comparison")
     ap.add_argument("--no-fp8", action="store_true", help="skip the FP8-weights decode")
+    ap.add_argument("--dynamic-steps", type=int, default=64,
+                    help="steps of the run-time scheduling comparison (0: skip it)")
     ap.add_argument("--trace-summary", action="store_true",
                     help="after the timed legs, trace one step at three positions and report per-stage times")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -485,6 +515,7 @@ def main():
                         "removed_by_resident_ms_per_token": round(ms_fused_same - ms_res_same, 5),
                         "what": "the same kernel and task graph launched once per dependency stage (stop-and-go), "
                                 "once per token, and once for all the steps"}
+    dynamic = dynamic_leg(torch, np, dec, g0, P, min(K, args.dynamic_steps), stream) if args.dynamic_steps > 0 else None
     task_trace = trace_leg(dec, g0, spread(P + 1, P + K - 1, 3)) if args.trace_summary else None
     prefill = None if args.no_prefill else prefill_leg(mk, torch, np, m, weights, prompt, nb, dec, g0, rf)
     finish(dec)
@@ -530,6 +561,8 @@ def main():
         "cpu_baseline": cpu,
         "pass_to_pass": pass_to_pass,
     }
+    if dynamic is not None:
+        out["dynamic_schedule"] = dynamic
     if prefill is not None:
         out["prefill"] = prefill
     if fp8 is not None:

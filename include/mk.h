@@ -223,6 +223,23 @@ mk_status mk_decode_n(mk_ctx* ctx, const int32_t* d_tokens_in, int n_seqs, int n
 mk_status mk_decode_step_static(mk_ctx* ctx, const int32_t* d_tokens_in, int n_seqs, int32_t* d_tokens_out,
                                 void* stream);
 
+/* The same decode step as mk_decode_step with the tasks scheduled at run time
+ * instead of ahead of time (the just-in-time mode of "MPK: A Compiler and
+ * Runtime for Mega-Kernelizing Tensor Programs", analogy 3; the event-driven
+ * runtime of "LLMs in einen MegaKernel kompilieren", "Part 2. Runtime"). No
+ * workgroup owns a queue: each takes the next slot of one device-wide ready
+ * queue and runs the task that lands there. A task's completion counts toward
+ * the event it signals; the completion that finishes an event appends the
+ * tasks that wait on it. The tasks and their arithmetic are those of
+ * mk_decode_step, so tokens and logits are identical; only which CU runs a
+ * task, and when, differ.
+ *   - One-sequence contexts with bf16 weights; n_seqs must be 1.
+ *   - Arguments and errors: as mk_decode_step, plus MK_ERR_UNSUPPORTED for
+ *     other contexts. A wait on an empty queue slot is watched like every
+ *     other wait. Asynchronous. */
+mk_status mk_decode_step_dynamic(mk_ctx* ctx, const int32_t* d_tokens_in, int n_seqs, int32_t* d_tokens_out,
+                                 void* stream);
+
 /* The same decode step as mk_decode_step, launched as one kernel dispatch per dependency stage
  * (QKV, attention, O projection, gate/up and down of each layer, then the LM head and the argmax):
  * the same kernel, task graph and arithmetic, so the results are identical. Each dispatch runs only

@@ -52,7 +52,7 @@ class mk_graph_info(ctypes.Structure):
 
 
 EXPORTS = ["mk_create", "mk_create_host", "mk_workspace_size", "mk_bind_memory", "mk_load_weights", "mk_decode_step",
-           "mk_decode_n", "mk_decode_step_static", "mk_decode_step_staged", "mk_prefill", "mk_read_fp8_weights", "mk_read_logits",
+           "mk_decode_n", "mk_decode_step_static", "mk_decode_step_dynamic", "mk_decode_step_staged", "mk_prefill", "mk_read_fp8_weights", "mk_read_logits",
            "mk_sync_check", "mk_graph_stats", "mk_graph_validate",
            "mk_graph_simulate", "mk_graph_corrupt", "mk_set_trace", "mk_destroy", "mk_status_str", "mk_last_error"]
 
@@ -89,6 +89,7 @@ def lib():
             "mk_decode_n": [vp, vp, ctypes.c_int, ctypes.c_int, vp, vp],
             "mk_decode_step_static": [vp, vp, ctypes.c_int, vp, vp],
             "mk_decode_step_staged": [vp, vp, ctypes.c_int, vp, vp],
+            "mk_decode_step_dynamic": [vp, vp, ctypes.c_int, vp, vp],
             "mk_prefill": [vp, ctypes.c_int, ctypes.POINTER(i32), ctypes.c_int, vp, vp],
             "mk_read_fp8_weights": [vp, ctypes.c_char_p, vp, vp, vp],
             "mk_read_logits": [vp, ctypes.c_int, ctypes.POINTER(ctypes.c_float), sz, vp],
@@ -185,6 +186,10 @@ def mk_decode_n(ctx, tokens_in, n_seqs, n_steps, tokens_out, stream=None):
 
 def mk_decode_step_static(ctx, tokens_in, n_seqs, tokens_out, stream=None):
     _check(lib().mk_decode_step_static(ctx, _vp(tokens_in), n_seqs, _vp(tokens_out), _vp(stream)))
+
+
+def mk_decode_step_dynamic(ctx, tokens_in, n_seqs, tokens_out, stream=None):
+    _check(lib().mk_decode_step_dynamic(ctx, _vp(tokens_in), n_seqs, _vp(tokens_out), _vp(stream)))
 
 
 def mk_decode_step_staged(ctx, tokens_in, n_seqs, tokens_out, stream=None):
@@ -319,6 +324,11 @@ class Decoder:
             tokens_out = self.torch.empty((n_steps, n_seqs), dtype=self.torch.int32, device=self.dev)
         mk_decode_n(self.ctx, tokens_in, n_seqs, n_steps, tokens_out, self.stream_ptr())
         return tokens_out
+
+    def step_dynamic(self, tokens_in, n_seqs=1, tokens_out=None):
+        """The same step with its tasks taken from a device-side ready queue at run time."""
+        mk_decode_step_dynamic(self.ctx, tokens_in, n_seqs, tokens_out if tokens_out is not None else tokens_in,
+                               self.stream_ptr())
 
     def step_staged(self, tokens_in, n_seqs=1, tokens_out=None):
         """The same step as one kernel dispatch per dependency stage (to measure pass-to-pass gaps)."""

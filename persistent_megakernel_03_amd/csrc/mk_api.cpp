@@ -23,6 +23,7 @@ hipError_t megakernel_occupancy(int* blocks_per_cu, size_t lds_bytes, int dh, in
 hipError_t launch_repack(const RepackArgs& a, int64_t units, hipStream_t stream);
 hipError_t launch_row_scales(const RepackArgs& a, int nrows, hipStream_t stream);
 hipError_t launch_repack_fp8(const RepackArgs& a, int64_t units, hipStream_t stream);
+hipError_t launch_jit_reset(int32_t* w, int n_events, int n_tasks, int n0, hipStream_t stream);
 hipError_t launch_repack_bias(const uint16_t* bq, const uint16_t* bk, const uint16_t* bv, int G, int dh, int nrows,
                               uint16_t* out, hipStream_t stream);
 hipError_t static_scratch_address(int device, void** out);
@@ -423,6 +424,13 @@ mk_status mk_bind_memory(mk_ctx* c, void* d_weights, void* const* d_k_pools, voi
     if ((e = up(h.sl.geoms, h.geoms, sizeof(h.geoms))) != hipSuccess) return e;
     if ((e = up(h.sl.rope, c->rope_host.data(), c->rope_host.size() * 4)) != hipSuccess) return e;
     if ((e = up(h.sl.pools, c->pool_table.data(), c->pool_table.size() * 8)) != hipSuccess) return e;
+    {  // dynamic scheduling tables: task -> event, then per event producers, first and end consumer
+      std::vector<int32_t> jt(h.jit_task_ev);
+      jt.insert(jt.end(), h.jit_ev_n.begin(), h.jit_ev_n.end());
+      jt.insert(jt.end(), h.jit_ev_c0.begin(), h.jit_ev_c0.end());
+      jt.insert(jt.end(), h.jit_ev_c1.begin(), h.jit_ev_c1.end());
+      if (!jt.empty() && (e = up(h.sl.jit_tab, jt.data(), jt.size() * 4)) != hipSuccess) return e;
+    }
     if ((e = hipMemset(S + h.sl.err, 0, E_COUNT * 4)) != hipSuccess) return e;
     return clear_working(h, S);
   };
@@ -530,6 +538,32 @@ mk_status mk_decode_step_static(mk_ctx* c, const int32_t* d_tokens_in, int n_seq
   p.epoch = 1;
   p.task_lo = 0;
   p.task_hi = (int32_t)g.tasks.size();
+  HIPCHK(launch_megakernel(p, g.n_cus, (size_t)g.lds_bytes, st, false));
+  return MK_OK;
+}
+
+mk_status mk_decode_step_dynamic(mk_ctx* c, const int32_t* d_tokens_in, int n_seqs, int32_t* d_tokens_out, void* stream) {
+  if (!c || !d_tokens_in || !d_tokens_out) return fail(MK_ERR_INVALID_ARG, "null argument");
+  if (!c->bound || !c->loaded) return fail(MK_ERR_STATE, "bind memory and load weights before decoding");
+  if (n_seqs != 1) return fail(MK_ERR_INVALID_ARG, "n_seqs must be 1");
+  const HostGraph& g = c->g;
+  if (!g.jit_ok || g.cfg.weight_format != MK_WEIGHTS_BF16)
+    return fail(MK_ERR_UNSUPPORTED, "dynamic scheduling runs one-sequence contexts with bf16 weights");
+  DeviceGuard dg(c->device);
+  hipStream_t st = (hipStream_t)stream;
+  if (mk_status s = reserve_epochs(g, c->d_scratch, c->epoch, 1, st)) return s;
+  KernelParams p = make_params(c, c->d_scratch);
+  p.tokens_in = d_tokens_in;
+  p.tokens_out = d_tokens_out;
+  p.n_active = 1;
+  p.n_steps = 1;
+  p.epoch = ++c->epoch;
+  p.task_lo = 0;
+  p.task_hi = (int32_t)g.tasks.size();
+  p.jit_tab = (const int32_t*)(c->d_scratch + g.sl.jit_tab);
+  p.jit_work = (int32_t*)(c->d_scratch + g.sl.jit_work);
+  p.n_events = (int32_t)g.events.size();
+  HIPCHK(launch_jit_reset(p.jit_work, p.n_events, p.task_hi, g.jit_n0, st));
   HIPCHK(launch_megakernel(p, g.n_cus, (size_t)g.lds_bytes, st, false));
   return MK_OK;
 }

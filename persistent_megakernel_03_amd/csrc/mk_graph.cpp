@@ -556,6 +556,35 @@ std::string build_graph(const mk_model_config& c, int n_cus, HostGraph& g) {
     g.tasks[t].sig_n = (int32_t)b.task_sig[t].size();
     for (auto& s : b.task_sig[t]) g.sig_slots.push_back(g.events[s.first].slot0 + s.second);
   }
+  // ---- dynamic scheduling tables: a task's completion counts toward the one event it signals; the
+  // event's consumers (the tasks that wait on it) are contiguous in the global order, and the tasks
+  // that wait on nothing open the step
+  {
+    const int T = (int)g.tasks.size(), E = (int)g.events.size();
+    g.jit_task_ev.assign(T, -1);
+    g.jit_ev_n.assign(E, 0);
+    g.jit_ev_c0.assign(E, -1);
+    g.jit_ev_c1.assign(E, -1);
+    bool ok = S == 1;
+    for (int t = 0; t < T; ++t) {
+      if (b.task_sig[t].size() > 1) ok = false;
+      if (!b.task_sig[t].empty()) g.jit_task_ev[t] = b.task_sig[t][0].first;
+      const int e = g.tasks[t].wait_ev;
+      if (e < 0) {
+        if (t != g.jit_n0) ok = false;  // the opening tasks form a prefix
+        g.jit_n0 = t + 1;
+        continue;
+      }
+      if (g.jit_ev_c0[e] < 0) g.jit_ev_c0[e] = t;
+      else if (g.jit_ev_c1[e] != t) ok = false;  // consumers must be contiguous
+      g.jit_ev_c1[e] = t + 1;
+    }
+    for (int e = 0; e < E; ++e) {
+      g.jit_ev_n[e] = b.ev_producers[e];
+      if (g.jit_ev_c0[e] < 0) g.jit_ev_c0[e] = g.jit_ev_c1[e] = 0;
+    }
+    g.jit_ok = ok;
+  }
   // the O and down tasks keep their residual rows in registers: at most 4 per thread of 512
   for (const TaskDesc& td : g.tasks)
     if (S == 1 && (td.type == T_OPROJ || td.type == T_DOWN) && td.row1 - td.row0 > 4 * 512) return "residual task too tall";
@@ -606,6 +635,8 @@ std::string build_graph(const mk_model_config& c, int n_cus, HostGraph& g) {
   g.sl.tokbuf = take((int64_t)std::max(g.max_pos, 64) * 4);
   g.sl.tokout = take(64 * 4);
   g.sl.pools = take((int64_t)2 * L * 8);
+  g.sl.jit_tab = take(((int64_t)g.tasks.size() + 3 * (int64_t)g.events.size()) * 4);
+  g.sl.jit_work = take((2 + (int64_t)g.events.size() + (int64_t)g.tasks.size()) * 4);
   if (S > 1) {  // chunked prefill: the rows of a step are consecutive positions of one sequence
     g.sl.pf_ptab = take((int64_t)S * c.max_blocks_per_seq * 4);
     g.sl.pf_ctx = take((int64_t)(g.max_pos / S + 2) * 16 * 4);
@@ -751,7 +782,69 @@ uint64_t sm_next(uint64_t& s) {
 }
 }  // namespace
 
+// The dynamic schedule of one step (what mk_decode_step_dynamic runs): tasks leave a FIFO ready queue
+// (filled first with the opening tasks) onto at most n_cus workgroups and finish in a random order;
+// a finished task counts toward its event, and the event's last producer appends the event's consumers.
+// A task of an ordered group (attention) finishes only after the group's earlier members. Checks that
+// every task runs exactly once, that no task starts before every earlier-positioned writer of an
+// element it reads has finished (partials excepted: they are polled), and that the queue never stalls.
+static std::string simulate_dynamic(const HostGraph& g, uint64_t seed) {
+  const int nt = (int)g.tasks.size(), ne = (int)g.events.size();
+  if (!g.jit_ok) return "";
+  std::vector<std::vector<std::vector<int>>> writers(S_COUNT);
+  for (int b = 0; b < S_COUNT; ++b) writers[b].resize(g.sym_size[b]);
+  for (int t = 0; t < nt; ++t)
+    for (const auto* as : {&g.acc[t], &g.comb_acc[t]})
+      for (const Access& a : *as)
+        if (a.write)
+          for (int64_t e = a.lo; e < a.hi; ++e) writers[a.buf][e].push_back(t);
+  std::vector<int> queue, cnt(ne, 0), done(nt, 0), started(nt, 0), running;
+  for (int t = 0; t < g.jit_n0; ++t) queue.push_back(t);
+  size_t head = 0;
+  uint64_t rng = seed * 0x9E3779B97F4A7C15ULL + 1;
+  auto rnd = [&]() { rng ^= rng << 13; rng ^= rng >> 7; rng ^= rng << 17; return rng; };
+  int finished = 0;
+  while (finished < nt) {
+    while ((int)running.size() < g.n_cus && head < queue.size()) {
+      const int t = queue[head++];
+      if (t < 0 || t >= nt || started[t]++) return "dynamic schedule: task " + std::to_string(t) + " queued twice";
+      for (const auto* as : {&g.acc[t], &g.comb_acc[t]})
+        for (const Access& a : *as) {
+          if (a.write || a.buf == S_PART || a.buf == S_BPART) continue;
+          for (int64_t e = a.lo; e < a.hi; ++e)
+            for (int w : writers[a.buf][e])
+              if (w < t && !done[w])
+                return "dynamic schedule: task " + std::to_string(t) + " started before its producer " + std::to_string(w);
+        }
+      running.push_back(t);
+    }
+    std::vector<int> can;
+    for (size_t i = 0; i < running.size(); ++i) {
+      const int t = running[i], gi = g.task_group[t];
+      bool ok = true;
+      if (gi >= 0 && g.group_ordered[gi])
+        for (int m = 0; m < t && ok; ++m)
+          if (g.task_group[m] == gi && !done[m]) ok = false;
+      if (ok) can.push_back((int)i);
+    }
+    if (can.empty()) return "dynamic schedule stalls with " + std::to_string(running.size()) + " tasks running";
+    const int i = can[rnd() % can.size()], t = running[i];
+    running.erase(running.begin() + i);
+    done[t] = 1;
+    ++finished;
+    const int e = g.jit_task_ev[t];
+    if (e >= 0 && ++cnt[e] == g.jit_ev_n[e])
+      for (int c = g.jit_ev_c0[e]; c < g.jit_ev_c1[e]; ++c) queue.push_back(c);
+  }
+  if ((int)queue.size() != nt) return "dynamic schedule: " + std::to_string(queue.size()) + " tasks queued of " + std::to_string(nt);
+  return "";
+}
+
 std::string simulate_graph(const HostGraph& g, uint64_t seed, int n_steps) {
+  if (n_steps > 0) {
+    const std::string d = simulate_dynamic(g, seed);
+    if (!d.empty()) return d;
+  }
   const int nt = (int)g.tasks.size();
   const int ng = (int)g.group_size.size();
   // Static writer/reader lists per element; a task's second-phase accesses count at its position.

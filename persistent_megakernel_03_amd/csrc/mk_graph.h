@@ -100,6 +100,10 @@ struct ScratchLayout {
   // batched graphs, chunked prefill: the rows' page table (copies of one sequence's row), their context
   // lengths (16 per chunk), the rows' logits and tokens
   int64_t pf_ptab = -1, pf_ctx = -1, pf_logits = -1, pf_tok = -1;
+  // dynamic scheduling: the read-only tables (task -> event [T], event -> producers, first and end
+  // consumer [3][E]) and the working memory a launch resets (ready-queue head and tail, per-event
+  // counts [E], the queue of task indices [T])
+  int64_t jit_tab = -1, jit_work = -1;
   int64_t total;
 };
 
@@ -179,6 +183,9 @@ struct KernelParams {
   int32_t attn_min_blocks;    // cache blocks per attention task at least (fewer tasks get blocks)
   int32_t prefill;            // batched graphs: 1 = the rows are consecutive positions of one sequence
   int32_t fp8_weights;        // 1: GEMV tiles hold E4M3 codes, row r's products scale by wscale[r]
+  const int32_t* jit_tab;     // dynamic scheduling tables (see ScratchLayout::jit_tab), or nullptr
+  int32_t* jit_work;          // dynamic scheduling working memory
+  int32_t n_events;
   const float* wscale;        // FP8 weights: 2^e of every packed GEMV row (TaskDesc::a1 indexes it)
   TraceRec* trace;            // per-task timestamps of the last step, or nullptr
 };

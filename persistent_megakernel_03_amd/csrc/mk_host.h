@@ -53,6 +53,12 @@ struct HostGraph {
   WeightLayout wl{};
   ScratchLayout sl{};
   int64_t sym_size[S_COUNT]{};
+  // Dynamic scheduling (one-sequence graphs): per task, the event its completion counts toward (-1:
+  // none); per event, its producer count and its consumer tasks [c0, c1), contiguous in the global
+  // order; the tasks ready when a step starts are [0, jit_n0).
+  std::vector<int32_t> jit_task_ev, jit_ev_n, jit_ev_c0, jit_ev_c1;
+  int32_t jit_n0 = 0;
+  bool jit_ok = false;
 };
 
 // Builds the graph; returns an empty string on success, else the reason.

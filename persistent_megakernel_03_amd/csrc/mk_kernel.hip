@@ -141,6 +141,8 @@ struct Ctl {
   uint64_t kred[NW];
   uint64_t t_ready;         // trace: when the running task's inputs were all present
   uint64_t t_streamed;      // trace: when its own streaming ended
+  int32_t jtask;            // dynamic scheduling: the task taken from the ready queue (< 0: none)
+  int32_t jpush, jc0, jn;   // the consumer range this task's completion released, and its queue slots
 };
 
 __device__ __forceinline__ float block_sum(float v, Ctl* ctl) {
@@ -275,8 +277,10 @@ __device__ __forceinline__ void poll_finish(const KernelParams& p, uint32_t ep, 
   }
 }
 
-// The watchdog's name for a wait on the next step's token (event indices name the other waits).
+// The watchdog's names for a wait on the next step's token and for a wait on a slot of the ready queue
+// (event indices name the other waits).
 constexpr uint32_t kWhatToken = 0xFFFFFFFEu;
+constexpr uint32_t kWhatQueue = 0xFFFFFFFDu;
 
 // A whole vector src[0, n): wave w polls the contiguous words [w * chunk, (w + 1) * chunk), chunk =
 // n / 8 rounded up to 64, lane l taking words l, l + 64, ..., so each load is one coalesced 512-byte
@@ -1846,7 +1850,13 @@ __device__ __forceinline__ void task_argmax(const KernelParams& p, uint32_t ep, 
 // One instantiation per (head dim, query heads per KV head rounded up to 2, 4 or 8): the
 // attention tile keeps GMAX x 8 query values and accumulators per lane in registers, and a
 // kernel's register budget is set by its largest path.
-template <int DH, int GMAX, bool BATCHED, bool FP8>
+// JIT: dynamic scheduling. Instead of walking its own queue, a workgroup takes the next slot of one
+// device-wide ready queue and runs the task that lands there. A task's completion counts toward the
+// one event it signals; the completion that finishes the event appends the event's consumer tasks
+// (contiguous in the global order) to the queue. The tasks that wait on nothing fill its first slots.
+// Slots are taken in order and a task waits only on tasks appended before it (attention merges on the
+// layer's earlier attention tasks), all of which some workgroup has already taken: every wait ends.
+template <int DH, int GMAX, bool BATCHED, bool FP8, bool JIT>
 __global__ __launch_bounds__(NT, 1) void mk_megakernel(KernelParams p) {
   extern __shared__ __attribute__((aligned(16))) unsigned char lds_raw[];
   static_assert(sizeof(Ctl) <= 1024, "control block fits its 1 KB");
@@ -1864,6 +1874,7 @@ __global__ __launch_bounds__(NT, 1) void mk_megakernel(KernelParams p) {
   int q0 = p.queue_off[cu], q1 = p.queue_off[cu + 1];
   while (q0 < q1 && p.queue_idx[q0] < p.task_lo) ++q0;
   while (q1 > q0 && p.queue_idx[q1 - 1] >= p.task_hi) --q1;
+  if constexpr (JIT) q0 = q1 = 0;  // no static queue: the loop below runs until the ready queue is done
   if (threadIdx.x < G_COUNT * (int)(sizeof(GemvGeom) / 4))
     ((int32_t*)ctl->geoms)[threadIdx.x] = ((const int32_t*)p.geoms)[threadIdx.x];
   for (int i = threadIdx.x; i < p.n_layers; i += NT) {
@@ -1876,6 +1887,7 @@ __global__ __launch_bounds__(NT, 1) void mk_megakernel(KernelParams p) {
     const int k = i >> 4, w = i & 15;
     ((int32_t*)&tq[k])[w] = ((const int32_t*)&p.tasks[p.queue_idx[q0 + k]])[w];
   }
+  if constexpr (JIT) q1 = 0x7FFFFFFF;
   WPipe wp;
   bool staged = false;  // this wave's LDS stage holds the next GEMV task's units
   // Steps run one after another, each with its own epoch. Every task of a step is an ancestor of the
@@ -1914,7 +1926,37 @@ __global__ __launch_bounds__(NT, 1) void mk_megakernel(KernelParams p) {
       }
       bar();
     }
-    const TaskDesc t = tq[qi - q0];
+    int tix = 0;  // JIT: the task's index in the global order
+    if constexpr (JIT) {
+      if (threadIdx.x == 0) {
+        int32_t* work = p.jit_work;
+        const int slot = __hip_atomic_fetch_add(&work[0], 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        int v = -1;  // -1: every task is taken; -2: the kernel is aborting
+        if (slot < p.task_hi) {
+          const uint32_t* qs = (const uint32_t*)(work + 2 + p.n_events + slot);
+          const uint64_t w0 = __builtin_amdgcn_s_memrealtime();
+          for (uint32_t pass = 1;; ++pass) {
+            v = (int)ldc(qs);
+            if (v >= 0) break;
+            if ((pass & 7u) == 0u) {
+              if (ldc(&p.err[E_ABORT])) { v = -2; break; }
+              if (__builtin_amdgcn_s_memrealtime() - w0 > p.watchdog_ticks) {
+                raise_error(p, ERR_TIMEOUT, kWhatQueue, ep);
+                stc(&p.err[E_ABORT], 1u);
+                v = -2;
+                break;
+              }
+            }
+            __builtin_amdgcn_s_sleep(1);
+          }
+        }
+        ctl->jtask = v;
+      }
+      bar();
+      tix = __builtin_amdgcn_readfirstlane(ctl->jtask);
+      if (tix < 0) break;
+    }
+    const TaskDesc t = JIT ? p.tasks[tix] : tq[qi - q0];
     // Only the LM head's partial maxima travel under flags (the argmax task waits for them); every
     // other input is a tagged activation that its consumer polls for inside the task.
     const int my_sig = (t.type == T_LMHEAD && (int)threadIdx.x < t.sig_n) ? p.sig_slots[t.sig_off + threadIdx.x] : -1;
@@ -1939,7 +1981,7 @@ __global__ __launch_bounds__(NT, 1) void mk_megakernel(KernelParams p) {
     } else if constexpr (BATCHED) {
       gemv_task_b(p, ep, step, t, lds, ctl, pools);
     } else {
-      gemv_task<FP8>(p, ep, step, t, lds, ctl, wp, pools, qi + 1 < q1 ? &tq[qi + 1 - q0] : nullptr, staged);
+      gemv_task<FP8>(p, ep, step, t, lds, ctl, wp, pools, (!JIT && qi + 1 < q1) ? &tq[qi + 1 - q0] : nullptr, staged);
     }
     // The LM head's stores must be complete before its flags go out; other tasks' consumers check
     // the tags themselves.
@@ -1958,7 +2000,35 @@ __global__ __launch_bounds__(NT, 1) void mk_megakernel(KernelParams p) {
       r.epoch = ep;
       r.xcc = __builtin_amdgcn_s_getreg(kHwRegXccId) & 0xFu;  // the XCD this CU sits on
       r.step = (uint32_t)step;
-      p.trace[p.queue_idx[qi]] = r;
+      p.trace[JIT ? tix : p.queue_idx[qi]] = r;
+    }
+    if constexpr (JIT) {
+      // (after the trace record, so that a consumer never starts before its producer's recorded end)
+      // count this completion toward its event; the one that finishes the event appends the event's
+      // consumers to the ready queue (one slot range, written by the whole workgroup)
+      if (threadIdx.x == 0) {
+        int push = -1, c0 = 0, n = 0;
+        const int e = p.jit_tab[tix];
+        if (e >= 0) {
+          __threadfence();
+          const int32_t* evt = p.jit_tab + p.task_hi;  // [3][E]: producers, first consumer, end
+          const int old = __hip_atomic_fetch_add(&p.jit_work[2 + e], 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+          if (old + 1 == evt[e]) {
+            c0 = evt[p.n_events + e];
+            n = evt[2 * p.n_events + e] - c0;
+            if (n > 0) push = __hip_atomic_fetch_add(&p.jit_work[1], n, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+          }
+        }
+        ctl->jpush = push;
+        ctl->jc0 = c0;
+        ctl->jn = n;
+      }
+      bar();
+      const int push = ctl->jpush;
+      if (push >= 0) {
+        uint32_t* q = (uint32_t*)(p.jit_work + 2 + p.n_events);
+        for (int i = threadIdx.x; i < ctl->jn; i += NT) stc(&q[push + i], (uint32_t)(ctl->jc0 + i));
+      }
     }
     if (++qi == q1 && ++step < p.n_steps) qi = q0;  // the next step walks the queue again
   }
@@ -2103,17 +2173,20 @@ extern "C" __global__ __launch_bounds__(256) void mk_repack_bias(const uint16_t*
 }
 
 // ----------------------------------------------------------------------------- host-side launchers
-template <bool B, bool F>
+template <bool B, bool F, bool J>
 static const void* megakernel_for_t(int dh, int g) {
   if (dh == 128)
-    return g <= 2 ? (const void*)mk_megakernel<128, 2, B, F> : g <= 4 ? (const void*)mk_megakernel<128, 4, B, F> : (const void*)mk_megakernel<128, 8, B, F>;
-  return g <= 2 ? (const void*)mk_megakernel<64, 2, B, F> : g <= 4 ? (const void*)mk_megakernel<64, 4, B, F> : (const void*)mk_megakernel<64, 8, B, F>;
+    return g <= 2 ? (const void*)mk_megakernel<128, 2, B, F, J> : g <= 4 ? (const void*)mk_megakernel<128, 4, B, F, J>
+                                                                         : (const void*)mk_megakernel<128, 8, B, F, J>;
+  return g <= 2 ? (const void*)mk_megakernel<64, 2, B, F, J> : g <= 4 ? (const void*)mk_megakernel<64, 4, B, F, J>
+                                                                       : (const void*)mk_megakernel<64, 8, B, F, J>;
 }
-// One sequence: GEMV tiles on the vector units, over bf16 or FP8 weights. Several: the batched
-// instantiation (MFMA tiles, bf16 weights).
-static const void* megakernel_for(int dh, int hq, int hk, bool batched, bool fp8) {
-  if (batched) return megakernel_for_t<true, false>(dh, hq / hk);
-  return fp8 ? megakernel_for_t<false, true>(dh, hq / hk) : megakernel_for_t<false, false>(dh, hq / hk);
+// One sequence: GEMV tiles on the vector units, over bf16 or FP8 weights, from static queues or (bf16)
+// the ready queue. Several: the batched instantiation (MFMA tiles, bf16 weights).
+static const void* megakernel_for(int dh, int hq, int hk, bool batched, bool fp8, bool jit) {
+  if (batched) return megakernel_for_t<true, false, false>(dh, hq / hk);
+  if (jit) return megakernel_for_t<false, false, true>(dh, hq / hk);
+  return fp8 ? megakernel_for_t<false, true, false>(dh, hq / hk) : megakernel_for_t<false, false, false>(dh, hq / hk);
 }
 
 hipError_t launch_megakernel(const KernelParams& p, int grid, size_t lds_bytes, hipStream_t stream, bool coop) {
@@ -2127,14 +2200,14 @@ hipError_t launch_megakernel(const KernelParams& p, int grid, size_t lds_bytes, 
   // the watchdog with an error, not in a hang.)
   static const bool coop_env = std::getenv("MK_COOPERATIVE_LAUNCH") != nullptr;
   if (coop || coop_env)
-    return hipLaunchCooperativeKernel(megakernel_for(p.dh, p.hq, p.hk, p.max_seqs > 1, p.fp8_weights != 0), dim3(grid), dim3(NT), args,
+    return hipLaunchCooperativeKernel(megakernel_for(p.dh, p.hq, p.hk, p.max_seqs > 1, p.fp8_weights != 0, p.jit_tab != nullptr), dim3(grid), dim3(NT), args,
                                       (unsigned)lds_bytes, stream);
-  return hipLaunchKernel(megakernel_for(p.dh, p.hq, p.hk, p.max_seqs > 1, p.fp8_weights != 0), dim3(grid), dim3(NT), args,
+  return hipLaunchKernel(megakernel_for(p.dh, p.hq, p.hk, p.max_seqs > 1, p.fp8_weights != 0, p.jit_tab != nullptr), dim3(grid), dim3(NT), args,
                          (unsigned)lds_bytes, stream);
 }
 
 hipError_t megakernel_occupancy(int* blocks_per_cu, size_t lds_bytes, int dh, int hq, int hk, bool batched, bool fp8) {
-  return hipOccupancyMaxActiveBlocksPerMultiprocessor(blocks_per_cu, megakernel_for(dh, hq, hk, batched, fp8), NT, lds_bytes);
+  return hipOccupancyMaxActiveBlocksPerMultiprocessor(blocks_per_cu, megakernel_for(dh, hq, hk, batched, fp8, false), NT, lds_bytes);
 }
 
 // ----------------------------------------------------------------------------- static scratch
@@ -2194,6 +2267,23 @@ hipError_t launch_row_scales(const RepackArgs& a, int nrows, hipStream_t stream)
 
 hipError_t launch_repack_fp8(const RepackArgs& a, int64_t units, hipStream_t stream) {
   hipLaunchKernelGGL(mk_repack_fp8, dim3((unsigned)units), dim3(64), 0, stream, a);
+  return hipGetLastError();
+}
+
+// Dynamic scheduling, before each launch: queue head 0, tail n0 (the opening tasks in slots 0..n0-1),
+// event counts 0, the other slots empty (-1). A kernel, not a memset, so the launch may be captured.
+extern "C" __global__ __launch_bounds__(256) void mk_jit_reset(int32_t* w, int n_events, int n_tasks, int n0) {
+  const int i = blockIdx.x * 256 + threadIdx.x;
+  if (i >= 2 + n_events + n_tasks) return;
+  int v = 0;
+  if (i == 1) v = n0;
+  else if (i >= 2 + n_events) v = (i - 2 - n_events) < n0 ? (i - 2 - n_events) : -1;
+  w[i] = v;
+}
+
+hipError_t launch_jit_reset(int32_t* w, int n_events, int n_tasks, int n0, hipStream_t stream) {
+  const int n = 2 + n_events + n_tasks;
+  hipLaunchKernelGGL(mk_jit_reset, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, stream, w, n_events, n_tasks, n0);
   return hipGetLastError();
 }
 

@@ -16,6 +16,7 @@ hipError_t launch_megakernel(const KernelParams&, int, size_t, hipStream_t, bool
 hipError_t megakernel_occupancy(int*, size_t, int, int, int, bool, bool) { return hipErrorNotSupported; }
 hipError_t launch_row_scales(const RepackArgs&, int, hipStream_t) { return hipErrorNotSupported; }
 hipError_t launch_repack_fp8(const RepackArgs&, int64_t, hipStream_t) { return hipErrorNotSupported; }
+hipError_t launch_jit_reset(int32_t*, int, int, int, hipStream_t) { return hipErrorNotSupported; }
 hipError_t launch_repack(const RepackArgs&, int64_t, hipStream_t) { return hipErrorNotSupported; }
 hipError_t launch_repack_bias(const uint16_t*, const uint16_t*, const uint16_t*, int, int, int, uint16_t*, hipStream_t) {
   return hipErrorNotSupported;
