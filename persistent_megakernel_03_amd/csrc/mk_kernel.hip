@@ -1,27 +1,27 @@
-// The persistent decode megakernel for gfx950 (CDNA4), and the weight re-layout kernel.
+// The persistent decode megakernel for gfx950 (CDNA4), and the weight re-layout kernels.
 //
 // One workgroup of 512 threads (8 wave64s) runs on each CU, and all of them must be resident at once
 // (the LDS allows one per CU, the grid is the CU count; multi-step launches are cooperative, so the
 // runtime guarantees it; a single step uses a plain launch on a device running nothing else, and a
-// wait that can never be met ends at the watchdog). Each workgroup walks its own task queue, once per
-// step of the launch. For each task it:
-//   - waits for its input event,
-//   - runs the tile,
-//   - publishes its epoch number into its flag slots.
-// This is the worker loop of the Mirage Persistent Kernel ("LLMs in einen MegaKernel
-// kompilieren", "Worker" and "Ereignisbasierte Ausführung"). The pages' separate scheduler
-// SMs are folded into the workers. The queues are built ahead of time (the AOT launch of
-// "MPK: A Compiler and Runtime for Mega-Kernelizing Tensor Programs", analogy 3). So the
-// scheduler's job reduces to one wave polling the event's flags. Every CU keeps streaming
-// weights; giving up CUs to scheduling would cost a share of the HBM stream.
+// wait that can never be met ends at the watchdog). Each workgroup walks its own task queue, built
+// ahead of time, once per step of the launch (the AOT mode of "MPK: A Compiler and Runtime for
+// Mega-Kernelizing Tensor Programs", analogy 3), or, in the run-time mode, takes tasks from one
+// device-wide ready queue. For each task it:
+//   - issues the loads that do not depend on this step (weights, cached K/V rows),
+//   - polls for its inputs: epoch-tagged activation words, each carrying the step that wrote it,
+//   - runs the tile and its epilogue, and stores its outputs tagged with the step's epoch.
+// This is the worker loop of the Mirage Persistent Kernel ("LLMs in einen MegaKernel kompilieren",
+// "Worker" and "Ereignisbasierte Ausführung"), with the pages' separate scheduler SMs folded into the
+// workers: every CU keeps streaming weights, and an event is the set of tags its consumer polls.
+// Only the LM head's partial maxima travel under flags (the argmax waits for them).
 //
 // Memory model. Data that one CU writes and another CU reads in the same step goes through
-// agent-scope atomic loads and stores (the sc1 cache policy). These are coherent across the
-// XCDs' separate L2 caches. Ordering uses one rule: a producer's waves wait for their
-// stores to complete (s_waitcnt vmcnt(0)) before one lane stores the flag. A consumer
-// polls the flags with agent-scope loads, and only after that issues its data loads.
-// Weights and the KV rows of earlier steps are immutable within a step. They are read with
-// plain nontemporal loads.
+// agent-scope atomic loads and stores (the sc1 cache policy), coherent across the XCDs' separate L2
+// caches. A tagged word is one 64-bit single-copy-atomic store (value | epoch << 32), so a consumer
+// that sees this step's epoch sees this step's value, whatever the order in which words land. For the
+// flags, a producer's waves wait for their stores to complete (s_waitcnt vmcnt(0)) before one lane
+// stores the flag, and the consumer issues its data loads only after the flags. Weights and the K/V
+// rows of earlier steps are immutable within a step and are read with plain nontemporal loads.
 #include <hip/hip_runtime.h>
 #include <cstdlib>
 #include <mutex>
