@@ -349,7 +349,10 @@ mk_status mk_graph_simulate(const mk_ctx* ctx, uint64_t seed, int n_steps);
  * 2 a task waits on a later producer (a cycle); 3 a flag slot with two writers;
  * 4 a producer that never publishes (a slot with no writer); 5 two tiles of a
  * stage overlapping (rows written twice); 6 a consumer with its wait removed;
- * 7 a stage's last tile ending early (rows never written).
+ * 7 a stage's last tile ending early (rows never written), 8 an event of the
+ * run-time scheduling tables losing its last consumer (never queued), 9 an
+ * event expecting one producer more than signal it (never complete); the last
+ * two are caught by mk_graph_simulate's run of the ready queue.
  * Errors: MK_ERR_STATE (a device context), MK_ERR_INVALID_ARG (unknown kind, or
  * the graph has no task of the kind's type). */
 mk_status mk_graph_corrupt(mk_ctx* ctx, int kind);

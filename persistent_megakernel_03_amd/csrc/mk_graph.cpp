@@ -1062,6 +1062,22 @@ std::string corrupt_graph(HostGraph& g, int kind) {
       g.tasks[t].row1 -= 1;
       return "";
     }
+    case 8: {  // run-time scheduling: an event's consumer range loses its last task (never queued)
+      for (size_t e = 0; e < g.jit_ev_c0.size(); ++e)
+        if (g.jit_ok && g.jit_ev_c1[e] - g.jit_ev_c0[e] >= 2) {
+          g.jit_ev_c1[e] -= 1;
+          return "";
+        }
+      return "no run-time scheduling tables";
+    }
+    case 9: {  // run-time scheduling: an event expects one producer more than signal it (never complete)
+      for (size_t e = 0; e < g.jit_ev_n.size(); ++e)
+        if (g.jit_ok && g.jit_ev_c1[e] > g.jit_ev_c0[e]) {
+          g.jit_ev_n[e] += 1;
+          return "";
+        }
+      return "no run-time scheduling tables";
+    }
     default:
       return "unknown corruption kind";
   }

@@ -342,6 +342,23 @@ def test_simulator_catches_a_consumer_that_does_not_wait(L, n_cus):
         mk.mk_destroy(ctx)
 
 
+@pytest.mark.parametrize("kind", [8, 9])
+@pytest.mark.parametrize("n_cus", [256, 7])
+def test_simulator_catches_broken_ready_queue_tables(L, kind, n_cus):
+    # the run-time scheduling tables: a consumer that is never queued, or an event that never completes;
+    # the static checks do not read these tables, the host run of the ready queue does
+    ctx = mk.mk_create_host(cfg_for(si.TINY, 3, 3, 2), n_cus)
+    try:
+        mk.mk_graph_simulate(ctx, 1, 1)
+        mk.mk_graph_corrupt(ctx, kind)
+        mk.mk_graph_validate(ctx)
+        with pytest.raises(mk.MKError) as e:
+            mk.mk_graph_simulate(ctx, 1, 1)
+        assert "dynamic schedule" in str(e.value), str(e.value)
+    finally:
+        mk.mk_destroy(ctx)
+
+
 def test_simulator_catches_rows_written_twice(L):
     # overlapping down tiles: the validator names it; the simulator's data checks stay consistent
     # (the extra row's second writer is the later task)
