@@ -1856,8 +1856,20 @@ __device__ __forceinline__ void task_argmax(const KernelParams& p, uint32_t ep, 
 // (contiguous in the global order) to the queue. The tasks that wait on nothing fill its first slots.
 // Slots are taken in order and a task waits only on tasks appended before it (attention merges on the
 // layer's earlier attention tasks), all of which some workgroup has already taken: every wait ends.
+// The kernel's parameters as a task reads them: scalar loads from the kernel-argument segment (the
+// kernel's one explicit argument sits at its offset 0), through a pointer made opaque so that the loads
+// happen when a task starts and cannot be hoisted out of the task loop. Held in scalar registers across
+// the whole persistent loop instead, they overflowed the scalar file, and the spills into vector-register
+// lanes made up about a sixth of the one-sequence kernel's code (76 KB before, 65 KB after).
+__device__ __forceinline__ const KernelParams& task_params() {
+  auto q = (const __attribute__((address_space(4))) KernelParams*)__builtin_amdgcn_kernarg_segment_ptr();
+  asm volatile("" : "+s"(q));
+  return *(const KernelParams*)q;
+}
+
 template <int DH, int GMAX, bool BATCHED, bool FP8, bool JIT>
-__global__ __launch_bounds__(NT, 1) void mk_megakernel(KernelParams p) {
+__global__ __launch_bounds__(NT, 1) void mk_megakernel(KernelParams launch_params) {
+  const KernelParams& p = launch_params;  // set-up; each task reads task_params()
   extern __shared__ __attribute__((aligned(16))) unsigned char lds_raw[];
   static_assert(sizeof(Ctl) <= 1024, "control block fits its 1 KB");
   Ctl* ctl = (Ctl*)lds_raw;
@@ -1895,6 +1907,7 @@ __global__ __launch_bounds__(NT, 1) void mk_megakernel(KernelParams p) {
   // no reader left in this one. One loop walks (step, task): a nested step loop keeps more values live
   // across the whole launch and costs registers.
   for (int step = 0, qi = q0; qi < q1;) {
+    const KernelParams& p = task_params();
     const uint32_t ep = p.epoch + (uint32_t)step;
     if (qi == q0) {
       // Context lengths: read at launch, then one more per step for the running sequences (the argmax
