@@ -348,9 +348,7 @@ __device__ __forceinline__ int xs_index(int i, int npieces) {
   return (e < 4) ? (p << 2) + e : (npieces << 2) + (p << 2) + (e - 4);
 }
 
-__device__ __forceinline__ void unit_fma(const v4u w, const float* xa, const float* xb, float& acc0, float& acc1) {
-  const v4f a = *(const v4f*)xa;
-  const v4f b = *(const v4f*)xb;
+__device__ __forceinline__ void unit_fma_v(const v4u w, const v4f a, const v4f b, float& acc0, float& acc1) {
   acc0 = fmaf(bf_lo(w.x), a.x, acc0);
   acc1 = fmaf(bf_hi(w.x), a.y, acc1);
   acc0 = fmaf(bf_lo(w.y), a.z, acc0);
@@ -360,13 +358,15 @@ __device__ __forceinline__ void unit_fma(const v4u w, const float* xa, const flo
   acc0 = fmaf(bf_lo(w.w), b.z, acc0);
   acc1 = fmaf(bf_hi(w.w), b.w, acc1);
 }
+__device__ __forceinline__ void unit_fma(const v4u w, const float* xa, const float* xb, float& acc0, float& acc1) {
+  unit_fma_v(w, *(const v4f*)xa, *(const v4f*)xb, acc0, acc1);
+}
 
 // FP8 weights: the lane's 16 bytes are the E4M3 codes of two pieces, the piece of bf16-layout unit
 // 2u (bytes 0..7, elements 0..7) and of unit 2u + 1 (bytes 8..15); the conversion to fp32 is exact.
 typedef float v2f __attribute__((ext_vector_type(2)));
-__device__ __forceinline__ void unit_fma8(const v4u w, const float* xa0, const float* xb0, const float* xa1,
-                                          const float* xb1, float& acc0, float& acc1) {
-  const v4f a0 = *(const v4f*)xa0, b0 = *(const v4f*)xb0, a1 = *(const v4f*)xa1, b1 = *(const v4f*)xb1;
+__device__ __forceinline__ void unit_fma8_v(const v4u w, const v4f a0, const v4f b0, const v4f a1, const v4f b1,
+                                            float& acc0, float& acc1) {
   v2f c = __builtin_amdgcn_cvt_pk_f32_fp8((int)w.x, false);
   acc0 = fmaf(c.x, a0.x, acc0);
   acc1 = fmaf(c.y, a0.y, acc1);
@@ -391,6 +391,10 @@ __device__ __forceinline__ void unit_fma8(const v4u w, const float* xa0, const f
   c = __builtin_amdgcn_cvt_pk_f32_fp8((int)w.w, true);
   acc0 = fmaf(c.x, b1.z, acc0);
   acc1 = fmaf(c.y, b1.w, acc1);
+}
+__device__ __forceinline__ void unit_fma8(const v4u w, const float* xa0, const float* xb0, const float* xa1,
+                                          const float* xb1, float& acc0, float& acc1) {
+  unit_fma8_v(w, *(const v4f*)xa0, *(const v4f*)xb0, *(const v4f*)xa1, *(const v4f*)xb1, acc0, acc1);
 }
 
 // Register pipeline of one wave's weight stream: NSLOT slots of one unit each. A task's first
@@ -426,7 +430,7 @@ __device__ __forceinline__ WaveRun wave_run(const KernelParams& p, const TaskDes
 // Loads are unconditional (units past the run re-read its last unit, a cache hit, and are never
 // consumed), so the in-order wait counter is exact: a slot is waited for only when consumed.
 __device__ __forceinline__ v4u load_unit(const WaveRun& w, int i) {
-  return __builtin_nontemporal_load(w.src + (size_t)min(i, w.nunits - 1) * 64);
+  return __builtin_nontemporal_load(w.src + (size_t)(uint32_t)min(i, w.nunits - 1) * 64);  // i >= 0, nunits >= 1
 }
 
 __device__ __forceinline__ bool is_gemv(int type) {
@@ -466,12 +470,83 @@ __device__ __forceinline__ void stage_units(const WaveRun& w) {
     }
 }
 
+// gemv_tile for rows of 4096 inputs (512 pieces: 64 lanes per row, 8 units per row). Each lane then
+// meets the same 8 pieces in every row it streams, so it holds their 64 inputs in registers for the
+// whole tile instead of reading them from LDS per unit. The position of a unit in its row is known at
+// compile time in every slot: the run starts at a row, the first round holds units 0..NSLOT-1 and the
+// stage the next kStageUnits, and every later round starts NSLOT + kStageUnits + NSLOT r, which is 2
+// mod 8 (FP8: unit i covers bf16-layout units 2i and 2i + 1). The arithmetic, and its order, are those
+// of the general tile below.
+template <bool FP8>
+__device__ __forceinline__ void gemv_tile_r512(const KernelParams& p, const TaskDesc& t, const GemvGeom gm, const float* xs,
+                                               float* ys, WPipe& wp, bool restage, const WaveRun next, const float* ysc) {
+  static_assert(NSLOT % 8 == 0 && (NSLOT + kStageUnits) % 8 == 2, "unit positions in the row are fixed per slot");
+  const WaveRun w = wave_run<FP8>(p, t, gm);
+  const int nunits = w.nunits;
+  if (nunits <= 0) return;
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int rows = t.row1 - t.row0;
+  v4f xa[8], xb[8];
+#pragma unroll
+  for (int u = 0; u < 8; ++u) {
+    xa[u] = *(const v4f*)(xs + (u * 64 + lane) * 4);
+    xb[u] = *(const v4f*)(xs + 512 * 4 + (u * 64 + lane) * 4);
+  }
+  int g = w.g0;
+  float acc0 = 0.f, acc1 = 0.f;
+  // unit of bf16-layout position ug (0..7) in its row; the row ends with position 7
+  auto unit = [&](const v4u& wv, const int ug) {
+    if constexpr (FP8) {
+      unit_fma8_v(wv, xa[ug], xb[ug], xa[ug + 1], xb[ug + 1], acc0, acc1);
+    } else {
+      unit_fma_v(wv, xa[ug], xb[ug], acc0, acc1);
+    }
+    if (ug + (FP8 ? 2 : 1) == 8) {
+      const float acc = lanes_sum(acc0 + acc1, 64);
+      if (lane == 0 && g < rows) ys[g] = FP8 ? acc * ysc[g] : acc;
+      acc0 = 0.f;
+      acc1 = 0.f;
+      ++g;
+    }
+  };
+  constexpr int US = FP8 ? 2 : 1;  // bf16-layout units per unit
+#pragma unroll
+  for (int j = 0; j < NSLOT; ++j) {
+    if (j < nunits) unit(wp.R[j], (US * j) & 7);
+    wp.R[j] = load_unit(w, j + NSLOT + kStageUnits);
+    __builtin_amdgcn_sched_barrier(0);
+  }
+  if (nunits > NSLOT) {
+    asm volatile("s_waitcnt vmcnt(%0)" ::"n"(NSLOT) : "memory");
+#pragma unroll
+    for (int j = 0; j < kStageUnits; ++j)
+      if (NSLOT + j < nunits) unit(g_stage[wave][j][lane], (US * (NSLOT + j)) & 7);
+  }
+  if (restage) {
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+    stage_units(next);
+  }
+  for (int i0 = NSLOT + kStageUnits; i0 < nunits; i0 += NSLOT) {
+#pragma unroll
+    for (int j = 0; j < NSLOT; ++j) {
+      if (i0 + j < nunits) unit(wp.R[j], (US * (NSLOT + kStageUnits + j)) & 7);
+      wp.R[j] = load_unit(w, i0 + j + NSLOT);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  }
+}
+
 // restage: once this task has read its own staged units, the stage receives those of run `next`.
 // FP8: each unit covers two bf16-layout units of the row group, and a finished row is scaled by its
 // row's 2^e (ysc, in LDS).
 template <bool FP8>
 __device__ __forceinline__ void gemv_tile(const KernelParams& p, const TaskDesc& t, const GemvGeom gm, const float* xs, float* ys,
                           WPipe& wp, bool restage, const WaveRun next, const float* ysc) {
+  if (gm.lpr == 64 && gm.S == 8) {
+    gemv_tile_r512<FP8>(p, t, gm, xs, ys, wp, restage, next, ysc);
+    return;
+  }
   const WaveRun w = wave_run<FP8>(p, t, gm);
   const int nunits = w.nunits;
   if (nunits <= 0) return;
