@@ -416,9 +416,22 @@ std::string build_graph(const mk_model_config& c, int n_cus, HostGraph& g) {
 
   int ev_x = -1;  // event "residual stream ready for this layer" (none before layer 0)
   int max_task_rows = 0;
+  // Each layer's T attention tasks, one per CU, spread over the CUs (the same CUs in every layer).
+  // When they are few, those CUs get no QKV and no O-projection task: an attention task then starts
+  // as soon as its CU has finished the previous layer's down projection, and its first cache rows
+  // arrive while the other CUs stream the QKV weights; the others hold their O tiles in registers
+  // through attention.
+  const int T = std::min(S * hk * g.splits, n_cus);  // the cut is balanced: one task per CU suffices
+  std::vector<char> attn_cu(n_cus, 0);
+  // at most one task per CU: spread; more: round-major (CU c runs tasks c, c + n_cus, ...), so that
+  // a merging task never waits on a task that is queued behind another merge
+  auto attn_cu_of = [&](int i) { return T <= n_cus ? (int)((int64_t)i * n_cus / T) : i % n_cus; };
+  for (int i = 0; i < T; ++i) attn_cu[attn_cu_of(i)] = 1;
+  const bool few_attn = (int)std::count(attn_cu.begin(), attn_cu.end(), 1) * 4 <= n_cus;
+  const std::vector<char>* skip_attn = few_attn ? &attn_cu : nullptr;
   for (int l = 0; l < L; ++l) {
     // ---- QKV: RMSNorm + GEMV + bias + RoPE + KV append
-    auto qkv = stage(T_QKV, l, G_QKV, Nqkv, d, lcm_i(4, g.geoms[G_QKV].rg), ev_x, nullptr);
+    auto qkv = stage(T_QKV, l, G_QKV, Nqkv, d, lcm_i(4, g.geoms[G_QKV].rg), ev_x, skip_attn);
     if (!err.empty()) return err;
     const int ev_qkv = b.new_event((int)qkv.size());
     for (size_t i = 0; i < qkv.size(); ++i) {
@@ -431,14 +444,10 @@ std::string build_graph(const mk_model_config& c, int n_cus, HostGraph& g) {
     // time; the task holding a segment's last block merges the others' partials of it. In the symbolic
     // model the layer's tasks form one group: each may merge any segment, and the last one stands for
     // the writers of the attention output.
-    const int T = std::min(S * hk * g.splits, n_cus);  // the cut is balanced: one task per CU suffices
     g.attn_tasks = T;
     // the device cuts the step's blocks with 32-bit products (blocks x tasks)
     if ((int64_t)S * hk * c.max_blocks_per_seq * T >= ((int64_t)1 << 32)) return "too many KV blocks x attention tasks";
     const int ev_att = b.new_event(T);
-    // CUs running attention get no O-projection task in the same layer when they are few: their
-    // register pipelines sit idle through attention, while the other CUs hold their O tiles there.
-    std::vector<char> attn_cu(n_cus, 0);
     {
       const int agrp = (int)g.group_size.size();
       g.group_size.push_back(T);
@@ -450,11 +459,7 @@ std::string build_graph(const mk_model_config& c, int n_cus, HostGraph& g) {
         t.wait_ev = ev_qkv;
         t.a2 = i;
         t.a3 = l * T + i;
-        // at most one task per CU: spread; more: round-major (CU c runs tasks c, c + n_cus, ...), so that
-        // a merging task never waits on a task that is queued behind another merge
-        const int cu = T <= n_cus ? (int)((int64_t)i * n_cus / T) : i % n_cus;
-        attn_cu[cu] = 1;
-        const int id = b.add_task(t, cu);
+        const int id = b.add_task(t, attn_cu_of(i));
         g.task_group[id] = agrp;
         g.task_comb[id] = 1;
         b.task_sig[id].push_back({ev_att, i});
@@ -468,8 +473,7 @@ std::string build_graph(const mk_model_config& c, int n_cus, HostGraph& g) {
       g.n_attn_groups = (l + 1) * S * hk;
     }
     // ---- O projection + residual
-    const bool few_attn = (int)std::count(attn_cu.begin(), attn_cu.end(), 1) * 4 <= n_cus;
-    auto op = stage(T_OPROJ, l, G_O, d, qd, g.geoms[G_O].rg, ev_att, few_attn ? &attn_cu : nullptr);
+    auto op = stage(T_OPROJ, l, G_O, d, qd, g.geoms[G_O].rg, ev_att, skip_attn);
     if (!err.empty()) return err;
     const int ev_o = b.new_event((int)op.size());
     for (size_t i = 0; i < op.size(); ++i) {

@@ -72,9 +72,10 @@ def test_one_sequence_attention_split_rule(L, blocks, attn_tasks):
     try:
         info = mk.mk_graph_stats(ctx)
         m = si.LLAMA8B
-        other = m.n_layers * 256 * 3 + 256 + 1  # QKV, gate/up and down on every CU, the LM head, the argmax
-        o_tasks = 256 - attn_tasks if attn_tasks * 4 <= 256 else 256  # O skips the attention CUs when they are few
-        assert info.n_tasks == other + m.n_layers * (attn_tasks + o_tasks)
+        other = m.n_layers * 256 * 2 + 256 + 1  # gate/up and down on every CU, the LM head, the argmax
+        # QKV and O skip the attention CUs when those are few
+        qo_tasks = 256 - attn_tasks if attn_tasks * 4 <= 256 else 256
+        assert info.n_tasks == other + m.n_layers * (attn_tasks + 2 * qo_tasks)
     finally:
         mk.mk_destroy(ctx)
 
