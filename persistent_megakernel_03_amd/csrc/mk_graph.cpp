@@ -482,12 +482,12 @@ std::string build_graph(const mk_model_config& c, int n_cus, HostGraph& g) {
       out_acc(op[i].id, T_OPROJ, l, op[i].r0, op[i].r1, op[i].comb);
     }
     // ---- RMSNorm + gate/up + SwiGLU
-    // One sequence: the CUs that ran attention (and no O projection) start gate/up early, and CUs on
+    // One sequence: the CUs that ran attention (and no QKV or O projection) start gate/up early, and CUs on
     // odd XCDs (workgroup i runs on XCD i % 8) stream it measurably slower; their row shares are
     // weighted so that the stage ends together (weights measured on the 8B decode).
     std::vector<double> gu_w(n_cus, 1.0);
     if (S == 1 && few_attn)
-      for (int cu = 0; cu < n_cus; ++cu) gu_w[cu] = 1.0 + (attn_cu[cu] ? 0.05 : 0.0) - ((cu & 1) ? 0.02 : 0.0);
+      for (int cu = 0; cu < n_cus; ++cu) gu_w[cu] = 1.0 + (attn_cu[cu] ? 0.10 : 0.0) - ((cu & 1) ? 0.02 : 0.0);
     auto gu = stage(T_GATEUP, l, G_GU, 2 * f, d, lcm_i(2, g.geoms[G_GU].rg), ev_o, nullptr, S == 1 && few_attn ? &gu_w : nullptr);
     if (!err.empty()) return err;
     const int ev_gu = b.new_event((int)gu.size());
