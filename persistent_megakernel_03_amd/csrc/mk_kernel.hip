@@ -484,7 +484,10 @@ __device__ __forceinline__ void gemv_tile_r512(const KernelParams& p, const Task
   const WaveRun w = wave_run<FP8>(p, t, gm);
   const int nunits = w.nunits;
   if (nunits <= 0) return;
-  const int lane = threadIdx.x & 63;
+  // the lane index made opaque per call: its input addresses are computed here, not held in
+  // registers through every other task
+  int lane = threadIdx.x & 63;
+  asm volatile("" : "+v"(lane));
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int rows = t.row1 - t.row0;
   v4f xa[8], xb[8];
@@ -1297,7 +1300,11 @@ template <bool FP8>
 __device__ __forceinline__ void gemv_task(const KernelParams& p, uint32_t ep, int step, const TaskDesc& t, float* lds,
                                           Ctl* ctl, WPipe& wp, uint16_t* const* pools, const TaskDesc* nxt,
                                           bool& staged) {
-  const int type = t.type, l = t.layer, s = 0, tid = threadIdx.x;
+  const int type = t.type, l = t.layer, s = 0;
+  // the thread index made opaque per task: per-thread offsets are computed here rather than hoisted
+  // out of the task loop and held in registers through every other task
+  int tid = threadIdx.x;
+  asm volatile("" : "+v"(tid));
   const uint32_t what = (uint32_t)t.wait_ev;
   const GemvGeom gm = ctl->geoms[t.geom];
   const int padded = gm.S * gm.lpr * 8, np = padded >> 3;
