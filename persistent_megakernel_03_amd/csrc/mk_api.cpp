@@ -219,6 +219,7 @@ KernelParams make_params(mk_ctx* c, const HostGraph& g, uint8_t* R, uint8_t* W, 
   p.attn_min_blocks = g.cfg.attn_min_blocks > 0 ? g.cfg.attn_min_blocks : kAttnMinBlocks;
   p.trace = &g == &c->g ? c->d_trace : nullptr;
   p.fp8_weights = m.weight_format == MK_WEIGHTS_FP8_E4M3 ? 1 : 0;
+  p.stage2_off = (int32_t)g.stage2_off;
   p.wscale = p.fp8_weights ? (const float*)(Wt + g.wl.scales) : nullptr;
   return p;
 }

@@ -670,10 +670,25 @@ std::string build_graph(const mk_model_config& c, int n_cus, HostGraph& g) {
   int max_q = 0;
   for (int cu = 0; cu < n_cus; ++cu) max_q = std::max(max_q, g.queue_off[cu + 1] - g.queue_off[cu]);
   g.max_queue = max_q;
-  // control block + pool pointers + this CU's task descriptors + the attention tasks' first blocks +
-  // the larger of the GEMV and attention working sets
-  g.lds_bytes = 1024 + align_up((int64_t)2 * L * 8, 256) + align_up((int64_t)max_q * (int64_t)sizeof(TaskDesc), 256) +
-                align_up((int64_t)(g.attn_tasks + 1) * 4, 256) + align_up(std::max(gemv_lds, attn_lds), 256);
+  // control block + pool pointers + this CU's task descriptors + the attention tasks' first blocks
+  const int64_t fixed_lds = 1024 + align_up((int64_t)2 * L * 8, 256) + align_up((int64_t)max_q * (int64_t)sizeof(TaskDesc), 256) +
+                            align_up((int64_t)(g.attn_tasks + 1) * 4, 256);
+  // One sequence: the second weight stage of the tasks with rows of 4096 inputs, after their input
+  // vector, results and row scales, when the LDS has room for it.
+  g.stage2_off = 0;
+  bool rows512 = false;
+  for (int i = 0; i < G_COUNT; ++i) rows512 = rows512 || (!g.geoms[i].mfma && g.geoms[i].lpr == 64 && g.geoms[i].S == 8);
+  if (S == 1 && rows512) {
+    const int planes = c.weight_format == MK_WEIGHTS_FP8_E4M3 ? 2 : 1;  // results (and FP8 row scales)
+    const int64_t off = align_up(4096 * 4 + planes * (int64_t)align_up(max_task_rows, 64) * 4, 1024);
+    const int64_t need = off + (int64_t)8 * kStage2Units * 1024;
+    if (fixed_lds + align_up(std::max({gemv_lds, attn_lds, need}), 256) + kStageBytes <= 160 * 1024) {
+      gemv_lds = std::max(gemv_lds, need);
+      g.stage2_off = off;
+    }
+  }
+  // ... + the larger of the GEMV and attention working sets
+  g.lds_bytes = fixed_lds + align_up(std::max(gemv_lds, attn_lds), 256);
   if (g.lds_bytes + (S == 1 ? kStageBytes : 0) > 160 * 1024) return "working set exceeds 160 KB of LDS";
   return "";
 }

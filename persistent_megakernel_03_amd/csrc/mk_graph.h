@@ -40,6 +40,10 @@ constexpr int kAttnMinBlocks = 1;
 // sequences of mixed lengths, about 24 blocks' streaming.
 constexpr int kAttnPieceBlocks = 24;
 constexpr int kStageBytes = 8 * kStageUnits * 1024;
+// One sequence, rows of 4096 inputs: a second stage of kStage2Units units per wave in the dynamic
+// working set, which such tasks use only in part (their input vector is 16 KB). With it a wave holds
+// 32 units (four rows) before its input arrives, all of a QKV task's share on 192 CUs.
+constexpr int kStage2Units = 6;
 // Size of the static device array that holds a step's working memory for the entry point that
 // allocates nothing (mk_decode_step_static); larger graphs are refused there.
 constexpr size_t kStaticScratchBytes = (size_t)64 << 20;
@@ -183,6 +187,7 @@ struct KernelParams {
   int32_t attn_min_blocks;    // cache blocks per attention task at least (fewer tasks get blocks)
   int32_t prefill;            // batched graphs: 1 = the rows are consecutive positions of one sequence
   int32_t fp8_weights;        // 1: GEMV tiles hold E4M3 codes, row r's products scale by wscale[r]
+  int32_t stage2_off;         // one sequence: byte offset of the second weight stage in the working set, or 0
   const int32_t* jit_tab;     // dynamic scheduling tables (see ScratchLayout::jit_tab), or nullptr
   int32_t* jit_work;          // dynamic scheduling working memory
   int32_t n_events;

@@ -31,6 +31,7 @@ struct HostGraph {
   int n_lm_parts = 0;
   int max_queue = 0;
   int64_t lds_bytes = 0;
+  int64_t stage2_off = 0;  // see KernelParams::stage2_off
   GemvGeom geoms[G_COUNT]{};
   std::vector<TaskDesc> tasks;               // global topological order
   std::vector<std::vector<Access>> acc;      // per task

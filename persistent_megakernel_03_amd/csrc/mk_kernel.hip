@@ -477,10 +477,12 @@ __device__ __forceinline__ void stage_units(const WaveRun& w) {
 // stage the next kStageUnits, and every later round starts NSLOT + kStageUnits + NSLOT r, which is 2
 // mod 8 (FP8: unit i covers bf16-layout units 2i and 2i + 1). The arithmetic, and its order, are those
 // of the general tile below.
-template <bool FP8>
+template <bool FP8, bool S2>
 __device__ __forceinline__ void gemv_tile_r512(const KernelParams& p, const TaskDesc& t, const GemvGeom gm, const float* xs,
                                                float* ys, WPipe& wp, bool restage, const WaveRun next, const float* ysc) {
-  static_assert(NSLOT % 8 == 0 && (NSLOT + kStageUnits) % 8 == 2, "unit positions in the row are fixed per slot");
+  static_assert(NSLOT % 8 == 0, "unit positions in the row are fixed per slot");
+  // units held before the register rounds: the first round, the stage and (S2) the second stage
+  constexpr int PRE = NSLOT + kStageUnits + (S2 ? kStage2Units : 0);
   const WaveRun w = wave_run<FP8>(p, t, gm);
   const int nunits = w.nunits;
   if (nunits <= 0) return;
@@ -517,27 +519,53 @@ __device__ __forceinline__ void gemv_tile_r512(const KernelParams& p, const Task
 #pragma unroll
   for (int j = 0; j < NSLOT; ++j) {
     if (j < nunits) unit(wp.R[j], (US * j) & 7);
-    wp.R[j] = load_unit(w, j + NSLOT + kStageUnits);
+    wp.R[j] = load_unit(w, j + PRE);
     __builtin_amdgcn_sched_barrier(0);
   }
   if (nunits > NSLOT) {
+    // both stages' DMA went out before this round's refills, the youngest NSLOT loads
     asm volatile("s_waitcnt vmcnt(%0)" ::"n"(NSLOT) : "memory");
 #pragma unroll
     for (int j = 0; j < kStageUnits; ++j)
       if (NSLOT + j < nunits) unit(g_stage[wave][j][lane], (US * (NSLOT + j)) & 7);
+    if constexpr (S2) {
+      const v4u* st2 = (const v4u*)((const char*)xs + p.stage2_off) + wave * kStage2Units * 64 + lane;
+#pragma unroll
+      for (int j = 0; j < kStage2Units; ++j)
+        if (NSLOT + kStageUnits + j < nunits) unit(st2[j * 64], (US * (NSLOT + kStageUnits + j)) & 7);
+    }
   }
   if (restage) {
     asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
     stage_units(next);
   }
-  for (int i0 = NSLOT + kStageUnits; i0 < nunits; i0 += NSLOT) {
+  for (int i0 = PRE; i0 < nunits; i0 += NSLOT) {
 #pragma unroll
     for (int j = 0; j < NSLOT; ++j) {
-      if (i0 + j < nunits) unit(wp.R[j], (US * (NSLOT + kStageUnits + j)) & 7);
+      if (i0 + j < nunits) unit(wp.R[j], (US * (PRE + j)) & 7);
       wp.R[j] = load_unit(w, i0 + j + NSLOT);
       __builtin_amdgcn_sched_barrier(0);
     }
   }
+}
+
+// One sequence, rows of 4096 inputs: the DMA of the wave's units NSLOT + kStageUnits .. + kStage2Units - 1
+// (those the run has) into its part of the second stage, at byte offset stage2_off of the working set
+// `ws`. Issued after the task's register units, so the polls before it do not wait for it.
+__device__ __forceinline__ void stage2_units(const WaveRun& w, const float* ws, int stage2_off) {
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+#pragma unroll
+  for (int j = 0; j < kStage2Units; ++j)
+    if (NSLOT + kStageUnits + j < w.nunits) {
+      const uint32_t dst = (uint32_t)(size_t)(__attribute__((address_space(3))) void*)((const char*)ws + stage2_off) +
+                           (uint32_t)((wave * kStage2Units + j) * 1024);
+      uint32_t keep;
+      asm volatile("s_mov_b32 %0, m0\n\ts_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, off nt\n\t"
+                   "s_nop 4\n\ts_mov_b32 m0, %0"
+                   : "=&s"(keep)
+                   : "v"(w.src + (size_t)(NSLOT + kStageUnits + j) * 64), "s"(dst)
+                   : "memory");
+    }
 }
 
 // restage: once this task has read its own staged units, the stage receives those of run `next`.
@@ -546,8 +574,8 @@ __device__ __forceinline__ void gemv_tile_r512(const KernelParams& p, const Task
 template <bool FP8>
 __device__ __forceinline__ void gemv_tile(const KernelParams& p, const TaskDesc& t, const GemvGeom gm, const float* xs, float* ys,
                           WPipe& wp, bool restage, const WaveRun next, const float* ysc) {
-  if (gm.lpr == 64 && gm.S == 8) {
-    gemv_tile_r512<FP8>(p, t, gm, xs, ys, wp, restage, next, ysc);
+  if (gm.lpr == 64 && gm.S == 8 && p.stage2_off > 0) {
+    gemv_tile_r512<FP8, true>(p, t, gm, xs, ys, wp, restage, next, ysc);
     return;
   }
   const WaveRun w = wave_run<FP8>(p, t, gm);
@@ -1410,9 +1438,11 @@ __device__ __forceinline__ void gemv_task(const KernelParams& p, uint32_t ep, in
 
   // the input vector, two-plane layout in LDS, zero past n
   float* xd = xs + xs_index(i0, np);
+  const bool second_stage = p.stage2_off > 0 && gm.lpr == 64 && gm.S == 8;
   if (in_embed) {
 #pragma unroll
     for (int j = NSLOT / 2; j < NSLOT; ++j) wp.R[j] = load_unit(wrun, j);
+    if (second_stage) stage2_units(wrun, xs, p.stage2_off);
     for (int i = tid; i < n; i += NT) xs[xs_index(i, np)] = bf2f(erow[i]);
   } else {
 #pragma unroll
@@ -1429,11 +1459,13 @@ __device__ __forceinline__ void gemv_task(const KernelParams& p, uint32_t ep, in
         if ((pending >> k) & 1u) w1[k] = ld_tag(rin, i0 * 8 + (k & 7) * 512, (k >> 3) * 4096);
 #pragma unroll
       for (int j = NSLOT / 2; j < NSLOT; ++j) wp.R[j] = load_unit(wrun, j);
+      if (second_stage) stage2_units(wrun, xs, p.stage2_off);
       poll_finish<32>(p, ep, w1, pending, what, [&](int k) { return ld_tag(rin, i0 * 8 + (k & 7) * 512, (k >> 3) * 4096); },
                       [&](int k, uint32_t b) { xd[32 * k] = __uint_as_float(b); });
     } else {
 #pragma unroll
       for (int j = NSLOT / 2; j < NSLOT; ++j) wp.R[j] = load_unit(wrun, j);
+      if (second_stage) stage2_units(wrun, xs, p.stage2_off);
     }
   }
   for (int i = n + tid; i < padded; i += NT) xs[xs_index(i, np)] = 0.f;
