@@ -427,8 +427,11 @@ __device__ __forceinline__ WaveRun wave_run(const KernelParams& p, const TaskDes
   return r;
 }
 
-// Loads are unconditional (units past the run re-read its last unit, a cache hit, and are never
-// consumed), so the in-order wait counter is exact: a slot is waited for only when consumed.
+// Within a round the loads are unconditional (units past the run re-read its last unit and are never
+// consumed), so the in-order wait counter is exact: a slot is waited for only when consumed. A round
+// whose refills would all lie past the run is written without loads (a branch on the wave-uniform
+// unit count around a whole round keeps the counts exact): such refills cost no bytes worth having,
+// but they sit in the in-order queue ahead of the next task's first loads and input poll.
 __device__ __forceinline__ v4u load_unit(const WaveRun& w, int i) {
   return __builtin_nontemporal_load(w.src + (size_t)(uint32_t)min(i, w.nunits - 1) * 64);  // i >= 0, nunits >= 1
 }
@@ -516,36 +519,55 @@ __device__ __forceinline__ void gemv_tile_r512(const KernelParams& p, const Task
     }
   };
   constexpr int US = FP8 ? 2 : 1;  // bf16-layout units per unit
+  const bool more = nunits > PRE;  // wave-uniform: the run goes on past the prefetched units
+  if (more) {
 #pragma unroll
-  for (int j = 0; j < NSLOT; ++j) {
-    if (j < nunits) unit(wp.R[j], (US * j) & 7);
-    wp.R[j] = load_unit(w, j + PRE);
-    __builtin_amdgcn_sched_barrier(0);
+    for (int j = 0; j < NSLOT; ++j) {
+      if (j < nunits) unit(wp.R[j], (US * j) & 7);
+      wp.R[j] = load_unit(w, j + PRE);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  } else {
+#pragma unroll
+    for (int j = 0; j < NSLOT; ++j)
+      if (j < nunits) unit(wp.R[j], (US * j) & 7);
   }
   if (nunits > NSLOT) {
-    // both stages' DMA went out before this round's refills, the youngest NSLOT loads
-    asm volatile("s_waitcnt vmcnt(%0)" ::"n"(NSLOT) : "memory");
+    // both stages' DMA went out before this round's refills, the youngest NSLOT loads (with no
+    // refills, everything outstanding)
+    if (more) asm volatile("s_waitcnt vmcnt(%0)" ::"n"(NSLOT) : "memory");
+    else asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    // staged units, each read one unit ahead of its use (the reads are issued before the row-end
+    // stores of the unit before, so they overlap its arithmetic)
+    const v4u* st2 = (const v4u*)((const char*)xs + p.stage2_off) + wave * kStage2Units * 64 + lane;
+    constexpr int NST = kStageUnits + kStage2Units;
+    auto staged_at = [&](int j) { return j < kStageUnits ? g_stage[wave][j][lane] : st2[(j - kStageUnits) * 64]; };
+    v4u cur = staged_at(0);
 #pragma unroll
-    for (int j = 0; j < kStageUnits; ++j)
-      if (NSLOT + j < nunits) unit(g_stage[wave][j][lane], (US * (NSLOT + j)) & 7);
-    if constexpr (S2) {
-      const v4u* st2 = (const v4u*)((const char*)xs + p.stage2_off) + wave * kStage2Units * 64 + lane;
-#pragma unroll
-      for (int j = 0; j < kStage2Units; ++j)
-        if (NSLOT + kStageUnits + j < nunits) unit(st2[j * 64], (US * (NSLOT + kStageUnits + j)) & 7);
+    for (int j = 0; j < NST; ++j) {
+      const v4u nxt = staged_at(j + 1 < NST ? j + 1 : j);
+      if (NSLOT + j < nunits) unit(cur, (US * (NSLOT + j)) & 7);
+      cur = nxt;
     }
   }
   if (restage) {
     asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
     stage_units(next);
   }
-  for (int i0 = PRE; i0 < nunits; i0 += NSLOT) {
+  // rounds whose refills still reach into the run, then the last round with no refills
+  int i0 = PRE;
+  for (; i0 + NSLOT < nunits; i0 += NSLOT) {
 #pragma unroll
     for (int j = 0; j < NSLOT; ++j) {
-      if (i0 + j < nunits) unit(wp.R[j], (US * (PRE + j)) & 7);
+      unit(wp.R[j], (US * (PRE + j)) & 7);
       wp.R[j] = load_unit(w, i0 + j + NSLOT);
       __builtin_amdgcn_sched_barrier(0);
     }
+  }
+  if (i0 < nunits) {
+#pragma unroll
+    for (int j = 0; j < NSLOT; ++j)
+      if (i0 + j < nunits) unit(wp.R[j], (US * (PRE + j)) & 7);
   }
 }
 
@@ -613,7 +635,8 @@ __device__ __forceinline__ void gemv_tile(const KernelParams& p, const TaskDesc&
   // then the rest through the registers again. Slot j holds unit i0 + j of its round and is refilled
   // with the unit NSLOT further on as soon as it has been consumed (the first round's refills skip
   // the staged units), so NSLOT - 1 loads stay in flight while a unit is processed. Refills past the
-  // run re-read its last unit (a cache hit). A scheduling barrier after each slot keeps each refill
+  // run re-read its last unit; the last round, whose refills would all lie past it, has none. A
+  // scheduling barrier after each slot keeps each refill
   // after its slot's use. The compiler still waits for most of a round's loads at the round's start
   // (the first fill is not kept in slot order), so about one round of loads is in flight per wave;
   // measured on the 8B decode, this streams slightly faster than a strict slot-by-slot pipeline
@@ -637,13 +660,20 @@ __device__ __forceinline__ void gemv_tile(const KernelParams& p, const TaskDesc&
     asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
     stage_units(next);
   }
-  for (int i0 = NSLOT + kStageUnits; i0 < nunits; i0 += NSLOT) {
+  // rounds whose refills still reach into the run, then the last round with no refills
+  int i0 = NSLOT + kStageUnits;
+  for (; i0 + NSLOT < nunits; i0 += NSLOT) {
 #pragma unroll
     for (int j = 0; j < NSLOT; ++j) {
-      if (i0 + j < nunits) unit(wp.R[j]);
+      unit(wp.R[j]);
       wp.R[j] = load_unit(w, i0 + j + NSLOT);
       __builtin_amdgcn_sched_barrier(0);
     }
+  }
+  if (i0 < nunits) {
+#pragma unroll
+    for (int j = 0; j < NSLOT; ++j)
+      if (i0 + j < nunits) unit(wp.R[j]);
   }
 }
 
