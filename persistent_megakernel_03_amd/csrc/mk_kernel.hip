@@ -1791,26 +1791,35 @@ __device__ __forceinline__ void gemv_task_b(const KernelParams& p, uint32_t ep, 
     const uint32_t* ab = afrag + (multi ? (b & 1) * 8192 : 0);
     int g = ia / ub, u = ia % ub;
     v4f cur = zero;
+    auto item = [&](int rr, int j) {
+      if (NSLOT * rr + j < cnt) {
+        const v4u* a = (const v4u*)(ab + (u * 64 + lane) * 8);
+        const v4u ahi = a[0], alo = a[1];
+        cur = mfma_bf16(wp.R[j], ahi, cur);
+        cur = mfma_bf16(wp.R[j], alo, cur);
+        if (++u == ub) {
+          flush(g, b, cur);
+          cur = zero;
+          u = 0;
+          ++g;
+        }
+      }
+    };
     for (int rr = 0; rr < rpb; ++rr) {
       const int r = b * rpb + rr;
-      // refills of the last round re-read one unit: nothing past the stream is fetched
-      const int nbase = r + 1 < nrounds ? round_base(r + 1) : last_unit;
+      if (r + 1 < nrounds) {
+        const int nbase = round_base(r + 1);
 #pragma unroll
-      for (int j = 0; j < NSLOT; ++j) {
-        if (NSLOT * rr + j < cnt) {
-          const v4u* a = (const v4u*)(ab + (u * 64 + lane) * 8);
-          const v4u ahi = a[0], alo = a[1];
-          cur = mfma_bf16(wp.R[j], ahi, cur);
-          cur = mfma_bf16(wp.R[j], alo, cur);
-          if (++u == ub) {
-            flush(g, b, cur);
-            cur = zero;
-            u = 0;
-            ++g;
-          }
+        for (int j = 0; j < NSLOT; ++j) {
+          item(rr, j);
+          wp.R[j] = load_w(nbase + j);
+          __builtin_amdgcn_sched_barrier(0);
         }
-        wp.R[j] = load_w(nbase + j);
-        __builtin_amdgcn_sched_barrier(0);
+      } else {
+        // the stream's last round: no refills (they would sit in the in-order queue ahead of the
+        // exchange's polls)
+#pragma unroll
+        for (int j = 0; j < NSLOT; ++j) item(rr, j);
       }
     }
     if (u != 0 && cnt > 0) flush(g, b, cur);  // the wave's items end inside a row group
