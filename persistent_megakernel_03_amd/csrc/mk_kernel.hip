@@ -1352,12 +1352,12 @@ __device__ __forceinline__ uint64_t block_max_u64(uint64_t k, Ctl* ctl) {
 // One shared path keeps the instruction footprint small. The kernel's code is larger than the
 // instruction cache, and code that a CU runs once per layer is otherwise fetched anew each time.
 // ep: the step's epoch; step: the step's index within this launch. nxt: the CU's next task in this
-// launch, or null. staged: on entry, whether this wave's stage already holds this task's units (staged
-// by the previous task); on return, whether it holds the next task's.
+// launch, or null. staged: on entry, whether this wave's stage (bit 0) and second stage (bit 1) already
+// hold this task's units (staged by the previous task); on return, whether they hold the next task's.
 template <bool FP8>
 __device__ __forceinline__ void gemv_task(const KernelParams& p, uint32_t ep, int step, const TaskDesc& t, float* lds,
                                           Ctl* ctl, WPipe& wp, uint16_t* const* pools, const TaskDesc* nxt,
-                                          bool& staged) {
+                                          int& staged) {
   const int type = t.type, l = t.layer, s = 0;
   // the thread index made opaque per task: per-thread offsets are computed here rather than hoisted
   // out of the task loop and held in registers through every other task
@@ -1391,18 +1391,28 @@ __device__ __forceinline__ void gemv_task(const KernelParams& p, uint32_t ep, in
   // The LDS stage's DMA goes out first, ahead of every other load of the task (see stage_units).
   // An O-projection task runs while HBM is nearly idle (its weights arrived during attention) and is
   // followed on its CU by a gate/up task: it fills the stage with that task's units, at once when
-  // its own units fit the registers, else as soon as it has read its own staged units.
+  // its own units fit the registers, else as soon as it has read its own staged units. When its own
+  // units also leave the second stage unused, it fills that one too, at once, while attention runs.
   WaveRun wrun = wave_run<FP8>(p, t, gm);
   if (wrun.nunits <= 0) wrun = dummy_run(p);
-  if (!staged) stage_units(wrun);
+  if (!(staged & 1)) stage_units(wrun);
+  const bool second_stage = p.stage2_off > 0 && gm.lpr == 64 && gm.S == 8;
+  const bool own_stage2 = second_stage && !(staged & 2);  // this task issues its second stage's DMA
   const bool restage_next = type == T_OPROJ && nxt != nullptr && is_gemv(nxt->type);
   WaveRun wnext = wrun;
+  int staged_next = 0;
   if (restage_next) {
-    wnext = wave_run<FP8>(p, *nxt, ctl->geoms[nxt->geom]);
+    const GemvGeom& gn = ctl->geoms[nxt->geom];
+    wnext = wave_run<FP8>(p, *nxt, gn);
     if (wnext.nunits <= 0) wnext = dummy_run(p);
     if (wrun.nunits <= NSLOT) stage_units(wnext);
+    staged_next = 1;
+    if (p.stage2_off > 0 && gn.lpr == 64 && gn.S == 8 && (!second_stage || wrun.nunits <= NSLOT + kStageUnits)) {
+      stage2_units(wnext, xs, p.stage2_off);
+      staged_next |= 2;
+    }
   }
-  staged = restage_next;
+  staged = staged_next;
   const __amdgpu_buffer_rsrc_t rin = tag_rsrc(src);
   const int i0 = poll_index(n, 0);
   uint32_t pending = in_embed ? 0u : first_words(min(poll_chunk(n) / 64, (n - i0 + 63) / 64));
@@ -1468,11 +1478,10 @@ __device__ __forceinline__ void gemv_task(const KernelParams& p, uint32_t ep, in
 
   // the input vector, two-plane layout in LDS, zero past n
   float* xd = xs + xs_index(i0, np);
-  const bool second_stage = p.stage2_off > 0 && gm.lpr == 64 && gm.S == 8;
   if (in_embed) {
 #pragma unroll
     for (int j = NSLOT / 2; j < NSLOT; ++j) wp.R[j] = load_unit(wrun, j);
-    if (second_stage) stage2_units(wrun, xs, p.stage2_off);
+    if (own_stage2) stage2_units(wrun, xs, p.stage2_off);
     for (int i = tid; i < n; i += NT) xs[xs_index(i, np)] = bf2f(erow[i]);
   } else {
 #pragma unroll
@@ -1489,13 +1498,13 @@ __device__ __forceinline__ void gemv_task(const KernelParams& p, uint32_t ep, in
         if ((pending >> k) & 1u) w1[k] = ld_tag(rin, i0 * 8 + (k & 7) * 512, (k >> 3) * 4096);
 #pragma unroll
       for (int j = NSLOT / 2; j < NSLOT; ++j) wp.R[j] = load_unit(wrun, j);
-      if (second_stage) stage2_units(wrun, xs, p.stage2_off);
+      if (own_stage2) stage2_units(wrun, xs, p.stage2_off);
       poll_finish<32>(p, ep, w1, pending, what, [&](int k) { return ld_tag(rin, i0 * 8 + (k & 7) * 512, (k >> 3) * 4096); },
                       [&](int k, uint32_t b) { xd[32 * k] = __uint_as_float(b); });
     } else {
 #pragma unroll
       for (int j = NSLOT / 2; j < NSLOT; ++j) wp.R[j] = load_unit(wrun, j);
-      if (second_stage) stage2_units(wrun, xs, p.stage2_off);
+      if (own_stage2) stage2_units(wrun, xs, p.stage2_off);
     }
   }
   for (int i = n + tid; i < padded; i += NT) xs[xs_index(i, np)] = 0.f;
@@ -2054,7 +2063,7 @@ __global__ __launch_bounds__(NT, 1) void mk_megakernel(KernelParams launch_param
   }
   if constexpr (JIT) q1 = 0x7FFFFFFF;
   WPipe wp;
-  bool staged = false;  // this wave's LDS stage holds the next GEMV task's units
+  int staged = 0;  // this wave's LDS stages hold the next GEMV task's units (bit 0: the stage, bit 1: the second)
   // Steps run one after another, each with its own epoch. Every task of a step is an ancestor of the
   // step's argmax, which every task of the next step follows, so a buffer rewritten in the next step has
   // no reader left in this one. One loop walks (step, task): a nested step loop keeps more values live
@@ -2138,9 +2147,9 @@ __global__ __launch_bounds__(NT, 1) void mk_megakernel(KernelParams launch_param
       // position groups in flight per wave: more for batches (long streams), fewer for one sequence
       // and for many heads per KV head (register budget)
       task_attn<DH, GMAX, (GMAX > 4 || !BATCHED) ? 4 : 8, BATCHED>(p, ep, t, lds, ctl, pools, alo);
-      staged = false;
+      staged = 0;
     } else if (t.type == T_ARGMAX) {
-      staged = false;
+      staged = 0;
       if (t.wait_ev >= 0) wait_event(p, ep, t, ctl);
       if (p.trace && threadIdx.x == 0) ctl->t_ready = __builtin_amdgcn_s_memrealtime();
       if (t.wait_ev < 0 || !ctl->aborted) task_argmax(p, ep, step, t, ctl);
