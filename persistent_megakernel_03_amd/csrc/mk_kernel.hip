@@ -2145,8 +2145,9 @@ __global__ __launch_bounds__(NT, 1) void mk_megakernel(KernelParams launch_param
     // them): an attention task its first keys and values, a GEMV its first weight units.
     if (t.type == T_ATTN) {
       // position groups in flight per wave: more for batches (long streams), fewer for one sequence
-      // and for many heads per KV head (register budget)
-      task_attn<DH, GMAX, (GMAX > 4 || !BATCHED) ? 4 : 8, BATCHED>(p, ep, t, lds, ctl, pools, alo);
+      // and for many heads per KV head (register budget: one sequence with 8 heads per KV head spills
+      // about 40 registers at 4 groups, 6 at 2)
+      task_attn<DH, GMAX, (GMAX > 4 && !BATCHED) ? 2 : (GMAX > 4 || !BATCHED) ? 4 : 8, BATCHED>(p, ep, t, lds, ctl, pools, alo);
       staged = 0;
     } else if (t.type == T_ARGMAX) {
       staged = 0;
