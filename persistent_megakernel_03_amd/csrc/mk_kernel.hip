@@ -1482,7 +1482,15 @@ __device__ __forceinline__ void gemv_task(const KernelParams& p, uint32_t ep, in
 #pragma unroll
     for (int j = NSLOT / 2; j < NSLOT; ++j) wp.R[j] = load_unit(wrun, j);
     if (own_stage2) stage2_units(wrun, xs, p.stage2_off);
-    for (int i = tid; i < n; i += NT) xs[xs_index(i, np)] = bf2f(erow[i]);
+    // one 16-byte piece (8 values) per thread and load, into both planes (n is a multiple of 8 and the
+    // row starts 16-byte aligned)
+    for (int pc = tid; 8 * pc < n; pc += NT) {
+      const v4u e = *(const v4u*)(erow + 8 * pc);
+      const v4f a = {bf_lo(e.x), bf_hi(e.x), bf_lo(e.y), bf_hi(e.y)};
+      const v4f b = {bf_lo(e.z), bf_hi(e.z), bf_lo(e.w), bf_hi(e.w)};
+      *(v4f*)(xs + 4 * pc) = a;
+      *(v4f*)(xs + 4 * np + 4 * pc) = b;
+    }
   } else {
 #pragma unroll
     for (int k = 0; k < 32; ++k) {
